@@ -1,0 +1,498 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every check here compares the oracle with a closed form, an invariant, a
+hand-derived fixture (tests/golden/), a library routine (numpy, scipy,
+torch CPU) or brute force over a differently-ordered computation.  The
+checks are chosen so that a plausible slip (dropped term, wrong sign, wrong
+pairing, transposed operand, wrong rounding rule) fails at least one of them;
+tests/test_oracle_mutants.py plants such slips in copies of the oracle and
+verifies that.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------
+def pin_f16():
+    # every binary16 pattern: decode against numpy, and encode round-trips
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float32)
+    got = oracle.f16_to_f32(allbits)
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite].view(np.uint32), ref[finite].view(np.uint32))
+    assert np.all(np.isnan(got[~finite]) == np.isnan(ref[~finite]))
+    enc = oracle.f32_to_f16(ref[finite])
+    assert np.array_equal(enc, allbits[finite])
+    # midpoints between neighbours (ties), and values just off them, vs numpy's cast
+    pos = allbits[(allbits < 0x7bff)]
+    lo = pos.view(np.float16).astype(np.float64)
+    hi = (pos + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)           # exact in float32
+    probes = np.concatenate([mid, np.nextafter(mid, np.float32(np.inf)),
+                             np.nextafter(mid, np.float32(-np.inf)), -mid])
+    probes = probes[::7]                               # a spread sample keeps it quick
+    with np.errstate(over="ignore"):
+        want = probes.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16(probes), want)
+    # overflow edge: 65504 is the largest finite, 65520 rounds to infinity
+    assert oracle.f32_to_f16([65504.0, 65519.996, 65520.0])[2] == 0x7c00
+    assert oracle.f32_to_f16([65519.996])[0] == 0x7bff
+
+
+def pin_bf16():
+    import torch
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-39).astype(np.float32),     # f32 subnormals
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+    ])
+    # exact ties: low 16 bits == 0x8000, both parities of bit 16
+    u = rng.integers(0, 2 ** 31, size=2000, dtype=np.uint64).astype(np.uint32)
+    ties = ((u & np.uint32(0xffff0000)) | np.uint32(0x8000)).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    x = np.concatenate([x, ties, -ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16(x), want)
+    back = oracle.bf16_to_f32(want)
+    assert np.array_equal(back, torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_f16_conversion():
+    pin_f16()
+
+
+def test_bf16_conversion():
+    pin_bf16()
+
+
+# ----------------------------------------------------------------------------
+# Q8_0 quantizer
+# ----------------------------------------------------------------------------
+def load_golden_blocks():
+    cases, cur = [], {}
+    with open(os.path.join(GOLDEN, "q8_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("# case:"):
+                cur = {"name": line.split(":", 1)[1].split()[0]}
+            elif line.startswith("x:"):
+                cur["x"] = np.array([float(v) for v in line[2:].split()], dtype=np.float32)
+            elif line.startswith("q:"):
+                cur["q"] = np.array([int(v) for v in line[2:].split()], dtype=np.int8)
+            elif line.startswith("d:"):
+                cur["d"] = int(line[2:].strip(), 16)
+                cases.append(cur)
+    return cases
+
+
+def pin_quantize_golden():
+    cases = load_golden_blocks()
+    assert len(cases) == 7
+    for c in cases:
+        assert c["x"].size == 32 and c["q"].size == 32, c["name"]
+        qs, d = oracle.q8_quantize(c["x"])
+        assert np.array_equal(qs, c["q"]), (c["name"], qs, c["q"])
+        assert int(d[0]) == c["d"], (c["name"], hex(int(d[0])))
+
+
+def pin_quantize_invariants():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 256)) * rng.uniform(1e-3, 1e3, size=(64, 1))).astype(np.float32)
+    qs, d = oracle.q8_quantize(x)
+    xb = x.reshape(64, 8, 32).astype(np.float64)
+    qb = qs.reshape(64, 8, 32).astype(np.float64)
+    amax = np.abs(x.reshape(64, 8, 32)).max(axis=2)
+    dfl = (amax / np.float32(127)).astype(np.float32)              # float division, as defined
+    # stored scale = f16 image of amax/127 (numpy's float16 cast as the rounding authority)
+    assert np.array_equal(d.reshape(64, 8), dfl.astype(np.float16).view(np.uint16))
+    # the element with the largest magnitude maps to +-127, and every code is
+    # within half a step of x / d
+    assert np.all(np.abs(qb).max(axis=2) == 127)
+    err = np.abs(xb / dfl[..., None].astype(np.float64) - qb)
+    assert err.max() <= 0.5 + 1e-4
+    assert np.all(np.sign(qb) * np.sign(xb) >= 0)                  # no sign flips
+
+
+def test_quantize_golden():
+    pin_quantize_golden()
+
+
+def test_quantize_invariants():
+    pin_quantize_invariants()
+
+
+# ----------------------------------------------------------------------------
+# block dots and matvec
+# ----------------------------------------------------------------------------
+def pin_block_dots():
+    rng = np.random.default_rng(3)
+    rows, cols = 7, 96                           # non-square, several blocks
+    wq = rng.integers(-128, 128, size=(rows, cols), dtype=np.int8)
+    xq = rng.integers(-128, 128, size=cols, dtype=np.int8)
+    got = oracle.q8_block_dots(wq, xq)
+    want = (wq.astype(np.int64) * xq.astype(np.int64)).reshape(rows, cols // 32, 32).sum(axis=2)
+    assert np.array_equal(got, want)
+    # extremes: 32 * (-128) * (-128) = 524288 fits int32 exactly
+    ext = oracle.q8_block_dots(np.full((1, 32), -128, np.int8), np.full(32, -128, np.int8))
+    assert ext[0, 0] == 524288
+    ext = oracle.q8_block_dots(np.full((1, 32), 127, np.int8), np.full(32, -128, np.int8))
+    assert ext[0, 0] == -32 * 127 * 128
+
+
+def pin_matvec():
+    rng = np.random.default_rng(4)
+    rows, cols = 37, 160
+    wq, wd = synthetic.q8_weight(rng, rows, cols)
+    xq = rng.integers(-127, 128, size=cols, dtype=np.int8)
+    xd = (np.abs(rng.normal(0, 0.05, size=cols // 32)).astype(np.float16)).view(np.uint16)
+    res = rng.standard_normal(rows).astype(np.float32)
+    # brute force: dequantize each operand with numpy's f16 decode, then one f64 dot
+    wdq = wq.astype(np.float64) * np.repeat(wd.view(np.float16).astype(np.float64), 32, axis=1)
+    xdq = xq.astype(np.float64) * np.repeat(xd.view(np.float16).astype(np.float64), 32)
+    want = wdq @ xdq
+    got = oracle.q8_matvec(wq, wd, xq, xd).astype(np.float64)
+    assert np.allclose(got, want, rtol=2e-7, atol=1e-12 * np.abs(want).max())
+    got_r = oracle.q8_matvec(wq, wd, xq, xd, residual=res).astype(np.float64)
+    assert np.allclose(got_r, want + res, rtol=2e-7, atol=1e-7)
+    # one-hot: a single non-zero code gives d_w * d_x * q_w * q_x exactly
+    xq1 = np.zeros(cols, np.int8); xq1[70] = -3
+    xd1 = np.zeros(cols // 32, np.uint16); xd1[2] = 0x3800          # 0.5
+    y1 = oracle.q8_matvec(wq, wd, xq1, xd1)
+    exact = wq[:, 70].astype(np.float64) * -3 * 0.5 * wd[:, 2].view(np.float16).astype(np.float64)
+    assert np.array_equal(y1.astype(np.float64), exact.astype(np.float32).astype(np.float64))
+
+
+def test_block_dots():
+    pin_block_dots()
+
+
+def test_matvec():
+    pin_matvec()
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm, RoPE, SwiGLU
+# ----------------------------------------------------------------------------
+def pin_rmsnorm():
+    n = 96
+    c = 3.0
+    g = np.linspace(0.5, 1.5, n).astype(np.float32)
+    y = oracle.rmsnorm(np.full(n, c, np.float32), g, eps=1e-6)
+    want = g.astype(np.float64) * c / math.sqrt(c * c + 1e-6)
+    assert np.allclose(y, want, rtol=1e-7, atol=0)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(n).astype(np.float32) * 7
+    u = oracle.rmsnorm(x, None, eps=0.0).astype(np.float64)
+    assert abs(np.mean(u * u) - 1.0) < 1e-6                       # unit RMS
+    assert np.all(np.sign(u) == np.sign(x))
+    # scale invariance and per-element gamma
+    assert np.allclose(oracle.rmsnorm(x * 4, None, eps=0.0), u, rtol=1e-6)
+    yg = oracle.rmsnorm(x, g, eps=0.0).astype(np.float64)
+    assert np.allclose(yg, u * g, rtol=1e-6)
+
+
+def pin_rope():
+    hd, theta = 64, 1e6
+    cos_t, sin_t = oracle.rope_table(40, hd, theta)
+    # table entries against the math library
+    for p, i in [(0, 0), (1, 0), (7, 3), (39, 31), (13, 17)]:
+        a = p * theta ** (-2.0 * i / hd)
+        assert cos_t[p, i] == np.float32(math.cos(a)) and sin_t[p, i] == np.float32(math.sin(a))
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(hd).astype(np.float32)
+    # pos 0 is the identity
+    assert np.array_equal(oracle.rope_neox(x, cos_t[0], sin_t[0]), x)
+    # NeoX pairing and rotation direction: e_0 rotates into (cos, sin) on (0, hd/2)
+    e0 = np.zeros(hd, np.float32); e0[0] = 1
+    r = oracle.rope_neox(e0, cos_t[5], sin_t[5])
+    assert r[0] == cos_t[5, 0] and r[hd // 2] == sin_t[5, 0] and np.count_nonzero(r) == 2
+    # pair norms preserved
+    y = oracle.rope_neox(x, cos_t[9], sin_t[9]).astype(np.float64)
+    xx = x.astype(np.float64)
+    n0 = xx[:hd // 2] ** 2 + xx[hd // 2:] ** 2
+    n1 = y[:hd // 2] ** 2 + y[hd // 2:] ** 2
+    assert np.allclose(n0, n1, rtol=1e-5)
+    # relative position: <R(m) q, R(n) k> depends on m - n only
+    k = rng.standard_normal(hd).astype(np.float32)
+    for m, n in [(30, 10), (25, 5), (39, 19)]:
+        lhs = np.dot(oracle.rope_neox(x, cos_t[m], sin_t[m]).astype(np.float64),
+                     oracle.rope_neox(k, cos_t[n], sin_t[n]).astype(np.float64))
+        rhs = np.dot(oracle.rope_neox(x, cos_t[m - n], sin_t[m - n]).astype(np.float64),
+                     k.astype(np.float64))
+        assert abs(lhs - rhs) < 1e-4 * (1 + abs(rhs))
+
+
+def pin_silu():
+    g = np.array([0.0, 1.0, -1.0, 30.0, -30.0, 2.5, -0.75], np.float32)
+    u = np.array([5.0, 2.0, 2.0, 1.0, 1.0, -3.0, 4.0], np.float32)
+    h = oracle.silu_mul(g, u).astype(np.float64)
+    want = scipy.special.expit(g.astype(np.float64)) * g * u
+    assert h[0] == 0.0
+    assert np.allclose(h, want, rtol=1e-7, atol=1e-30)
+    assert abs(h[3] - 30.0) < 1e-6                                 # silu(z) -> z
+
+
+def test_rmsnorm():
+    pin_rmsnorm()
+
+
+def test_rope():
+    pin_rope()
+
+
+def test_silu():
+    pin_silu()
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def _bf16(a):
+    return (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_attention():
+    rng = np.random.default_rng(8)
+    n_q, n_kv, hd, ctx = 8, 2, 32, 50
+    G = n_q // n_kv
+    K = rng.standard_normal((n_kv, ctx, hd)).astype(np.float32)
+    V = rng.standard_normal((n_kv, ctx, hd)).astype(np.float32)
+    q = rng.standard_normal(n_q * hd).astype(np.float32)
+    scale = 1 / math.sqrt(hd)
+    hs, ps = ctx * hd, hd
+    # brute force with scipy's softmax over the window, both dtypes
+    for dtype in (0, 1):
+        Kc, Vc = (K, V) if dtype == 0 else (_bf16(K), _bf16(V))
+        Kf = K.astype(np.float64) if dtype == 0 else _bf16_f64(Kc)
+        Vf = V.astype(np.float64) if dtype == 0 else _bf16_f64(Vc)
+        for start, length in [(0, ctx), (17, 20), (49, 1)]:
+            got = oracle.attention(q, n_q, n_kv, hd, Kc, Vc, dtype, hs, ps, start, length, scale)
+            for h in range(n_q):
+                g = h // G
+                s = Kf[g, start:start + length] @ q[h * hd:(h + 1) * hd].astype(np.float64) * scale
+                want = scipy.special.softmax(s) @ Vf[g, start:start + length]
+                assert np.allclose(got[h * hd:(h + 1) * hd], want, rtol=1e-6, atol=1e-7)
+    # one position: output is that V row exactly
+    got = oracle.attention(q, n_q, n_kv, hd, K, V, 0, hs, ps, 33, 1, scale)
+    for h in range(n_q):
+        assert np.array_equal(got[h * hd:(h + 1) * hd], V[h // G, 33])
+    # q = 0: uniform weights, output is the mean of V over the window
+    got = oracle.attention(np.zeros_like(q), n_q, n_kv, hd, K, V, 0, hs, ps, 5, 40, scale)
+    for h in range(n_q):
+        assert np.allclose(got[h * hd:(h + 1) * hd], V[h // G, 5:45].astype(np.float64).mean(0), rtol=1e-6, atol=1e-7)
+    # GQA head map: V constant per kv head -> output of head h is h // G
+    Vg = np.broadcast_to(np.arange(n_kv, dtype=np.float32)[:, None, None], V.shape).copy()
+    got = oracle.attention(q, n_q, n_kv, hd, K, Vg, 0, hs, ps, 0, ctx, scale)
+    for h in range(n_q):
+        assert np.allclose(got[h * hd:(h + 1) * hd], h // G, atol=1e-6)
+    # one dominant score picks that row
+    Kd = K.copy(); Kd[:, 21] = 0
+    for g in range(n_kv):
+        Kd[g, 21] = 50 * q[g * G * hd:(g * G + 1) * hd]
+    got = oracle.attention(q, n_q, n_kv, hd, Kd, V, 0, hs, ps, 0, ctx, scale)
+    for g in range(n_kv):
+        assert np.allclose(got[g * G * hd:(g * G + 1) * hd], V[g, 21], atol=1e-6)
+    # non-default strides: a cache laid out [ctx, n_kv, hd] gives the same result
+    Kt = np.ascontiguousarray(K.transpose(1, 0, 2)); Vt = np.ascontiguousarray(V.transpose(1, 0, 2))
+    a = oracle.attention(q, n_q, n_kv, hd, K, V, 0, hs, ps, 3, 30, scale)
+    b = oracle.attention(q, n_q, n_kv, hd, Kt, Vt, 0, hd, n_kv * hd, 3, 30, scale)
+    assert np.array_equal(a, b)
+    # the method's own reformulation (online softmax in f64) matches the two-pass form
+    g, h = 1, 5
+    m, l, acc = -np.inf, 0.0, np.zeros(hd)
+    for j in range(ctx):
+        s = float(np.dot(K[g, j].astype(np.float64), q[h * hd:(h + 1) * hd].astype(np.float64)) * scale)
+        mn = max(m, s)
+        c = math.exp(m - mn) if m != -np.inf else 0.0
+        l = l * c + math.exp(s - mn)
+        acc = acc * c + math.exp(s - mn) * V[g, j].astype(np.float64)
+        m = mn
+    got = oracle.attention(q, n_q, n_kv, hd, K, V, 0, hs, ps, 0, ctx, scale)
+    assert np.allclose(got[h * hd:(h + 1) * hd], acc / l, rtol=1e-6, atol=1e-7)
+
+
+def test_attention():
+    pin_attention()
+
+
+# ----------------------------------------------------------------------------
+# MoE
+# ----------------------------------------------------------------------------
+def pin_moe_route():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((16, 128)).astype(np.float32)
+    logits[3, 10] = logits[3, 90] = 5.0                            # exact tie: lower id first
+    ids, w = oracle.moe_route(logits, 8)
+    order = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :8]
+    assert np.array_equal(ids, order)
+    assert ids[3, 0] == 10 and ids[3, 1] == 90
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(p, order, axis=1), rtol=1e-6)
+
+
+def pin_moe_block():
+    rng = np.random.default_rng(10)
+    H, I, E, k, T = 64, 32, 6, 2, 3
+    gq, gd = synthetic.q8_weight(rng, E * 2 * I, H)
+    dq, dd = synthetic.q8_weight(rng, E * H, I)
+    gq, gd = gq.reshape(E, 2 * I, H), gd.reshape(E, 2 * I, H // 32)
+    dq, dd = dq.reshape(E, H, I), dd.reshape(E, H, I // 32)
+    x = rng.standard_normal((T, H)).astype(np.float32) * 3
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    out, tr = oracle.moe_block(H, I, E, k, gq, gd, dq, dd, x, logits, trace=True)
+
+    def deq(q, d):
+        return q.astype(np.float64) * np.repeat(d.view(np.float16).astype(np.float64), 32, axis=-1)
+
+    # brute force in numpy over dequantized operands; the quantized inputs of
+    # each matvec are the oracle's (pinned separately above)
+    for t in range(T):
+        acc = np.zeros(H)
+        for s in range(k):
+            e = tr["ids"][t, s]
+            y1 = deq(gq[e], gd[e]) @ deq(tr["xq"][t], tr["xd"][t])
+            assert np.allclose(tr["y1"][t, s], y1, rtol=1e-6, atol=1e-7)
+            g32 = tr["y1"][t, s].astype(np.float64)          # stage boundary is float32
+            h = (scipy.special.expit(g32[:I]) * g32[:I] * g32[I:]).astype(np.float32)
+            hq, hd = oracle.q8_quantize(h)
+            diff = hq.astype(int) - tr["hq"][t, s].astype(int)
+            assert np.abs(diff).max() <= 1 and np.count_nonzero(diff) <= 1
+            y2 = deq(dq[e], dd[e]) @ deq(tr["hq"][t, s], tr["hd"][t, s])
+            assert np.allclose(tr["y2"][t, s], y2, rtol=1e-6, atol=1e-7)
+            acc += tr["w"][t, s] * y2
+        assert np.allclose(out[t], acc, rtol=1e-6, atol=1e-6)
+    # one expert, k = 1, weight 1: the block is the plain two-matvec FFN
+    out1, tr1 = oracle.moe_block(H, I, 1, 1, gq[:1], gd[:1], dq[:1], dd[:1], x, logits[:, :1], trace=True)
+    assert np.allclose(tr1["w"], 1.0)
+    y1 = oracle.q8_matvec(gq[0], gd[0], *oracle.q8_quantize(x[1]))
+    h = oracle.silu_mul(y1[:I], y1[I:])
+    y2 = oracle.q8_matvec(dq[0], dd[0], *oracle.q8_quantize(h))
+    assert np.array_equal(out1[1], y2)
+
+
+def test_moe_route():
+    pin_moe_route()
+
+
+def test_moe_block():
+    pin_moe_block()
+
+
+# ----------------------------------------------------------------------------
+# decode layer: composition of the pinned stages, checked against a numpy
+# float64 re-composition (brute force) on a small shape
+# ----------------------------------------------------------------------------
+def _np_layer(cfg, w, x, pos, kc, vc):
+    """Independent numpy composition of the layer (float64 math, float32 at
+    stage boundaries, the oracle's pinned quantizer for the Q8 steps)."""
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    eps = cfg["eps"]
+
+    def deq(q, d):
+        return q.astype(np.float64) * np.repeat(d.view(np.float16).astype(np.float64), 32, axis=-1)
+
+    def rms(v, g):
+        v = v.astype(np.float64)
+        r = v / np.sqrt(np.mean(v * v) + eps)
+        return (r * (1.0 if g is None else g.astype(np.float64))).astype(np.float32)
+
+    def mv(qname, a, res=None):
+        aq, ad = oracle.q8_quantize(a)
+        y = deq(w[qname + "_qs"], w[qname + "_d"]) @ deq(aq, ad)
+        if res is not None:
+            y = y + res.astype(np.float64)
+        return y.astype(np.float32)
+
+    half = hd // 2
+    ang = pos * cfg["theta"] ** (-2.0 * np.arange(half) / hd)
+    c, s = np.cos(ang).astype(np.float32).astype(np.float64), np.sin(ang).astype(np.float32).astype(np.float64)
+
+    def rope(v):
+        v = v.astype(np.float64)
+        a, b = v[:half], v[half:]
+        return np.concatenate([a * c - b * s, a * s + b * c]).astype(np.float32)
+
+    qkv = mv("qkv", rms(x, w["g_in"]))
+    qd, kvd = nq * hd, nkv * hd
+    q = np.concatenate([rope(rms(qkv[h * hd:(h + 1) * hd], w["g_q"])) for h in range(nq)])
+    k = np.concatenate([rope(rms(qkv[qd + g * hd:qd + (g + 1) * hd], w["g_k"])) for g in range(nkv)])
+    v = qkv[qd + kvd:]
+    if cfg["v_unit_norm"]:
+        v = np.concatenate([rms(v[g * hd:(g + 1) * hd], None) for g in range(nkv)])
+    kc, vc = kc.copy(), vc.copy()
+    if cfg["kv_dtype"] == 0:
+        kc[:, pos] = k.reshape(nkv, hd); vc[:, pos] = v.reshape(nkv, hd)
+        Kf, Vf = kc.astype(np.float64), vc.astype(np.float64)
+    else:
+        import torch
+        kb = torch.from_numpy(k.reshape(nkv, hd)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        vb = torch.from_numpy(v.reshape(nkv, hd)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        kc[:, pos] = kb; vc[:, pos] = vb
+        Kf, Vf = _bf16_f64(kc), _bf16_f64(vc)
+    start = max(0, pos - cfg["window"] + 1) if cfg["window"] else 0
+    G = nq // nkv
+    att = np.concatenate([
+        scipy.special.softmax(Kf[h // G, start:pos + 1] @ q[h * hd:(h + 1) * hd].astype(np.float64)
+                              * cfg["attn_scale"]) @ Vf[h // G, start:pos + 1] for h in range(nq)
+    ]).astype(np.float32)
+    if cfg["kind"] == 0:
+        x1 = mv("o", att, res=x)
+        gu = mv("gu", rms(x1, w["g_post"]))
+        h = (scipy.special.expit(gu[:I].astype(np.float64)) * gu[:I] * gu[I:]).astype(np.float32)
+        return mv("dn", h, res=x1)
+    o = mv("o", att)
+    return (x.astype(np.float64) + rms(o, w["g_post"])).astype(np.float32)
+
+
+def _small_layer(kind, kv_dtype, seed):
+    rng = np.random.default_rng(seed)
+    cfg = dict(kind=kind, hidden=128, n_q=4, n_kv=2, head_dim=32, ffn=96 if kind == 0 else 0,
+               kv_dtype=kv_dtype, ctx=24, window=8 if kind == 1 else 0, eps=1e-6, theta=1e6,
+               max_ctx=24, qk_norm=1, v_unit_norm=1 if kind == 1 else 0)
+    cfg["attn_scale"] = 1 / math.sqrt(cfg["head_dim"])
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    w = dict(g_in=synthetic.gamma(rng, H), g_q=synthetic.gamma(rng, hd), g_k=synthetic.gamma(rng, hd),
+             g_post=synthetic.gamma(rng, H))
+    w["qkv_qs"], w["qkv_d"] = synthetic.q8_weight(rng, nq * hd + 2 * nkv * hd, H)
+    w["o_qs"], w["o_d"] = synthetic.q8_weight(rng, H, nq * hd)
+    if I:
+        w["gu_qs"], w["gu_d"] = synthetic.q8_weight(rng, 2 * I, H)
+        w["dn_qs"], w["dn_d"] = synthetic.q8_weight(rng, H, I)
+    w["rope_cos"], w["rope_sin"] = oracle.rope_table(cfg["max_ctx"], hd, cfg["theta"])
+    x = synthetic.activations(rng, H)
+    kc = synthetic.kv_cache(rng, nkv, cfg["max_ctx"], hd, kv_dtype)
+    vc = synthetic.kv_cache(rng, nkv, cfg["max_ctx"], hd, kv_dtype)
+    return cfg, w, x, kc, vc
+
+
+def pin_layer(kind, kv_dtype, seed=11):
+    cfg, w, x, kc, vc = _small_layer(kind, kv_dtype, seed)
+    pos = cfg["ctx"] - 1
+    got, kc2, vc2, tr = oracle.decode_layer(cfg, w, x, pos, kc, vc, trace=True)
+    want = _np_layer(cfg, w, x, pos, kc, vc)
+    err = np.abs(got.astype(np.float64) - want)
+    assert np.all(err <= np.maximum(1e-3 * np.abs(want), 1e-4)), err.max()
+    # only row pos of each cache changes
+    changed = np.any(kc2 != kc, axis=2)
+    assert not changed[:, :pos].any() and not changed[:, pos + 1:].any()
+
+
+@pytest.mark.parametrize("kind,kv_dtype", [(0, 0), (0, 1), (1, 1)])
+def test_layer_composition(kind, kv_dtype):
+    pin_layer(kind, kv_dtype)
