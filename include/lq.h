@@ -1,0 +1,297 @@
+/*
+ * lq.h -- C ABI of the Q8_0 single-token decode-layer library for AMD
+ * Instinct MI355X (gfx950).  Library: liblq.so (hand-written HIP kernels).
+ *
+ * The operations are the decode hot path that these inference-engine design
+ * pages describe (cited by page title and section):
+ *   [LAT] "Design: lattice-inference": Current Design (Q8_0 NEON matvec with
+ *         int8 x int8 products into int32; fused attention with online
+ *         softmax; fused per-head Q/K norm + RoPE), Invariants INV-2
+ *         (head_dim % 4 == 0), INV-3 (num_heads % kv_heads == 0), INV-7
+ *         (fused QKV weight [q_dim + 2*kv_dim, hidden]), INV-8 (buffers
+ *         pre-allocated, no allocation in the forward pass).
+ *   [CUR] "Current Inference Path -- Architecture Map" (hf2q): section 3
+ *         (per-token decode sequence), section 4 (rms_norm F=1/2/3, NeoX
+ *         RoPE, index-driven quantized matvec for MoE), section 7 (KV views
+ *         with a non-zero start offset; offsets are element counts).
+ *   [ENG] "Inference Engine" (larql): BLAS-Fused Attention (scale
+ *         1/sqrt(head_dim), softmax, GQA with any ratio).
+ *   [TGT] "Target Inference Architecture: hf2q on mlx-native": section 3.2
+ *         (decode op list), section 3.3 (buffer flow and layouts), section
+ *         4.2 (buffers carry no shape metadata; the caller tracks shapes),
+ *         section 6.3 (GGML block layout; [num_experts, n, k] expert layout).
+ *
+ * Conventions (all entry points)
+ *   - Every pointer named as device memory is caller-owned GPU memory; the
+ *     library never allocates or frees on these calls.  Host pointers are
+ *     named as such.  Scratch space comes in through (workspace,
+ *     workspace_bytes), sized by the matching *_workspace_size() query.
+ *   - stream is a hipStream_t passed as void* (NULL: the null stream).  Calls
+ *     only enqueue work; none synchronizes the host.
+ *   - Sizes, offsets and strides are int64_t ELEMENT counts, never bytes.
+ *   - f16 and bf16 values are uint16_t bit patterns.
+ *   - A nonzero lq_status means nothing was enqueued (argument checks run on
+ *     the host before any launch), except LQ_ERR_HIP, which reports a launch
+ *     failure.  lq_last_error() then returns a message (thread-local).
+ *     Faults inside kernels surface at the caller's next synchronization.
+ *   - Zero-sized work (rows == 0, n_rows == 0, ...) is a no-op returning
+ *     LQ_OK.
+ *   - Calls are stateless and reentrant; concurrent calls must not share
+ *     output or workspace buffers.
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lq_status;
+#define LQ_OK               0
+#define LQ_ERR_NULL         1   /* a required pointer is NULL */
+#define LQ_ERR_SHAPE        2   /* sizes violate the operation's definition */
+#define LQ_ERR_ALIGN        3   /* a pointer or stride breaks the alignment below */
+#define LQ_ERR_WORKSPACE    4   /* workspace NULL or smaller than the query says */
+#define LQ_ERR_HIP          5   /* the HIP runtime reported an error on launch */
+#define LQ_ERR_UNSUPPORTED  6   /* valid by definition, outside this build's kernels */
+
+#define LQ_KV_F32   0
+#define LQ_KV_BF16  1
+
+/* Q8_0 weight matrix in structure-of-arrays form ([LAT] Current Design;
+ * GGML Q8_0 semantics per [TGT] section 6.3): row r, block b (32 columns)
+ * dequantizes to f16(d[r*cols/32 + b]) * qs[r*cols + 32*b + i].
+ *   qs:  device, int8 [rows, cols], row-major, 16-byte aligned.
+ *   d:   device, f16 bits [rows, cols/32], 2-byte aligned.
+ *   cols must be a positive multiple of 32.
+ * lq_q8_pack_ggml() converts the interleaved 34-byte GGML blocks to this. */
+typedef struct lq_q8_weight {
+    const int8_t*   qs;
+    const uint16_t* d;
+    int64_t rows;
+    int64_t cols;
+} lq_q8_weight;
+
+/* ---------------------------------------------------------------- misc */
+int32_t     lq_version(void);
+const char* lq_status_string(lq_status s);
+const char* lq_last_error(void);
+
+/* Host-only helper: GGML Q8_0 blocks (per 32 values: f16 scale, then 32
+ * int8 codes; 34 bytes, [TGT] section 6.3 "GGML block order") for a
+ * [rows, cols] matrix, row-major, into SoA qs [rows, cols] and d
+ * [rows, cols/32].  All pointers are HOST memory.  cols % 32 == 0. */
+lq_status lq_q8_pack_ggml(const void* blocks, int64_t rows, int64_t cols,
+                          int8_t* qs, uint16_t* d);
+
+/* Host-only helper: RoPE cos/sin tables [max_ctx, head_dim/2] for angle
+ * pos * theta^(-2i/head_dim), computed in double and stored as float
+ * ([LAT] Current Design: rope_table_max_seq_len).  HOST memory. */
+lq_status lq_rope_table(int64_t max_ctx, int64_t head_dim, double theta,
+                        float* cos_out, float* sin_out);
+
+/* ---------------------------------------------------------------- Q8_0 */
+/* Quantize n_rows independent vectors of n floats (n % 32 == 0) to Q8_0:
+ * per 32-block d = amax/127 (float), codes = round-half-away(x * (1/d))
+ * clamped to [-127, 127] (0 when amax == 0), scale stored as f16 (RNE).
+ * x: device f32 [n_rows, n], 16-byte aligned.  qs: device int8 [n_rows, n],
+ * 16-byte aligned.  d: device f16 bits [n_rows, n/32]. */
+lq_status lq_q8_quantize_act(const float* x, int64_t n_rows, int64_t n,
+                             int8_t* qs, uint16_t* d, void* stream);
+
+/* Fused RMSNorm + Q8_0 quantize of n_rows vectors of n floats:
+ * y = gamma * x / sqrt(mean(x^2) + eps) ([CUR] section 4, F=2 weighted;
+ * gamma == NULL gives the unit-weight F=1 form), then as
+ * lq_q8_quantize_act.  gamma: device f32 [n]. */
+lq_status lq_rmsnorm_q8(const float* x, int64_t n_rows, int64_t n, const float* gamma,
+                        float eps, int8_t* qs, uint16_t* d, void* stream);
+
+/* SwiGLU + Q8_0 quantize: for each of n_rows rows of gate_up [n_rows, 2*ffn]
+ * (gate in columns [0, ffn), up in [ffn, 2*ffn)), h = silu(gate) * up with
+ * silu(z) = z / (1 + exp(-z)), then quantize h as lq_q8_quantize_act
+ * ([TGT] section 3.2: gate, activation, up, mul).  ffn % 32 == 0.
+ * gate_up: device f32, 16-byte aligned. */
+lq_status lq_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn,
+                       int8_t* qs, uint16_t* d, void* stream);
+
+/* Q8_0 matvec ([LAT] Current Design, NEON 4-row matvec): for every row r,
+ *   dot[r,b] = sum_{i<32} qs_w[r,32b+i] * x_qs[32b+i]        (int32, exact)
+ *   y[r]     = residual[r] + sum_b f16(d_w[r,b]) * f16(x_d[b]) * dot[r,b]
+ * with the float sum in an unspecified order (each term is exact in f32
+ * before accumulation).  residual may be NULL.  x_qs: device int8 [cols],
+ * 16-byte aligned; x_d: device f16 bits [cols/32]; y, residual: device f32
+ * [rows].  y may alias residual. */
+lq_status lq_q8_matvec(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d,
+                       const float* residual, float* y, void* stream);
+
+/* Test tap: the int32 block dots dot[r,b] that lq_q8_matvec forms, written
+ * to dots (device int32 [rows, cols/32]), computed by the same device code. */
+lq_status lq_q8_block_dots(const lq_q8_weight* w, const int8_t* x_qs, int32_t* dots,
+                           void* stream);
+
+/* ---------------------------------------------------------------- norm + RoPE */
+/* In place, for each of n_heads heads of head_dim floats starting at
+ * x + h*head_stride ([LAT] Current Design: fused_qk_norm_rope; [CUR]
+ * section 4: RMSNorm, then the NeoX rotation of pairs (i, i + head_dim/2)):
+ *   x <- gamma * x / sqrt(mean(x^2) + eps)   (gamma NULL: unit weight)
+ *   (a, b) <- (a*c - b*s, a*s + b*c),  c, s = rope_cos/sin[pos*head_dim/2 + i]
+ * rope_cos == rope_sin == NULL skips the rotation.  head_dim even, 2..512.
+ * x: device f32, 4-byte aligned; gamma: device f32 [head_dim];
+ * rope tables: device f32 [rope_len, head_dim/2] (see lq_rope_table), with
+ * pos < rope_len. */
+lq_status lq_rmsnorm_rope(float* x, int64_t n_heads, int64_t head_dim, int64_t head_stride,
+                          const float* gamma, float eps, const float* rope_cos,
+                          const float* rope_sin, int64_t rope_len, int64_t pos, void* stream);
+
+/* KV-cache append in place ([CUR] section 1 kv-cache-kernel in-place;
+ * [TGT] section 6.1 step 6): for every kv head g and dim e,
+ *   k_cache[g*head_stride + pos*pos_stride + e] = cvt(k[g*head_dim + e])
+ * (same for v), cvt = identity (LQ_KV_F32) or f32->bf16 round-to-nearest-
+ * even (LQ_KV_BF16).  k, v: device f32 [n_kv, head_dim].  max_ctx is the
+ * number of positions allocated per head: pos < max_ctx. */
+lq_status lq_kv_append(const float* k, const float* v, int64_t n_kv, int64_t head_dim,
+                       void* k_cache, void* v_cache, int32_t kv_dtype,
+                       int64_t head_stride, int64_t pos_stride, int64_t max_ctx, int64_t pos,
+                       void* stream);
+
+/* ---------------------------------------------------------------- attention */
+/* GQA decode attention ([ENG] BLAS-Fused Attention; [LAT] fused_attention
+ * with online softmax, GQA rows per workgroup): for every query head h,
+ * with kv head g = h / (n_q / n_kv) (consecutive query heads share a kv
+ * head) and positions j in [start, start + len):
+ *   s_j   = scale * <q[h], K[g, j]>
+ *   out_h = sum_j softmax(s)_j * V[g, j]
+ * K[g, j] starts at element g*head_stride + j*pos_stride of the cache
+ * (element offsets, never bytes: [CUR] section 7).  The GPU computes the
+ * softmax online over splits of the positions and combines the splits.
+ *   q: device f32 [n_q, head_dim]; out: device f32 [n_q, head_dim].
+ *   caches: device f32 or bf16 (kv_dtype), 16-byte aligned, with
+ *   head_stride and pos_stride multiples of 16 bytes; max_ctx is the number
+ *   of positions allocated per head: start + len <= max_ctx.
+ * Shapes: n_q % n_kv == 0 (INV-3), head_dim % 4 == 0 (INV-2); this build
+ * also needs head_dim % 8 == 0 for bf16, head_dim <= 512 and
+ * n_q / n_kv <= 8 (else LQ_ERR_UNSUPPORTED).  len == 0 writes zeros. */
+size_t lq_gqa_decode_attn_workspace_size(int64_t n_q, int64_t n_kv, int64_t head_dim,
+                                         int64_t len);
+lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                             const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                             int64_t head_stride, int64_t pos_stride, int64_t max_ctx,
+                             int64_t start, int64_t len, float scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- MoE */
+/* Router ([TGT] section 3.2: softmax, argsort, gather of the top-k
+ * probabilities): per token t, p = softmax(logits[t, :E]); ids[t, s] are
+ * the k experts with the largest logits (equivalently probabilities), in
+ * descending order, ties to the lower id; w[t, s] = p[ids[t, s]] (no
+ * renormalisation).  logits: device f32 [T, E]; ids: device int32 [T, k];
+ * w: device f32 [T, k].  E <= 1024, k <= min(E, 32). */
+lq_status lq_moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k,
+                            int32_t* ids, float* w, void* stream);
+
+/* Index-driven Q8_0 matvec, one row-set per (token, slot) ([CUR] section 4,
+ * moe_kernel: each (token, slot) selects an expert's quantized weights by
+ * id; [TGT] section 6.3: experts byte-contiguous as [n_experts, rows, cols]):
+ *   y[t, s, r] = sum_b f16(dW_e[r,b]) * f16(dx[b]) * dot(W_e[r, b], x[b]),
+ *   e = ids[t, s],  x = x_qs/x_d row t (x_per_slot == 0) or row t*k + s
+ *   (x_per_slot == 1).
+ * w describes ONE expert (rows, cols); expert e's codes start at
+ * w->qs + e*rows*cols and its scales at w->d + e*rows*cols/32.  Each touched
+ * expert's weights are streamed once for all of its (t, s) rows.
+ * ids live on the device and are not checked on the host: a (t, s) whose id
+ * is outside [0, n_experts) gets y = 0 and increments the int32 counter at
+ * the start of the workspace (read it after synchronizing).
+ * y: device f32 [T, k, rows]. */
+size_t lq_moe_workspace_size(int64_t T, int64_t k, int64_t n_experts);
+lq_status lq_moe_q8_matvec_id(const lq_q8_weight* w, int64_t n_experts,
+                              const int8_t* x_qs, const uint16_t* x_d, int32_t x_per_slot,
+                              const int32_t* ids, int64_t T, int64_t k, float* y,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weighted sum over slots ([TGT] section 3.2 weighted_sum):
+ * out[t, r] = sum_{s<k} w[t, s] * y[t, s, r], slots summed in order s = 0..k-1.
+ * y: device f32 [T, k, rows]; w: device f32 [T, k]; out: device f32 [T, rows]. */
+lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k,
+                              int64_t rows, float* out, void* stream);
+
+/* Whole MoE FFN block for T tokens ([CUR] section 3 item i, fused path):
+ * route -> Q8(x) -> gate_up id-matvec -> SwiGLU + Q8 -> down id-matvec ->
+ * weighted sum.  No host synchronization. */
+typedef struct lq_moe_desc {
+    int64_t hidden, ffn, n_experts, top_k;
+    lq_q8_weight w_gate_up;   /* one expert: rows 2*ffn (gate rows, then up rows), cols hidden */
+    lq_q8_weight w_down;      /* one expert: rows hidden, cols ffn */
+} lq_moe_desc;
+
+/* Optional device buffers; a non-NULL tap replaces the workspace buffer for
+ * that intermediate, so the caller can read it after synchronizing. */
+typedef struct lq_moe_taps {
+    int32_t* ids; float* w;           /* [T, k] */
+    int8_t* xq; uint16_t* xd;         /* [T, hidden], [T, hidden/32] */
+    float* y1;                        /* [T, k, 2*ffn] */
+    int8_t* hq; uint16_t* hd;         /* [T, k, ffn], [T, k, ffn/32] */
+    float* y2;                        /* [T, k, hidden] */
+} lq_moe_taps;
+
+size_t lq_moe_block_workspace_size(const lq_moe_desc* m, int64_t T);
+lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const float* logits, int64_t T,
+                       float* out, const lq_moe_taps* taps,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- decode layer */
+#define LQ_LAYER_PRENORM_FFN     0   /* x -> norm -> QKV -> qk-norm/RoPE -> KV append -> attn -> O + x
+                                        -> norm -> gate_up -> SwiGLU -> down + x1 */
+#define LQ_LAYER_ATTN_POSTNORM   1   /* Gemma attention block: ... -> attn -> O -> norm -> + x */
+
+typedef struct lq_layer_desc {
+    int64_t hidden, n_q, n_kv, head_dim;
+    int64_t ffn;              /* used by LQ_LAYER_PRENORM_FFN */
+    int64_t max_ctx;          /* positions allocated per kv head in each cache */
+    int64_t window;           /* 0: full causal context; W: positions [pos-W+1, pos] */
+    float eps, attn_scale;
+    int32_t kind;
+    int32_t kv_dtype;
+    int32_t qk_norm;          /* per-head RMSNorm of q (g_q) and k (g_k) */
+    int32_t v_unit_norm;      /* unit-weight RMSNorm of v ([CUR] section 3, rms_norm_unit) */
+    lq_q8_weight w_qkv;       /* [n_q*hd + 2*n_kv*hd, hidden] (INV-7): q rows, k rows, v rows */
+    lq_q8_weight w_o;         /* [hidden, n_q*hd] */
+    lq_q8_weight w_gate_up;   /* [2*ffn, hidden]: gate rows, then up rows */
+    lq_q8_weight w_down;      /* [hidden, ffn] */
+    const float *g_in;        /* [hidden] input norm */
+    const float *g_q, *g_k;   /* [head_dim] */
+    const float *g_post;      /* [hidden] post-attention norm */
+    void *k_cache, *v_cache;  /* [n_kv, max_ctx, head_dim], contiguous */
+    const float *rope_cos, *rope_sin;   /* [max_ctx, head_dim/2] */
+} lq_layer_desc;
+
+/* Optional device buffers for the layer's intermediates (a non-NULL tap
+ * replaces the workspace buffer; read after synchronizing). */
+typedef struct lq_layer_taps {
+    int8_t* xq; uint16_t* xd;  /* Q8 of the input norm [hidden], [hidden/32] */
+    float* qkv;                /* fused projection; q and k parts after norm + RoPE, v after its norm */
+    float* attn;               /* attention output [n_q*hd] */
+    int8_t* aq; uint16_t* ad;  /* Q8 of the attention output */
+    float* x1;                 /* PRENORM_FFN: x + O projection; ATTN_POSTNORM: the O
+                                  projection before the post-attention norm [hidden] */
+    int8_t* nq; uint16_t* nd;  /* Q8 of the post-attention norm (PRENORM_FFN) */
+    float* gu;                 /* gate/up projection [2*ffn] */
+    int8_t* hq; uint16_t* hd;  /* Q8 of silu(gate) * up [ffn] */
+} lq_layer_taps;
+
+/* One decode token through one layer ([CUR] section 3 sequence; [TGT]
+ * section 3.2, one queue and no intermediate host synchronization): x
+ * (device f32 [hidden]) is updated in place; k and v of the token are
+ * written into the caches at pos (pos < max_ctx); attention covers the
+ * window ending at pos.  taps may be NULL. */
+size_t lq_decode_layer_workspace_size(const lq_layer_desc* L);
+lq_status lq_decode_layer(const lq_layer_desc* L, float* x, int64_t pos,
+                          const lq_layer_taps* taps, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LQ_H */

@@ -1,0 +1,460 @@
+// k_moe.hip -- MoE routing and the index-driven Q8_0 matvec for gfx950.
+//
+// "Current Inference Path -- Architecture Map" (section 3 item i: router
+// softmax, top-k, expert dispatch, weighted reduction; section 4 moe_kernel:
+// each (token, slot) row selects an expert's quantized weights by id) and
+// "Target Inference Architecture: hf2q on mlx-native" (section 3.2:
+// softmax, argsort, gather, quantized_matmul_id x2, weighted_sum; section
+// 6.3: experts byte-contiguous as [num_experts, n, k]).
+//
+// Decode batches are small (16 tokens x top-8 here), so a (token, slot)
+// touches few rows per expert; what matters is that every touched expert's
+// weights stream from HBM exactly once.  A gather step lists, per active
+// expert, its (token, slot) rows in ascending order; the matvec then gives
+// each workgroup one expert and a block of rows, loads those weight rows
+// into VGPRs once, and applies them to every listed slot.  No float atomics
+// are used, so results are deterministic.
+#include <math.h>
+
+#include "lq_device.h"
+#include "lq_internal.h"
+
+namespace lq {
+
+constexpr int kMoeMaxExperts = 4096;
+constexpr int kMoeMaxSlots = 8192;
+
+// Workspace layout (int32 units):
+//   [0] invalid-id counter, [1] active expert count,
+//   [2, 2+E) active expert ids, [2+E, 3+2E) slot offsets per active expert,
+//   [3+2E, 3+2E+T*k) slot indices grouped by expert.
+struct MoeWs {
+    int32_t* base;
+    int64_t E;
+    __host__ __device__ int32_t* invalid() const { return base; }
+    __host__ __device__ int32_t* n_active() const { return base + 1; }
+    __host__ __device__ int32_t* active() const { return base + 2; }
+    __host__ __device__ int32_t* offsets() const { return base + 2 + E; }
+    __host__ __device__ int32_t* slots() const { return base + 3 + 2 * E; }
+};
+
+size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts) {
+    return round_up((size_t)(3 + 2 * n_experts + T * k) * sizeof(int32_t), 256);
+}
+
+// ---- router: one wave per token --------------------------------------------
+__global__ __launch_bounds__(64) void k_moe_route(const float* __restrict__ logits, int E, int k,
+                                                  int32_t* __restrict__ ids, float* __restrict__ w) {
+    constexpr int PER = 16;   // E <= 1024
+    const int t = blockIdx.x, lane = threadIdx.x;
+    const float* lt = logits + (int64_t)t * E;
+    float v[PER];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? lt[e] : -INFINITY;
+        mx = fmaxf(mx, v[i]);
+    }
+    mx = wave_max(mx);
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) z += (lane + 64 * i < E) ? expf(v[i] - mx) : 0.0f;
+    z = wave_sum(z);
+    for (int s = 0; s < k; ++s) {
+        // lane-local best (largest value, then lowest id)
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+        // wave argmax with the same ordering
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (lane == 0) {
+            ids[(int64_t)t * k + s] = bi;
+            w[(int64_t)t * k + s] = expf(bv - mx) / z;
+        }
+        // remove the chosen expert
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i == bi) v[i] = -INFINITY;
+        // a -inf logit can tie with removed entries; keep ids distinct by
+        // marking removed ones below every real value
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i == bi) v[i] = __int_as_float(0xff800001u);   // NaN never wins
+    }
+}
+
+// ---- gather: group (token, slot) rows by expert ------------------------------
+// One workgroup.  Thread e (strided) scans the ids in order and collects the
+// slots of expert e, so each expert's list is ascending and the result is
+// deterministic.  Rows of slots with an out-of-range id are zeroed in y0 and
+// y1 (either may be NULL) and counted.
+__global__ __launch_bounds__(256) void k_moe_gather(const int32_t* __restrict__ ids, int nslots, int E,
+                                                    int32_t* wsbase, float* y0, int64_t rows0, float* y1,
+                                                    int64_t rows1) {
+    __shared__ int32_t cnt[kMoeMaxExperts];
+    __shared__ int32_t off[kMoeMaxExperts + 1];
+    MoeWs ws{wsbase, E};
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nslots; i += 256) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0, acc = 0, bad = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = acc;
+            if (cnt[e] > 0) {
+                ws.active()[n] = e;
+                ws.offsets()[n] = acc;
+                ++n;
+            }
+            acc += cnt[e];
+        }
+        ws.offsets()[n] = acc;
+        *ws.n_active() = n;
+        bad = nslots - acc;
+        *ws.invalid() = bad;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        if (cnt[e] == 0) continue;
+        int p = off[e];
+        for (int i = 0; i < nslots; ++i)
+            if (ids[i] == e) ws.slots()[p++] = i;
+    }
+    // zero the outputs of invalid slots
+    for (int i = 0; i < nslots; ++i) {
+        const int e = ids[i];
+        if (e >= 0 && e < E) continue;
+        if (y0)
+            for (int64_t r = threadIdx.x; r < rows0; r += 256) y0[(int64_t)i * rows0 + r] = 0.0f;
+        if (y1)
+            for (int64_t r = threadIdx.x; r < rows1; r += 256) y1[(int64_t)i * rows1 + r] = 0.0f;
+    }
+}
+
+__device__ __forceinline__ int dot16(int4 a, int4 b) {
+    int p = __builtin_amdgcn_sdot4(a.x, b.x, 0, false);
+    p = __builtin_amdgcn_sdot4(a.y, b.y, p, false);
+    p = __builtin_amdgcn_sdot4(a.z, b.z, p, false);
+    p = __builtin_amdgcn_sdot4(a.w, b.w, p, false);
+    return p;
+}
+
+// ---- index-driven matvec ------------------------------------------------------
+// blockIdx.x = active-expert index * rowblocks + row block.  Each wave holds
+// RPW weight rows (NCH 1 KB chunks each) in VGPRs and applies them to every
+// slot of its expert: same lane mapping and block-dot arithmetic as the
+// dense Q8_0 matvec.
+template <int NCH, int RPW>
+__global__ __launch_bounds__(256) void k_moe_matvec_id(const int8_t* __restrict__ wq,
+                                                       const uint16_t* __restrict__ wd, int rows,
+                                                       int cols, const int8_t* __restrict__ xq,
+                                                       const uint16_t* __restrict__ xd, int x_per_slot,
+                                                       int k, const int32_t* __restrict__ wsbase, int E,
+                                                       int rowblocks, float* __restrict__ y) {
+    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
+    const int ai = blockIdx.x / rowblocks, rb = blockIdx.x - ai * rowblocks;
+    if (ai >= *ws.n_active()) return;
+    const int e = ws.active()[ai];
+    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = cols >> 5;
+    const int r0 = (rb * 4 + wave) * RPW;
+    if (r0 >= rows) return;
+    const int8_t* we = wq + (int64_t)e * rows * cols;
+    const uint16_t* de = wd + (int64_t)e * rows * nb;
+
+    int4 wv[RPW][NCH];
+    float wsc[RPW][NCH];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = r0 + i;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            if (r < rows && off < cols) {
+                wv[i][c] = load_stream16(we + (int64_t)r * cols + off);
+                wsc[i][c] = f16_to_f32(de[(int64_t)r * nb + (off >> 5)]);
+            } else {
+                wv[i][c] = make_int4(0, 0, 0, 0);
+                wsc[i][c] = 0.0f;
+            }
+        }
+    }
+    for (int si = s0; si < s1; ++si) {
+        const int slot = ws.slots()[si];
+        const int64_t xrow = x_per_slot ? slot : slot / k;
+        int4 xv[NCH];
+        float xs[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            if (off < cols) {
+                xv[c] = *reinterpret_cast<const int4*>(xq + xrow * cols + off);
+                xs[c] = f16_to_f32(xd[xrow * nb + (off >> 5)]);
+            } else {
+                xv[c] = make_int4(0, 0, 0, 0);
+                xs[c] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int p = dot16(wv[i][c], xv[c]);
+                const int blk = p + dpp_i<kQuadXor1>(p);
+                const float t = (float)blk * (wsc[i][c] * xs[c]);
+                acc += (lane & 1) ? 0.0f : t;
+            }
+            acc = wave_sum(acc);
+            const int r = r0 + i;
+            if (lane == 0 && r < rows) y[(int64_t)slot * rows + r] = acc;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_moe_weighted_sum(const float* __restrict__ y,
+                                                          const float* __restrict__ w, int64_t T,
+                                                          int k, int64_t rows, float* __restrict__ out) {
+    const int64_t n = T * rows;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i / rows, r = i - t * rows;
+        float acc = 0.0f;
+        for (int s = 0; s < k; ++s) acc = fmaf(w[t * k + s], y[(t * k + s) * rows + r], acc);
+        out[i] = acc;
+    }
+}
+
+// ---- host --------------------------------------------------------------------
+
+lq_status launch_moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
+                           float* w, hipStream_t s) {
+    if (T == 0) return LQ_OK;
+    hipLaunchKernelGGL(k_moe_route, dim3((unsigned)T), dim3(64), 0, s, logits, (int)E, (int)k, ids, w);
+    return check_launch("moe_route");
+}
+
+static lq_status launch_gather(const int32_t* ids, int64_t nslots, int64_t E, void* ws, float* y0,
+                               int64_t rows0, float* y1, int64_t rows1, hipStream_t s) {
+    hipLaunchKernelGGL(k_moe_gather, dim3(1), dim3(256), 0, s, ids, (int)nslots, (int)E,
+                       static_cast<int32_t*>(ws), y0, rows0, y1, rows1);
+    return check_launch("moe_gather");
+}
+
+template <int NCH>
+static void launch_id_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int rows, int cols,
+                          const int8_t* xq, const uint16_t* xd, int x_per_slot, int k,
+                          const int32_t* ws, int E, float* y) {
+    constexpr int RPW = NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1);
+    const int rowblocks = (rows + 4 * RPW - 1) / (4 * RPW);
+    hipLaunchKernelGGL((k_moe_matvec_id<NCH, RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, wq, wd,
+                       rows, cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
+}
+
+static lq_status launch_id_gathered(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                                    int64_t E, const int8_t* xq, const uint16_t* xd, int32_t x_per_slot,
+                                    int64_t k, const void* ws, float* y, hipStream_t s) {
+    const int nch = (int)((cols + 1023) / 1024);
+    const int32_t* w32 = static_cast<const int32_t*>(ws);
+#define LQ_ID_CASE(N)                                                                                      \
+    case N:                                                                                                \
+        launch_id_nch<N>(s, wq, wd, (int)rows, (int)cols, xq, xd, x_per_slot, (int)k, w32, (int)E, y); \
+        break;
+    switch (nch) {
+        LQ_ID_CASE(1) LQ_ID_CASE(2) LQ_ID_CASE(3) LQ_ID_CASE(4)
+        LQ_ID_CASE(5) LQ_ID_CASE(6) LQ_ID_CASE(7) LQ_ID_CASE(8)
+        default: return fail(LQ_ERR_UNSUPPORTED, "moe matvec: cols > 8192");
+    }
+#undef LQ_ID_CASE
+    return check_launch("moe_matvec_id");
+}
+
+lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                               int64_t n_experts, const int8_t* xq, const uint16_t* xd,
+                               int32_t x_per_slot, const int32_t* ids, int64_t T, int64_t k,
+                               float* y, void* ws, hipStream_t s) {
+    lq_status st = launch_gather(ids, T * k, n_experts, ws, y, rows, nullptr, 0, s);
+    if (st != LQ_OK) return st;
+    return launch_id_gathered(wq, wd, rows, cols, n_experts, xq, xd, x_per_slot, k, ws, y, s);
+}
+
+lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
+                                  float* out, hipStream_t s) {
+    const int64_t n = T * rows;
+    if (n == 0) return LQ_OK;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    hipLaunchKernelGGL(k_moe_weighted_sum, dim3((unsigned)grid), dim3(256), 0, s, y, w, T, (int)k, rows, out);
+    return check_launch("moe_weighted_sum");
+}
+
+static lq_status check_moe_weight(const char* fn, const lq_q8_weight* w, int64_t n_experts) {
+    lq_status st = check_weight(w, fn);
+    if (st != LQ_OK) return st;
+    if (n_experts <= 0 || n_experts > kMoeMaxExperts)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: n_experts=%lld (1..%d)", fn, (long long)n_experts, kMoeMaxExperts);
+    if (w->cols > 8192 || w->rows > 0x7fffffffLL / 4)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: expert rows=%lld cols=%lld too large", fn, (long long)w->rows,
+                    (long long)w->cols);
+    return LQ_OK;
+}
+
+}  // namespace lq
+
+using namespace lq;
+
+extern "C" lq_status lq_moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
+                                       float* w, void* stream) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E)
+        return fail(LQ_ERR_SHAPE, "lq_moe_route_topk: T=%lld E=%lld k=%lld", (long long)T, (long long)E, (long long)k);
+    if (E > 1024 || k > 32) return fail(LQ_ERR_UNSUPPORTED, "lq_moe_route_topk: E <= 1024 and k <= 32");
+    if (T == 0) return LQ_OK;
+    if (T > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "lq_moe_route_topk: T too large");
+    if (!logits || !ids || !w) return fail(LQ_ERR_NULL, "lq_moe_route_topk: NULL pointer");
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4))
+        return fail(LQ_ERR_ALIGN, "lq_moe_route_topk: misaligned pointer");
+    return launch_moe_route(logits, T, E, k, ids, w, as_stream(stream));
+}
+
+extern "C" size_t lq_moe_workspace_size(int64_t T, int64_t k, int64_t n_experts) {
+    if (T < 0 || k <= 0 || n_experts <= 0) return 0;
+    return moe_ws_bytes(T, k, n_experts);
+}
+
+extern "C" lq_status lq_moe_q8_matvec_id(const lq_q8_weight* w, int64_t n_experts, const int8_t* x_qs,
+                                         const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids,
+                                         int64_t T, int64_t k, float* y, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    const char* fn = "lq_moe_q8_matvec_id";
+    lq_status st = check_moe_weight(fn, w, n_experts);
+    if (st != LQ_OK) return st;
+    if (T < 0 || k <= 0 || (x_per_slot != 0 && x_per_slot != 1))
+        return fail(LQ_ERR_SHAPE, "%s: T=%lld k=%lld x_per_slot=%d", fn, (long long)T, (long long)k, x_per_slot);
+    if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
+    if (T == 0 || w->rows == 0) return LQ_OK;
+    if (!x_qs || !x_d || !ids || !y) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(x_qs, 16) || !aligned(x_d, 2) || !aligned(ids, 4) || !aligned(y, 4))
+        return fail(LQ_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const size_t need = moe_ws_bytes(T, k, n_experts);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+    return launch_moe_matvec_id(w->qs, w->d, w->rows, w->cols, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y,
+                                workspace, as_stream(stream));
+}
+
+extern "C" lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
+                                         float* out, void* stream) {
+    if (T < 0 || k <= 0 || rows < 0)
+        return fail(LQ_ERR_SHAPE, "lq_moe_weighted_sum: T=%lld k=%lld rows=%lld", (long long)T, (long long)k,
+                    (long long)rows);
+    if (T == 0 || rows == 0) return LQ_OK;
+    if (!y || !w || !out) return fail(LQ_ERR_NULL, "lq_moe_weighted_sum: NULL pointer");
+    if (!aligned(y, 4) || !aligned(w, 4) || !aligned(out, 4))
+        return fail(LQ_ERR_ALIGN, "lq_moe_weighted_sum: misaligned pointer");
+    return launch_moe_weighted_sum(y, w, T, k, rows, out, as_stream(stream));
+}
+
+// ---- whole block ---------------------------------------------------------------
+namespace {
+struct MoeBuffers {
+    int32_t* ids; float* w; int8_t* xq; uint16_t* xd; float* y1; int8_t* hq; uint16_t* hd; float* y2;
+    void* gather;
+    size_t total;
+};
+
+MoeBuffers moe_layout(const lq_moe_desc* m, int64_t T, char* base, const lq_moe_taps* taps) {
+    const int64_t H = m->hidden, I = m->ffn, k = m->top_k, S = T * k;
+    MoeBuffers b{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += round_up(bytes, 256);
+        return p;
+    };
+    b.gather = take(moe_ws_bytes(T, k, m->n_experts));
+    b.ids = reinterpret_cast<int32_t*>(take(S * 4));
+    b.w = reinterpret_cast<float*>(take(S * 4));
+    b.xq = reinterpret_cast<int8_t*>(take(T * H));
+    b.xd = reinterpret_cast<uint16_t*>(take(T * (H / 32) * 2));
+    b.y1 = reinterpret_cast<float*>(take(S * 2 * I * 4));
+    b.hq = reinterpret_cast<int8_t*>(take(S * I));
+    b.hd = reinterpret_cast<uint16_t*>(take(S * (I / 32) * 2));
+    b.y2 = reinterpret_cast<float*>(take(S * H * 4));
+    b.total = off;
+    if (taps) {
+        if (taps->ids) b.ids = taps->ids;
+        if (taps->w) b.w = taps->w;
+        if (taps->xq) b.xq = taps->xq;
+        if (taps->xd) b.xd = taps->xd;
+        if (taps->y1) b.y1 = taps->y1;
+        if (taps->hq) b.hq = taps->hq;
+        if (taps->hd) b.hd = taps->hd;
+        if (taps->y2) b.y2 = taps->y2;
+    }
+    return b;
+}
+}  // namespace
+
+extern "C" size_t lq_moe_block_workspace_size(const lq_moe_desc* m, int64_t T) {
+    if (!m || T < 0 || m->top_k <= 0 || m->n_experts <= 0) return 0;
+    return moe_layout(m, T, nullptr, nullptr).total;
+}
+
+extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const float* logits, int64_t T,
+                                  float* out, const lq_moe_taps* taps, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    const char* fn = "lq_moe_block";
+    if (!m) return fail(LQ_ERR_NULL, "%s: descriptor is NULL", fn);
+    const int64_t H = m->hidden, I = m->ffn, E = m->n_experts, k = m->top_k;
+    if (T < 0 || H <= 0 || I <= 0 || H % 32 || I % 32 || k <= 0 || k > E)
+        return fail(LQ_ERR_SHAPE, "%s: T=%lld hidden=%lld ffn=%lld E=%lld k=%lld", fn, (long long)T, (long long)H,
+                    (long long)I, (long long)E, (long long)k);
+    if (m->w_gate_up.rows != 2 * I || m->w_gate_up.cols != H || m->w_down.rows != H || m->w_down.cols != I)
+        return fail(LQ_ERR_SHAPE, "%s: expert weight shapes do not match hidden/ffn", fn);
+    lq_status st = check_moe_weight(fn, &m->w_gate_up, E);
+    if (st == LQ_OK) st = check_moe_weight(fn, &m->w_down, E);
+    if (st != LQ_OK) return st;
+    if (E > 1024 || k > 32) return fail(LQ_ERR_UNSUPPORTED, "%s: E <= 1024 and k <= 32", fn);
+    if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
+    if (T == 0) return LQ_OK;
+    if (!x || !logits || !out) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(out, 4))
+        return fail(LQ_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+    const size_t need = moe_layout(m, T, nullptr, nullptr).total;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned), got %zu", fn, need,
+                    workspace_bytes);
+    MoeBuffers b = moe_layout(m, T, static_cast<char*>(workspace), taps);
+    hipStream_t s = as_stream(stream);
+    const int64_t S = T * k;
+    if ((st = launch_moe_route(logits, T, E, k, b.ids, b.w, s)) != LQ_OK) return st;
+    if ((st = launch_gather(b.ids, S, E, b.gather, b.y1, 2 * I, b.y2, H, s)) != LQ_OK) return st;
+    if ((st = launch_q8_quantize(x, T * (H / 32), b.xq, b.xd, s)) != LQ_OK) return st;
+    if ((st = launch_id_gathered(m->w_gate_up.qs, m->w_gate_up.d, 2 * I, H, E, b.xq, b.xd, 0, k, b.gather, b.y1,
+                                 s)) != LQ_OK)
+        return st;
+    if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
+    if ((st = launch_id_gathered(m->w_down.qs, m->w_down.d, H, I, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK)
+        return st;
+    return launch_moe_weighted_sum(b.y2, b.w, T, k, H, out, s);
+}

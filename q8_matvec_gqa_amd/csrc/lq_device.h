@@ -1,0 +1,137 @@
+// lq_device.h -- device helpers shared by the gfx950 kernels of liblq.
+//
+// Wavefront-64 reductions use DPP row permutes inside each 16-lane row and
+// gfx950's v_permlane16_swap / v_permlane32_swap across rows, so no LDS
+// round trip is needed for a full-wave reduction.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lq {
+
+constexpr int kWave = 64;
+
+// ---- number formats --------------------------------------------------------
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// v_cvt_f16_f32: round to nearest even, f16 subnormals kept (f16 denormals
+// are enabled in the default gfx950 FP mode).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// f32 -> bf16, round to nearest even on the bit pattern; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---- 16-byte loads ----------------------------------------------------------
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) 16-byte load for data read exactly once (weights).
+__device__ __forceinline__ int4 load_stream16(const void* p) {
+    const v4i_t v = __builtin_nontemporal_load(reinterpret_cast<const v4i_t*>(p));
+    return make_int4(v.x, v.y, v.z, v.w);
+}
+
+// ---- DPP / permlane --------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of N consecutive lanes (N = 2..64, power of two);
+// every lane of a group receives the group sum.  The mirror steps pair lanes
+// whose values are already equal across the sub-groups combined so far, so
+// they act as the xor-4 / xor-8 butterfly steps.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power of two");
+    if constexpr (N >= 2) v += dpp<kQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp<kQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp<kRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp<kRowMirror>(v);
+    if constexpr (N >= 32) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (N >= 64) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power of two");
+    if constexpr (N >= 2) v = fmaxf(v, dpp<kQuadXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp<kQuadXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp<kRowHalfMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp<kRowMirror>(v));
+    if constexpr (N >= 32) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (N >= 64) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+
+// ---- Q8_0 block quantization of 32 floats held by one lane ------------------
+// Scale d = amax/127 (correctly rounded float division), codes =
+// round-half-away-from-zero(x * (1/d)) clamped to [-127, 127], 0 for amax 0.
+// Writes 32 codes (two 16-byte stores) and the f16 scale bits.
+__device__ __forceinline__ void quantize_block32(const float (&v)[32], int8_t* __restrict__ qs,
+                                                 uint16_t* __restrict__ d) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float db = amax / 127.0f;
+    const float inv = (db != 0.0f) ? 1.0f / db : 0.0f;
+    uint32_t packed[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r = roundf(v[4 * w + j] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            word |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
+        }
+        packed[w] = word;
+    }
+    int4* q4 = reinterpret_cast<int4*>(qs);
+    q4[0] = make_int4((int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]);
+    q4[1] = make_int4((int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]);
+    *d = f32_to_f16(db);
+}
+
+__device__ __forceinline__ void load32(const float* __restrict__ p, float (&v)[32]) {
+    const float4* p4 = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float4 t = p4[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+}
+
+}  // namespace lq

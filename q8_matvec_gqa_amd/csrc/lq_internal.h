@@ -1,0 +1,77 @@
+// lq_internal.h -- host-side internals of liblq: error reporting and the
+// unchecked launchers that the public entry points and the composites
+// (decode layer, MoE block) share.  Every launcher assumes its arguments were
+// validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lq.h"
+
+namespace lq {
+
+// Records a thread-local message for lq_last_error() and returns s.
+lq_status fail(lq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Maps a pending HIP launch error to LQ_ERR_HIP.
+lq_status check_launch(const char* what);
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Validates an lq_q8_weight (pointers, cols % 32, alignment).
+lq_status check_weight(const lq_q8_weight* w, const char* name);
+
+// ---- launchers (k_quant.hip) ------------------------------------------------
+lq_status launch_q8_quantize(const float* x, int64_t n_blocks, int8_t* qs, uint16_t* d,
+                             hipStream_t s);
+lq_status launch_rmsnorm_q8(const float* x, int64_t n_rows, int64_t n, const float* gamma,
+                            float eps, int8_t* qs, uint16_t* d, hipStream_t s);
+lq_status launch_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn, int8_t* qs,
+                           uint16_t* d, hipStream_t s);
+// out = res + gamma * o / sqrt(mean(o^2) + eps) for one vector (n % 4 == 0).
+lq_status launch_rmsnorm_add(const float* o, int64_t n, const float* gamma, float eps, const float* res,
+                             float* out, hipStream_t s);
+
+// ---- launchers (k_matvec.hip) -----------------------------------------------
+lq_status launch_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                           const int8_t* xq, const uint16_t* xd, const float* residual, float* y,
+                           int32_t* dots, hipStream_t s);
+
+// ---- launchers (k_norm_rope.hip) ----------------------------------------------
+lq_status launch_rmsnorm_rope(float* x, int64_t n_heads, int64_t hd, int64_t head_stride,
+                              const float* gamma, float eps, const float* rope_cos,
+                              const float* rope_sin, int64_t pos, hipStream_t s);
+lq_status launch_kv_append(const float* k, const float* v, int64_t n_kv, int64_t hd, void* kc,
+                           void* vc, int32_t kv_dtype, int64_t head_stride, int64_t pos_stride,
+                           int64_t pos, hipStream_t s);
+// Decode-layer step after the QKV projection: per-head q/k RMSNorm (if
+// qk_norm) + NeoX RoPE in place on qkv, optional unit norm of v, then the
+// append of k and v at pos.
+lq_status launch_qkv_post(float* qkv, int64_t n_q, int64_t n_kv, int64_t hd, const float* g_q,
+                          const float* g_k, int32_t qk_norm, int32_t v_unit_norm, float eps,
+                          const float* rope_cos, const float* rope_sin, int64_t pos, void* kc,
+                          void* vc, int32_t kv_dtype, int64_t head_stride, int64_t pos_stride,
+                          hipStream_t s);
+
+// ---- launchers (k_attn.hip) ---------------------------------------------------
+bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype);
+size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len);
+lq_status launch_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd, const void* kc,
+                           const void* vc, int32_t kv_dtype, int64_t head_stride,
+                           int64_t pos_stride, int64_t start, int64_t len, float scale,
+                           float* out, void* ws, hipStream_t s);
+
+// ---- launchers (k_moe.hip) ----------------------------------------------------
+size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts);
+lq_status launch_moe_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
+                           float* w, hipStream_t s);
+lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                               int64_t n_experts, const int8_t* xq, const uint16_t* xd,
+                               int32_t x_per_slot, const int32_t* ids, int64_t T, int64_t k,
+                               float* y, void* ws, hipStream_t s);
+lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k,
+                                  int64_t rows, float* out, hipStream_t s);
+
+}  // namespace lq

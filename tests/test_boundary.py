@@ -1,0 +1,193 @@
+"""The C-ABI boundary without a GPU.
+
+* liblq.so loads and exports every function that include/lq.h declares,
+  and the Python binding covers exactly those names.
+* Argument validation runs on the host before any launch: every invalid
+  call returns its documented status and touches no device (fake, aligned
+  addresses are enough).  Zero-sized work returns LQ_OK with no launch.
+* The host-only helpers (GGML block packing, RoPE tables) run here and are
+  checked against numpy and the oracle.
+"""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lq.h")
+
+lq = pytest.importorskip("q8_matvec_gqa_amd")
+
+A = 0x10000   # a fake, 256-byte aligned device address: validation never dereferences it.
+# Every call below is invalid or empty, so none of them launches a kernel.
+S0 = 0        # explicit null stream: no torch.cuda involvement
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(lq_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert len(names) >= 20, names
+    lib = C.CDLL(lq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/lq.h but not exported"
+    assert sorted(lq.exported_names()) == names
+
+
+def test_status_strings():
+    assert lq.lq_version() >= 1
+    for s in range(7):
+        assert lq.lq_status_string(s)
+    assert lq.lq_status_string(99) == "unknown status"
+
+
+def st(fn, *args, **kw):
+    return fn(*args, stream=S0, check=False, **kw)
+
+
+def test_quantize_validation():
+    assert st(lq.lq_q8_quantize_act, A, 1, 33, A, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q8_quantize_act, A, -1, 32, A, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q8_quantize_act, None, 1, 32, A, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q8_quantize_act, A + 4, 1, 32, A, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q8_quantize_act, A, 0, 32, None, None) == lq.LQ_OK        # empty: no launch
+    assert st(lq.lq_rmsnorm_q8, A, 1, 64, A + 4, 1e-6, A, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_rmsnorm_q8, A, 1, 64, A, -1.0, A, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_swiglu_q8, A, 1, 48, A, A) == lq.LQ_ERR_SHAPE
+
+
+def test_matvec_validation():
+    w = lq.lq_q8_weight(A, A, 10, 64)
+    assert st(lq.lq_q8_matvec, None, A, A, None, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q8_matvec, lq.lq_q8_weight(A, A, 10, 48), A, A, None, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q8_matvec, lq.lq_q8_weight(A + 8, A, 10, 64), A, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q8_matvec, w, A + 1, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q8_matvec, w, A, A, None, None) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q8_matvec, lq.lq_q8_weight(None, None, 0, 64), None, None, None, None) == lq.LQ_OK
+    assert st(lq.lq_q8_block_dots, w, A, None) == lq.LQ_ERR_NULL
+
+
+def test_norm_rope_kv_validation():
+    assert st(lq.lq_rmsnorm_rope, A, 4, 63, 63, None, 1e-6, None, None, 0, 0) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_rmsnorm_rope, A, 4, 1024, 1024, None, 1e-6, None, None, 0, 0) == lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_rmsnorm_rope, A, 4, 64, 32, None, 1e-6, None, None, 0, 0) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_rmsnorm_rope, A, 4, 64, 64, None, 1e-6, A, None, 10, 0) == lq.LQ_ERR_NULL
+    assert st(lq.lq_rmsnorm_rope, A, 4, 64, 64, None, 1e-6, A, A, 10, 10) == lq.LQ_ERR_SHAPE   # pos past the table
+    assert st(lq.lq_rmsnorm_rope, A, 0, 64, 64, None, 1e-6, None, None, 0, 0) == lq.LQ_OK
+    assert st(lq.lq_kv_append, A, A, 2, 64, A, A, 7, 64 * 8, 64, 8, 0) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_kv_append, A, A, 2, 64, A, A, 1, 64 * 8, 32, 8, 0) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_kv_append, A, A, 2, 64, A, A, 1, 64 * 8, 64, 8, 8) == lq.LQ_ERR_SHAPE     # pos past the cache
+
+
+def test_attention_validation():
+    def call(n_q=8, n_kv=2, hd=64, dtype=1, hs=64 * 100, ps=64, max_ctx=100, start=0, length=100,
+             ws=A, wsb=1 << 20):
+        return st(lq.lq_gqa_decode_attn, A, n_q, n_kv, hd, A, A, dtype, hs, ps, max_ctx, start, length,
+                  0.125, A, ws, wsb)
+    assert call(n_q=7) == lq.LQ_ERR_SHAPE                      # INV-3
+    assert call(hd=66, ps=66, hs=6600) == lq.LQ_ERR_SHAPE      # INV-2
+    assert call(start=50, length=51) == lq.LQ_ERR_SHAPE        # window past the allocation
+    assert call(start=-1, length=10) == lq.LQ_ERR_SHAPE
+    assert call(hd=1024, ps=1024, hs=102400) == lq.LQ_ERR_UNSUPPORTED
+    assert call(n_q=18, n_kv=2) == lq.LQ_ERR_UNSUPPORTED       # G = 9
+    assert call(hd=68, ps=68, hs=6800) == lq.LQ_ERR_UNSUPPORTED   # bf16 needs head_dim % 8
+    assert call(ps=60) == lq.LQ_ERR_SHAPE
+    assert call(dtype=1, ps=68, hs=6800) == lq.LQ_ERR_ALIGN    # 136-byte rows are not 16-byte multiples
+    need = lq.lq_gqa_decode_attn_workspace_size(32, 8, 128, 8192)
+    assert need > 0
+    assert st(lq.lq_gqa_decode_attn, A, 32, 8, 128, A, A, 1, 128 * 8192, 128, 8192, 0, 8192, 0.1, A,
+              A, need - 1) == lq.LQ_ERR_WORKSPACE
+    assert st(lq.lq_gqa_decode_attn, A, 32, 8, 128, A, A, 1, 128 * 8192, 128, 8192, 0, 8192, 0.1, A,
+              None, need) == lq.LQ_ERR_WORKSPACE
+    # workspace need grows with the attended length (the layer sizes it for the longest window)
+    sizes = [lq.lq_gqa_decode_attn_workspace_size(32, 8, 128, n) for n in (1, 64, 1000, 4096, 8192, 65536)]
+    assert sizes == sorted(sizes)
+
+
+def test_moe_validation():
+    w = lq.lq_q8_weight(A, A, 1408, 2816)
+    wsb = lq.lq_moe_workspace_size(16, 8, 128)
+    assert wsb > 0
+    assert st(lq.lq_moe_route_topk, A, 16, 128, 0, A, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_route_topk, A, 16, 128, 129, A, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_route_topk, A, 16, 2048, 8, A, A) == lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_moe_q8_matvec_id, w, 128, A, A, 2, A, 16, 8, A, A, wsb) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_q8_matvec_id, w, 128, A, A, 0, A, 16, 8, A, A, wsb - 4) == lq.LQ_ERR_WORKSPACE
+    assert st(lq.lq_moe_q8_matvec_id, w, 0, A, A, 0, A, 16, 8, A, A, wsb) == lq.LQ_ERR_UNSUPPORTED
+    d = lq.lq_moe_desc(2816, 704, 128, 8, lq.lq_q8_weight(A, A, 1408, 2816), lq.lq_q8_weight(A, A, 2816, 704))
+    need = lq.lq_moe_block_workspace_size(d, 16)
+    assert need > 0
+    assert st(lq.lq_moe_block, d, A, A, 16, A, None, A, need - 1) == lq.LQ_ERR_WORKSPACE
+    bad = lq.lq_moe_desc(2816, 704, 128, 8, lq.lq_q8_weight(A, A, 1400, 2816), lq.lq_q8_weight(A, A, 2816, 704))
+    assert st(lq.lq_moe_block, bad, A, A, 16, A, None, A, need) == lq.LQ_ERR_SHAPE
+
+
+def _layer_desc(**over):
+    H, nq, nkv, hd, I, ctx = 4096, 32, 8, 128, 12288, 8192
+    d = lq.lq_layer_desc(
+        hidden=H, n_q=nq, n_kv=nkv, head_dim=hd, ffn=I, max_ctx=ctx, window=0, eps=1e-6,
+        attn_scale=1 / math.sqrt(hd), kind=0, kv_dtype=1, qk_norm=1, v_unit_norm=0,
+        w_qkv=lq.lq_q8_weight(A, A, nq * hd + 2 * nkv * hd, H), w_o=lq.lq_q8_weight(A, A, H, nq * hd),
+        w_gate_up=lq.lq_q8_weight(A, A, 2 * I, H), w_down=lq.lq_q8_weight(A, A, H, I),
+        g_in=A, g_q=A, g_k=A, g_post=A, k_cache=A, v_cache=A, rope_cos=A, rope_sin=A)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_layer_validation():
+    d = _layer_desc()
+    need = lq.lq_decode_layer_workspace_size(d)
+    assert need > 0
+    call = lambda desc, pos=8191, wsb=need, ws=A: st(lq.lq_decode_layer, desc, A, pos, None, ws, wsb)
+    assert call(d, wsb=need - 1) == lq.LQ_ERR_WORKSPACE
+    assert call(d, ws=A + 16) == lq.LQ_ERR_WORKSPACE          # workspace must be 256-byte aligned
+    assert call(d, pos=8192) == lq.LQ_ERR_SHAPE
+    assert call(_layer_desc(n_q=30)) == lq.LQ_ERR_SHAPE       # 30 % 8
+    assert call(_layer_desc(kind=5)) == lq.LQ_ERR_SHAPE
+    assert call(_layer_desc(w_o=lq.lq_q8_weight(A, A, 4096, 4000))) == lq.LQ_ERR_SHAPE
+    assert call(_layer_desc(ffn=12300)) == lq.LQ_ERR_SHAPE
+    assert call(_layer_desc(g_in=None)) == lq.LQ_ERR_NULL
+    assert call(_layer_desc(rope_cos=None)) == lq.LQ_ERR_NULL
+    assert call(_layer_desc(k_cache=A + 2)) == lq.LQ_ERR_ALIGN
+    assert call(_layer_desc(window=-1)) == lq.LQ_ERR_SHAPE
+    assert lq.lq_decode_layer_workspace_size(None) == 0
+
+
+def test_pack_ggml_host():
+    rng = np.random.default_rng(0)
+    rows, cols = 5, 96
+    qs = rng.integers(-128, 128, size=(rows, cols), dtype=np.int8)
+    d = rng.integers(0, 1 << 16, size=(rows, cols // 32), dtype=np.uint16)
+    blocks = np.zeros((rows * cols // 32, 34), dtype=np.uint8)
+    blocks[:, 0:2] = d.reshape(-1, 1).view(np.uint8).reshape(-1, 2)   # little-endian f16 scale
+    blocks[:, 2:] = qs.reshape(-1, 32).view(np.uint8)
+    out_qs = np.zeros_like(qs)
+    out_d = np.zeros_like(d)
+    lq.lq_q8_pack_ggml(blocks, rows, cols, out_qs, out_d)
+    assert np.array_equal(out_qs, qs) and np.array_equal(out_d, d)
+    assert lq.lq_q8_pack_ggml(blocks, rows, 33, out_qs, out_d, check=False) == lq.LQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("hd", [64, 80, 128, 256, 512])
+def test_rope_table_host(hd):
+    ctx, theta = 8192, 1e6
+    c = np.zeros((ctx, hd // 2), np.float32)
+    s = np.zeros((ctx, hd // 2), np.float32)
+    lq.lq_rope_table(ctx, hd, theta, c, s)
+    oc, os_ = oracle.rope_table(ctx, hd, theta)
+    # the two tables are independent double-precision evaluations rounded to
+    # float; they may differ in the last float bit
+    assert np.abs(c.astype(np.float64) - oc).max() <= 2 ** -23
+    assert np.abs(s.astype(np.float64) - os_).max() <= 2 ** -23
+    assert lq.lq_rope_table(ctx, 63, theta, c, s, check=False) == lq.LQ_ERR_SHAPE

@@ -1,0 +1,310 @@
+"""Per-operation parity of the HIP path (through the C ABI) with the oracle.
+
+Bar: integer work (Q8_0 codes and scales from identical float inputs, int32
+block dots, MoE ids) bit-exact; float outputs within |gpu - ref| <=
+max(1e-3 |ref|, 1e-4).  Quantized codes of float values that the two sides
+compute in different rounding orders use the near-boundary rule of
+tests/lqtest.py.  Sizes span several tiles with ragged tails, plus the
+workloads' full shapes.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+lq = pytest.importorskip("q8_matvec_gqa_amd")
+from lqtest import (assert_close, assert_q8_near, dev, empty, host, sync, torch_mod,  # noqa: E402
+                    workspace)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ------------------------------------------------------------------ quantize
+def test_quantize_golden_blocks():
+    from test_oracle_pins import load_golden_blocks
+    cases = load_golden_blocks()
+    x = np.concatenate([c["x"] for c in cases])
+    xq, xd = empty(x.size, np.int8), empty(x.size // 32, np.uint16)
+    lq.lq_q8_quantize_act(dev(x), 1, x.size, xq, xd)
+    sync()
+    assert np.array_equal(host(xq), np.concatenate([c["q"] for c in cases]))
+    assert np.array_equal(host(xd, np.uint16), np.array([c["d"] for c in cases], np.uint16))
+
+
+@pytest.mark.parametrize("n_rows,n,scale", [(1, 32, 1.0), (3, 4096, 1.0), (7, 12288, 1.0),
+                                            (5, 9728, 1e-3), (2, 2816, 3e-6), (1, 64 * 1000 + 32, 50.0)])
+def test_quantize_bit_exact(n_rows, n, scale):
+    x = (synthetic.activations(rng(n), n_rows, n) * np.float32(scale)).astype(np.float32)
+    x[0, :32] = 0.0                                             # an all-zero block
+    xq, xd = empty((n_rows, n), np.int8), empty((n_rows, n // 32), np.uint16)
+    lq.lq_q8_quantize_act(dev(x), n_rows, n, xq, xd)
+    sync()
+    rq, rd = oracle.q8_quantize(x)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xd, np.uint16), rd)   # includes f16-subnormal scales at scale 3e-6
+
+
+@pytest.mark.parametrize("n_rows,n", [(1, 1024), (1, 4096), (2, 2816), (3, 2560)])
+def test_rmsnorm_q8(n_rows, n):
+    r = rng(100 + n)
+    x = synthetic.activations(r, n_rows, n) * 3
+    g = synthetic.gamma(r, n)
+    xq, xd = empty((n_rows, n), np.int8), empty((n_rows, n // 32), np.uint16)
+    lq.lq_rmsnorm_q8(dev(x), n_rows, n, dev(g), 1e-6, xq, xd)
+    sync()
+    for i in range(n_rows):
+        ref = oracle.rmsnorm(x[i], g, 1e-6)
+        assert_q8_near(host(xq)[i], host(xd, np.uint16)[i], ref, f"row {i}")
+    lq.lq_rmsnorm_q8(dev(x), n_rows, n, None, 1e-6, xq, xd)    # unit-weight form
+    sync()
+    for i in range(n_rows):
+        assert_q8_near(host(xq)[i], host(xd, np.uint16)[i], oracle.rmsnorm(x[i], None, 1e-6), f"unit {i}")
+
+
+@pytest.mark.parametrize("n_rows,ffn", [(1, 3072), (1, 12288), (128, 704), (3, 96)])
+def test_swiglu_q8(n_rows, ffn):
+    gu = synthetic.activations(rng(ffn + n_rows), n_rows, 2 * ffn) * 2
+    hq, hd = empty((n_rows, ffn), np.int8), empty((n_rows, ffn // 32), np.uint16)
+    lq.lq_swiglu_q8(dev(gu), n_rows, ffn, hq, hd)
+    sync()
+    for i in range(n_rows):
+        ref = oracle.silu_mul(gu[i, :ffn], gu[i, ffn:])
+        assert_q8_near(host(hq)[i], host(hd, np.uint16)[i], ref, f"row {i}")
+
+
+# ------------------------------------------------------------------ block dots / matvec
+DOT_SHAPES = [(1, 32), (3, 64), (5, 1024), (37, 1056), (64, 2560), (9, 2816), (17, 4096), (4, 9728),
+              (13, 12288), (3, 16384), (2, 17408)]     # 17408 > 16 KB: the generic path
+
+
+@pytest.mark.parametrize("rows,cols", DOT_SHAPES)
+def test_block_dots_bit_exact(rows, cols):
+    r = rng(rows * 7 + cols)
+    wq = r.integers(-128, 128, size=(rows, cols), dtype=np.int8)
+    wq[0, :32] = -128                                     # extreme block: 524288
+    xq = r.integers(-127, 128, size=cols, dtype=np.int8)
+    xq[:32] = -128
+    wd = np.zeros((rows, cols // 32), np.uint16)
+    dots = empty((rows, cols // 32), np.int32)
+    lq.lq_q8_block_dots(lq.q8_weight(dev(wq), dev(wd)), dev(xq), dots)
+    sync()
+    ref = oracle.q8_block_dots(wq, xq)
+    assert ref[0, 0] == 524288
+    assert np.array_equal(host(dots), ref)
+
+
+MATVEC_SHAPES = DOT_SHAPES[1:] + [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288),
+                                  (10240, 2816), (2816, 8192), (1, 4096), (255, 3072)]
+
+
+@pytest.mark.parametrize("rows,cols", MATVEC_SHAPES)
+def test_matvec(rows, cols):
+    r = rng(rows + 3 * cols)
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    x = synthetic.activations(r, cols)
+    xq, xd = oracle.q8_quantize(x)
+    res = synthetic.activations(r, rows)
+    W = lq.q8_weight(dev(wq), dev(wd))
+    y = empty(rows, np.float32)
+    lq.lq_q8_matvec(W, dev(xq), dev(xd), None, y)
+    y_res = dev(res)
+    lq.lq_q8_matvec(W, dev(xq), dev(xd), y_res, y_res)        # y aliases residual
+    sync()
+    assert_close(host(y), oracle.q8_matvec(wq, wd, xq, xd), "matvec")
+    assert_close(host(y_res), oracle.q8_matvec(wq, wd, xq, xd, residual=res), "matvec+residual")
+
+
+def test_matvec_deterministic():
+    r = rng(5)
+    wq, wd = synthetic.q8_weight(r, 24576, 4096)
+    xq, xd = oracle.q8_quantize(synthetic.activations(r, 4096))
+    W = lq.q8_weight(dev(wq), dev(wd))
+    a, b = empty(24576, np.float32), empty(24576, np.float32)
+    lq.lq_q8_matvec(W, dev(xq), dev(xd), None, a)
+    lq.lq_q8_matvec(W, dev(xq), dev(xd), None, b)
+    sync()
+    assert np.array_equal(host(a), host(b))
+
+
+# ------------------------------------------------------------------ norm + RoPE, KV append
+@pytest.mark.parametrize("n_heads,hd,stride,use_gamma,use_rope,pos", [
+    (16, 64, 64, True, True, 127), (32, 80, 96, True, True, 2047), (32, 128, 128, True, True, 8191),
+    (8, 256, 256, False, True, 5000), (2, 512, 520, True, False, 0), (3, 2, 2, True, True, 7)])
+def test_rmsnorm_rope(n_heads, hd, stride, use_gamma, use_rope, pos):
+    r = rng(hd + pos)
+    x = synthetic.activations(r, n_heads * stride) * 2
+    g = synthetic.gamma(r, hd) if use_gamma else None
+    ctx = pos + 1
+    c = np.zeros((ctx, hd // 2), np.float32)
+    s = np.zeros((ctx, hd // 2), np.float32)
+    lq.lq_rope_table(ctx, hd, 1e6, c, s)
+    xt = dev(x)
+    lq.lq_rmsnorm_rope(xt, n_heads, hd, stride, None if g is None else dev(g), 1e-6,
+                       dev(c) if use_rope else None, dev(s) if use_rope else None, ctx, pos)
+    sync()
+    got = host(xt)
+    oc, os_ = oracle.rope_table(ctx, hd, 1e6)
+    want = x.copy()
+    for h in range(n_heads):
+        v = oracle.rmsnorm(x[h * stride:h * stride + hd], g, 1e-6)
+        if use_rope:
+            v = oracle.rope_neox(v, oc[pos], os_[pos])
+        want[h * stride:h * stride + hd] = v
+    assert_close(got, want, "rmsnorm_rope")     # includes the untouched gaps between heads
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_kv_append(dtype):
+    r = rng(11 + dtype)
+    n_kv, hd, ctx, pos = 8, 128, 64, 37
+    kc = synthetic.kv_cache(r, n_kv, ctx, hd, dtype)
+    vc = synthetic.kv_cache(r, n_kv, ctx, hd, dtype)
+    k = synthetic.activations(r, n_kv * hd)
+    v = synthetic.activations(r, n_kv * hd)
+    kt, vt = dev(kc), dev(vc)
+    lq.lq_kv_append(dev(k), dev(v), n_kv, hd, kt, vt, dtype, ctx * hd, hd, ctx, pos)
+    sync()
+    dt = np.float32 if dtype == 0 else np.uint16
+    gk, gv = host(kt, dt), host(vt, dt)
+    ek, ev = kc.copy(), vc.copy()
+    conv = (lambda a: a) if dtype == 0 else oracle.f32_to_bf16
+    ek[:, pos] = conv(k).reshape(n_kv, hd)
+    ev[:, pos] = conv(v).reshape(n_kv, hd)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+
+
+# ------------------------------------------------------------------ attention
+def run_attn(q, n_q, n_kv, hd, kc, vc, dtype, hs, ps, max_ctx, start, length, scale):
+    out = empty(n_q * hd, np.float32)
+    need = lq.lq_gqa_decode_attn_workspace_size(n_q, n_kv, hd, length)
+    ws = workspace(need)
+    lq.lq_gqa_decode_attn(dev(q), n_q, n_kv, hd, dev(kc), dev(vc), dtype, hs, ps, max_ctx, start, length,
+                          scale, out, ws, ws.numel())
+    sync()
+    return host(out)
+
+
+ATTN_CASES = [
+    # n_q, n_kv, hd, dtype, ctx, start, len
+    (16, 8, 64, 0, 128, 0, 128),          # tiny layer shape
+    (32, 8, 80, 1, 2048, 0, 2048),        # 4B-like
+    (32, 8, 128, 1, 8192, 0, 8192),       # 8B-like (headline)
+    (16, 8, 256, 1, 8192, 7168, 1024),    # Gemma sliding: window with start > 0
+    (16, 2, 512, 1, 8192, 0, 8192),       # Gemma global
+    (32, 8, 128, 1, 300, 0, 1),           # one position
+    (32, 8, 128, 1, 300, 0, 63), (32, 8, 128, 1, 300, 0, 65), (32, 8, 128, 1, 3000, 1, 2999),
+    (8, 8, 64, 1, 200, 10, 150),          # G = 1 (generic instance)
+    (20, 4, 64, 1, 500, 3, 333),          # G = 5 (generic instance)
+    (16, 2, 128, 1, 1000, 0, 1000),       # G = 8
+    (8, 2, 96, 0, 700, 100, 555),         # f32, head_dim 96 (generic)
+    (8, 2, 512, 0, 200, 0, 200),          # f32, head_dim 512 (two chunks per lane in V)
+    (4, 4, 8, 1, 130, 0, 130),            # head_dim 8: one 16-byte chunk per row
+]
+
+
+@pytest.mark.parametrize("n_q,n_kv,hd,dtype,ctx,start,length", ATTN_CASES)
+def test_attention(n_q, n_kv, hd, dtype, ctx, start, length):
+    r = rng(n_q * hd + ctx + start)
+    kc = synthetic.kv_cache(r, n_kv, ctx, hd, dtype)
+    vc = synthetic.kv_cache(r, n_kv, ctx, hd, dtype)
+    q = synthetic.activations(r, n_q * hd)
+    scale = 1 / math.sqrt(hd)
+    got = run_attn(q, n_q, n_kv, hd, kc, vc, dtype, ctx * hd, hd, ctx, start, length, scale)
+    want = oracle.attention(q, n_q, n_kv, hd, kc, vc, dtype, ctx * hd, hd, start, length, scale)
+    assert_close(got, want, "attention")
+
+
+def test_attention_strided_layout():
+    """Cache laid out [ctx, n_kv, hd]: head stride hd, position stride n_kv*hd."""
+    r = rng(77)
+    n_q, n_kv, hd, ctx = 32, 8, 128, 1500
+    kc = synthetic.kv_cache(r, ctx, n_kv, hd, 1)
+    vc = synthetic.kv_cache(r, ctx, n_kv, hd, 1)
+    q = synthetic.activations(r, n_q * hd)
+    got = run_attn(q, n_q, n_kv, hd, kc, vc, 1, hd, n_kv * hd, ctx, 200, 1300, 0.1)
+    want = oracle.attention(q, n_q, n_kv, hd, kc, vc, 1, hd, n_kv * hd, 200, 1300, 0.1)
+    assert_close(got, want, "attention strided")
+
+
+def test_attention_empty_window_writes_zeros():
+    out = dev(np.full(64 * 4, 7.0, np.float32))
+    lq.lq_gqa_decode_attn(dev(np.zeros(256, np.float32)), 4, 2, 64, None, None, 1, 64 * 10, 64, 10, 0, 0,
+                          0.125, out, None, 0)
+    sync()
+    assert np.all(host(out) == 0)
+
+
+def test_attention_deterministic():
+    r = rng(3)
+    n_q, n_kv, hd, ctx = 32, 8, 128, 8192
+    kc = synthetic.kv_cache(r, n_kv, ctx, hd, 1)
+    vc = synthetic.kv_cache(r, n_kv, ctx, hd, 1)
+    q = synthetic.activations(r, n_q * hd)
+    a = run_attn(q, n_q, n_kv, hd, kc, vc, 1, ctx * hd, hd, ctx, 0, ctx, 0.088)
+    b = run_attn(q, n_q, n_kv, hd, kc, vc, 1, ctx * hd, hd, ctx, 0, ctx, 0.088)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ MoE pieces
+def test_moe_route():
+    r = rng(21)
+    logits = synthetic.activations(r, 16, 128)
+    logits[5, 7] = logits[5, 100] = 4.0                    # tie: lower id first
+    ids, w = empty((16, 8), np.int32), empty((16, 8), np.float32)
+    lq.lq_moe_route_topk(dev(logits), 16, 128, 8, ids, w)
+    sync()
+    rid, rw = oracle.moe_route(logits, 8)
+    assert np.array_equal(host(ids), rid)
+    assert host(ids)[5, 0] == 7 and host(ids)[5, 1] == 100
+    assert_close(host(w), rw, "route weights")
+
+
+def test_moe_matvec_id_and_weighted_sum():
+    r = rng(22)
+    E, rows, cols, T, k = 12, 200, 704, 5, 3
+    wq, wd = synthetic.q8_weight(r, E * rows, cols)
+    wq, wd = wq.reshape(E, rows, cols), wd.reshape(E, rows, cols // 32)
+    x = synthetic.activations(r, T * k, cols)
+    xq, xd = oracle.q8_quantize(x)
+    ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[0, 0] = ids[1, 0] = ids[2, 1] = 4                   # an expert with several slots
+    ids[4, 2] = 99                                          # out of range: zeros and counted
+    ids[3, 1] = -1
+    wqt, wdt = dev(wq), dev(wd)
+    W = lq.lq_q8_weight(wqt.data_ptr(), wdt.data_ptr(), rows, cols)
+    y = dev(np.full((T * k, rows), 5.0, np.float32))
+    ws = workspace(lq.lq_moe_workspace_size(T, k, E))
+    for per_slot in (1, 0):
+        xrows = slice(None) if per_slot else slice(0, T * k, k)    # per token: rows 0, k, 2k, ...
+        xq_use = xq if per_slot else np.ascontiguousarray(xq[xrows])
+        xd_use = xd if per_slot else np.ascontiguousarray(xd[xrows])
+        lq.lq_moe_q8_matvec_id(W, E, dev(xq_use), dev(xd_use), per_slot, dev(ids), T, k, y, ws, ws.numel())
+        sync()
+        got = host(y).reshape(T, k, rows)
+        for t in range(T):
+            for s in range(k):
+                e = ids[t, s]
+                xi = t * k + s if per_slot else t
+                if 0 <= e < E:
+                    ref = oracle.q8_matvec(wq[e], wd[e], xq_use[xi if per_slot else t], xd_use[xi if per_slot else t])
+                    assert_close(got[t, s], ref, f"slot {t},{s}")
+                else:
+                    assert np.all(got[t, s] == 0)
+        assert host(ws[:4].view(dtype=torch_mod().int32))[0] == 2     # invalid-id counter
+    # weighted sum over slots, slots in order
+    wts = synthetic.activations(r, T, k)
+    out = empty((T, rows), np.float32)
+    lq.lq_moe_weighted_sum(y, dev(wts), T, k, rows, out)
+    sync()
+    want = np.einsum("ts,tsr->tr", wts.astype(np.float64), host(y).reshape(T, k, rows).astype(np.float64))
+    assert_close(host(out), want, "weighted sum")
