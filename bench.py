@@ -128,84 +128,56 @@ def time_stack(layers, xs, pos, steps, warmup, torch):
     return start.elapsed_time(end) / steps, eager_ms
 
 
-def time_launches(fns, torch, rounds):
-    """Per-launch HIP-event timing on the current stream (the one the library
-    launches on).  fns: list of (tag, callable).  Returns {tag: [ms, ...]}."""
-    out = {}
-    for _ in range(rounds):
-        evs = []
-        for tag, fn in fns:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            evs.append((tag, a, b))
-        torch.cuda.synchronize()
-        for tag, a, b in evs:
-            out.setdefault(tag, []).append(a.elapsed_time(b))
-    return out
-
-
-def kernel_measurements(cfg, layers, torch, rounds):
-    import q8_matvec_gqa_amd as lq
+def layer_kernels(cfg, nsplit_used):
+    """Names and algorithmic bytes of the kernels the decode layer launches,
+    in launch order (matching lq_decode_layer_timed's events)."""
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
     es = 4 if cfg["kv_dtype"] == 0 else 2
     pos = cfg["pos"]
-    start = max(0, pos - cfg["window"] + 1) if cfg["window"] else 0
-    L = pos - start + 1
-    # matvec launches exactly as the layer makes them (same entry, same shapes)
-    shapes = [("qkv", nq * hd + 2 * nkv * hd, H, False), ("o", H, nq * hd, True)]
-    if I:
-        shapes += [("gate_up", 2 * I, H, False), ("down", H, I, True)]
-    scratch = {}
-    fns = []
-    for li, lay in enumerate(layers):
-        t = lay.t
-        for tag, rows, cols, res in shapes:
-            key = {"qkv": "qkv", "o": "o", "gate_up": "gu", "down": "dn"}[tag]
-            W = lq.q8_weight(t[key + "_qs"], t[key + "_d"])
-            if cols not in scratch:
-                scratch[cols] = (torch.randint(-127, 128, (cols,), dtype=torch.int8, device="cuda"),
-                                 (torch.rand(cols // 32, device="cuda") * 0.01 + 0.001).half().view(torch.int16))
-            xq, xd = scratch[cols]
-            y = torch.empty(rows, device="cuda")
-            r = torch.zeros(rows, device="cuda") if res else None
-            fns.append((f"matvec:{tag}", (lambda W=W, xq=xq, xd=xd, r=r, y=y:
-                                          lq.lq_q8_matvec(W, xq, xd, r, y))))
-    # attention launches as the layer makes them
-    ws_need = lq.lq_gqa_decode_attn_workspace_size(nq, nkv, hd, L)
-    ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device="cuda")
-    q = torch.randn(nq * hd, device="cuda")
-    o = torch.empty(nq * hd, device="cuda")
-    for lay in layers:
-        kc, vc = lay.t["k_cache"], lay.t["v_cache"]
-        fns.append(("attn", (lambda kc=kc, vc=vc: lq.lq_gqa_decode_attn(
-            q, nq, nkv, hd, kc, vc, cfg["kv_dtype"], cfg["max_ctx"] * hd, hd, cfg["max_ctx"], start, L,
-            cfg["attn_scale"], o, ws, ws.numel()))))
-    for tag, fn in fns[: len(fns)]:          # warm every launch once
-        fn()
+    L = min(cfg["window"], pos + 1) if cfg["window"] else pos + 1
+    qkv_rows = nq * hd + 2 * nkv * hd
+    q8w = lambda r, c: r * c * 34 // 32
+    ks = [("qkv_matvec", "k_mv<NCH=%d,NORM,STORE>" % math.ceil(H / 1024),
+           q8w(qkv_rows, H) + 8 * H + 4 * qkv_rows),
+          ("attn_split", "k_attn_split", attn_bytes(nq, nkv, hd, L, es) + 4 * qkv_rows)]
+    if nsplit_used:
+        ks.append(("attn_combine", "k_attn_combine", 0))
+    if cfg["kind"] == 0:
+        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 8 * H),
+               ("gate_up_matvec", "k_mv<NCH=%d,NORM,SWIGLU>" % math.ceil(H / 1024), q8w(2 * I, H) + 8 * H + 4 * I),
+               ("down_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(I / 1024), q8w(H, I) + 4 * I + 8 * H)]
+    else:
+        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,STORE>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 4 * H),
+               ("post_norm_add", "k_rmsnorm_add", 16 * H)]
+    return ks
+
+
+def kernel_measurements(cfg, layers, xs, torch, rounds):
+    """Times every kernel of the decode layer with start/stop HIP events that
+    the runtime stamps at each dispatch of the layer (lq_decode_layer_timed),
+    on the stream the layer runs on."""
+    import q8_matvec_gqa_amd as lq
+    n_k = lq.lq_decode_layer_kernel_count(layers[0].desc)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_k)]
+    for e in evs:
+        e.record()
     torch.cuda.synchronize()
-    times = time_launches(fns, torch, rounds)
+    names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5))
+    assert len(names) == n_k, (len(names), n_k)
+    times = [[] for _ in range(n_k)]
+    for r in range(rounds + 1):
+        for li, lay in enumerate(layers):
+            lq.lq_decode_layer_timed(lay.desc, xs[li], cfg["pos"], None, lay.ws, lay.ws_bytes, evs)
+            torch.cuda.synchronize()
+            if r == 0:
+                continue                      # warm round
+            for k in range(n_k):
+                times[k].append(evs[2 * k].elapsed_time(evs[2 * k + 1]) * 1e3)
     per = {}
-    for tag, ts in times.items():
-        if tag.startswith("matvec:"):
-            name = tag.split(":")[1]
-            rows, cols, res = [(r_, c_, s_) for t_, r_, c_, s_ in shapes if t_ == name][0]
-            b = matvec_bytes(rows, cols, res)
-            kernel = f"k_q8_matvec<NCH={math.ceil(cols / 1024)}>"
-        else:
-            b = attn_bytes(nq, nkv, hd, L, es)
-            kernel = "k_attn_split+k_attn_combine"
-        per[tag] = dict(kernel=kernel, launches=len(ts), avg_us=1e3 * float(np.mean(ts)),
-                        min_us=1e3 * float(np.min(ts)), bytes=b)
-    # group by kernel instance, as a profiler aggregates by kernel name
-    groups = {}
-    for tag, p in per.items():
-        g_ = groups.setdefault(p["kernel"], dict(launches=0, time_us=0.0, bytes=0))
-        g_["launches"] += p["launches"]
-        g_["time_us"] += p["avg_us"] * p["launches"]
-        g_["bytes"] += p["bytes"] * p["launches"]
-    return per, groups
+    for (tag, kernel, b), ts in zip(names, times):
+        per[tag] = dict(kernel=kernel, launches=len(ts), avg_us=float(np.mean(ts)), min_us=float(np.min(ts)),
+                        bytes=int(b))
+    return per
 
 
 def cpu_baseline(workload, seconds):
@@ -262,18 +234,19 @@ def main():
     ms_step, eager_ms = time_stack(layers, xs, cfg["pos"], args.steps, args.warmup, torch)
     us_layer = ms_step * 1e3 / R
     log(f"{us_layer:.2f} us/token/layer (graph), eager {eager_ms * 1e3 / R:.2f}")
-    per, groups = kernel_measurements(cfg, layers, torch, args.rounds)
-    dom = max((g for g in groups if g.startswith("k_q8_matvec")), key=lambda g: groups[g]["time_us"])
-    gd = groups[dom]
-    dom_bytes = gd["bytes"] / gd["launches"]
-    dom_us = gd["time_us"] / gd["launches"]
-    dom_gbs = dom_bytes / dom_us / 1e3
-    ga = groups["k_attn_split+k_attn_combine"]
-    at_us = ga["time_us"] / ga["launches"]
-    at_gbs = (ga["bytes"] / ga["launches"]) / at_us / 1e3
-    for tag, p in sorted(per.items()):
-        log(f"{tag:16s} {p['avg_us']:8.2f} us avg ({p['min_us']:.2f} min) "
-            f"{p['bytes'] / p['avg_us'] / 1e3:8.1f} GB/s")
+    per = kernel_measurements(cfg, layers, xs, torch, args.rounds)
+    dom_tag = "gate_up_matvec" if "gate_up_matvec" in per else "qkv_matvec"
+    dom = per[dom_tag]
+    dom_gbs = dom["bytes"] / (dom["avg_us"] * 1e3)
+    at_us = per["attn_split"]["avg_us"] + (per["attn_combine"]["avg_us"] if "attn_combine" in per else 0.0)
+    at_bytes = per["attn_split"]["bytes"]
+    at_gbs = at_bytes / (at_us * 1e3)
+    mv_tags = [t for t in per if t.endswith("_matvec")]
+    mv_us = sum(per[t]["avg_us"] for t in mv_tags)
+    mv_bytes = sum(per[t]["bytes"] for t in mv_tags)
+    for tag, p in per.items():
+        gbs = p["bytes"] / (p["avg_us"] * 1e3)
+        log(f"{tag:16s} {p['avg_us']:8.2f} us avg ({p['min_us']:.2f} min) {gbs:8.1f} GB/s  [{p['kernel']}]")
     result = {
         "metric": "decode-layer us/token + achieved HBM GB/s (% peak), Q8_0 matvec & GQA attn",
         "value": round(us_layer, 3),
@@ -294,14 +267,16 @@ def main():
         "layer_bytes": per_layer_bytes,
         "layer_GBps": round(per_layer_bytes / (us_layer * 1e3), 1),
         "eager_us_per_layer": round(eager_ms * 1e3 / R, 3),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(dom_bytes), "avg_launch_us": round(dom_us, 3)},
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"] + " (" + dom_tag + ")", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3)},
         "attn_roofline": {"bound": "hbm", "kernel": "k_attn_split+k_attn_combine", "achieved": round(at_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4),
-                          "bytes_per_launch": int(ga["bytes"] / ga["launches"]), "avg_launch_us": round(at_us, 3)},
+                          "bytes_per_launch": at_bytes, "avg_launch_us": round(at_us, 3)},
+        "matvec_total": {"us": round(mv_us, 3), "bytes": mv_bytes, "GBps": round(mv_bytes / (mv_us * 1e3), 1),
+                         "frac": round(mv_bytes / (mv_us * 1e3) / HBM_PEAK_GBS, 4)},
         "kernels": {t: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in p.items()}
-                    for t, p in sorted(per.items())},
+                    for t, p in per.items()},
     }
     if not args.no_cpu:
         log("oracle CPU baseline")

@@ -267,29 +267,48 @@ typedef struct lq_layer_desc {
     const float *rope_cos, *rope_sin;   /* [max_ctx, head_dim/2] */
 } lq_layer_desc;
 
-/* Optional device buffers for the layer's intermediates (a non-NULL tap
- * replaces the workspace buffer; read after synchronizing). */
+/* Optional device buffers for the layer's intermediates; read them after
+ * synchronizing.  The f32 ones (qkv, attn, x1, h) replace the workspace
+ * buffer of that intermediate.  The Q8_0 ones are the quantized inputs that
+ * the matvec kernels build in on-chip memory; when a tap is given, one
+ * workgroup also writes its copy there. */
 typedef struct lq_layer_taps {
     int8_t* xq; uint16_t* xd;  /* Q8 of the input norm [hidden], [hidden/32] */
-    float* qkv;                /* fused projection; q and k parts after norm + RoPE, v after its norm */
+    float* qkv;                /* raw fused projection [n_q*hd + 2*n_kv*hd] */
     float* attn;               /* attention output [n_q*hd] */
     int8_t* aq; uint16_t* ad;  /* Q8 of the attention output */
     float* x1;                 /* PRENORM_FFN: x + O projection; ATTN_POSTNORM: the O
                                   projection before the post-attention norm [hidden] */
     int8_t* nq; uint16_t* nd;  /* Q8 of the post-attention norm (PRENORM_FFN) */
-    float* gu;                 /* gate/up projection [2*ffn] */
-    int8_t* hq; uint16_t* hd;  /* Q8 of silu(gate) * up [ffn] */
+    float* h;                  /* silu(gate) * up [ffn] */
+    int8_t* hq; uint16_t* hd;  /* Q8 of h */
 } lq_layer_taps;
 
 /* One decode token through one layer ([CUR] section 3 sequence; [TGT]
  * section 3.2, one queue and no intermediate host synchronization): x
  * (device f32 [hidden]) is updated in place; k and v of the token are
  * written into the caches at pos (pos < max_ctx); attention covers the
- * window ending at pos.  taps may be NULL. */
+ * window ending at pos.  taps may be NULL.
+ * This build's kernels need head_dim % 8 == 0 (<= 512), hidden, n_q*head_dim
+ * and ffn <= 16384, and 16-byte aligned x, norm weights, RoPE tables and
+ * caches (LQ_ERR_UNSUPPORTED / LQ_ERR_ALIGN otherwise). */
 size_t lq_decode_layer_workspace_size(const lq_layer_desc* L);
 lq_status lq_decode_layer(const lq_layer_desc* L, float* x, int64_t pos,
                           const lq_layer_taps* taps, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Measurement entry point: lq_decode_layer with every kernel launched with a
+ * start/stop hipEvent_t pair on `stream` (hipExtLaunchKernelGGL: the runtime
+ * stamps the events at that dispatch's own start and end), so a caller can
+ * time each kernel of the layer on the stream it runs on.  Kernel k uses
+ * events[2k] and events[2k+1].  events: host array of n_events hipEvent_t
+ * handles (passed as void*) created by the caller; n_events must be at
+ * least 2 * lq_decode_layer_kernel_count(L).  Same results as
+ * lq_decode_layer. */
+int32_t lq_decode_layer_kernel_count(const lq_layer_desc* L);
+lq_status lq_decode_layer_timed(const lq_layer_desc* L, float* x, int64_t pos,
+                                const lq_layer_taps* taps, void* workspace, size_t workspace_bytes,
+                                void* const* events, int32_t n_events, void* stream);
 
 #ifdef __cplusplus
 }

@@ -69,7 +69,7 @@ class lq_layer_desc(C.Structure):
 
 
 class lq_layer_taps(C.Structure):
-    _fields_ = [(n, _P) for n in ("xq", "xd", "qkv", "attn", "aq", "ad", "x1", "nq", "nd", "gu", "hq", "hd")]
+    _fields_ = [(n, _P) for n in ("xq", "xd", "qkv", "attn", "aq", "ad", "x1", "nq", "nd", "h", "hq", "hd")]
 
 
 _W = C.POINTER(lq_q8_weight)
@@ -99,6 +99,9 @@ _SIGS = {
     "lq_decode_layer_workspace_size": (_SZ, [C.POINTER(lq_layer_desc)]),
     "lq_decode_layer": (_I32, [C.POINTER(lq_layer_desc), _P, _I64, C.POINTER(lq_layer_taps), _P, _SZ,
                                _P]),
+    "lq_decode_layer_kernel_count": (_I32, [C.POINTER(lq_layer_desc)]),
+    "lq_decode_layer_timed": (_I32, [C.POINTER(lq_layer_desc), _P, _I64, C.POINTER(lq_layer_taps), _P, _SZ,
+                                     C.POINTER(_P), _I32, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -258,3 +261,15 @@ def lq_decode_layer_workspace_size(desc):
 def lq_decode_layer(desc, x, pos, taps, workspace, workspace_bytes, stream=None, check=True):
     return _check(_lib.lq_decode_layer(_ref(desc), _ptr(x), pos, _ref(taps), _ptr(workspace),
                                        workspace_bytes, _stream(stream)), check)
+
+
+def lq_decode_layer_kernel_count(desc):
+    return _lib.lq_decode_layer_kernel_count(_ref(desc))
+
+
+def lq_decode_layer_timed(desc, x, pos, taps, workspace, workspace_bytes, events, stream=None, check=True):
+    """events: list of torch.cuda.Event (created with enable_timing) or raw hipEvent_t addresses."""
+    handles = [e if isinstance(e, int) else e.cuda_event for e in events]
+    arr = (_P * len(handles))(*handles)
+    return _check(_lib.lq_decode_layer_timed(_ref(desc), _ptr(x), pos, _ref(taps), _ptr(workspace),
+                                             workspace_bytes, arr, len(handles), _stream(stream)), check)

@@ -16,14 +16,10 @@ namespace lq {
 namespace {
 
 struct LayerBuffers {
-    int8_t* xq; uint16_t* xd;
     float* qkv;
     float* attn;
-    int8_t* aq; uint16_t* ad;
     float* x1;
-    int8_t* nq; uint16_t* nd;
-    float* gu;
-    int8_t* hq; uint16_t* hd;
+    float* h;
     void* attn_ws;
     size_t total;
 };
@@ -42,33 +38,17 @@ LayerBuffers layout(const lq_layer_desc* L, char* base, const lq_layer_taps* tap
         off += round_up(bytes ? bytes : 1, 256);
         return p;
     };
-    b.xq = reinterpret_cast<int8_t*>(take(H));
-    b.xd = reinterpret_cast<uint16_t*>(take(H / 32 * 2));
     b.qkv = reinterpret_cast<float*>(take((qd + 2 * kvd) * 4));
     b.attn = reinterpret_cast<float*>(take(qd * 4));
-    b.aq = reinterpret_cast<int8_t*>(take(qd));
-    b.ad = reinterpret_cast<uint16_t*>(take(qd / 32 * 2));
     b.x1 = reinterpret_cast<float*>(take(H * 4));
-    b.nq = reinterpret_cast<int8_t*>(take(H));
-    b.nd = reinterpret_cast<uint16_t*>(take(H / 32 * 2));
-    b.gu = reinterpret_cast<float*>(take(2 * I * 4));
-    b.hq = reinterpret_cast<int8_t*>(take(I));
-    b.hd = reinterpret_cast<uint16_t*>(take(I / 32 * 2));
+    b.h = reinterpret_cast<float*>(take(I * 4));
     b.attn_ws = take(attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, max_attn_len(L)));
     b.total = off;
     if (taps) {
-        if (taps->xq) b.xq = taps->xq;
-        if (taps->xd) b.xd = taps->xd;
         if (taps->qkv) b.qkv = taps->qkv;
         if (taps->attn) b.attn = taps->attn;
-        if (taps->aq) b.aq = taps->aq;
-        if (taps->ad) b.ad = taps->ad;
         if (taps->x1) b.x1 = taps->x1;
-        if (taps->nq) b.nq = taps->nq;
-        if (taps->nd) b.nd = taps->nd;
-        if (taps->gu) b.gu = taps->gu;
-        if (taps->hq) b.hq = taps->hq;
-        if (taps->hd) b.hd = taps->hd;
+        if (taps->h) b.h = taps->h;
     }
     return b;
 }
@@ -99,7 +79,7 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
             return fail(LQ_ERR_SHAPE, "%s: ffn=%lld with w_gate_up [2*ffn, hidden] and w_down [hidden, ffn]", fn,
                         (long long)I);
     }
-    if (hd > 512 || !attn_supported(nq, nkv, hd, L->kv_dtype))
+    if (hd > 512 || hd % 8 || !attn_supported(nq, nkv, hd, L->kv_dtype))
         return fail(LQ_ERR_UNSUPPORTED, "%s: head_dim=%lld G=%lld kv_dtype=%d not built", fn, (long long)hd,
                     (long long)(nq / nkv), L->kv_dtype);
     lq_status st;
@@ -114,10 +94,25 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
         return fail(LQ_ERR_NULL, "%s: NULL pointer (x, g_in, caches and RoPE tables are required)", fn);
     if (L->qk_norm && (!L->g_q || !L->g_k)) return fail(LQ_ERR_NULL, "%s: qk_norm needs g_q and g_k", fn);
     if (!aligned(x, 16) || !aligned(L->g_in, 16) || (L->g_post && !aligned(L->g_post, 16)) ||
-        !aligned(L->k_cache, 16) || !aligned(L->v_cache, 16))
-        return fail(LQ_ERR_ALIGN, "%s: x, norm weights and caches must be 16-byte aligned", fn);
+        (L->g_q && !aligned(L->g_q, 16)) || (L->g_k && !aligned(L->g_k, 16)) || !aligned(L->rope_cos, 16) ||
+        !aligned(L->rope_sin, 16) || !aligned(L->k_cache, 16) || !aligned(L->v_cache, 16))
+        return fail(LQ_ERR_ALIGN, "%s: x, norm weights, RoPE tables and caches must be 16-byte aligned", fn);
     const size_t es = L->kv_dtype == LQ_KV_F32 ? 4 : 2;
     if ((hd * es) % 16) return fail(LQ_ERR_ALIGN, "%s: cache rows must be a multiple of 16 bytes", fn);
+    if (H > 16384 || nq * hd > 16384 || (L->kind == LQ_LAYER_PRENORM_FFN && L->ffn > 16384) ||
+        L->w_qkv.rows > 0x7fffffffLL || 2 * L->ffn > 0x7fffffffLL)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: matvec inputs are limited to 16384 columns", fn);
+    return LQ_OK;
+}
+
+lq_status validate_taps(const lq_layer_taps* t) {
+    if (!t) return LQ_OK;
+    const void* f32s[] = {t->qkv, t->attn, t->x1, t->h, t->xq, t->aq, t->nq, t->hq};
+    for (const void* p : f32s)
+        if (p && !aligned(p, 16)) return fail(LQ_ERR_ALIGN, "lq_decode_layer: tap buffers must be 16-byte aligned");
+    const void* d16[] = {t->xd, t->ad, t->nd, t->hd};
+    for (const void* p : d16)
+        if (p && !aligned(p, 2)) return fail(LQ_ERR_ALIGN, "lq_decode_layer: scale taps must be 2-byte aligned");
     return LQ_OK;
 }
 
@@ -131,48 +126,97 @@ extern "C" size_t lq_decode_layer_workspace_size(const lq_layer_desc* L) {
     return layout(L, nullptr, nullptr).total;
 }
 
+namespace {
+using Marks = LaunchMarks;
+
+int kernel_count(const lq_layer_desc* L, int64_t len) {
+    // QKV, attention (+ split combine), O, then gate_up and down, or the post-norm add
+    const bool combine = attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, len) > 0;
+    return 3 + (combine ? 1 : 0) + (L->kind == LQ_LAYER_PRENORM_FFN ? 2 : 1);
+}
+
+lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_layer_taps* taps, void* workspace,
+                    size_t workspace_bytes, Marks& mk, hipStream_t s);
+}  // namespace
+
+extern "C" int32_t lq_decode_layer_kernel_count(const lq_layer_desc* L) {
+    if (!L) return 0;
+    return kernel_count(L, (L->window > 0 && L->window < L->max_ctx) ? L->window : L->max_ctx);
+}
+
 extern "C" lq_status lq_decode_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_layer_taps* taps,
                                      void* workspace, size_t workspace_bytes, void* stream) {
+    Marks mk{nullptr, 0, 0};
+    return run_layer(L, x, pos, taps, workspace, workspace_bytes, mk, as_stream(stream));
+}
+
+extern "C" lq_status lq_decode_layer_timed(const lq_layer_desc* L, float* x, int64_t pos,
+                                           const lq_layer_taps* taps, void* workspace, size_t workspace_bytes,
+                                           void* const* events, int32_t n_events, void* stream) {
+    if (!events) return fail(LQ_ERR_NULL, "lq_decode_layer_timed: events is NULL");
+    if (!L) return fail(LQ_ERR_NULL, "lq_decode_layer_timed: descriptor is NULL");
+    if (pos < 0 || pos >= L->max_ctx) return fail(LQ_ERR_SHAPE, "lq_decode_layer_timed: pos out of range");
+    int64_t start = 0;
+    if (L->window > 0 && pos - L->window + 1 > 0) start = pos - L->window + 1;
+    const int need = 2 * kernel_count(L, pos - start + 1);
+    if (n_events < need)
+        return fail(LQ_ERR_SHAPE, "lq_decode_layer_timed: needs %d events, got %d", need, n_events);
+    Marks mk{events, n_events, 0};
+    return run_layer(L, x, pos, taps, workspace, workspace_bytes, mk, as_stream(stream));
+}
+
+namespace {
+lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_layer_taps* taps, void* workspace,
+                    size_t workspace_bytes, Marks& mk, hipStream_t s) {
     lq_status st = validate(L, x, pos);
     if (st != LQ_OK) return st;
+    if ((st = validate_taps(taps)) != LQ_OK) return st;
     const size_t need = layout(L, nullptr, nullptr).total;
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(LQ_ERR_WORKSPACE, "lq_decode_layer: workspace needs %zu bytes (256-byte aligned), got %zu", need,
                     workspace_bytes);
     const LayerBuffers b = layout(L, static_cast<char*>(workspace), taps);
-    hipStream_t s = as_stream(stream);
     const int64_t H = L->hidden, nq = L->n_q, nkv = L->n_kv, hd = L->head_dim, qd = nq * hd;
     const int64_t head_stride = L->max_ctx * hd, pos_stride = hd;
     int64_t start = 0;
     if (L->window > 0 && pos - L->window + 1 > 0) start = pos - L->window + 1;
     const int64_t len = pos - start + 1;
 
-    // attention block
-    if ((st = launch_rmsnorm_q8(x, 1, H, L->g_in, L->eps, b.xq, b.xd, s)) != LQ_OK) return st;
-    if ((st = launch_q8_matvec(L->w_qkv.qs, L->w_qkv.d, L->w_qkv.rows, H, b.xq, b.xd, nullptr, b.qkv, nullptr, s)) !=
-        LQ_OK)
+    const lq_layer_taps T = taps ? *taps : lq_layer_taps{};
+    MvArgs m{};
+
+    // attention block: QKV projection with the input RMSNorm + Q8 built in-kernel
+    m = MvArgs{};
+    m.wq = L->w_qkv.qs; m.wd = L->w_qkv.d; m.rows = (int)L->w_qkv.rows; m.cols = (int)H;
+    m.x = x; m.gamma = L->g_in; m.eps = L->eps; m.y = b.qkv; m.tap_q = T.xq; m.tap_d = T.xd;
+    if ((st = launch_mv(m, PRO_NORM, EPI_STORE, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    // attention, with the per-head norms, RoPE and the KV append in its prologue
+    const int64_t half = hd / 2;
+    if ((st = launch_attention_fused(b.qkv, nq, nkv, hd, L->g_q, L->g_k, L->qk_norm, L->v_unit_norm, L->eps,
+                                     L->rope_cos + pos * half, L->rope_sin + pos * half, L->k_cache, L->v_cache,
+                                     L->kv_dtype, head_stride, pos_stride, start, len, L->attn_scale, b.attn,
+                                     b.attn_ws, s, &mk)) != LQ_OK)
         return st;
-    if ((st = launch_qkv_post(b.qkv, nq, nkv, hd, L->g_q, L->g_k, L->qk_norm, L->v_unit_norm, L->eps, L->rope_cos,
-                              L->rope_sin, pos, L->k_cache, L->v_cache, L->kv_dtype, head_stride, pos_stride, s)) !=
-        LQ_OK)
-        return st;
-    if ((st = launch_attention(b.qkv, nq, nkv, hd, L->k_cache, L->v_cache, L->kv_dtype, head_stride, pos_stride,
-                               start, len, L->attn_scale, b.attn, b.attn_ws, s)) != LQ_OK)
-        return st;
-    if ((st = launch_q8_quantize(b.attn, qd / 32, b.aq, b.ad, s)) != LQ_OK) return st;
+    // O projection, quantizing the attention output in-kernel
+    m = MvArgs{};
+    m.wq = L->w_o.qs; m.wd = L->w_o.d; m.rows = (int)H; m.cols = (int)qd;
+    m.x = b.attn; m.y = b.x1; m.tap_q = T.aq; m.tap_d = T.ad;
     if (L->kind == LQ_LAYER_ATTN_POSTNORM) {
-        // o (into the x1 buffer) -> post-attention norm -> + x
-        if ((st = launch_q8_matvec(L->w_o.qs, L->w_o.d, H, qd, b.aq, b.ad, nullptr, b.x1, nullptr, s)) != LQ_OK)
-            return st;
-        return launch_rmsnorm_add(b.x1, H, L->g_post, L->eps, x, x, s);
+        if ((st = launch_mv(m, PRO_QUANT, EPI_STORE, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+        return launch_rmsnorm_add(b.x1, H, L->g_post, L->eps, x, x, s, &mk);
     }
-    if ((st = launch_q8_matvec(L->w_o.qs, L->w_o.d, H, qd, b.aq, b.ad, x, b.x1, nullptr, s)) != LQ_OK) return st;
-    // FFN block
+    m.res = x;
+    if ((st = launch_mv(m, PRO_QUANT, EPI_RESID, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    // FFN: gate/up with the post-attention RMSNorm + Q8 in-kernel and SwiGLU on row pairs
     const int64_t I = L->ffn;
-    if ((st = launch_rmsnorm_q8(b.x1, 1, H, L->g_post, L->eps, b.nq, b.nd, s)) != LQ_OK) return st;
-    if ((st = launch_q8_matvec(L->w_gate_up.qs, L->w_gate_up.d, 2 * I, H, b.nq, b.nd, nullptr, b.gu, nullptr, s)) !=
-        LQ_OK)
-        return st;
-    if ((st = launch_swiglu_q8(b.gu, 1, I, b.hq, b.hd, s)) != LQ_OK) return st;
-    return launch_q8_matvec(L->w_down.qs, L->w_down.d, H, I, b.hq, b.hd, b.x1, x, nullptr, s);
+    m = MvArgs{};
+    m.wq = L->w_gate_up.qs; m.wd = L->w_gate_up.d; m.rows = (int)I; m.cols = (int)H;
+    m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = b.h; m.tap_q = T.nq; m.tap_d = T.nd;
+    if ((st = launch_mv(m, PRO_NORM, EPI_SWIGLU, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    // down projection, quantizing h in-kernel, plus the residual
+    m = MvArgs{};
+    m.wq = L->w_down.qs; m.wd = L->w_down.d; m.rows = (int)H; m.cols = (int)I;
+    m.x = b.h; m.res = b.x1; m.y = x; m.tap_q = T.hq; m.tap_d = T.hd;
+    return launch_mv(m, PRO_QUANT, EPI_RESID, s, kMvWgPerCu, &mk);
 }
+}  // namespace

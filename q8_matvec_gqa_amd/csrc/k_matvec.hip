@@ -139,6 +139,238 @@ __global__ __launch_bounds__(256) void k_q8_matvec_any(const int8_t* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused matvec: prologue x -> Q8_0 in LDS, grid-stride rows with prefetch,
+// epilogue store / residual / SwiGLU.
+//
+// Prologues (PRO_*): the workgroup builds the quantized activation itself,
+//   Q8    : codes and scales already in memory (copied to LDS);
+//   QUANT : f32 x quantized per 32-block into LDS;
+//   NORM  : f32 x -> RMSNorm(gamma) -> quantized into LDS.
+//   Every workgroup computes the same bits, so the layer needs no separate
+//   normalise / quantize launches.  The first row group's weight loads are
+//   issued before the prologue so HBM latency overlaps it.
+// Epilogues (EPI_*): y[r] = acc; y[r] = res[r] + acc; or, with the gate rows
+//   [0, rows) and up rows [rows, 2*rows) of a gate_up weight processed in
+//   pairs, y[r] = silu(acc_gate) * acc_up.
+// Each wave owns a fixed 16-byte K-slice per 1 KB chunk, so its activation
+// slice is copied from LDS to VGPRs once and reused for every row.
+// ---------------------------------------------------------------------------
+constexpr int kMaxCols = 16384;
+
+template <int NCH, int RPW>
+struct RowGroup {
+    int4 w[RPW][NCH];
+    uint32_t d[RPW][NCH];
+};
+
+template <int NCH, int RPW, int EPI>
+__device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int lane, RowGroup<NCH, RPW>& G) {
+    const int nb = a.cols >> 5;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        // SwiGLU pairs: even i -> gate row, odd i -> the matching up row
+        int64_t r;
+        if constexpr (EPI == EPI_SWIGLU) r = (g * (RPW / 2) + i / 2) + (i & 1) * (int64_t)a.rows;
+        else r = g * RPW + i;
+        const bool ok = (EPI == EPI_SWIGLU) ? (g * (RPW / 2) + i / 2 < a.rows) : (r < a.rows);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            if (ok && off < a.cols) {
+                G.w[i][c] = load_stream16(a.wq + r * a.cols + off);
+                G.d[i][c] = a.wd[r * nb + (off >> 5)];
+            } else {
+                G.w[i][c] = make_int4(0, 0, 0, 0);
+                G.d[i][c] = 0;
+            }
+        }
+    }
+}
+
+template <int NCH, int RPW, int EPI>
+__device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int lane, const RowGroup<NCH, RPW>& G,
+                                              const int4 (&xv)[NCH], const float (&xs)[NCH]) {
+    float acc[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float t = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int p = dot16(G.w[i][c], xv[c]);
+            const int blk = p + dpp_i<kQuadXor1>(p);
+            const float v = (float)blk * (f16_to_f32(G.d[i][c]) * xs[c]);
+            t += (lane & 1) ? 0.0f : v;
+        }
+        acc[i] = wave_sum(t);
+    }
+    if (lane != 0) return;
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < RPW / 2; ++j) {
+            const int64_t r = g * (RPW / 2) + j;
+            if (r < a.rows) {
+                const float gt = acc[2 * j], up = acc[2 * j + 1];
+                a.y[r] = (gt / (1.0f + expf(-gt))) * up;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int64_t r = g * RPW + i;
+            if (r < a.rows) a.y[r] = (EPI == EPI_RESID) ? a.res[r] + acc[i] : acc[i];
+        }
+    }
+}
+
+template <int NCH, int RPW, int PRO, int EPI>
+__global__ __launch_bounds__(256) void k_mv(MvArgs a) {
+    __shared__ __attribute__((aligned(16))) int8_t xq_s[PRO == PRO_Q8 ? 16 : kMaxCols];
+    __shared__ float xs_s[PRO == PRO_Q8 ? 1 : kMaxCols / 32];
+    __shared__ float red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = a.cols >> 5;
+    constexpr int OUT_PER_GROUP = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
+    const int64_t ngroups = (a.rows + OUT_PER_GROUP - 1) / OUT_PER_GROUP;
+    const int64_t gstride = (int64_t)gridDim.x * 4;
+    int64_t g = (int64_t)blockIdx.x * 4 + wave;
+
+    // first row group in flight before the prologue
+    RowGroup<NCH, RPW> A, B;
+    if (g < ngroups) load_group<NCH, RPW, EPI>(a, g, lane, A);
+
+    int4 xv[NCH];
+    float xs[NCH];
+    if constexpr (PRO == PRO_Q8) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            xv[c] = make_int4(0, 0, 0, 0);
+            xs[c] = 0.0f;
+            if (off < a.cols) {
+                xv[c] = *reinterpret_cast<const int4*>(a.xq + off);
+                xs[c] = f16_to_f32(a.xd[off >> 5]);
+            }
+        }
+    } else {
+        float rinv = 1.0f;
+        if constexpr (PRO == PRO_NORM) {
+            float ss = 0.0f;
+            for (int i = threadIdx.x * 4; i < a.cols; i += 1024) {
+                const float4 t = *reinterpret_cast<const float4*>(a.x + i);
+                ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) red[wave] = ss;
+            __syncthreads();
+            ss = (red[0] + red[1]) + (red[2] + red[3]);
+            rinv = 1.0f / sqrtf(ss / (float)a.cols + a.eps);
+        }
+        const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
+        for (int b = threadIdx.x; b < nb; b += 256) {
+            float v[32];
+            load32(a.x + 32 * b, v);
+            if constexpr (PRO == PRO_NORM) {
+                if (a.gamma) {
+                    float gm[32];
+                    load32(a.gamma + 32 * b, gm);
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) v[i] = (v[i] * rinv) * gm[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) v[i] = v[i] * rinv;
+                }
+            }
+            uint32_t packed[8];
+            const uint16_t db = quantize_block32_packed(v, packed);
+            store_codes32(xq_s + 32 * b, packed);
+            xs_s[b] = f16_to_f32(db);
+            if (tap) {
+                store_codes32(a.tap_q + 32 * b, packed);
+                a.tap_d[b] = db;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            xv[c] = make_int4(0, 0, 0, 0);
+            xs[c] = 0.0f;
+            if (off < a.cols) {
+                xv[c] = *reinterpret_cast<const int4*>(xq_s + off);
+                xs[c] = xs_s[off >> 5];
+            }
+        }
+    }
+
+    // grid-stride over row groups, next group prefetched while this one is consumed
+    while (g < ngroups) {
+        const int64_t gn = g + gstride;
+        if (gn < ngroups) load_group<NCH, RPW, EPI>(a, gn, lane, B);
+        consume_group<NCH, RPW, EPI>(a, g, lane, A, xv, xs);
+        g = gn;
+        if (g >= ngroups) break;
+        const int64_t gn2 = g + gstride;
+        if (gn2 < ngroups) load_group<NCH, RPW, EPI>(a, gn2, lane, A);
+        consume_group<NCH, RPW, EPI>(a, g, lane, B, xv, xs);
+        g = gn2;
+    }
+}
+
+// Rows per wave and workgroups per CU for each shape class.
+template <int NCH> struct MvShape {
+    static constexpr int RPW = NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1);
+};
+
+// Grid: never more workgroups than can be resident at once (so no wave of
+// late workgroups repeats the prologue), and every wave gets the same number
+// of row groups (no half-empty tail).
+template <int NCH, int PRO, int EPI>
+static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
+    constexpr int RPW = (EPI == EPI_SWIGLU) ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1)
+                                            : MvShape<NCH>::RPW;
+    constexpr int OUT = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
+    auto kern = k_mv<NCH, RPW, PRO, EPI>;
+    static int resident = -1;     // workgroups per CU this instance can keep resident
+    if (resident < 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+        resident = n;
+    }
+    int per_cu = resident < wg_per_cu ? resident : wg_per_cu;
+    const int64_t groups = (a.rows + OUT - 1) / OUT;
+    const int64_t cap_waves = 4LL * kNumCUs * per_cu;
+    const int64_t iters = (groups + cap_waves - 1) / cap_waves;
+    int64_t grid = (groups + 4 * iters - 1) / (4 * iters);
+    if (grid < 1) grid = 1;
+    launch_marked(mk, kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+}
+
+template <int PRO, int EPI>
+static lq_status launch_mv_pe(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
+    const int nch = (a.cols + 1023) / 1024;
+#define LQ_MV2(N) \
+    case N: launch_mv_nch<N, PRO, EPI>(a, s, wg_per_cu, mk); break;
+    switch (nch) {
+        LQ_MV2(1) LQ_MV2(2) LQ_MV2(3) LQ_MV2(4) LQ_MV2(5) LQ_MV2(6) LQ_MV2(7) LQ_MV2(8)
+        LQ_MV2(9) LQ_MV2(10) LQ_MV2(11) LQ_MV2(12) LQ_MV2(13) LQ_MV2(14) LQ_MV2(15) LQ_MV2(16)
+        default: return fail(LQ_ERR_UNSUPPORTED, "fused matvec: cols > %d", kMaxCols);
+    }
+#undef LQ_MV2
+    return check_launch("fused matvec");
+}
+
+lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
+    if (a.rows == 0) return LQ_OK;
+#define LQ_PE(P, E) \
+    if (pro == P && epi == E) return launch_mv_pe<P, E>(a, s, wg_per_cu, mk);
+    LQ_PE(PRO_Q8, EPI_STORE) LQ_PE(PRO_Q8, EPI_RESID) LQ_PE(PRO_Q8, EPI_SWIGLU)
+    LQ_PE(PRO_QUANT, EPI_STORE) LQ_PE(PRO_QUANT, EPI_RESID)
+    LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU)
+#undef LQ_PE
+    return fail(LQ_ERR_UNSUPPORTED, "fused matvec: prologue %d / epilogue %d not built", pro, epi);
+}
+
 template <int NCH, bool DOTS>
 static void launch_nch(int grid, hipStream_t s, const int8_t* wq, const uint16_t* wd, int64_t rows,
                        int cols, const int8_t* xq, const uint16_t* xd, const float* res, float* y,
@@ -208,6 +440,12 @@ extern "C" lq_status lq_q8_matvec(const lq_q8_weight* w, const int8_t* x_qs, con
     if (!y) return fail(LQ_ERR_NULL, "lq_q8_matvec: y is NULL");
     if (!aligned(y, 4) || (residual && !aligned(residual, 4)))
         return fail(LQ_ERR_ALIGN, "lq_q8_matvec: y and residual must be 4-byte aligned");
+    if (w->cols <= kMaxCols && w->rows <= 0x7fffffffLL) {
+        MvArgs a{};
+        a.wq = w->qs; a.wd = w->d; a.rows = (int)w->rows; a.cols = (int)w->cols;
+        a.xq = x_qs; a.xd = x_d; a.res = residual; a.y = y;
+        return launch_mv(a, PRO_Q8, residual ? EPI_RESID : EPI_STORE, as_stream(stream), kMvWgPerCu);
+    }
     return launch_q8_matvec(w->qs, w->d, w->rows, w->cols, x_qs, x_d, residual, y, nullptr,
                             as_stream(stream));
 }

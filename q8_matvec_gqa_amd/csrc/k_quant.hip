@@ -127,9 +127,9 @@ lq_status launch_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn, in
 }
 
 lq_status launch_rmsnorm_add(const float* o, int64_t n, const float* gamma, float eps, const float* res,
-                             float* out, hipStream_t s) {
+                             float* out, hipStream_t s, LaunchMarks* mk) {
     if (n == 0) return LQ_OK;
-    hipLaunchKernelGGL(k_rmsnorm_add, dim3(1), dim3(256), 0, s, o, n, gamma, eps, res, out);
+    launch_marked(mk, k_rmsnorm_add, dim3(1), dim3(256), 0, s, o, n, gamma, eps, res, out);
     return check_launch("rmsnorm_add");
 }
 

@@ -99,15 +99,13 @@ __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 // ---- Q8_0 block quantization of 32 floats held by one lane ------------------
 // Scale d = amax/127 (correctly rounded float division), codes =
 // round-half-away-from-zero(x * (1/d)) clamped to [-127, 127], 0 for amax 0.
-// Writes 32 codes (two 16-byte stores) and the f16 scale bits.
-__device__ __forceinline__ void quantize_block32(const float (&v)[32], int8_t* __restrict__ qs,
-                                                 uint16_t* __restrict__ d) {
+// Returns the f16 scale bits; the 32 codes come back packed 4 per word.
+__device__ __forceinline__ uint16_t quantize_block32_packed(const float (&v)[32], uint32_t (&packed)[8]) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const float db = amax / 127.0f;
     const float inv = (db != 0.0f) ? 1.0f / db : 0.0f;
-    uint32_t packed[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         uint32_t word = 0;
@@ -119,10 +117,22 @@ __device__ __forceinline__ void quantize_block32(const float (&v)[32], int8_t* _
         }
         packed[w] = word;
     }
+    return f32_to_f16(db);
+}
+
+__device__ __forceinline__ void store_codes32(int8_t* qs, const uint32_t (&packed)[8]) {
     int4* q4 = reinterpret_cast<int4*>(qs);
     q4[0] = make_int4((int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]);
     q4[1] = make_int4((int)packed[4], (int)packed[5], (int)packed[6], (int)packed[7]);
-    *d = f32_to_f16(db);
+}
+
+// Quantize 32 floats and write 32 codes (two 16-byte stores) and the f16 scale.
+__device__ __forceinline__ void quantize_block32(const float (&v)[32], int8_t* __restrict__ qs,
+                                                 uint16_t* __restrict__ d) {
+    uint32_t packed[8];
+    const uint16_t db = quantize_block32_packed(v, packed);
+    store_codes32(qs, packed);
+    *d = db;
 }
 
 __device__ __forceinline__ void load32(const float* __restrict__ p, float (&v)[32]) {

@@ -3,6 +3,7 @@
 // (decode layer, MoE block) share.  Every launcher assumes its arguments were
 // validated by the caller.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,6 +11,36 @@
 #include "../../include/lq.h"
 
 namespace lq {
+
+constexpr int kNumCUs = 256;   // MI355X compute units
+
+// Optional per-kernel timing for the measurement entry point of the decode
+// layer: kernel k of a run gets the start/stop event pair (ev[2k], ev[2k+1]),
+// stamped by the runtime at that dispatch's own start and end.
+struct LaunchMarks {
+    void* const* ev;
+    int n, k;
+    bool next(hipEvent_t* start, hipEvent_t* stop) {
+        const bool ok = ev && 2 * k + 1 < n;
+        if (ok) {
+            *start = reinterpret_cast<hipEvent_t>(ev[2 * k]);
+            *stop = reinterpret_cast<hipEvent_t>(ev[2 * k + 1]);
+        }
+        ++k;
+        return ok;
+    }
+};
+
+// Launches a kernel, with start/stop events when timing marks are given.
+template <typename K, typename... Args>
+inline void launch_marked(LaunchMarks* mk, K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                          Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (mk && mk->next(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 // Records a thread-local message for lq_last_error() and returns s.
 lq_status fail(lq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -32,12 +63,35 @@ lq_status launch_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn, in
                            uint16_t* d, hipStream_t s);
 // out = res + gamma * o / sqrt(mean(o^2) + eps) for one vector (n % 4 == 0).
 lq_status launch_rmsnorm_add(const float* o, int64_t n, const float* gamma, float eps, const float* res,
-                             float* out, hipStream_t s);
+                             float* out, hipStream_t s, struct LaunchMarks* mk = nullptr);
 
 // ---- launchers (k_matvec.hip) -----------------------------------------------
 lq_status launch_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
                            const int8_t* xq, const uint16_t* xd, const float* residual, float* y,
                            int32_t* dots, hipStream_t s);
+
+// Fused matvec (see k_matvec.hip): prologue PRO_* builds the Q8_0 input,
+// epilogue EPI_* stores, adds a residual or applies SwiGLU to row pairs.
+enum { PRO_Q8 = 0, PRO_QUANT = 1, PRO_NORM = 2 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+constexpr int kMvWgPerCu = 4;   // upper bound on resident workgroups of 4 waves per CU
+struct MvArgs {
+    const int8_t* wq;
+    const uint16_t* wd;
+    int rows;            // output rows (SwiGLU: rows of h; the weight has 2*rows)
+    int cols;            // <= 16384
+    const int8_t* xq;    // PRO_Q8: codes and scales in memory
+    const uint16_t* xd;
+    const float* x;      // PRO_QUANT / PRO_NORM: f32 input
+    const float* gamma;  // PRO_NORM (NULL: unit weight)
+    float eps;
+    const float* res;    // EPI_RESID (may alias y)
+    float* y;
+    int8_t* tap_q;       // optional: workgroup 0 writes the Q8_0 input it built
+    uint16_t* tap_d;
+};
+lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per_cu,
+                    LaunchMarks* mk = nullptr);
 
 // ---- launchers (k_norm_rope.hip) ----------------------------------------------
 lq_status launch_rmsnorm_rope(float* x, int64_t n_heads, int64_t hd, int64_t head_stride,
@@ -62,6 +116,15 @@ lq_status launch_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd
                            const void* vc, int32_t kv_dtype, int64_t head_stride,
                            int64_t pos_stride, int64_t start, int64_t len, float scale,
                            float* out, void* ws, hipStream_t s);
+// Decode-layer attention with the per-head q/k RMSNorm + NeoX RoPE, the v
+// unit norm and the KV append (at start + len - 1) done in the kernel's
+// prologue; qkv is the raw fused projection.  rope rows are at that position.
+lq_status launch_attention_fused(const float* qkv, int64_t n_q, int64_t n_kv, int64_t hd, const float* g_q,
+                                 const float* g_k, int32_t qk_norm, int32_t v_unit_norm, float eps,
+                                 const float* rope_cos_row, const float* rope_sin_row, void* kc, void* vc,
+                                 int32_t kv_dtype, int64_t head_stride, int64_t pos_stride, int64_t start,
+                                 int64_t len, float scale, float* out, void* ws, hipStream_t s,
+                                 LaunchMarks* marks = nullptr);
 
 // ---- launchers (k_moe.hip) ----------------------------------------------------
 size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts);

@@ -54,7 +54,7 @@ class DeviceLayer:
                     attn=e(qd, torch.float32), aq=e(qd, torch.int8), ad=e(qd // 32, torch.int16),
                     x1=e(H, torch.float32))
         if I:
-            bufs.update(nq=e(H, torch.int8), nd=e(H // 32, torch.int16), gu=e(2 * I, torch.float32),
+            bufs.update(nq=e(H, torch.int8), nd=e(H // 32, torch.int16), h=e(I, torch.float32),
                         hq=e(I, torch.int8), hd=e(I // 32, torch.int16))
         taps = lq_layer_taps(**{k: v.data_ptr() for k, v in bufs.items()})
         return taps, bufs

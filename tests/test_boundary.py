@@ -162,6 +162,10 @@ def test_layer_validation():
     assert call(_layer_desc(k_cache=A + 2)) == lq.LQ_ERR_ALIGN
     assert call(_layer_desc(window=-1)) == lq.LQ_ERR_SHAPE
     assert lq.lq_decode_layer_workspace_size(None) == 0
+    n = lq.lq_decode_layer_kernel_count(d)
+    assert n == 6                                            # QKV, attention split + combine, O, gate_up, down
+    assert st(lq.lq_decode_layer_timed, d, A, 8191, None, A, need, [A] * (2 * n - 1)) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_decode_layer_timed, d, A, 8192, None, A, need, [A] * (2 * n)) == lq.LQ_ERR_SHAPE
 
 
 def test_pack_ggml_host():
