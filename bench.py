@@ -180,6 +180,138 @@ def kernel_measurements(cfg, layers, xs, torch, rounds):
     return per
 
 
+def calib_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain elementwise copy of known size (reads nbytes, writes nbytes),
+    run for the PMC calibration of FETCH_SIZE / WRITE_SIZE."""
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)          # the only negation kernel in the run
+    torch.cuda.synchronize()
+    return nbytes
+
+
+# ---------------------------------------------------------------- profiles
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["q8_matvec_gqa_amd/csrc/k_matvec.hip", "q8_matvec_gqa_amd/csrc/lq_device.h",
+                  "q8_matvec_gqa_amd/csrc/lq_internal.h"]
+
+
+def source_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _kernel_match(name, tag):
+    """rocprofv3 kernel names -> the layer's kernel tags."""
+    if tag == "gate_up_matvec":
+        return "k_mv<4, 4, 2, 2>" in name
+    if tag == "copy":
+        return "neg" in name.lower()
+    raise ValueError(tag)
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, out_path, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel and of
+    the calibration copy -> HBM bytes per launch, written as a text summary."""
+    def per_kernel(d, counter):
+        rows = _read_csv(_find(d, "counter_collection.csv"))
+        out = {"gate_up_matvec": [], "copy": []}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            for tag in out:
+                if _kernel_match(r["Kernel_Name"], tag):
+                    out[tag].append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v) if v else float("nan"), len(v)) for k, v in out.items()}
+
+    f = per_kernel(fetch_dir, "FETCH_SIZE")
+    w = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+    f_scale = copy_bytes / (f["copy"][0] * 1024.0)
+    w_scale = copy_bytes / (w["copy"][0] * 1024.0)
+    fetch_b = f["gate_up_matvec"][0] * 1024.0 * f_scale
+    write_b = w["gate_up_matvec"][0] * 1024.0 * w_scale
+    cfg = synthetic.layer_cfg(workload)
+    algo = dict((t, b) for t, _, b in layer_kernels(cfg, True))["gate_up_matvec"]
+    lines = [
+        f"# HBM traffic of the gate_up matvec (k_mv<NCH=4, RPW=4, NORM, SWIGLU>), {workload}",
+        f"command_fetch: {command.replace('WRITE_SIZE', 'FETCH_SIZE')}",
+        f"command_write: {command.replace('FETCH_SIZE', 'WRITE_SIZE')}",
+        f"source_sha256: {source_hash(KERNEL_SOURCES)}",
+        f"dispatches_fetch: {f['gate_up_matvec'][1]}",
+        f"dispatches_write: {w['gate_up_matvec'][1]}",
+        f"fetch_kib_per_dispatch: {f['gate_up_matvec'][0]:.1f}",
+        f"write_kib_per_dispatch: {w['gate_up_matvec'][0]:.1f}",
+        f"copy_calibration_bytes: {copy_bytes}",
+        f"copy_fetch_kib: {f['copy'][0]:.1f}  (scale {f_scale:.4f})",
+        f"copy_write_kib: {w['copy'][0]:.1f}  (scale {w_scale:.4f})",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}",
+    ]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic(workload):
+    """traffic_bytes_per_launch from the committed PMC summary, or None when
+    the summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"gate_up_matvec_{workload}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash(KERNEL_SOURCES):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def summarize_trace(trace_dir, out_dir, workload, command):
+    """Kernel-trace statistics of a bench run -> one text summary per kernel
+    of the layer (average duration over the run's dispatches)."""
+    import statistics
+    rows = _read_csv(_find(trace_dir, "kernel_trace.csv"))
+    groups = {}
+    for r in rows:
+        n = r["Kernel_Name"]
+        if "lq::" not in n:
+            continue
+        groups.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# rocprofv3 kernel trace of bench.py, {workload}", f"command: {command}",
+             "kernel | dispatches | avg_us | median_us | min_us | max_us"]
+    for n, ts in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{n} | {len(ts)} | {statistics.mean(ts):.3f} | {statistics.median(ts):.3f} | "
+                     f"{min(ts):.3f} | {max(ts):.3f}")
+    out = os.path.join(out_dir, f"decode_layer_{workload}.trace.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(workload, seconds):
     import oracle
     cfg, w = synthetic.layer_inputs(workload, seed=0)
@@ -208,7 +340,23 @@ def main():
     ap.add_argument("--rounds", type=int, default=5, help="rounds of per-launch kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calib-copy", action="store_true", help="also run the PMC calibration copy (1 GiB)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write the kernel-trace summary from a rocprofv3 --kernel-trace folder and exit")
+    ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
+    ap.add_argument("--profiles-dir", default=PROFILES, help="where the summaries are written")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        os.makedirs(args.profiles_dir, exist_ok=True)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      os.path.join(args.profiles_dir, f"gate_up_matvec_{args.workload}.pmc.txt"), args.command)
+        return
+    if args.summarize_trace:
+        os.makedirs(args.profiles_dir, exist_ok=True)
+        summarize_trace(args.summarize_trace, args.profiles_dir, args.workload, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -269,7 +417,8 @@ def main():
         "eager_us_per_layer": round(eager_ms * 1e3 / R, 3),
         "roofline": {"bound": "hbm", "kernel": dom["kernel"] + " (" + dom_tag + ")", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3)},
+                     "traffic": load_traffic(args.workload) if dom_tag == "gate_up_matvec" else None,
+                     "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3)},
         "attn_roofline": {"bound": "hbm", "kernel": "k_attn_split+k_attn_combine", "achieved": round(at_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_launch": at_bytes, "avg_launch_us": round(at_us, 3)},
@@ -278,6 +427,8 @@ def main():
         "kernels": {t: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in p.items()}
                     for t, p in per.items()},
     }
+    if args.calib_copy:
+        calib_copy(torch)
     if not args.no_cpu:
         log("oracle CPU baseline")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)

@@ -87,49 +87,79 @@ struct AttnArgs {
 
 }  // namespace
 
-// One head vector of hd floats, by one wave: RMSNorm over the head (optional,
-// weights gamma, or none for a unit norm), then NeoX RoPE (optional: element
-// i pairs with i + hd/2 and uses the table entry of the lower index), times
-// `scale`.  Lane l handles elements l + 64j; it reads the RoPE partner of
-// each of its elements straight from `raw`, so lanes exchange nothing but the
-// sum of squares.  The result goes to dst (LDS); when kv_dst is set it is
-// also stored there as KV (a cache row), and dst then holds the stored value.
-template <typename KV>
-__device__ __forceinline__ void head_vec(const float* __restrict__ raw, const float* __restrict__ gamma,
-                                         const float* __restrict__ cs, const float* __restrict__ sn, int hd,
-                                         bool norm, bool rope, float eps, float scale, int lane, float* dst,
-                                         KV* kv_dst) {
-    constexpr int EPL = 8;                          // hd <= 512
+// The prologue's head vectors, by one wave each: RMSNorm over the head
+// (optional, weights gamma, or none for a unit norm), then NeoX RoPE
+// (optional: element i pairs with i + hd/2 and uses the table entry of the
+// lower index), times `scale`.  Lane l handles elements l + 64j and reads the
+// RoPE partner of each straight from the source, so lanes exchange nothing
+// but the sum of squares.  Loading and computing are separate so the loads
+// can be issued before the wave's K/V loads (the vector memory counter
+// retires loads in order).
+struct HeadSrc {
+    const float* raw;
+    const float* gamma;   // NULL: no weights
+    bool norm, rope;
+    float scale;
+};
+
+template <int EPL>
+struct HeadIn {
+    float own[EPL], par[EPL], ga[EPL], gb[EPL], cs[EPL], sn[EPL];   // as loaded
+};
+
+// Issues the loads only: every load comes from a valid address (absent
+// tables are replaced by the source row, elements past hd by element 0) and
+// the values are selected in head_finish, so nothing here waits on them.
+template <int EPL>
+__device__ __forceinline__ void head_load(HeadIn<EPL>& in, const HeadSrc& h, const float* __restrict__ cs,
+                                          const float* __restrict__ sn, int hd, int lane) {
     const int half = hd >> 1;
-    float own[EPL], par[EPL];
+    const float* gp = h.gamma ? h.gamma : h.raw;
+    const float* cp = h.rope ? cs : h.raw;
+    const float* sp = h.rope ? sn : h.raw;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int i0 = lane + 64 * j;
+        const int i = i0 < hd ? i0 : 0;
+        const bool first = i < half;
+        const int pi = first ? i + half : i - half;
+        const int t = first ? i : pi;
+        in.own[j] = h.raw[i];
+        in.par[j] = h.raw[pi];
+        in.ga[j] = gp[i];
+        in.gb[j] = gp[pi];
+        in.cs[j] = cp[t];
+        in.sn[j] = sp[t];
+    }
+}
+
+// Writes the head to dst (LDS); with kv_dst also stores it as KV (a cache
+// row), and dst then holds the stored value.
+template <typename KV, int EPL>
+__device__ __forceinline__ void head_finish(const HeadIn<EPL>& in, const HeadSrc& h, int hd, float eps, int lane,
+                                            float* dst, KV* kv_dst) {
+    const int half = hd >> 1;
+    const bool wg = h.gamma != nullptr;
+    float own[EPL];
     float ss = 0.0f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-        const int i = lane + 64 * j;
-        own[j] = 0.0f;
-        par[j] = 0.0f;
-        if (i < hd) {
-            own[j] = raw[i];
-            if (rope) par[j] = raw[i < half ? i + half : i - half];
-        }
+        own[j] = lane + 64 * j < hd ? in.own[j] : 0.0f;
         ss += own[j] * own[j];
     }
     float rinv = 1.0f;
-    if (norm) rinv = 1.0f / sqrtf(wave_sum(ss) / (float)hd + eps);
+    if (h.norm) rinv = 1.0f / sqrtf(wave_sum(ss) / (float)hd + eps);
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
         const int i = lane + 64 * j;
         if (i < hd) {
-            const bool first = i < half;
-            const int pi = first ? i + half : i - half;
-            const float av = own[j] * rinv * (gamma ? gamma[i] : 1.0f);
+            const float av = own[j] * rinv * (wg ? in.ga[j] : 1.0f);
             float y = av;
-            if (rope) {
-                const float bv = par[j] * rinv * (gamma ? gamma[pi] : 1.0f);
-                const int t = first ? i : pi;
-                y = first ? av * cs[t] - bv * sn[t] : bv * sn[t] + av * cs[t];
+            if (h.rope) {
+                const float bv = in.par[j] * rinv * (wg ? in.gb[j] : 1.0f);
+                y = i < half ? av * in.cs[j] - bv * in.sn[j] : bv * in.sn[j] + av * in.cs[j];
             }
-            y *= scale;
+            y *= h.scale;
             if (kv_dst) {
                 if constexpr (sizeof(KV) == 4) {
                     kv_dst[i] = y;
@@ -166,14 +196,16 @@ __device__ __forceinline__ int4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // One split of the positions of one kv head, all G query heads of it.
 //   KV: float or uint16_t (bf16).  CM: chunks (16 bytes) per row at most, so
 //   head_dim <= CM * CE; GM: query heads per kv head at most; NP: lanes per
-//   position in the K phase; TILE: positions per wave iteration.
-// The loops run over CM and GM; rows shorter than CM chunks load zeros past
-// their end and query heads past G are zero, so exact shapes (CM*CE ==
-// head_dim, GM == G) do no wasted work and padded ones stay correct.
-template <typename KV, int CM, int GM, int NP, int TILE>
-__global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
+//   position in the K phase; TILE: positions per wave iteration; EX: the
+//   shape is exact (head_dim == CM * CE, G == GM), known at compile time;
+//   WPE: waves per SIMD the register budget is set for (workgroups per CU).
+// Inexact shapes run the same loops over CM and GM: rows shorter than CM
+// chunks load zeros past their end and query heads past G are zero.
+template <typename KV, int CM, int GM, int NP, int TILE, bool EX, int WPE>
+__global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     constexpr int CE = KvTraits<KV>::CE;
     constexpr int HDM = CM * CE;                  // largest head_dim
+    constexpr int EPL = (HDM + 63) / 64;          // prologue elements per lane
     constexpr int CPL = (CM + NP - 1) / NP;       // K chunks per lane
     constexpr int TP = kWave / NP;                // positions per K step
     constexpr int KSTEPS = TILE / TP;
@@ -181,7 +213,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
     constexpr int VTP = kWave / VC;               // positions per V step
     constexpr int VCPL = (CM + 63) / 64;          // V chunks per lane
     constexpr int VSTEPS = (TILE + VTP - 1) / VTP;
-    static_assert(TILE % TP == 0 && TILE <= 64 && HDM <= 512 && GM <= 8, "tile shape");
+    // softmax: HPP heads side by side, TW lanes (>= TILE) per head
+    constexpr int TW = TILE <= 4 ? 4 : TILE <= 8 ? 8 : TILE <= 16 ? 16 : TILE <= 32 ? 32 : 64;
+    constexpr int HPP = kWave / TW < GM ? kWave / TW : GM;
+    constexpr int NPASS = GM / HPP;
+    static_assert(TILE % TP == 0 && TILE <= 64 && HDM <= 512 && GM <= 8 && GM % HPP == 0, "tile shape");
     constexpr int RED = kWavesPerWG * kRedFloats;
 
     __shared__ float sc[kWavesPerWG][TILE][GM];   // per wave: scores, then probabilities
@@ -192,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = blockIdx.y, split = blockIdx.x;
-    const int hd = a.hd, G = a.G, C = hd / CE;
+    const int hd = EX ? HDM : a.hd, G = EX ? GM : a.G, C = EX ? CM : hd / CE;
     const int64_t end = a.start + a.len;
     const int64_t ps0 = a.start + (int64_t)split * a.tiles_per_split * TILE;
     const int64_t ps1 = ps0 + (int64_t)a.tiles_per_split * TILE < end ? ps0 + (int64_t)a.tiles_per_split * TILE : end;
@@ -240,39 +276,64 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
         }
     };
 
-    // ---- first tile in flight before the prologue
+    // ---- prologue items: the G query heads of this kv head (pre-scaled by
+    // scale*log2(e)), wave w taking heads w, w+4, ...; in the decode layer
+    // they are normalised and rotated here, and the wave whose tiles hold the
+    // new position also builds the new k and v rows and appends them to the
+    // caches (it alone reads them back, from LDS).
+    const int t_new = lp_new >= 0 ? lp_new / TILE : -1;
+    const bool owner = t_new >= 0 && t_new % kWavesPerWG == wave;
+    const int n_qi = wave < G ? (G - wave + kWavesPerWG - 1) / kWavesPerWG : 0;
+    const int n_items = n_qi + (owner ? 2 : 0);
+    auto item_src = [&](int i) -> HeadSrc {
+        if (i < n_qi) {
+            const float* raw = a.q + (int64_t)(g * G + wave + kWavesPerWG * i) * hd;
+            if (!a.fused) return HeadSrc{raw, nullptr, false, false, a.qscale};
+            return HeadSrc{raw, a.qk_norm ? a.g_q : nullptr, a.qk_norm != 0, true, a.qscale};
+        }
+        const float* kraw = a.q + (int64_t)a.n_q * hd + (int64_t)g * hd;
+        if (i == n_qi) return HeadSrc{kraw, a.qk_norm ? a.g_k : nullptr, a.qk_norm != 0, true, 1.0f};
+        return HeadSrc{kraw + (int64_t)a.n_kv * hd, nullptr, a.v_unit_norm != 0, false, 1.0f};
+    };
+    auto item_run = [&](int i, const HeadIn<EPL>& in, const HeadSrc& src) {
+        if (i < n_qi) {
+            head_finish<KV, EPL>(in, src, hd, a.eps, lane, q_lds + (wave + kWavesPerWG * i) * HDM, nullptr);
+        } else {
+            const int64_t row = (int64_t)g * a.head_stride + pos_new * a.pos_stride;
+            KV* cache = static_cast<KV*>(i == n_qi ? a.kc_w : a.vc_w);
+            head_finish<KV, EPL>(in, src, hd, a.eps, lane, kv_new[i - n_qi], cache + row);
+        }
+    };
+
+    // the items' inputs are read before the wave's first K/V tile (all of
+    // them when they fit in registers), the tile before the items are
+    // computed
+    constexpr int MAXI = (GM + kWavesPerWG - 1) / kWavesPerWG + 2;
+    constexpr int EARLY = MAXI * 6 * EPL <= 72 ? MAXI : 1;
+    HeadIn<EPL> hin[EARLY];
+    HeadSrc srcs[EARLY];
+#pragma unroll
+    for (int i = 0; i < EARLY; ++i) {
+        if (i < n_items) {
+            srcs[i] = item_src(i);
+            head_load<EPL>(hin[i], srcs[i], a.rope_cos, a.rope_sin, hd, lane);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of the tile's
     int t = wave;
     int4 kr[KSTEPS][CPL];
     int4 vr[VSTEPS][VCPL];
     load_k(t, kr);
     load_v(t, vr);
-
-    // ---- prologue, one head vector per wave at a time, into LDS: the query
-    // heads of this kv head, pre-scaled by scale*log2(e).  In the decode
-    // layer the raw projection is normalised and rotated here, and the
-    // workgroup whose positions include the new one also builds the new k and
-    // v rows and appends them to the caches.
-    {
-        const bool mine = lp_new >= 0;
-        const int items = G + (mine ? 2 : 0);
-        for (int it = wave; it < items; it += kWavesPerWG) {
-            if (!a.fused) {
-                head_vec<KV>(a.q + (int64_t)(g * G + it) * hd, nullptr, nullptr, nullptr, hd, false, false, 0.0f,
-                             a.qscale, lane, q_lds + it * HDM, nullptr);
-            } else if (it < G) {
-                head_vec<KV>(a.q + (int64_t)(g * G + it) * hd, a.qk_norm ? a.g_q : nullptr, a.rope_cos, a.rope_sin,
-                             hd, a.qk_norm, true, a.eps, a.qscale, lane, q_lds + it * HDM, nullptr);
-            } else {
-                const float* kraw = a.q + (int64_t)a.n_q * hd + (int64_t)g * hd;
-                const int64_t row = (int64_t)g * a.head_stride + pos_new * a.pos_stride;
-                if (it == G)
-                    head_vec<KV>(kraw, a.qk_norm ? a.g_k : nullptr, a.rope_cos, a.rope_sin, hd, a.qk_norm, true,
-                                 a.eps, 1.0f, lane, kv_new[0], static_cast<KV*>(a.kc_w) + row);
-                else
-                    head_vec<KV>(kraw + (int64_t)a.n_kv * hd, nullptr, nullptr, nullptr, hd, a.v_unit_norm, false,
-                                 a.eps, 1.0f, lane, kv_new[1], static_cast<KV*>(a.vc_w) + row);
-            }
-        }
+#pragma unroll
+    for (int i = 0; i < EARLY; ++i)
+        if (i < n_items) item_run(i, hin[i], srcs[i]);
+    for (int i = EARLY; i < n_items; ++i) {
+        const HeadSrc src = item_src(i);
+        head_load<EPL>(hin[0], src, a.rope_cos, a.rope_sin, hd, lane);
+        item_run(i, hin[0], src);
+    }
+    if (!EX) {
         // zero the padding: query heads past G, dims past head_dim
         for (int i = threadIdx.x; i < GM * HDM; i += 256)
             if (i / HDM >= G || i % HDM >= hd) q_lds[i] = 0.0f;
@@ -292,16 +353,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
             }
         }
 
-    float m[GM], l[GM], acc[GM][VCPL][CE];
+    // softmax state: lane (hs, sp) keeps head pass*HPP + hs
+    const int hs = lane / TW, sp = lane % TW;
+    float ms[NPASS], ls[NPASS], acc[GM][VCPL][CE];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
+    for (int ps = 0; ps < NPASS; ++ps) {
+        ms[ps] = -INFINITY;
+        ls[ps] = 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
 #pragma unroll
         for (int c = 0; c < VCPL; ++c)
 #pragma unroll
             for (int e = 0; e < CE; ++e) acc[h][c][e] = 0.0f;
-    }
 
     for (; t < n_tiles; t += kWavesPerWG) {
         const int lp0 = t * TILE;                        // first position of the tile, split-local
@@ -351,27 +416,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
         }
         wave_lds_sync();
 
-        // ---- softmax over the tile, lane = position
+        // ---- softmax over the tile: HPP heads at once, lane = (head, position)
         float alpha[GM], pn[GM];
         {
-            const bool ok = lane < TILE && lp0 + lane < n_pos;
+            const bool ok = hs < HPP && sp < TILE && lp0 + sp < n_pos;
+            const int spc = sp < TILE ? sp : 0;
 #pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                const float s = ok ? sc[wave][lane < TILE ? lane : 0][h] : -INFINITY;
-                const float mt = wave_max(s);
-                const float mn = fmaxf(m[h], mt);
-                float p = 0.0f;
-                if (mn == -INFINITY) {
-                    alpha[h] = 1.0f;
-                } else {
-                    alpha[h] = exp2f(m[h] - mn);
-                    p = ok ? exp2f(s - mn) : 0.0f;
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const int h = ps * HPP + (hs < HPP ? hs : 0);
+                const float s = ok ? sc[wave][spc][h] : -INFINITY;
+                const float mn = fmaxf(ms[ps], group_max<TW>(s));
+                const bool live = mn != -INFINITY;
+                const float al = live ? exp2f(ms[ps] - mn) : 1.0f;
+                const float p = (ok && live) ? exp2f(s - mn) : 0.0f;
+                ls[ps] = ls[ps] * al + p;
+                ms[ps] = mn;
+#pragma unroll
+                for (int j = 0; j < HPP; ++j) {
+                    alpha[ps * HPP + j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), j * TW));
+                    pn[ps * HPP + j] = pt_new >= 0
+                        ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j * TW + pt_new)) : 0.0f;
                 }
-                l[h] = l[h] * alpha[h] + p;
-                m[h] = mn;
-                pn[h] = pt_new >= 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), pt_new)) : 0.0f;
                 // the new position's V term is added from LDS below
-                if (lane < TILE) sc[wave][lane][h] = (lane == pt_new) ? 0.0f : p;
+                if (hs < HPP && sp < TILE) sc[wave][sp][h] = (sp == pt_new) ? 0.0f : p;
             }
         }
         wave_lds_sync();
@@ -420,15 +487,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
     // ---- combine the waves of this workgroup (fixed order: waves, then
     // position groups), in chunks of heads that fit the LDS buffer
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        const float ls = wave_sum(l[h]);
-        if (lane == 0) {
-            wm[wave][h] = m[h];
-            wl[wave][h] = ls;
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const float lsum = group_sum<TW>(ls[ps]);
+        if (sp == 0 && hs < HPP) {
+            wm[wave][ps * HPP + hs] = ms[ps];
+            wl[wave][ps * HPP + hs] = lsum;
         }
     }
     constexpr int per_head = VTP * HDM;
-    constexpr int HC = kRedFloats / per_head >= 1 ? kRedFloats / per_head : 1;
+    constexpr int HC = kRedFloats / per_head < GM ? kRedFloats / per_head : GM;
     static_assert(per_head <= kRedFloats, "combine buffer");
     for (int h0 = 0; h0 < G; h0 += HC) {
         const int h1 = h0 + HC < G ? h0 + HC : G;
@@ -481,46 +548,75 @@ __global__ __launch_bounds__(256, 2) void k_attn_split(AttnArgs a) {
     }
 }
 
-// Rescale and sum the split partials.  One wave per (query head, 64 dims):
-// lane s reads the split maxima, the wave forms the split weights
-// exp2(m_s - M) and the total L once, then every lane sums its dim over the
-// splits with 16 loads in flight.
+// Rescale and sum the split partials: one workgroup per (query head, 64
+// dims), wave w taking the splits s = w (mod 4).  Lane j reads the maximum and
+// sum of the wave's split j while every lane's partial-vector loads are
+// already in flight; the wave forms its weights exp2(m_s - M_w), sums its
+// splits, and wave 0 merges the four waves in a fixed order.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-    __shared__ float wts[kWavesPerWG][kMaxSplitsC];
+    constexpr int kBatch = 16;
+    __shared__ float wts[kWavesPerWG][kWave];
+    __shared__ float gm[kWavesPerWG], gl[kWavesPerWG], gacc[kWavesPerWG][kWave];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int chunks = (a.hd + 63) / 64;
-    const int unit = blockIdx.x * kWavesPerWG + wave;
-    if (unit >= a.n_q * chunks) return;
-    const int hq = unit / chunks, d = (unit - hq * chunks) * 64 + lane;
-    const int g = hq / a.G, h = hq - g * a.G;
-    const int S = a.nsplit, G = a.G, hd = a.hd;
+    const int hq = blockIdx.y, d = blockIdx.x * kWave + lane;
+    const int G = a.G, hd = a.hd, S = a.nsplit;
+    const int g = hq / G, h = hq - g * G;
     const int64_t base = (int64_t)g * S * G + h;          // slot of split s = base + s*G
-    float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, a.part_m[base + (int64_t)s * G]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int s = lane; s < S; s += 64) {
-        const float ms = a.part_m[base + (int64_t)s * G];
-        const float e = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-        wts[wave][s] = e;
-        L += e * a.part_l[base + (int64_t)s * G];
+    const int ns = S > wave ? (S - wave + kWavesPerWG - 1) / kWavesPerWG : 0;   // this wave's splits (<= 64)
+    const bool dl = d < hd;
+
+    float mj = -INFINITY, lj = 0.0f;
+    if (lane < ns) {
+        const int64_t slot = base + (int64_t)(wave + kWavesPerWG * lane) * G;
+        mj = a.part_m[slot];
+        lj = a.part_l[slot];
     }
-    L = wave_sum(L);
+    // partial vectors: loads from clamped, valid slots; values past the
+    // wave's splits are dropped by their zero weight
+    const int dc = dl ? d : 0;
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int uc = u < ns ? u : (ns > 0 ? ns - 1 : 0);
+        const int64_t slot = base + (int64_t)(ns > 0 ? wave + kWavesPerWG * uc : 0) * G;
+        v[u] = a.part_acc[slot * hd + dc];
+    }
+    const float Mw = wave_max(mj);
+    const float wj = (mj == -INFINITY) ? 0.0f : exp2f(mj - Mw);
+    const float Lw = wave_sum(wj * lj);
+    wts[wave][lane] = wj;
     wave_lds_sync();
-    if (d >= hd) return;
-    const float* acc = a.part_acc + base * hd + d;
-    const int64_t stride = (int64_t)G * hd;
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int s = 0;
-    for (; s + 16 <= S; s += 16) {
-        float v[16];
+    float sum = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = acc[(int64_t)(s + u) * stride];
+    for (int u = 0; u < kBatch; ++u) sum = fmaf(wts[wave][u], v[u], sum);     // wts is 0 past ns
+    for (int u0 = kBatch; u0 < ns; u0 += kBatch) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) sum[u & 3] = fmaf(wts[wave][s + u], v[u], sum[u & 3]);
+        for (int u = 0; u < kBatch; ++u) {
+            const int uc = u0 + u < ns ? u0 + u : ns - 1;
+            v[u] = a.part_acc[(base + (int64_t)(wave + kWavesPerWG * uc) * G) * hd + dc];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) sum = fmaf(wts[wave][u0 + u < kWave ? u0 + u : kWave - 1], v[u], sum);
     }
-    for (; s < S; ++s) sum[0] = fmaf(wts[wave][s], acc[(int64_t)s * stride], sum[0]);
-    a.out[(int64_t)hq * hd + d] = ((sum[0] + sum[1]) + (sum[2] + sum[3])) / L;
+    if (lane == 0) {
+        gm[wave] = Mw;
+        gl[wave] = Lw;
+    }
+    gacc[wave][lane] = sum;
+    __syncthreads();
+    if (wave == 0 && dl) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, gm[w]);
+        float L = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerWG; ++w) {
+            const float e = (gm[w] == -INFINITY) ? 0.0f : exp2f(gm[w] - M);
+            L = fmaf(e, gl[w], L);
+            acc = fmaf(e, gacc[w][lane], acc);
+        }
+        a.out[(int64_t)hq * hd + d] = acc / L;
+    }
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {
@@ -535,7 +631,6 @@ struct Plan {
     int nsplit, tiles_per_split;
 };
 
-constexpr int kTargetWGs = 512;    // two workgroups of 4 waves per CU
 constexpr int kMaxSplits = kMaxSplitsC;
 
 using SplitFn = void (*)(dim3, hipStream_t, const AttnArgs&, LaunchMarks*);
@@ -545,29 +640,30 @@ struct Variant {
     int c;       // chunks per row (head_dim / CE), exact
     int g;       // G, exact
     int tile;
+    int wpe;     // workgroups per CU resident at once
     SplitFn fn;
 };
 
-template <typename KV, int CM, int GM, int NP, int TILE>
+template <typename KV, int CM, int GM, int NP, int TILE, int WPE = 2, bool EX = true>
 void launch_split(dim3 grid, hipStream_t s, const AttnArgs& a, LaunchMarks* mk) {
-    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE>, grid, dim3(256), 0, s, a);
+    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE, EX, WPE>, grid, dim3(256), 0, s, a);
 }
 
-// Exact shapes of the common models; <KV, chunks, G, lanes per position, tile>.
+// Exact shapes of the common models; <KV, chunks, G, lanes per position, tile, WGs per CU>.
 const Variant kVariants[] = {
-    {LQ_KV_F32, 16, 2, 32, launch_split<float, 16, 2, 8, 32>},          // head_dim 64
-    {LQ_KV_F32, 16, 4, 32, launch_split<float, 16, 4, 8, 32>},
-    {LQ_KV_F32, 32, 4, 16, launch_split<float, 32, 4, 16, 16>},         // head_dim 128
-    {LQ_KV_BF16, 8, 2, 32, launch_split<uint16_t, 8, 2, 8, 32>},        // head_dim 64
-    {LQ_KV_BF16, 8, 4, 32, launch_split<uint16_t, 8, 4, 8, 32>},
-    {LQ_KV_BF16, 10, 2, 32, launch_split<uint16_t, 10, 2, 8, 32>},      // head_dim 80
-    {LQ_KV_BF16, 10, 4, 32, launch_split<uint16_t, 10, 4, 8, 32>},
-    {LQ_KV_BF16, 16, 2, 32, launch_split<uint16_t, 16, 2, 8, 32>},      // head_dim 128
-    {LQ_KV_BF16, 16, 4, 32, launch_split<uint16_t, 16, 4, 8, 32>},
-    {LQ_KV_BF16, 16, 8, 16, launch_split<uint16_t, 16, 8, 16, 16>},
-    {LQ_KV_BF16, 32, 2, 16, launch_split<uint16_t, 32, 2, 16, 16>},     // head_dim 256
-    {LQ_KV_BF16, 32, 4, 16, launch_split<uint16_t, 32, 4, 16, 16>},
-    {LQ_KV_BF16, 64, 8, 8, launch_split<uint16_t, 64, 8, 64, 8>},       // head_dim 512
+    {LQ_KV_F32, 16, 2, 32, 2, launch_split<float, 16, 2, 8, 32>},          // head_dim 64
+    {LQ_KV_F32, 16, 4, 32, 2, launch_split<float, 16, 4, 8, 32>},
+    {LQ_KV_F32, 32, 4, 16, 2, launch_split<float, 32, 4, 16, 16>},         // head_dim 128
+    {LQ_KV_BF16, 8, 2, 32, 2, launch_split<uint16_t, 8, 2, 8, 32>},        // head_dim 64
+    {LQ_KV_BF16, 8, 4, 32, 2, launch_split<uint16_t, 8, 4, 8, 32>},
+    {LQ_KV_BF16, 10, 2, 32, 2, launch_split<uint16_t, 10, 2, 8, 32>},      // head_dim 80
+    {LQ_KV_BF16, 10, 4, 32, 2, launch_split<uint16_t, 10, 4, 8, 32>},
+    {LQ_KV_BF16, 16, 2, 32, 2, launch_split<uint16_t, 16, 2, 8, 32>},      // head_dim 128
+    {LQ_KV_BF16, 16, 4, 32, 2, launch_split<uint16_t, 16, 4, 8, 32>},
+    {LQ_KV_BF16, 16, 8, 16, 2, launch_split<uint16_t, 16, 8, 16, 16>},
+    {LQ_KV_BF16, 32, 2, 16, 2, launch_split<uint16_t, 32, 2, 16, 16>},     // head_dim 256
+    {LQ_KV_BF16, 32, 4, 16, 2, launch_split<uint16_t, 32, 4, 16, 16>},
+    {LQ_KV_BF16, 64, 8, 8, 2, launch_split<uint16_t, 64, 8, 64, 8>},       // head_dim 512
 };
 
 int ce_of(int32_t dtype) { return dtype == LQ_KV_F32 ? 4 : 8; }
@@ -575,20 +671,21 @@ int ce_of(int32_t dtype) { return dtype == LQ_KV_F32 ? 4 : 8; }
 struct Pick {
     SplitFn fn;
     int tile;
+    int wpe;
 };
 
 Pick pick(int32_t dtype, int64_t hd, int64_t G) {
     const int c = (int)(hd / ce_of(dtype));
     for (const Variant& v : kVariants)
-        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile};
+        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe};
     // any head_dim <= 512 and G <= 8: padded loops, one position per K step
-    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4>, 4};
-    return Pick{launch_split<uint16_t, 64, 8, 64, 8>, 8};
+    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2};
+    return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2};
 }
 
-Plan make_plan(int64_t n_kv, int64_t len, int tile) {
+Plan make_plan(int64_t n_kv, int64_t len, int tile, int wpe) {
     const int64_t tiles = (len + tile - 1) / tile;
-    int64_t ns = (kTargetWGs + n_kv - 1) / n_kv;
+    int64_t ns = ((int64_t)kNumCUs * wpe + n_kv - 1) / n_kv;             // one resident round of workgroups
     const int64_t by_tiles = (tiles + kWavesPerWG - 1) / kWavesPerWG;   // every wave gets a tile
     if (ns > by_tiles) ns = by_tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
@@ -610,7 +707,8 @@ bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype) {
 
 static size_t ws_bytes_for(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t dtype) {
     if (len <= 0 || n_kv <= 0) return 0;
-    const Plan p = make_plan(n_kv, len, pick(dtype, hd, n_q / n_kv).tile);
+    const Pick pk = pick(dtype, hd, n_q / n_kv);
+    const Plan p = make_plan(n_kv, len, pk.tile, pk.wpe);
     if (p.nsplit == 1) return 0;
     const int64_t slots = n_kv * p.nsplit * (n_q / n_kv);
     return (size_t)(slots * (hd + 2)) * sizeof(float);
@@ -627,7 +725,7 @@ static lq_status launch_common(AttnArgs& a, int64_t n_q, int64_t n_kv, int64_t h
                                void* ws, hipStream_t s, LaunchMarks* marks = nullptr) {
     const int64_t G = n_q / n_kv;
     const Pick pk = pick(kv_dtype, hd, G);
-    const Plan p = make_plan(n_kv, a.len, pk.tile);
+    const Plan p = make_plan(n_kv, a.len, pk.tile, pk.wpe);
     // buffer offsets inside one split stay below 2^31 bytes
     const int64_t es = kv_dtype == LQ_KV_F32 ? 4 : 2;
     if (((int64_t)p.tiles_per_split * pk.tile + 64) * a.pos_stride * es >= (int64_t(1) << 31))
@@ -645,8 +743,7 @@ static lq_status launch_common(AttnArgs& a, int64_t n_q, int64_t n_kv, int64_t h
     pk.fn(dim3((unsigned)p.nsplit, (unsigned)n_kv), s, a, marks);
     lq_status st = check_launch("attention split");
     if (st != LQ_OK || p.nsplit == 1) return st;
-    const int units = (int)(n_q * ((hd + 63) / 64));
-    launch_marked(marks, k_attn_combine, dim3((unsigned)((units + kWavesPerWG - 1) / kWavesPerWG)), dim3(256), 0,
+    launch_marked(marks, k_attn_combine, dim3((unsigned)((hd + kWave - 1) / kWave), (unsigned)n_q), dim3(256), 0,
                   s, a);
     return check_launch("attention combine");
 }
@@ -725,7 +822,7 @@ extern "C" lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_k
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn, need,
                     workspace_bytes);
-    if (n_kv > 65535) return fail(LQ_ERR_UNSUPPORTED, "%s: too many kv heads", fn);
+    if (n_q > 65535) return fail(LQ_ERR_UNSUPPORTED, "%s: too many query heads", fn);
     return launch_attention(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_stride, pos_stride, start,
                             len, scale, out, workspace, as_stream(stream));
 }

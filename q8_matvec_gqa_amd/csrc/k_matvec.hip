@@ -156,6 +156,12 @@ __global__ __launch_bounds__(256) void k_q8_matvec_any(const int8_t* __restrict_
 // Each wave owns a fixed 16-byte K-slice per 1 KB chunk, so its activation
 // slice is copied from LDS to VGPRs once and reused for every row.
 // ---------------------------------------------------------------------------
+// Waves per SIMD each instance is compiled for: two where the weight double
+// buffer and the activation slice fit in 256 VGPRs, else one (long rows,
+// wide SwiGLU pairs), rather than spilling.
+template <int NCH, int EPI> struct MvWpe {
+    static constexpr int value = (NCH > 8 || (EPI == EPI_SWIGLU && NCH > 5)) ? 1 : 2;
+};
 constexpr int kMaxCols = 16384;
 
 template <int NCH, int RPW>
@@ -164,6 +170,10 @@ struct RowGroup {
     uint32_t d[RPW][NCH];
 };
 
+// Loads are unconditional, from clamped addresses: rows past the end reload
+// the last row (never stored) and 16-byte slices past the last column reload
+// the row's last slice (their activation slice is zero).  No branches sit
+// between the loads, so nothing forces an early wait on them.
 template <int NCH, int RPW, int EPI>
 __device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int lane, RowGroup<NCH, RPW>& G) {
     const int nb = a.cols >> 5;
@@ -171,35 +181,62 @@ __device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int lane,
     for (int i = 0; i < RPW; ++i) {
         // SwiGLU pairs: even i -> gate row, odd i -> the matching up row
         int64_t r;
-        if constexpr (EPI == EPI_SWIGLU) r = (g * (RPW / 2) + i / 2) + (i & 1) * (int64_t)a.rows;
-        else r = g * RPW + i;
-        const bool ok = (EPI == EPI_SWIGLU) ? (g * (RPW / 2) + i / 2 < a.rows) : (r < a.rows);
+        if constexpr (EPI == EPI_SWIGLU) {
+            int64_t o = g * (RPW / 2) + i / 2;
+            if (o >= a.rows) o = a.rows - 1;
+            r = o + (i & 1) * (int64_t)a.rows;
+        } else {
+            r = g * RPW + i;
+            if (r >= a.rows) r = a.rows - 1;
+        }
+        const int8_t* wr = a.wq + r * a.cols;
+        const uint16_t* dr = a.wd + r * nb;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int off = c * 1024 + lane * 16;
-            if (ok && off < a.cols) {
-                G.w[i][c] = load_stream16(a.wq + r * a.cols + off);
-                G.d[i][c] = a.wd[r * nb + (off >> 5)];
-            } else {
-                G.w[i][c] = make_int4(0, 0, 0, 0);
-                G.d[i][c] = 0;
-            }
+            int off = c * 1024 + lane * 16;
+            if (off >= a.cols) off = a.cols - 16;
+            G.w[i][c] = load_stream16(wr + off);
+            G.d[i][c] = dr[off >> 5];
         }
     }
 }
 
-template <int NCH, int RPW, int EPI>
+// The wave's activation slice (16 bytes of codes and the block scale per
+// 1 KB chunk): held in VGPRs, or for long rows (XL) read from LDS at each
+// use to keep the register budget for the weight double buffer.
+template <int NCH, bool XL>
+struct XAct {
+    int4 v[XL ? 1 : NCH];
+    float s[XL ? 1 : NCH];
+    const int8_t* q_lds;
+    const float* s_lds;
+    __device__ __forceinline__ void get(int c, int lane, int4& x4, float& xs) const {
+        if constexpr (XL) {
+            const int off = c * 1024 + lane * 16;
+            x4 = *reinterpret_cast<const int4*>(q_lds + off);
+            xs = s_lds[off >> 5];
+        } else {
+            x4 = v[c];
+            xs = s[c];
+        }
+    }
+};
+
+template <int NCH, int RPW, int EPI, bool XL>
 __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int lane, const RowGroup<NCH, RPW>& G,
-                                              const int4 (&xv)[NCH], const float (&xs)[NCH]) {
+                                              const XAct<NCH, XL>& x) {
     float acc[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         float t = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int p = dot16(G.w[i][c], xv[c]);
+            int4 x4;
+            float xsc;
+            x.get(c, lane, x4, xsc);
+            const int p = dot16(G.w[i][c], x4);
             const int blk = p + dpp_i<kQuadXor1>(p);
-            const float v = (float)blk * (f16_to_f32(G.d[i][c]) * xs[c]);
+            const float v = (float)blk * (f16_to_f32(G.d[i][c]) * xsc);
             t += (lane & 1) ? 0.0f : v;
         }
         acc[i] = wave_sum(t);
@@ -224,9 +261,11 @@ __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int la
 }
 
 template <int NCH, int RPW, int PRO, int EPI>
-__global__ __launch_bounds__(256) void k_mv(MvArgs a) {
-    __shared__ __attribute__((aligned(16))) int8_t xq_s[PRO == PRO_Q8 ? 16 : kMaxCols];
-    __shared__ float xs_s[PRO == PRO_Q8 ? 1 : kMaxCols / 32];
+__global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) {
+    constexpr bool XL = NCH > 8;                          // activation slice from LDS
+    constexpr bool LDS_X = (PRO != PRO_Q8) || XL;
+    __shared__ __attribute__((aligned(16))) int8_t xq_s[LDS_X ? kMaxCols : 16];
+    __shared__ float xs_s[LDS_X ? kMaxCols / 32 : 1];
     __shared__ float red[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = a.cols >> 5;
@@ -235,91 +274,171 @@ __global__ __launch_bounds__(256) void k_mv(MvArgs a) {
     const int64_t gstride = (int64_t)gridDim.x * 4;
     int64_t g = (int64_t)blockIdx.x * 4 + wave;
 
-    // first row group in flight before the prologue
+    // The prologue's own loads (x, and gamma when it fits in registers; or
+    // the Q8 activation that goes to LDS) are issued first, then the first
+    // row group's weights: loads retire in order, so the prologue can compute
+    // while the weights are in flight.
+    constexpr int BPT = (NCH * 32 + 255) / 256;          // activation blocks per thread
+    constexpr bool EARLY_G = (PRO == PRO_NORM) && BPT == 1;
+    constexpr int QPT = (NCH * 64 + 255) / 256;          // Q8 16-byte slices per thread (XL copy)
+    float xf[PRO != PRO_Q8 ? BPT : 1][32];
+    float gf[EARLY_G ? BPT : 1][32];
+    int4 qc[(PRO == PRO_Q8 && XL) ? QPT : 1];
+    float dc[(PRO == PRO_Q8 && XL) ? BPT : 1];
+    if constexpr (PRO != PRO_Q8) {
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int b = threadIdx.x + 256 * k;
+            const int bc = b < nb ? b : 0;                // valid address; values dropped below
+            load32(a.x + 32 * bc, xf[k]);
+            if constexpr (EARLY_G) load32((a.gamma ? a.gamma : a.x) + 32 * bc, gf[k]);
+        }
+    } else if constexpr (XL) {
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+            const int i = threadIdx.x + 256 * k;          // 16-byte slice
+            const int ic = i * 16 < a.cols ? i : 0;
+            qc[k] = *reinterpret_cast<const int4*>(a.xq + 16 * ic);
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int b = threadIdx.x + 256 * k;
+            dc[k] = f16_to_f32(a.xd[b < nb ? b : 0]);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     RowGroup<NCH, RPW> A, B;
-    if (g < ngroups) load_group<NCH, RPW, EPI>(a, g, lane, A);
+    load_group<NCH, RPW, EPI>(a, g, lane, A);            // clamped: waves past the end reload the last group
 
-    int4 xv[NCH];
-    float xs[NCH];
-    if constexpr (PRO == PRO_Q8) {
+    XAct<NCH, XL> x;
+    x.q_lds = xq_s;
+    x.s_lds = xs_s;
+    if constexpr (PRO == PRO_Q8 && !XL) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int off = c * 1024 + lane * 16;
-            xv[c] = make_int4(0, 0, 0, 0);
-            xs[c] = 0.0f;
+            x.v[c] = make_int4(0, 0, 0, 0);
+            x.s[c] = 0.0f;
             if (off < a.cols) {
-                xv[c] = *reinterpret_cast<const int4*>(a.xq + off);
-                xs[c] = f16_to_f32(a.xd[off >> 5]);
+                x.v[c] = *reinterpret_cast<const int4*>(a.xq + off);
+                x.s[c] = f16_to_f32(a.xd[off >> 5]);
             }
         }
     } else {
-        float rinv = 1.0f;
-        if constexpr (PRO == PRO_NORM) {
-            float ss = 0.0f;
-            for (int i = threadIdx.x * 4; i < a.cols; i += 1024) {
-                const float4 t = *reinterpret_cast<const float4*>(a.x + i);
-                ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+        if constexpr (PRO == PRO_Q8) {
+#pragma unroll
+            for (int k = 0; k < QPT; ++k) {
+                const int i = threadIdx.x + 256 * k;
+                if (i * 16 < a.cols) *reinterpret_cast<int4*>(xq_s + 16 * i) = qc[k];
             }
-            ss = wave_sum(ss);
-            if (lane == 0) red[wave] = ss;
-            __syncthreads();
-            ss = (red[0] + red[1]) + (red[2] + red[3]);
-            rinv = 1.0f / sqrtf(ss / (float)a.cols + a.eps);
-        }
-        const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
-        for (int b = threadIdx.x; b < nb; b += 256) {
-            float v[32];
-            load32(a.x + 32 * b, v);
+#pragma unroll
+            for (int k = 0; k < BPT; ++k) {
+                const int b = threadIdx.x + 256 * k;
+                if (b < nb) xs_s[b] = dc[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < BPT; ++k)
+                if (threadIdx.x + 256 * k >= nb)
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) xf[k][i] = 0.0f;
+            float rinv = 1.0f;
             if constexpr (PRO == PRO_NORM) {
-                if (a.gamma) {
-                    float gm[32];
-                    load32(a.gamma + 32 * b, gm);
+                float ss = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) v[i] = (v[i] * rinv) * gm[i];
-                } else {
+                for (int k = 0; k < BPT; ++k)
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) v[i] = v[i] * rinv;
+                    for (int i = 0; i < 32; ++i) ss += xf[k][i] * xf[k][i];
+                ss = wave_sum(ss);
+                if (lane == 0) red[wave] = ss;
+                __syncthreads();
+                ss = (red[0] + red[1]) + (red[2] + red[3]);
+                rinv = 1.0f / sqrtf(ss / (float)a.cols + a.eps);
+            }
+            const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
+#pragma unroll
+            for (int k = 0; k < BPT; ++k) {
+                const int b = threadIdx.x + 256 * k;
+                if (b < nb) {
+                    float v[32];
+                    if constexpr (PRO == PRO_NORM) {
+                        if (a.gamma) {
+                            float gm[32];
+                            if constexpr (EARLY_G) {
+#pragma unroll
+                                for (int i = 0; i < 32; ++i) gm[i] = gf[k][i];
+                            } else {
+                                load32(a.gamma + 32 * b, gm);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 32; ++i) v[i] = (xf[k][i] * rinv) * gm[i];
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 32; ++i) v[i] = xf[k][i] * rinv;
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) v[i] = xf[k][i];
+                    }
+                    uint32_t packed[8];
+                    const uint16_t db = quantize_block32_packed(v, packed);
+                    store_codes32(xq_s + 32 * b, packed);
+                    xs_s[b] = f16_to_f32(db);
+                    if (tap) {
+                        store_codes32(a.tap_q + 32 * b, packed);
+                        a.tap_d[b] = db;
+                    }
                 }
             }
-            uint32_t packed[8];
-            const uint16_t db = quantize_block32_packed(v, packed);
-            store_codes32(xq_s + 32 * b, packed);
-            xs_s[b] = f16_to_f32(db);
-            if (tap) {
-                store_codes32(a.tap_q + 32 * b, packed);
-                a.tap_d[b] = db;
-            }
+        }
+        if constexpr (XL) {
+            // slices past the last column read as zero
+            for (int i = a.cols + 16 * threadIdx.x; i < NCH * 1024; i += 16 * 256)
+                *reinterpret_cast<int4*>(xq_s + i) = make_int4(0, 0, 0, 0);
+            for (int b = nb + threadIdx.x; b < NCH * 32; b += 256) xs_s[b] = 0.0f;
         }
         __syncthreads();
+        if constexpr (!XL) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int off = c * 1024 + lane * 16;
-            xv[c] = make_int4(0, 0, 0, 0);
-            xs[c] = 0.0f;
-            if (off < a.cols) {
-                xv[c] = *reinterpret_cast<const int4*>(xq_s + off);
-                xs[c] = xs_s[off >> 5];
+            for (int c = 0; c < NCH; ++c) {
+                const int off = c * 1024 + lane * 16;
+                x.v[c] = make_int4(0, 0, 0, 0);
+                x.s[c] = 0.0f;
+                if (off < a.cols) {
+                    x.v[c] = *reinterpret_cast<const int4*>(xq_s + off);
+                    x.s[c] = xs_s[off >> 5];
+                }
             }
         }
     }
 
-    // grid-stride over row groups, next group prefetched while this one is consumed
-    while (g < ngroups) {
-        const int64_t gn = g + gstride;
-        if (gn < ngroups) load_group<NCH, RPW, EPI>(a, gn, lane, B);
-        consume_group<NCH, RPW, EPI>(a, g, lane, A, xv, xs);
-        g = gn;
-        if (g >= ngroups) break;
-        const int64_t gn2 = g + gstride;
-        if (gn2 < ngroups) load_group<NCH, RPW, EPI>(a, gn2, lane, A);
-        consume_group<NCH, RPW, EPI>(a, g, lane, B, xv, xs);
-        g = gn2;
+    // grid-stride over row groups, the next group's loads issued before the
+    // current one is consumed.  Every load sits in straight-line code ahead
+    // of its consumer (the last step is peeled), so each wait covers exactly
+    // the loads it needs.
+    if (g >= ngroups) return;
+    while (true) {
+        const int64_t g1 = g + gstride;
+        if (g1 >= ngroups) {
+            consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x);
+            return;
+        }
+        load_group<NCH, RPW, EPI>(a, g1, lane, B);
+        consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x);
+        const int64_t g2 = g1 + gstride;
+        if (g2 >= ngroups) {
+            consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x);
+            return;
+        }
+        load_group<NCH, RPW, EPI>(a, g2, lane, A);
+        consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x);
+        g = g2;
     }
 }
 
 // Rows per wave and workgroups per CU for each shape class.
 template <int NCH> struct MvShape {
-    static constexpr int RPW = NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1);
+    static constexpr int RPW = NCH <= 2 ? 4 : (NCH <= 4 ? 2 : 1);
 };
 
 // Grid: never more workgroups than can be resident at once (so no wave of
