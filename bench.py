@@ -223,7 +223,8 @@ def _find(dirpath, suffix):
 def _kernel_match(name, tag):
     """rocprofv3 kernel names -> the layer's kernel tags."""
     if tag == "gate_up_matvec":
-        return "k_mv<4, 4, 2, 2>" in name
+        import re
+        return re.search(r"k_mv<\d+, \d+, 2, 2>", name) is not None     # the RMSNorm + SwiGLU instance
     if tag == "copy":
         return "neg" in name.lower()
     raise ValueError(tag)
@@ -253,7 +254,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, command):
     cfg = synthetic.layer_cfg(workload)
     algo = dict((t, b) for t, _, b in layer_kernels(cfg, True))["gate_up_matvec"]
     lines = [
-        f"# HBM traffic of the gate_up matvec (k_mv<NCH=4, RPW=4, NORM, SWIGLU>), {workload}",
+        f"# HBM traffic of the gate_up matvec (k_mv<NCH, RPW, NORM, SWIGLU>), {workload}",
         f"command_fetch: {command.replace('WRITE_SIZE', 'FETCH_SIZE')}",
         f"command_write: {command.replace('FETCH_SIZE', 'WRITE_SIZE')}",
         f"source_sha256: {source_hash(KERNEL_SOURCES)}",
