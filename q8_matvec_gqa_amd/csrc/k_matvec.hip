@@ -260,27 +260,28 @@ __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int la
     }
 }
 
-template <int NCH, int RPW, int PRO, int EPI>
-__global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) {
+template <int NCH, int RPW, int PRO, int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) {
+    constexpr int NT = WAVES * 64;
     constexpr bool XL = NCH > 8;                          // activation slice from LDS
     constexpr bool LDS_X = (PRO != PRO_Q8) || XL;
     __shared__ __attribute__((aligned(16))) int8_t xq_s[LDS_X ? kMaxCols : 16];
     __shared__ float xs_s[LDS_X ? kMaxCols / 32 : 1];
-    __shared__ float red[4];
+    __shared__ float red[WAVES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = a.cols >> 5;
     constexpr int OUT_PER_GROUP = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
     const int64_t ngroups = (a.rows + OUT_PER_GROUP - 1) / OUT_PER_GROUP;
-    const int64_t gstride = (int64_t)gridDim.x * 4;
-    int64_t g = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t gstride = (int64_t)gridDim.x * WAVES;
+    int64_t g = (int64_t)blockIdx.x * WAVES + wave;
 
     // The prologue's own loads (x, and gamma when it fits in registers; or
     // the Q8 activation that goes to LDS) are issued first, then the first
     // row group's weights: loads retire in order, so the prologue can compute
     // while the weights are in flight.
-    constexpr int BPT = (NCH * 32 + 255) / 256;          // activation blocks per thread
+    constexpr int BPT = (NCH * 32 + NT - 1) / NT;          // activation blocks per thread
     constexpr bool EARLY_G = (PRO == PRO_NORM) && BPT == 1;
-    constexpr int QPT = (NCH * 64 + 255) / 256;          // Q8 16-byte slices per thread (XL copy)
+    constexpr int QPT = (NCH * 64 + NT - 1) / NT;          // Q8 16-byte slices per thread (XL copy)
     float xf[PRO != PRO_Q8 ? BPT : 1][32];
     float gf[EARLY_G ? BPT : 1][32];
     int4 qc[(PRO == PRO_Q8 && XL) ? QPT : 1];
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) 
     if constexpr (PRO != PRO_Q8) {
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
-            const int b = threadIdx.x + 256 * k;
+            const int b = threadIdx.x + NT * k;
             const int bc = b < nb ? b : 0;                // valid address; values dropped below
             load32(a.x + 32 * bc, xf[k]);
             if constexpr (EARLY_G) load32((a.gamma ? a.gamma : a.x) + 32 * bc, gf[k]);
@@ -296,13 +297,13 @@ __global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) 
     } else if constexpr (XL) {
 #pragma unroll
         for (int k = 0; k < QPT; ++k) {
-            const int i = threadIdx.x + 256 * k;          // 16-byte slice
+            const int i = threadIdx.x + NT * k;          // 16-byte slice
             const int ic = i * 16 < a.cols ? i : 0;
             qc[k] = *reinterpret_cast<const int4*>(a.xq + 16 * ic);
         }
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
-            const int b = threadIdx.x + 256 * k;
+            const int b = threadIdx.x + NT * k;
             dc[k] = f16_to_f32(a.xd[b < nb ? b : 0]);
         }
     }
@@ -328,18 +329,18 @@ __global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) 
         if constexpr (PRO == PRO_Q8) {
 #pragma unroll
             for (int k = 0; k < QPT; ++k) {
-                const int i = threadIdx.x + 256 * k;
+                const int i = threadIdx.x + NT * k;
                 if (i * 16 < a.cols) *reinterpret_cast<int4*>(xq_s + 16 * i) = qc[k];
             }
 #pragma unroll
             for (int k = 0; k < BPT; ++k) {
-                const int b = threadIdx.x + 256 * k;
+                const int b = threadIdx.x + NT * k;
                 if (b < nb) xs_s[b] = dc[k];
             }
         } else {
 #pragma unroll
             for (int k = 0; k < BPT; ++k)
-                if (threadIdx.x + 256 * k >= nb)
+                if (threadIdx.x + NT * k >= nb)
 #pragma unroll
                     for (int i = 0; i < 32; ++i) xf[k][i] = 0.0f;
             float rinv = 1.0f;
@@ -352,13 +353,15 @@ __global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) 
                 ss = wave_sum(ss);
                 if (lane == 0) red[wave] = ss;
                 __syncthreads();
-                ss = (red[0] + red[1]) + (red[2] + red[3]);
+                ss = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) ss += red[w];
                 rinv = 1.0f / sqrtf(ss / (float)a.cols + a.eps);
             }
             const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
 #pragma unroll
             for (int k = 0; k < BPT; ++k) {
-                const int b = threadIdx.x + 256 * k;
+                const int b = threadIdx.x + NT * k;
                 if (b < nb) {
                     float v[32];
                     if constexpr (PRO == PRO_NORM) {
@@ -393,9 +396,9 @@ __global__ __launch_bounds__(256, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) 
         }
         if constexpr (XL) {
             // slices past the last column read as zero
-            for (int i = a.cols + 16 * threadIdx.x; i < NCH * 1024; i += 16 * 256)
+            for (int i = a.cols + 16 * threadIdx.x; i < NCH * 1024; i += 16 * NT)
                 *reinterpret_cast<int4*>(xq_s + i) = make_int4(0, 0, 0, 0);
-            for (int b = nb + threadIdx.x; b < NCH * 32; b += 256) xs_s[b] = 0.0f;
+            for (int b = nb + threadIdx.x; b < NCH * 32; b += NT) xs_s[b] = 0.0f;
         }
         __syncthreads();
         if constexpr (!XL) {
@@ -444,25 +447,33 @@ template <int NCH> struct MvShape {
 // Grid: never more workgroups than can be resident at once (so no wave of
 // late workgroups repeats the prologue), and every wave gets the same number
 // of row groups (no half-empty tail).
+// Waves per workgroup: every workgroup builds the activation in its
+// prologue, so wider workgroups repeat that work fewer times; SwiGLU pairs and
+// long rows keep 4 (their register budget allows no more).
+template <int NCH, int EPI> struct MvWaves {
+    static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU) ? 4 : 8;
+};
 template <int NCH, int PRO, int EPI>
 static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
     constexpr int RPW = (EPI == EPI_SWIGLU) ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1)
                                             : MvShape<NCH>::RPW;
     constexpr int OUT = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
-    auto kern = k_mv<NCH, RPW, PRO, EPI>;
+    constexpr int WAVES = MvWaves<NCH, EPI>::value;
+    auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
     static int resident = -1;     // workgroups per CU this instance can keep resident
     if (resident < 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WAVES * 64, 0) != hipSuccess || n < 1) n = 1;
         resident = n;
     }
-    int per_cu = resident < wg_per_cu ? resident : wg_per_cu;
+    const int cap_wg = wg_per_cu * 4 / WAVES > 0 ? wg_per_cu * 4 / WAVES : 1;
+    const int per_cu = resident < cap_wg ? resident : cap_wg;
     const int64_t groups = (a.rows + OUT - 1) / OUT;
-    const int64_t cap_waves = 4LL * kNumCUs * per_cu;
+    const int64_t cap_waves = (int64_t)WAVES * kNumCUs * per_cu;
     const int64_t iters = (groups + cap_waves - 1) / cap_waves;
-    int64_t grid = (groups + 4 * iters - 1) / (4 * iters);
+    int64_t grid = (groups + WAVES * iters - 1) / (WAVES * iters);
     if (grid < 1) grid = 1;
-    launch_marked(mk, kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    launch_marked(mk, kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a);
 }
 
 template <int PRO, int EPI>
