@@ -268,10 +268,13 @@ typedef struct lq_layer_desc {
 } lq_layer_desc;
 
 /* Optional device buffers for the layer's intermediates; read them after
- * synchronizing.  The f32 ones (qkv, attn, x1, h) replace the workspace
- * buffer of that intermediate.  The Q8_0 ones are the quantized inputs that
- * the matvec kernels build in on-chip memory; when a tap is given, one
- * workgroup also writes its copy there. */
+ * synchronizing.  qkv, attn and x1 replace the workspace buffer of that
+ * intermediate; h (silu(gate) * up, never otherwise stored) is written when
+ * given.  xq/xd, aq/ad and nq/nd are the quantized inputs that the matvec
+ * kernels build in on-chip memory; when a tap is given, one workgroup also
+ * writes its copy there.  hq/hd (given together, else neither is written)
+ * replace the workspace buffer of the quantized h that the gate_up
+ * epilogue produces and the down projection reads. */
 typedef struct lq_layer_taps {
     int8_t* xq; uint16_t* xd;  /* Q8 of the input norm [hidden], [hidden/32] */
     float* qkv;                /* raw fused projection [n_q*hd + 2*n_kv*hd] */

@@ -19,7 +19,8 @@ struct LayerBuffers {
     float* qkv;
     float* attn;
     float* x1;
-    float* h;
+    int8_t* hq;          // Q8_0 of silu(gate) * up, written by the gate_up epilogue
+    uint16_t* hd;
     void* attn_ws;
     size_t total;
 };
@@ -41,14 +42,18 @@ LayerBuffers layout(const lq_layer_desc* L, char* base, const lq_layer_taps* tap
     b.qkv = reinterpret_cast<float*>(take((qd + 2 * kvd) * 4));
     b.attn = reinterpret_cast<float*>(take(qd * 4));
     b.x1 = reinterpret_cast<float*>(take(H * 4));
-    b.h = reinterpret_cast<float*>(take(I * 4));
+    b.hq = reinterpret_cast<int8_t*>(take(I));
+    b.hd = reinterpret_cast<uint16_t*>(take(I / 32 * 2));
     b.attn_ws = take(attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, max_attn_len(L)));
     b.total = off;
     if (taps) {
         if (taps->qkv) b.qkv = taps->qkv;
         if (taps->attn) b.attn = taps->attn;
         if (taps->x1) b.x1 = taps->x1;
-        if (taps->h) b.h = taps->h;
+        if (taps->hq && taps->hd) {
+            b.hq = taps->hq;
+            b.hd = taps->hd;
+        }
     }
     return b;
 }
@@ -207,16 +212,19 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
     }
     m.res = x;
     if ((st = launch_mv(m, PRO_QUANT, EPI_RESID, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
-    // FFN: gate/up with the post-attention RMSNorm + Q8 in-kernel and SwiGLU on row pairs
+    // FFN: gate/up with the post-attention RMSNorm + Q8 in-kernel, SwiGLU on
+    // row pairs, and the Q8_0 of the SwiGLU output built by the workgroup that
+    // owns each 32-value block
     const int64_t I = L->ffn;
     m = MvArgs{};
     m.wq = L->w_gate_up.qs; m.wd = L->w_gate_up.d; m.rows = (int)I; m.cols = (int)H;
-    m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = b.h; m.tap_q = T.nq; m.tap_d = T.nd;
-    if ((st = launch_mv(m, PRO_NORM, EPI_SWIGLU, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
-    // down projection, quantizing h in-kernel, plus the residual
+    m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = T.h; m.yq = b.hq; m.yd = b.hd;
+    m.tap_q = T.nq; m.tap_d = T.nd;
+    if ((st = launch_mv(m, PRO_NORM, EPI_SWIGLU_Q8, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    // down projection on the Q8_0 h, plus the residual
     m = MvArgs{};
     m.wq = L->w_down.qs; m.wd = L->w_down.d; m.rows = (int)H; m.cols = (int)I;
-    m.x = b.h; m.res = b.x1; m.y = x; m.tap_q = T.hq; m.tap_d = T.hd;
-    return launch_mv(m, PRO_QUANT, EPI_RESID, s, kMvWgPerCu, &mk);
+    m.xq = b.hq; m.xd = b.hd; m.res = b.x1; m.y = x;
+    return launch_mv(m, PRO_Q8, EPI_RESID, s, kMvWgPerCu, &mk);
 }
 }  // namespace

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_q8_matvec_any(const int8_t* __restrict_
 // buffer and the activation slice fit in 256 VGPRs, else one (long rows,
 // wide SwiGLU pairs), rather than spilling.
 template <int NCH, int EPI> struct MvWpe {
-    static constexpr int value = (NCH > 8 || (EPI == EPI_SWIGLU && NCH > 5)) ? 1 : 2;
+    static constexpr int value = (NCH > 8 || ((EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) && NCH > 5)) ? 1 : 2;
 };
 constexpr int kMaxCols = 16384;
 
@@ -181,7 +181,7 @@ __device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int lane,
     for (int i = 0; i < RPW; ++i) {
         // SwiGLU pairs: even i -> gate row, odd i -> the matching up row
         int64_t r;
-        if constexpr (EPI == EPI_SWIGLU) {
+        if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) {
             int64_t o = g * (RPW / 2) + i / 2;
             if (o >= a.rows) o = a.rows - 1;
             r = o + (i & 1) * (int64_t)a.rows;
@@ -209,12 +209,12 @@ struct XAct {
     int4 v[XL ? 1 : NCH];
     float s[XL ? 1 : NCH];
     const int8_t* q_lds;
-    const float* s_lds;
+    const uint16_t* s_lds;     // f16 bits
     __device__ __forceinline__ void get(int c, int lane, int4& x4, float& xs) const {
         if constexpr (XL) {
             const int off = c * 1024 + lane * 16;
             x4 = *reinterpret_cast<const int4*>(q_lds + off);
-            xs = s_lds[off >> 5];
+            xs = f16_to_f32(s_lds[off >> 5]);
         } else {
             x4 = v[c];
             xs = s[c];
@@ -224,7 +224,7 @@ struct XAct {
 
 template <int NCH, int RPW, int EPI, bool XL>
 __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int lane, const RowGroup<NCH, RPW>& G,
-                                              const XAct<NCH, XL>& x) {
+                                              const XAct<NCH, XL>& x, float* hs) {
     float acc[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -242,13 +242,19 @@ __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int la
         acc[i] = wave_sum(t);
     }
     if (lane != 0) return;
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) {
 #pragma unroll
         for (int j = 0; j < RPW / 2; ++j) {
             const int64_t r = g * (RPW / 2) + j;
             if (r < a.rows) {
                 const float gt = acc[2 * j], up = acc[2 * j + 1];
-                a.y[r] = (gt / (1.0f + expf(-gt))) * up;
+                const float h = (gt / (1.0f + expf(-gt))) * up;
+                if constexpr (EPI == EPI_SWIGLU_Q8) {
+                    hs[r & 31] = h;               // the workgroup's 32-value block, quantized at the end
+                    if (a.y) a.y[r] = h;
+                } else {
+                    a.y[r] = h;
+                }
             }
         }
     } else {
@@ -266,14 +272,23 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
     constexpr bool XL = NCH > 8;                          // activation slice from LDS
     constexpr bool LDS_X = (PRO != PRO_Q8) || XL;
     __shared__ __attribute__((aligned(16))) int8_t xq_s[LDS_X ? kMaxCols : 16];
-    __shared__ float xs_s[LDS_X ? kMaxCols / 32 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t xs_s[LDS_X ? kMaxCols / 32 : 8];
     __shared__ float red[WAVES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = a.cols >> 5;
-    constexpr int OUT_PER_GROUP = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
+    constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
+    constexpr int OUT_PER_GROUP = SW ? RPW / 2 : RPW;
     const int64_t ngroups = (a.rows + OUT_PER_GROUP - 1) / OUT_PER_GROUP;
-    const int64_t gstride = (int64_t)gridDim.x * WAVES;
-    int64_t g = (int64_t)blockIdx.x * WAVES + wave;
+    // Groups of a wave: grid-stride; or, for EPI_SWIGLU_Q8, the workgroup
+    // owns one 32-output block and each wave a contiguous slice of it.
+    constexpr int BLK_GROUPS = 32 / OUT_PER_GROUP;
+    static_assert(EPI != EPI_SWIGLU_Q8 || BLK_GROUPS % WAVES == 0, "block split over the waves");
+    const int64_t gstride = EPI == EPI_SWIGLU_Q8 ? 1 : (int64_t)gridDim.x * WAVES;
+    int64_t g = EPI == EPI_SWIGLU_Q8 ? (int64_t)blockIdx.x * BLK_GROUPS + wave * (BLK_GROUPS / WAVES)
+                                     : (int64_t)blockIdx.x * WAVES + wave;
+    const int64_t gend = EPI == EPI_SWIGLU_Q8 ? (g + BLK_GROUPS / WAVES < ngroups ? g + BLK_GROUPS / WAVES : ngroups)
+                                              : ngroups;
+    __shared__ float hs[EPI == EPI_SWIGLU_Q8 ? 32 : 1];
 
     // The prologue's own loads (x, and gamma when it fits in registers; or
     // the Q8 activation that goes to LDS) are issued first, then the first
@@ -281,11 +296,8 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
     // while the weights are in flight.
     constexpr int BPT = (NCH * 32 + NT - 1) / NT;          // activation blocks per thread
     constexpr bool EARLY_G = (PRO == PRO_NORM) && BPT == 1;
-    constexpr int QPT = (NCH * 64 + NT - 1) / NT;          // Q8 16-byte slices per thread (XL copy)
     float xf[PRO != PRO_Q8 ? BPT : 1][32];
     float gf[EARLY_G ? BPT : 1][32];
-    int4 qc[(PRO == PRO_Q8 && XL) ? QPT : 1];
-    float dc[(PRO == PRO_Q8 && XL) ? BPT : 1];
     if constexpr (PRO != PRO_Q8) {
 #pragma unroll
         for (int k = 0; k < BPT; ++k) {
@@ -295,16 +307,24 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             if constexpr (EARLY_G) load32((a.gamma ? a.gamma : a.x) + 32 * bc, gf[k]);
         }
     } else if constexpr (XL) {
+        // codes and scales straight into LDS (global_load_lds: no registers),
+        // 16 bytes per lane, whole waves; slices past the end are not loaded
+        using gptr = const __attribute__((address_space(1))) void*;
+        using lptr = __attribute__((address_space(3))) void*;
+        const int nq16 = a.cols >> 4;
+        for (int s0 = wave * 64; s0 < nq16; s0 += NT)
+            if (s0 + lane < nq16)
+                __builtin_amdgcn_global_load_lds((gptr)(a.xq + 16 * (s0 + lane)), (lptr)(xq_s + 16 * s0), 16, 0, 0);
+    }
+    // XL Q8 scales: early register loads (the 2-byte LDS copy writes one
+    // dword per lane), stored to LDS once the weight loads are in flight
+    constexpr int SPT = (PRO == PRO_Q8 && XL) ? (NCH * 32 + NT - 1) / NT : 1;
+    uint32_t sc_early[SPT];
+    if constexpr (PRO == PRO_Q8 && XL) {
 #pragma unroll
-        for (int k = 0; k < QPT; ++k) {
-            const int i = threadIdx.x + NT * k;          // 16-byte slice
-            const int ic = i * 16 < a.cols ? i : 0;
-            qc[k] = *reinterpret_cast<const int4*>(a.xq + 16 * ic);
-        }
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
+        for (int k = 0; k < SPT; ++k) {
             const int b = threadIdx.x + NT * k;
-            dc[k] = f16_to_f32(a.xd[b < nb ? b : 0]);
+            sc_early[k] = a.xd[b < nb ? b : nb - 1];
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -327,15 +347,16 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
         }
     } else {
         if constexpr (PRO == PRO_Q8) {
+            // the LDS copies and scale loads issued above must have landed;
+            // they precede the first group's weight loads (RPW*NCH codes +
+            // RPW*NCH scales), so waiting until only those are outstanding
+            // does not wait for the weights
+            constexpr int WL = 2 * RPW * NCH < 63 ? 2 * RPW * NCH : 63;     // vmcnt holds at most 63
+            __builtin_amdgcn_s_waitcnt((WL & 15) | ((WL >> 4) << 14) | (7 << 4) | (15 << 8));
 #pragma unroll
-            for (int k = 0; k < QPT; ++k) {
-                const int i = threadIdx.x + NT * k;
-                if (i * 16 < a.cols) *reinterpret_cast<int4*>(xq_s + 16 * i) = qc[k];
-            }
-#pragma unroll
-            for (int k = 0; k < BPT; ++k) {
+            for (int k = 0; k < SPT; ++k) {
                 const int b = threadIdx.x + NT * k;
-                if (b < nb) xs_s[b] = dc[k];
+                if (b < nb) xs_s[b] = (uint16_t)sc_early[k];
             }
         } else {
 #pragma unroll
@@ -386,7 +407,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
                     uint32_t packed[8];
                     const uint16_t db = quantize_block32_packed(v, packed);
                     store_codes32(xq_s + 32 * b, packed);
-                    xs_s[b] = f16_to_f32(db);
+                    xs_s[b] = db;
                     if (tap) {
                         store_codes32(a.tap_q + 32 * b, packed);
                         a.tap_d[b] = db;
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             // slices past the last column read as zero
             for (int i = a.cols + 16 * threadIdx.x; i < NCH * 1024; i += 16 * NT)
                 *reinterpret_cast<int4*>(xq_s + i) = make_int4(0, 0, 0, 0);
-            for (int b = nb + threadIdx.x; b < NCH * 32; b += NT) xs_s[b] = 0.0f;
+            for (int b = nb + threadIdx.x; b < NCH * 32; b += NT) xs_s[b] = 0;
         }
         __syncthreads();
         if constexpr (!XL) {
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
                 x.s[c] = 0.0f;
                 if (off < a.cols) {
                     x.v[c] = *reinterpret_cast<const int4*>(xq_s + off);
-                    x.s[c] = xs_s[off >> 5];
+                    x.s[c] = f16_to_f32(xs_s[off >> 5]);
                 }
             }
         }
@@ -419,23 +440,40 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
     // current one is consumed.  Every load sits in straight-line code ahead
     // of its consumer (the last step is peeled), so each wait covers exactly
     // the loads it needs.
-    if (g >= ngroups) return;
-    while (true) {
+    while (g < gend) {
         const int64_t g1 = g + gstride;
-        if (g1 >= ngroups) {
-            consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x);
-            return;
+        if (g1 >= gend) {
+            consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x, hs);
+            break;
         }
         load_group<NCH, RPW, EPI>(a, g1, lane, B);
-        consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x);
+        consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x, hs);
         const int64_t g2 = g1 + gstride;
-        if (g2 >= ngroups) {
-            consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x);
-            return;
+        if (g2 >= gend) {
+            consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x, hs);
+            break;
         }
         load_group<NCH, RPW, EPI>(a, g2, lane, A);
-        consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x);
+        consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x, hs);
         g = g2;
+    }
+
+    if constexpr (EPI == EPI_SWIGLU_Q8) {
+        // Q8_0 of the workgroup's 32 outputs: lane i of wave 0 holds value i
+        // (the same rule as every other quantizer here: d = amax/127,
+        // codes round-half-away(v * (1/d)) clamped to +-127)
+        __syncthreads();
+        const int64_t b = blockIdx.x;
+        if (wave == 0) {
+            const bool mine = lane < 32 && 32 * b + lane < a.rows;
+            const float v = mine ? hs[lane & 31] : 0.0f;
+            const float amax = group_max<32>(fabsf(v));      // lanes 0-31: the block's amax
+            const float d = amax / 127.0f;
+            const float inv = (d != 0.0f) ? 1.0f / d : 0.0f;
+            const float r = fminf(fmaxf(roundf(v * inv), -127.0f), 127.0f);
+            if (mine) a.yq[32 * b + lane] = (int8_t)(int32_t)r;
+            if (lane == 0) a.yd[b] = f32_to_f16(d);
+        }
     }
 }
 
@@ -451,13 +489,13 @@ template <int NCH> struct MvShape {
 // prologue, so wider workgroups repeat that work fewer times; SwiGLU pairs and
 // long rows keep 4 (their register budget allows no more).
 template <int NCH, int EPI> struct MvWaves {
-    static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU) ? 4 : 8;
+    static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 4 : 8;
 };
 template <int NCH, int PRO, int EPI>
 static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
-    constexpr int RPW = (EPI == EPI_SWIGLU) ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1)
-                                            : MvShape<NCH>::RPW;
-    constexpr int OUT = (EPI == EPI_SWIGLU) ? RPW / 2 : RPW;
+    constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
+    constexpr int RPW = SW ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1) : MvShape<NCH>::RPW;
+    constexpr int OUT = SW ? RPW / 2 : RPW;
     constexpr int WAVES = MvWaves<NCH, EPI>::value;
     auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
     static int resident = -1;     // workgroups per CU this instance can keep resident
@@ -472,6 +510,7 @@ static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchM
     const int64_t cap_waves = (int64_t)WAVES * kNumCUs * per_cu;
     const int64_t iters = (groups + cap_waves - 1) / cap_waves;
     int64_t grid = (groups + WAVES * iters - 1) / (WAVES * iters);
+    if (EPI == EPI_SWIGLU_Q8) grid = (a.rows + 31) / 32;        // one workgroup per 32-output block
     if (grid < 1) grid = 1;
     launch_marked(mk, kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a);
 }
@@ -496,7 +535,7 @@ lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per
     if (pro == P && epi == E) return launch_mv_pe<P, E>(a, s, wg_per_cu, mk);
     LQ_PE(PRO_Q8, EPI_STORE) LQ_PE(PRO_Q8, EPI_RESID) LQ_PE(PRO_Q8, EPI_SWIGLU)
     LQ_PE(PRO_QUANT, EPI_STORE) LQ_PE(PRO_QUANT, EPI_RESID)
-    LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU)
+    LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU) LQ_PE(PRO_NORM, EPI_SWIGLU_Q8)
 #undef LQ_PE
     return fail(LQ_ERR_UNSUPPORTED, "fused matvec: prologue %d / epilogue %d not built", pro, epi);
 }

@@ -71,9 +71,11 @@ lq_status launch_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, i
                            int32_t* dots, hipStream_t s);
 
 // Fused matvec (see k_matvec.hip): prologue PRO_* builds the Q8_0 input,
-// epilogue EPI_* stores, adds a residual or applies SwiGLU to row pairs.
+// epilogue EPI_* stores, adds a residual or applies SwiGLU to row pairs;
+// EPI_SWIGLU_Q8 also quantizes the SwiGLU output to Q8_0 (yq, yd), each
+// workgroup owning whole 32-value blocks.
 enum { PRO_Q8 = 0, PRO_QUANT = 1, PRO_NORM = 2 };
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_SWIGLU_Q8 = 3 };
 constexpr int kMvWgPerCu = 4;   // upper bound on resident workgroups of 4 waves per CU
 struct MvArgs {
     const int8_t* wq;
@@ -86,7 +88,9 @@ struct MvArgs {
     const float* gamma;  // PRO_NORM (NULL: unit weight)
     float eps;
     const float* res;    // EPI_RESID (may alias y)
-    float* y;
+    float* y;            // EPI_SWIGLU_Q8: optional (NULL: f32 output not written)
+    int8_t* yq;          // EPI_SWIGLU_Q8: Q8_0 codes [rows] and scales [rows/32]
+    uint16_t* yd;
     int8_t* tap_q;       // optional: workgroup 0 writes the Q8_0 input it built
     uint16_t* tap_d;
 };
