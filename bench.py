@@ -180,6 +180,112 @@ def kernel_measurements(cfg, layers, xs, torch, rounds):
     return per
 
 
+def measure_layer(workload, steps, warmup, rounds, min_stack_bytes, torch):
+    """A graph-captured stack of R distinct layers (>= min_stack_bytes of
+    weights and KV, so the Infinity Cache cannot serve them), timed over
+    `steps` replays, plus per-kernel launch durations from HIP events."""
+    from q8_matvec_gqa_amd.layers import DeviceLayer
+    cfg = synthetic.layer_cfg(workload)
+    mv_b, at_b = layer_bytes(cfg)
+    R = max(8, math.ceil(min_stack_bytes / (mv_b + at_b)))
+    log(f"workload {workload}: {(mv_b + at_b) / 1e6:.1f} MB/layer, stack of {R} layers")
+    layers, xs = [], []
+    for i in range(R):
+        w = device_layer_inputs(cfg, seed=1000 + i, torch=torch)
+        layers.append(DeviceLayer(cfg, w, torch))
+        xs.append(w["x"])
+    torch.cuda.synchronize()
+    ms_step, eager_ms = time_stack(layers, xs, cfg["pos"], steps, warmup, torch)
+    us_layer = ms_step * 1e3 / R
+    log(f"{workload}: {us_layer:.2f} us/token/layer (graph), eager {eager_ms * 1e3 / R:.2f}")
+    per = kernel_measurements(cfg, layers, xs, torch, rounds)
+    at_us = per["attn_split"]["avg_us"] + (per["attn_combine"]["avg_us"] if "attn_combine" in per else 0.0)
+    at_bytes = per["attn_split"]["bytes"]
+    at_gbs = at_bytes / (at_us * 1e3)
+    mv_tags = [t for t in per if t.endswith("_matvec")]
+    mv_us = sum(per[t]["avg_us"] for t in mv_tags)
+    mv_bytes = sum(per[t]["bytes"] for t in mv_tags)
+    del layers, xs
+    return {
+        "R": R, "ms_step": ms_step, "us_layer": us_layer, "eager_us_layer": eager_ms * 1e3 / R,
+        "layer_bytes": mv_b + at_b, "per": per,
+        "attn": {"bound": "hbm", "kernel": "k_attn_split+k_attn_combine", "achieved": round(at_gbs, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4),
+                 "bytes_per_launch": at_bytes, "avg_launch_us": round(at_us, 3)},
+        "matvec": {"us": round(mv_us, 3), "bytes": mv_bytes, "GBps": round(mv_bytes / (mv_us * 1e3), 1),
+                   "frac": round(mv_bytes / (mv_us * 1e3) / HBM_PEAK_GBS, 4)},
+    }
+
+
+def device_moe_inputs(c, seed, torch):
+    """MoE block inputs drawn on the GPU (same distributions as synthetic.py)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    H, I, E, T = c["hidden"], c["ffn"], c["n_experts"], c["tokens"]
+
+    def q8(rows, cols):
+        qs = torch.randint(-127, 128, (rows, cols), dtype=torch.int8, device="cuda", generator=g)
+        d = (torch.randn(rows, cols // 32, device="cuda", generator=g).abs() * (0.02 / 127)).half()
+        return qs, d.view(torch.int16)
+
+    w = {"x": torch.randn(T, H, device="cuda", generator=g), "logits": torch.randn(T, E, device="cuda", generator=g)}
+    w["gu_qs"], w["gu_d"] = q8(E * 2 * I, H)
+    w["dn_qs"], w["dn_d"] = q8(E * H, I)
+    return w
+
+
+def measure_moe(name, steps, torch):
+    """The MoE block (route, gather, id-matvecs, SwiGLU, weighted sum) on R
+    replicas of all expert weights, graph-captured.  Algorithmic bytes: the
+    experts the routing touches (counted per replica from the same top-k)
+    at 34 B per 32 weights, plus activations."""
+    from q8_matvec_gqa_amd.layers import DeviceMoe
+    c = dict(synthetic.MOE_WORKLOADS[name])
+    H, I, E, T, k = c["hidden"], c["ffn"], c["n_experts"], c["tokens"], c["top_k"]
+    expert_bytes = 3 * I * H * 34 // 32
+    R = max(2, math.ceil(1.5e9 / (E * expert_bytes)))
+    mods, ins, outs, touched = [], [], [], []
+    for i in range(R):
+        w = device_moe_inputs(c, 2000 + i, torch)
+        mods.append(DeviceMoe(c, w, torch))
+        ins.append((w["x"], w["logits"]))
+        outs.append(torch.empty(T, H, device="cuda"))
+        ids = torch.topk(torch.softmax(w["logits"].double(), dim=1), k, dim=1).indices
+        touched.append(int(torch.unique(ids).numel()))
+        del w
+    block_bytes = [n * expert_bytes + T * H * 8 + T * E * 4 for n in touched]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for i in range(R):
+        mods[i].run(ins[i][0], ins[i][1], outs[i])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(R):
+                mods[i].run(ins[i][0], ins[i][1], outs[i])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_block = e0.elapsed_time(e1) * 1e3 / (steps * R)
+    mean_bytes = sum(block_bytes) / R
+    gbs = mean_bytes / (us_block * 1e3)
+    log(f"{name}: {us_block:.2f} us/block ({us_block / T:.2f} us/token), {gbs:.1f} GB/s, "
+        f"touched experts {touched}")
+    del mods, ins, outs, graph
+    return {"workload": name, "us_per_block": round(us_block, 3), "tokens": T,
+            "us_per_token": round(us_block / T, 3), "touched_experts": touched,
+            "bytes_per_block": int(mean_bytes), "GBps": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "replicas": R, "graph": True}
+
+
 def calib_copy(torch, nbytes=1 << 30, reps=3):
     """A plain elementwise copy of known size (reads nbytes, writes nbytes),
     run for the PMC calibration of FETCH_SIZE / WRITE_SIZE."""
@@ -341,6 +447,7 @@ def main():
     ap.add_argument("--rounds", type=int, default=5, help="rounds of per-launch kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other configs and the MoE block")
     ap.add_argument("--calib-copy", action="store_true", help="also run the PMC calibration copy (1 GiB)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
@@ -365,37 +472,18 @@ def main():
 
     import torch
     import q8_matvec_gqa_amd as lq  # noqa: F401  (fails loudly without liblq.so)
-    from q8_matvec_gqa_amd.layers import DeviceLayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synthetic.layer_cfg(args.workload)
-    mv_b, at_b = layer_bytes(cfg)
-    per_layer_bytes = mv_b + at_b
-    R = max(8, math.ceil(args.min_stack_bytes / per_layer_bytes))
-    log(f"workload {args.workload}: {per_layer_bytes / 1e6:.1f} MB/layer, stack of {R} layers")
-    layers, xs = [], []
-    for i in range(R):
-        w = device_layer_inputs(cfg, seed=1000 + i, torch=torch)
-        layers.append(DeviceLayer(cfg, w, torch))
-        xs.append(w["x"])
-    torch.cuda.synchronize()
-    log("stack built; timing graph replays")
-    ms_step, eager_ms = time_stack(layers, xs, cfg["pos"], args.steps, args.warmup, torch)
-    us_layer = ms_step * 1e3 / R
-    log(f"{us_layer:.2f} us/token/layer (graph), eager {eager_ms * 1e3 / R:.2f}")
-    per = kernel_measurements(cfg, layers, xs, torch, args.rounds)
-    dom_tag = "gate_up_matvec" if "gate_up_matvec" in per else "qkv_matvec"
-    dom = per[dom_tag]
-    dom_gbs = dom["bytes"] / (dom["avg_us"] * 1e3)
-    at_us = per["attn_split"]["avg_us"] + (per["attn_combine"]["avg_us"] if "attn_combine" in per else 0.0)
-    at_bytes = per["attn_split"]["bytes"]
-    at_gbs = at_bytes / (at_us * 1e3)
-    mv_tags = [t for t in per if t.endswith("_matvec")]
-    mv_us = sum(per[t]["avg_us"] for t in mv_tags)
-    mv_bytes = sum(per[t]["bytes"] for t in mv_tags)
+    m = measure_layer(args.workload, args.steps, args.warmup, args.rounds, args.min_stack_bytes, torch)
+    per, us_layer, R = m["per"], m["us_layer"], m["R"]
+    per_layer_bytes = m["layer_bytes"]
     for tag, p in per.items():
         gbs = p["bytes"] / (p["avg_us"] * 1e3)
         log(f"{tag:16s} {p['avg_us']:8.2f} us avg ({p['min_us']:.2f} min) {gbs:8.1f} GB/s  [{p['kernel']}]")
+    dom_tag = "gate_up_matvec" if "gate_up_matvec" in per else "qkv_matvec"
+    dom = per[dom_tag]
+    dom_gbs = dom["bytes"] / (dom["avg_us"] * 1e3)
     result = {
         "metric": "decode-layer us/token + achieved HBM GB/s (% peak), Q8_0 matvec & GQA attn",
         "value": round(us_layer, 3),
@@ -403,7 +491,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(m["ms_step"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -415,19 +503,36 @@ def main():
                    "tokens_per_step": 1, "graph": True},
         "layer_bytes": per_layer_bytes,
         "layer_GBps": round(per_layer_bytes / (us_layer * 1e3), 1),
-        "eager_us_per_layer": round(eager_ms * 1e3 / R, 3),
+        "eager_us_per_layer": round(m["eager_us_layer"], 3),
         "roofline": {"bound": "hbm", "kernel": dom["kernel"] + " (" + dom_tag + ")", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(args.workload) if dom_tag == "gate_up_matvec" else None,
                      "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3)},
-        "attn_roofline": {"bound": "hbm", "kernel": "k_attn_split+k_attn_combine", "achieved": round(at_gbs, 1),
-                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(at_gbs / HBM_PEAK_GBS, 4),
-                          "bytes_per_launch": at_bytes, "avg_launch_us": round(at_us, 3)},
-        "matvec_total": {"us": round(mv_us, 3), "bytes": mv_bytes, "GBps": round(mv_bytes / (mv_us * 1e3), 1),
-                         "frac": round(mv_bytes / (mv_us * 1e3) / HBM_PEAK_GBS, 4)},
+        "attn_roofline": m["attn"],
+        "matvec_total": m["matvec"],
         "kernels": {t: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in p.items()}
                     for t, p in per.items()},
     }
+    del m
+    torch.cuda.empty_cache()
+    if not args.headline_only:
+        others = {}
+        for wl in synthetic.WORKLOADS:
+            if wl == args.workload:
+                continue
+            o = measure_layer(wl, max(10, args.steps // 4), 3, 2, args.min_stack_bytes, torch)
+            others[wl] = {"us_per_layer": round(o["us_layer"], 3), "layers_per_step": o["R"],
+                          "layer_bytes": o["layer_bytes"],
+                          "layer_GBps": round(o["layer_bytes"] / (o["us_layer"] * 1e3), 1),
+                          "layer_frac": round(o["layer_bytes"] / (o["us_layer"] * 1e3) / HBM_PEAK_GBS, 4),
+                          "attn": o["attn"], "matvec": o["matvec"],
+                          "kernels_us": {t: round(p["avg_us"], 3) for t, p in o["per"].items()}}
+            del o
+            torch.cuda.empty_cache()
+        result["other_configs"] = others
+        for name in synthetic.MOE_WORKLOADS:
+            result["moe_block"] = measure_moe(name, max(10, args.steps // 2), torch)
+            torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)
     if not args.no_cpu:

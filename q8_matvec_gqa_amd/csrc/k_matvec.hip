@@ -486,9 +486,9 @@ template <int NCH> struct MvShape {
 // late workgroups repeats the prologue), and every wave gets the same number
 // of row groups (no half-empty tail).
 // Waves per workgroup: every workgroup builds the activation in its
-// prologue, so wider workgroups repeat that work fewer times; SwiGLU pairs and
-// long rows keep 4 (their register budget allows no more).
-template <int NCH, int EPI> struct MvWaves {
+// prologue, so wider workgroups repeat that work fewer times; SwiGLU pairs
+// and long rows keep 4 (their register budget allows no more).
+template <int NCH, int PRO, int EPI> struct MvWaves {
     static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 4 : 8;
 };
 template <int NCH, int PRO, int EPI>
@@ -496,7 +496,7 @@ static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchM
     constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
     constexpr int RPW = SW ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1) : MvShape<NCH>::RPW;
     constexpr int OUT = SW ? RPW / 2 : RPW;
-    constexpr int WAVES = MvWaves<NCH, EPI>::value;
+    constexpr int WAVES = MvWaves<NCH, PRO, EPI>::value;
     auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
     static int resident = -1;     // workgroups per CU this instance can keep resident
     if (resident < 0) {
