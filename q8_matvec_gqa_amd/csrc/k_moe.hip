@@ -43,11 +43,12 @@ size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts) {
 }
 
 // ---- router: one wave per token --------------------------------------------
-__global__ __launch_bounds__(64) void k_moe_route(const float* __restrict__ logits, int E, int k,
-                                                  int32_t* __restrict__ ids, float* __restrict__ w) {
+// Softmax over the token's E logits, then the k largest (ties: lower id);
+// the weights are the probabilities themselves.  Lane 0 writes id and weight
+// of each pick to ids/w and, when sids is given, the id to sids (LDS).
+__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k, int lane,
+                                            int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
     constexpr int PER = 16;   // E <= 1024
-    const int t = blockIdx.x, lane = threadIdx.x;
-    const float* lt = logits + (int64_t)t * E;
     float v[PER];
     float mx = -INFINITY;
 #pragma unroll
@@ -73,82 +74,167 @@ __global__ __launch_bounds__(64) void k_moe_route(const float* __restrict__ logi
                 bi = e;
             }
         }
-        // wave argmax with the same ordering
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        // wave argmax with the same ordering: the largest value, then the
+        // lowest id among the lanes holding it
+        const float m = wave_max(bv);
+        bi = wave_min_i(bv == m ? bi : 0x7fffffff);
+        bv = m;
         if (lane == 0) {
-            ids[(int64_t)t * k + s] = bi;
-            w[(int64_t)t * k + s] = expf(bv - mx) / z;
+            ids[s] = bi;
+            w[s] = expf(bv - mx) / z;
+            if (sids) sids[s] = bi;
         }
-        // remove the chosen expert
+        // remove the chosen expert, below every real value (NaN never wins)
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            if (lane + 64 * i == bi) v[i] = -INFINITY;
-        // a -inf logit can tie with removed entries; keep ids distinct by
-        // marking removed ones below every real value
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (lane + 64 * i == bi) v[i] = __int_as_float(0xff800001u);   // NaN never wins
+            if (lane + 64 * i == bi) v[i] = __int_as_float(0xff800001u);
     }
 }
 
+__global__ __launch_bounds__(64) void k_moe_route(const float* __restrict__ logits, int E, int k,
+                                                  int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int t = blockIdx.x;
+    route_token(logits + (int64_t)t * E, E, k, threadIdx.x, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr);
+}
+
 // ---- gather: group (token, slot) rows by expert ------------------------------
-// One workgroup.  Thread e (strided) scans the ids in order and collects the
-// slots of expert e, so each expert's list is ascending and the result is
-// deterministic.  Rows of slots with an out-of-range id are zeroed in y0 and
-// y1 (either may be NULL) and counted.
-__global__ __launch_bounds__(256) void k_moe_gather(const int32_t* __restrict__ ids, int nslots, int E,
-                                                    int32_t* wsbase, float* y0, int64_t rows0, float* y1,
-                                                    int64_t rows1) {
-    __shared__ int32_t cnt[kMoeMaxExperts];
-    __shared__ int32_t off[kMoeMaxExperts + 1];
-    MoeWs ws{wsbase, E};
-    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+// One workgroup of kGatherThreads, the slot ids already in LDS.  Counts per
+// expert (LDS atomics), one block-wide exclusive scan of (count, active)
+// pairs gives each expert its offset and its index in the active list (in
+// expert order), and every slot then takes a place in its expert's list.
+// Rows of slots with an out-of-range id are zeroed in y0 and y1 (either may
+// be NULL) and counted.
+constexpr int kGatherThreads = 1024;
+constexpr int kGatherEpt = kMoeMaxExperts / kGatherThreads;    // experts per thread
+
+// Exclusive scan of one int per thread over the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
     __syncthreads();
-    for (int i = threadIdx.x; i < nslots; i += 256) {
-        const int e = ids[i];
+    if (wave == 0) {
+        int t = lane < kGatherThreads / 64 ? tmp[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kGatherThreads / 64; off <<= 1) {
+            const int y = __shfl_up(t, off);
+            if (lane >= off) t += y;
+        }
+        if (lane < kGatherThreads / 64) tmp[lane] = t;
+    }
+    __syncthreads();
+    const int base = wave ? tmp[wave - 1] : 0;
+    *total = tmp[kGatherThreads / 64 - 1];
+    __syncthreads();
+    return base + x - v;
+}
+
+__device__ void gather_lds(const int32_t* sids, int nslots, int E, MoeWs ws, int32_t* cnt, int* tmp, float* y0,
+                           int64_t rows0, float* y1, int64_t rows1) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kGatherThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int i = tid; i < nslots; i += kGatherThreads) {
+        const int e = sids[i];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int n = 0, acc = 0, bad = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = acc;
-            if (cnt[e] > 0) {
-                ws.active()[n] = e;
-                ws.offsets()[n] = acc;
-                ++n;
-            }
-            acc += cnt[e];
+    // thread tid owns experts [tid*EPT, tid*EPT + EPT); pack (count << 13 | active)
+    int c[kGatherEpt], local = 0;
+#pragma unroll
+    for (int j = 0; j < kGatherEpt; ++j) {
+        const int e = tid * kGatherEpt + j;
+        c[j] = e < E ? cnt[e] : 0;
+        local += (c[j] << 13) | (c[j] > 0 ? 1 : 0);
+    }
+    int total;
+    int run = block_excl_scan(local, tmp, &total);
+    int32_t* act = ws.active();
+    int32_t* offs = ws.offsets();
+#pragma unroll
+    for (int j = 0; j < kGatherEpt; ++j) {
+        const int e = tid * kGatherEpt + j;
+        if (c[j] > 0) {
+            const int idx = run & 0x1fff, off = run >> 13;
+            act[idx] = e;
+            offs[idx] = off;
+            cnt[e] = off;                  // becomes the fill cursor of expert e
         }
-        ws.offsets()[n] = acc;
-        *ws.n_active() = n;
-        bad = nslots - acc;
-        *ws.invalid() = bad;
+        run += (c[j] << 13) | (c[j] > 0 ? 1 : 0);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-        if (cnt[e] == 0) continue;
-        int p = off[e];
-        for (int i = 0; i < nslots; ++i)
-            if (ids[i] == e) ws.slots()[p++] = i;
+    // each slot takes the next place in its expert's list; the order inside a
+    // list does not change any result (every slot's rows are computed on
+    // their own), only which iteration of the matvec handles it
+    for (int i = tid; i < nslots; i += kGatherThreads) {
+        const int e = sids[i];
+        if (e >= 0 && e < E) ws.slots()[atomicAdd(&cnt[e], 1)] = i;
     }
-    // zero the outputs of invalid slots
-    for (int i = 0; i < nslots; ++i) {
-        const int e = ids[i];
-        if (e >= 0 && e < E) continue;
-        if (y0)
-            for (int64_t r = threadIdx.x; r < rows0; r += 256) y0[(int64_t)i * rows0 + r] = 0.0f;
-        if (y1)
-            for (int64_t r = threadIdx.x; r < rows1; r += 256) y1[(int64_t)i * rows1 + r] = 0.0f;
+    const int n_active = total & 0x1fff, listed = total >> 13;
+    if (tid == 0) {
+        offs[n_active] = listed;
+        *ws.n_active() = n_active;
+        *ws.invalid() = nslots - listed;
     }
+    if (listed < nslots) {
+        // zero the outputs of invalid slots
+        for (int i = 0; i < nslots; ++i) {
+            const int e = sids[i];
+            if (e >= 0 && e < E) continue;
+            if (y0)
+                for (int64_t r = tid; r < rows0; r += kGatherThreads) y0[(int64_t)i * rows0 + r] = 0.0f;
+            if (y1)
+                for (int64_t r = tid; r < rows1; r += kGatherThreads) y1[(int64_t)i * rows1 + r] = 0.0f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kGatherThreads) void k_moe_gather(const int32_t* __restrict__ ids, int nslots, int E,
+                                                               int32_t* wsbase, float* y0, int64_t rows0,
+                                                               float* y1, int64_t rows1) {
+    __shared__ int32_t sids[kMoeMaxSlots];
+    __shared__ int32_t cnt[kMoeMaxExperts];
+    __shared__ int tmp[kGatherThreads / 64];
+    for (int i = threadIdx.x; i < nslots; i += kGatherThreads) sids[i] = ids[i];
+    __syncthreads();
+    gather_lds(sids, nslots, E, MoeWs{wsbase, E}, cnt, tmp, y0, rows0, y1, rows1);
+}
+
+// The MoE block's first step in one launch: workgroup 0 routes every token
+// (one wave per token at a time) and gathers the slots by expert; the other
+// workgroups quantize x to Q8_0, kPrepQuantBlocks 32-blocks each (one per
+// thread, so each SIMD has one busy wave).
+constexpr int kPrepQuantBlocks = 256;
+__global__ __launch_bounds__(kGatherThreads) void k_moe_prep(const float* __restrict__ logits,
+                                                             const float* __restrict__ x, int T, int E, int k,
+                                                             int H, int32_t* __restrict__ ids,
+                                                             float* __restrict__ w, int32_t* wsbase,
+                                                             int8_t* __restrict__ xq, uint16_t* __restrict__ xd,
+                                                             float* y0, int64_t rows0, float* y1, int64_t rows1) {
+    __shared__ int32_t sids[kMoeMaxSlots];
+    __shared__ int32_t cnt[kMoeMaxExperts];
+    __shared__ int tmp[kGatherThreads / 64];
+    if (blockIdx.x > 0) {
+        const int64_t nbx = (int64_t)T * (H / 32);
+        const int64_t b = (int64_t)(blockIdx.x - 1) * kPrepQuantBlocks + threadIdx.x;
+        if (threadIdx.x < kPrepQuantBlocks && b < nbx) {
+            float v[32];
+            load32(x + 32 * b, v);
+            quantize_block32(v, xq + 32 * b, xd + b);
+        }
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += kGatherThreads / 64)
+        route_token(logits + (int64_t)t * E, E, k, lane, ids + (int64_t)t * k, w + (int64_t)t * k,
+                    sids + (int64_t)t * k);
+    __syncthreads();
+    gather_lds(sids, T * k, E, MoeWs{wsbase, E}, cnt, tmp, y0, rows0, y1, rows1);
 }
 
 __device__ __forceinline__ int dot16(int4 a, int4 b) {
@@ -256,7 +342,7 @@ lq_status launch_moe_route(const float* logits, int64_t T, int64_t E, int64_t k,
 
 static lq_status launch_gather(const int32_t* ids, int64_t nslots, int64_t E, void* ws, float* y0,
                                int64_t rows0, float* y1, int64_t rows1, hipStream_t s) {
-    hipLaunchKernelGGL(k_moe_gather, dim3(1), dim3(256), 0, s, ids, (int)nslots, (int)E,
+    hipLaunchKernelGGL(k_moe_gather, dim3(1), dim3(kGatherThreads), 0, s, ids, (int)nslots, (int)E,
                        static_cast<int32_t*>(ws), y0, rows0, y1, rows1);
     return check_launch("moe_gather");
 }
@@ -265,7 +351,9 @@ template <int NCH>
 static void launch_id_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int rows, int cols,
                           const int8_t* xq, const uint16_t* xd, int x_per_slot, int k,
                           const int32_t* ws, int E, float* y) {
-    constexpr int RPW = NCH <= 4 ? 4 : (NCH <= 8 ? 2 : 1);
+    // rows per wave: short rows (<= 2 KB) 4, longer ones 2 (measured on the
+    // 128-expert block: more, smaller workgroups keep more loads in flight)
+    constexpr int RPW = NCH <= 2 ? 4 : 2;
     const int rowblocks = (rows + 4 * RPW - 1) / (4 * RPW);
     hipLaunchKernelGGL((k_moe_matvec_id<NCH, RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, wq, wd,
                        rows, cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
@@ -447,9 +535,10 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     MoeBuffers b = moe_layout(m, T, static_cast<char*>(workspace), taps);
     hipStream_t s = as_stream(stream);
     const int64_t S = T * k;
-    if ((st = launch_moe_route(logits, T, E, k, b.ids, b.w, s)) != LQ_OK) return st;
-    if ((st = launch_gather(b.ids, S, E, b.gather, b.y1, 2 * I, b.y2, H, s)) != LQ_OK) return st;
-    if ((st = launch_q8_quantize(x, T * (H / 32), b.xq, b.xd, s)) != LQ_OK) return st;
+    const int64_t prep_grid = 1 + (T * (H / 32) + kPrepQuantBlocks - 1) / kPrepQuantBlocks;
+    hipLaunchKernelGGL(k_moe_prep, dim3((unsigned)prep_grid), dim3(kGatherThreads), 0, s, logits, x, (int)T, (int)E, (int)k, (int)H,
+                       b.ids, b.w, static_cast<int32_t*>(b.gather), b.xq, b.xd, b.y1, 2 * I, b.y2, H);
+    if ((st = check_launch("moe_prep")) != LQ_OK) return st;
     if ((st = launch_id_gathered(m->w_gate_up.qs, m->w_gate_up.d, 2 * I, H, E, b.xq, b.xd, 0, k, b.gather, b.y1,
                                  s)) != LQ_OK)
         return st;

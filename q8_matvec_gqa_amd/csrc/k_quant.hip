@@ -78,23 +78,48 @@ __global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu,
 // out = res + gamma * o / sqrt(mean(o^2) + eps): the weighted RMSNorm with
 // residual add ("Current Inference Path -- Architecture Map", section 4,
 // rms_norm F=3).  One workgroup, one vector.  out may alias res.
-__global__ __launch_bounds__(256) void k_rmsnorm_add(const float* __restrict__ o, int64_t n,
-                                                     const float* __restrict__ gamma, float eps,
-                                                     const float* res, float* out) {
-    __shared__ float red[4];
+// One workgroup of 1024 threads; every load (o, gamma, res: up to 4 float4
+// each per thread for n <= 16384) is issued before the first use, so the
+// whole op costs one memory round trip.
+constexpr int kNormAddThreads = 1024;
+constexpr int kNormAddIters = 4;     // 4 * 1024 * 4 = 16384 elements
+__global__ __launch_bounds__(kNormAddThreads) void k_rmsnorm_add(const float* __restrict__ o, int64_t n,
+                                                                 const float* __restrict__ gamma, float eps,
+                                                                 const float* res, float* out) {
+    __shared__ float red[kNormAddThreads / 64];
+    const int n4 = (int)(n >> 2);
+    float4 ov[kNormAddIters], gv[kNormAddIters], rv[kNormAddIters];
     float ss = 0.0f;
-    for (int64_t i = (int64_t)threadIdx.x * 4; i < n; i += 1024) {
-        float4 t = *reinterpret_cast<const float4*>(o + i);
-        ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+#pragma unroll
+    for (int k = 0; k < kNormAddIters; ++k) {
+        const int i = threadIdx.x + kNormAddThreads * k;
+        const int ic = i < n4 ? i : 0;                       // valid address; dropped below
+        ov[k] = reinterpret_cast<const float4*>(o)[ic];
+        gv[k] = gamma ? reinterpret_cast<const float4*>(gamma)[ic] : make_float4(1.f, 1.f, 1.f, 1.f);
+        rv[k] = reinterpret_cast<const float4*>(res)[ic];
     }
+#pragma unroll
+    for (int k = 0; k < kNormAddIters; ++k)
+        if ((int)threadIdx.x + kNormAddThreads * k < n4)
+            ss += ov[k].x * ov[k].x + ov[k].y * ov[k].y + ov[k].z * ov[k].z + ov[k].w * ov[k].w;
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    ss = (red[0] + red[1]) + (red[2] + red[3]);
+    ss = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNormAddThreads / 64; ++w) ss += red[w];
     const float rinv = 1.0f / sqrtf(ss / (float)n + eps);
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-        const float g = gamma ? gamma[i] : 1.0f;
-        out[i] = res[i] + (o[i] * rinv) * g;
+#pragma unroll
+    for (int k = 0; k < kNormAddIters; ++k) {
+        const int i = threadIdx.x + kNormAddThreads * k;
+        if (i < n4) {
+            float4 y;
+            y.x = rv[k].x + (ov[k].x * rinv) * gv[k].x;
+            y.y = rv[k].y + (ov[k].y * rinv) * gv[k].y;
+            y.z = rv[k].z + (ov[k].z * rinv) * gv[k].z;
+            y.w = rv[k].w + (ov[k].w * rinv) * gv[k].w;
+            reinterpret_cast<float4*>(out)[i] = y;
+        }
     }
 }
 
@@ -129,7 +154,7 @@ lq_status launch_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn, in
 lq_status launch_rmsnorm_add(const float* o, int64_t n, const float* gamma, float eps, const float* res,
                              float* out, hipStream_t s, LaunchMarks* mk) {
     if (n == 0) return LQ_OK;
-    launch_marked(mk, k_rmsnorm_add, dim3(1), dim3(256), 0, s, o, n, gamma, eps, res, out);
+    launch_marked(mk, k_rmsnorm_add, dim3(1), dim3(kNormAddThreads), 0, s, o, n, gamma, eps, res, out);
     return check_launch("rmsnorm_add");
 }
 

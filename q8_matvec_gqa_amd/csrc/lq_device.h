@@ -93,6 +93,17 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// Minimum of an int over the wave (same DPP/permlane steps as group_max<64>).
+__device__ __forceinline__ int wave_min_i(int v) {
+    v = min(v, dpp_i<kQuadXor1>(v));
+    v = min(v, dpp_i<kQuadXor2>(v));
+    v = min(v, dpp_i<kRowHalfMirror>(v));
+    v = min(v, dpp_i<kRowMirror>(v));
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = min((int)r[0], (int)r[1]);
+    r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return min((int)r[0], (int)r[1]);
+}
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
