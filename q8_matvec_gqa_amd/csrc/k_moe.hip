@@ -319,6 +319,102 @@ __global__ __launch_bounds__(256) void k_moe_matvec_id(const int8_t* __restrict_
     }
 }
 
+// ---- gate/up id-matvec with SwiGLU and the Q8_0 of h in the epilogue --------
+// blockIdx.x = active-expert index * (ffn/32) + h block.  A workgroup of 16
+// waves owns one 32-value block of h for its expert: wave w holds the gate
+// rows j and up rows j + ffn of its 2 outputs j (NCH 1 KB chunks each) in
+// VGPRs and, for every listed slot, computes h_j = silu(gate_j) * up_j; the
+// block is then quantized by wave 0 with the same rule as every other
+// quantizer here.  y1 (gate/up values, [slots, 2*ffn]) is written when given.
+constexpr int kGuWaves = 16, kGuPairs = 2;
+template <int NCH>
+__global__ __launch_bounds__(kGuWaves * 64) void k_moe_gu_swiglu_q8(const int8_t* __restrict__ wq,
+                                                                   const uint16_t* __restrict__ wd, int ffn,
+                                                                   int cols, const int8_t* __restrict__ xq,
+                                                                   const uint16_t* __restrict__ xd, int k,
+                                                                   const int32_t* __restrict__ wsbase, int E,
+                                                                   float* __restrict__ y1,
+                                                                   int8_t* __restrict__ hq,
+                                                                   uint16_t* __restrict__ hdq) {
+    constexpr int RPW = 2 * kGuPairs;
+    __shared__ float hs[32];
+    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
+    const int nblk = ffn >> 5;
+    const int ai = blockIdx.x / nblk, hb = blockIdx.x - ai * nblk;
+    if (ai >= *ws.n_active()) return;                 // uniform over the workgroup
+    const int e = ws.active()[ai];
+    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = cols >> 5;
+    const int rows = 2 * ffn;
+    const int8_t* we = wq + (int64_t)e * rows * cols;
+    const uint16_t* de = wd + (int64_t)e * rows * nb;
+    const int j0 = hb * 32 + wave * kGuPairs;         // this wave's outputs j0 .. j0+kGuPairs-1
+
+    int4 wv[RPW][NCH];
+    float wsc[RPW][NCH];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = j0 + (i >> 1) + (i & 1) * ffn;  // even i: gate row, odd i: up row
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            int off = c * 1024 + lane * 16;
+            if (off >= cols) off = cols - 16;         // a valid slice; its activation slice is zero
+            wv[i][c] = load_stream16(we + (int64_t)r * cols + off);
+            wsc[i][c] = f16_to_f32(de[(int64_t)r * nb + (off >> 5)]);
+        }
+    }
+    for (int si = s0; si < s1; ++si) {
+        const int slot = ws.slots()[si];
+        const int64_t xrow = slot / k;
+        int4 xv[NCH];
+        float xs[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int off = c * 1024 + lane * 16;
+            const int oc = off < cols ? off : cols - 16;
+            xv[c] = *reinterpret_cast<const int4*>(xq + xrow * cols + oc);
+            xs[c] = off < cols ? f16_to_f32(xd[xrow * nb + (oc >> 5)]) : 0.0f;
+            if (off >= cols) xv[c] = make_int4(0, 0, 0, 0);
+        }
+        float acc[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float t = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int p = dot16(wv[i][c], xv[c]);
+                const int blk = p + dpp_i<kQuadXor1>(p);
+                const float v = (float)blk * (wsc[i][c] * xs[c]);
+                t += (lane & 1) ? 0.0f : v;
+            }
+            acc[i] = wave_sum(t);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int jj = 0; jj < kGuPairs; ++jj) {
+                const float gt = acc[2 * jj], up = acc[2 * jj + 1];
+                hs[wave * kGuPairs + jj] = (gt / (1.0f + expf(-gt))) * up;
+                if (y1) {
+                    y1[(int64_t)slot * rows + j0 + jj] = gt;
+                    y1[(int64_t)slot * rows + ffn + j0 + jj] = up;
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const float v = lane < 32 ? hs[lane] : 0.0f;
+            const float amax = group_max<32>(fabsf(v));
+            const float d = amax / 127.0f;
+            const float inv = (d != 0.0f) ? 1.0f / d : 0.0f;
+            const float r = fminf(fmaxf(roundf(v * inv), -127.0f), 127.0f);
+            if (lane < 32) hq[(int64_t)slot * ffn + hb * 32 + lane] = (int8_t)(int32_t)r;
+            if (lane == 0) hdq[(int64_t)slot * nblk + hb] = f32_to_f16(d);
+        }
+        __syncthreads();                             // hs is rewritten by the next slot
+    }
+}
+
 __global__ __launch_bounds__(256) void k_moe_weighted_sum(const float* __restrict__ y,
                                                           const float* __restrict__ w, int64_t T,
                                                           int k, int64_t rows, float* __restrict__ out) {
@@ -375,6 +471,30 @@ static lq_status launch_id_gathered(const int8_t* wq, const uint16_t* wd, int64_
     }
 #undef LQ_ID_CASE
     return check_launch("moe_matvec_id");
+}
+
+template <int NCH>
+static void launch_gu_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int ffn, int cols, const int8_t* xq,
+                          const uint16_t* xd, int k, const int32_t* ws, int E, float* y1, int8_t* hq, uint16_t* hd) {
+    hipLaunchKernelGGL((k_moe_gu_swiglu_q8<NCH>), dim3((unsigned)(E * (ffn / 32))), dim3(kGuWaves * 64), 0, s, wq,
+                       wd, ffn, cols, xq, xd, k, ws, E, y1, hq, hd);
+}
+
+static lq_status launch_gu_swiglu_q8(const int8_t* wq, const uint16_t* wd, int64_t ffn, int64_t cols, int64_t E,
+                                     const int8_t* xq, const uint16_t* xd, int64_t k, const void* ws, float* y1,
+                                     int8_t* hq, uint16_t* hd, hipStream_t s) {
+    const int nch = (int)((cols + 1023) / 1024);
+    const int32_t* w32 = static_cast<const int32_t*>(ws);
+#define LQ_GU_CASE(N)                                                                                     \
+    case N:                                                                                               \
+        launch_gu_nch<N>(s, wq, wd, (int)ffn, (int)cols, xq, xd, (int)k, w32, (int)E, y1, hq, hd); \
+        break;
+    switch (nch) {
+        LQ_GU_CASE(1) LQ_GU_CASE(2) LQ_GU_CASE(3) LQ_GU_CASE(4)
+        default: return fail(LQ_ERR_UNSUPPORTED, "moe gate/up: hidden > 4096 in the fused SwiGLU path");
+    }
+#undef LQ_GU_CASE
+    return check_launch("moe_gate_up_swiglu_q8");
 }
 
 lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
@@ -539,10 +659,16 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     hipLaunchKernelGGL(k_moe_prep, dim3((unsigned)prep_grid), dim3(kGatherThreads), 0, s, logits, x, (int)T, (int)E, (int)k, (int)H,
                        b.ids, b.w, static_cast<int32_t*>(b.gather), b.xq, b.xd, b.y1, 2 * I, b.y2, H);
     if ((st = check_launch("moe_prep")) != LQ_OK) return st;
-    if ((st = launch_id_gathered(m->w_gate_up.qs, m->w_gate_up.d, 2 * I, H, E, b.xq, b.xd, 0, k, b.gather, b.y1,
-                                 s)) != LQ_OK)
-        return st;
-    if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
+    if (H <= 4096) {
+        if ((st = launch_gu_swiglu_q8(m->w_gate_up.qs, m->w_gate_up.d, I, H, E, b.xq, b.xd, k, b.gather,
+                                      taps ? taps->y1 : nullptr, b.hq, b.hd, s)) != LQ_OK)
+            return st;
+    } else {
+        if ((st = launch_id_gathered(m->w_gate_up.qs, m->w_gate_up.d, 2 * I, H, E, b.xq, b.xd, 0, k, b.gather,
+                                     b.y1, s)) != LQ_OK)
+            return st;
+        if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
+    }
     if ((st = launch_id_gathered(m->w_down.qs, m->w_down.d, H, I, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK)
         return st;
     return launch_moe_weighted_sum(b.y2, b.w, T, k, H, out, s);
