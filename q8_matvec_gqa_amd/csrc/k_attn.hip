@@ -198,11 +198,13 @@ __device__ __forceinline__ int4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 //   head_dim <= CM * CE; GM: query heads per kv head at most; NP: lanes per
 //   position in the K phase; TILE: positions per wave iteration; EX: the
 //   shape is exact (head_dim == CM * CE, G == GM), known at compile time;
-//   WPE: waves per SIMD the register budget is set for (workgroups per CU).
+//   WPE: waves per SIMD the register budget is set for; NW: waves per
+//   workgroup (more waves: fewer splits, so fewer partials to combine).
 // Inexact shapes run the same loops over CM and GM: rows shorter than CM
 // chunks load zeros past their end and query heads past G are zero.
-template <typename KV, int CM, int GM, int NP, int TILE, bool EX, int WPE>
-__global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
+template <typename KV, int CM, int GM, int NP, int TILE, bool EX, int WPE, int NW>
+__global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
+    constexpr int NT = NW * 64;
     constexpr int CE = KvTraits<KV>::CE;
     constexpr int HDM = CM * CE;                  // largest head_dim
     constexpr int EPL = (HDM + 63) / 64;          // prologue elements per lane
@@ -218,10 +220,10 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     constexpr int HPP = kWave / TW < GM ? kWave / TW : GM;
     constexpr int NPASS = GM / HPP;
     static_assert(TILE % TP == 0 && TILE <= 64 && HDM <= 512 && GM <= 8 && GM % HPP == 0, "tile shape");
-    constexpr int RED = kWavesPerWG * kRedFloats;
+    constexpr int RED = NW * kRedFloats;
 
-    __shared__ float sc[kWavesPerWG][TILE][GM];   // per wave: scores, then probabilities
-    __shared__ float wm[kWavesPerWG][GM], wl[kWavesPerWG][GM];
+    __shared__ float sc[NW][TILE][GM];   // per wave: scores, then probabilities
+    __shared__ float wm[NW][GM], wl[NW][GM];
     __shared__ __attribute__((aligned(16))) float q_lds[GM * HDM];
     __shared__ __attribute__((aligned(16))) float kv_new[2][HDM];     // new k and v rows, as stored
     __shared__ __attribute__((aligned(16))) float red[RED];
@@ -282,12 +284,12 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     // new position also builds the new k and v rows and appends them to the
     // caches (it alone reads them back, from LDS).
     const int t_new = lp_new >= 0 ? lp_new / TILE : -1;
-    const bool owner = t_new >= 0 && t_new % kWavesPerWG == wave;
-    const int n_qi = wave < G ? (G - wave + kWavesPerWG - 1) / kWavesPerWG : 0;
+    const bool owner = t_new >= 0 && t_new % NW == wave;
+    const int n_qi = wave < G ? (G - wave + NW - 1) / NW : 0;
     const int n_items = n_qi + (owner ? 2 : 0);
     auto item_src = [&](int i) -> HeadSrc {
         if (i < n_qi) {
-            const float* raw = a.q + (int64_t)(g * G + wave + kWavesPerWG * i) * hd;
+            const float* raw = a.q + (int64_t)(g * G + wave + NW * i) * hd;
             if (!a.fused) return HeadSrc{raw, nullptr, false, false, a.qscale};
             return HeadSrc{raw, a.qk_norm ? a.g_q : nullptr, a.qk_norm != 0, true, a.qscale};
         }
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     };
     auto item_run = [&](int i, const HeadIn<EPL>& in, const HeadSrc& src) {
         if (i < n_qi) {
-            head_finish<KV, EPL>(in, src, hd, a.eps, lane, q_lds + (wave + kWavesPerWG * i) * HDM, nullptr);
+            head_finish<KV, EPL>(in, src, hd, a.eps, lane, q_lds + (wave + NW * i) * HDM, nullptr);
         } else {
             const int64_t row = (int64_t)g * a.head_stride + pos_new * a.pos_stride;
             KV* cache = static_cast<KV*>(i == n_qi ? a.kc_w : a.vc_w);
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     // the items' inputs are read before the wave's first K/V tile (all of
     // them when they fit in registers), the tile before the items are
     // computed
-    constexpr int MAXI = (GM + kWavesPerWG - 1) / kWavesPerWG + 2;
+    constexpr int MAXI = (GM + NW - 1) / NW + 2;
     constexpr int EARLY = MAXI * 6 * EPL <= 72 ? MAXI : 1;
     HeadIn<EPL> hin[EARLY];
     HeadSrc srcs[EARLY];
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
     }
     if (!EX) {
         // zero the padding: query heads past G, dims past head_dim
-        for (int i = threadIdx.x; i < GM * HDM; i += 256)
+        for (int i = threadIdx.x; i < GM * HDM; i += NT)
             if (i / HDM >= G || i % HDM >= hd) q_lds[i] = 0.0f;
     }
     __syncthreads();
@@ -368,9 +370,9 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < CE; ++e) acc[h][c][e] = 0.0f;
 
-    for (; t < n_tiles; t += kWavesPerWG) {
+    for (; t < n_tiles; t += NW) {
         const int lp0 = t * TILE;                        // first position of the tile, split-local
-        const int next = t + kWavesPerWG;
+        const int next = t + NW;
         const int pt_new = (lp_new >= lp0 && lp_new < lp0 + TILE) ? lp_new - lp0 : -1;
 
         // ---- K phase: scores of the tile
@@ -388,11 +390,17 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
 #pragma unroll
                     for (int e = 0; e < CE; ++e) part[h] = fmaf(qr[h][c][e], kf[e], part[h]);
             }
+            if constexpr (NP == 64 && GM == 8) {
+                // one position per step: reduce-scatter, lane group h holds head h
+                const float sum = wave_sum8_scatter(part);
+                if ((lane & 7) == 0) sc[wave][st][(lane >> 3) & 7] = sum;
+            } else {
 #pragma unroll
-            for (int h = 0; h < GM; ++h) part[h] = group_sum<NP>(part[h]);
-            if (kk == 0) {
+                for (int h = 0; h < GM; ++h) part[h] = group_sum<NP>(part[h]);
+                if (kk == 0) {
 #pragma unroll
-                for (int h = 0; h < GM; ++h) sc[wave][st * TP + kp][h] = part[h];
+                    for (int h = 0; h < GM; ++h) sc[wave][st * TP + kp][h] = part[h];
+                }
             }
         }
         if (next < n_tiles) load_k(next, kr);
@@ -494,6 +502,25 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
             wl[wave][ps * HPP + hs] = lsum;
         }
     }
+    // per head: the workgroup maximum, each wave's weight exp2(m_w - M) and
+    // the weighted sum of the l's, once, before the per-element loop
+    __shared__ float wf[NW][GM], hM[GM], hL[GM];
+    __syncthreads();
+    if (threadIdx.x < G) {
+        const int h = threadIdx.x;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][h]);
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float ew = (wm[w][h] == -INFINITY) ? 0.0f : exp2f(wm[w][h] - M);
+            wf[w][h] = ew;
+            L += ew * wl[w][h];
+        }
+        hM[h] = M;
+        hL[h] = L;
+    }
     constexpr int per_head = VTP * HDM;
     constexpr int HC = kRedFloats / per_head < GM ? kRedFloats / per_head : GM;
     static_assert(per_head <= kRedFloats, "combine buffer");
@@ -518,29 +545,24 @@ __global__ __launch_bounds__(256, WPE) void k_attn_split(AttnArgs a) {
         }
         __syncthreads();
         const int n_el = (h1 - h0) * hd;
-        for (int idx = threadIdx.x; idx < n_el; idx += 256) {
+        for (int idx = threadIdx.x; idx < n_el; idx += NT) {
             const int hh = idx / hd, d = idx - hh * hd, h = h0 + hh;
-            float M = -INFINITY;
+            float S = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, wm[w][h]);
-            float L = 0.0f, S = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWavesPerWG; ++w) {
-                const float ew = (wm[w][h] == -INFINITY) ? 0.0f : exp2f(wm[w][h] - M);
+            for (int w = 0; w < NW; ++w) {
                 float sw = 0.0f;
 #pragma unroll
                 for (int v = 0; v < VTP; ++v) sw += red[w * kRedFloats + (hh * VTP + v) * HDM + d];
-                L += ew * wl[w][h];
-                S += ew * sw;
+                S += wf[w][h] * sw;
             }
             if (a.nsplit == 1) {
-                a.out[(int64_t)(g * G + h) * hd + d] = S / L;
+                a.out[(int64_t)(g * G + h) * hd + d] = S / hL[h];
             } else {
                 const int64_t slot = ((int64_t)g * a.nsplit + split) * G + h;
                 a.part_acc[slot * hd + d] = S;
                 if (d == 0) {
-                    a.part_m[slot] = M;
-                    a.part_l[slot] = L;
+                    a.part_m[slot] = hM[h];
+                    a.part_l[slot] = hL[h];
                 }
             }
         }
@@ -640,30 +662,31 @@ struct Variant {
     int c;       // chunks per row (head_dim / CE), exact
     int g;       // G, exact
     int tile;
-    int wpe;     // workgroups per CU resident at once
+    int wpe;     // waves per SIMD resident at once
+    int nw;      // waves per workgroup
     SplitFn fn;
 };
 
-template <typename KV, int CM, int GM, int NP, int TILE, int WPE = 2, bool EX = true>
+template <typename KV, int CM, int GM, int NP, int TILE, int WPE = 2, bool EX = true, int NW = 4>
 void launch_split(dim3 grid, hipStream_t s, const AttnArgs& a, LaunchMarks* mk) {
-    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE, EX, WPE>, grid, dim3(256), 0, s, a);
+    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE, EX, WPE, NW>, grid, dim3(NW * 64), 0, s, a);
 }
 
 // Exact shapes of the common models; <KV, chunks, G, lanes per position, tile, WGs per CU>.
 const Variant kVariants[] = {
-    {LQ_KV_F32, 16, 2, 32, 2, launch_split<float, 16, 2, 8, 32>},          // head_dim 64
-    {LQ_KV_F32, 16, 4, 32, 2, launch_split<float, 16, 4, 8, 32>},
-    {LQ_KV_F32, 32, 4, 16, 2, launch_split<float, 32, 4, 16, 16>},         // head_dim 128
-    {LQ_KV_BF16, 8, 2, 32, 2, launch_split<uint16_t, 8, 2, 8, 32>},        // head_dim 64
-    {LQ_KV_BF16, 8, 4, 32, 2, launch_split<uint16_t, 8, 4, 8, 32>},
-    {LQ_KV_BF16, 10, 2, 32, 2, launch_split<uint16_t, 10, 2, 8, 32>},      // head_dim 80
-    {LQ_KV_BF16, 10, 4, 32, 2, launch_split<uint16_t, 10, 4, 8, 32>},
-    {LQ_KV_BF16, 16, 2, 32, 2, launch_split<uint16_t, 16, 2, 8, 32>},      // head_dim 128
-    {LQ_KV_BF16, 16, 4, 32, 2, launch_split<uint16_t, 16, 4, 8, 32>},
-    {LQ_KV_BF16, 16, 8, 16, 2, launch_split<uint16_t, 16, 8, 16, 16>},
-    {LQ_KV_BF16, 32, 2, 16, 2, launch_split<uint16_t, 32, 2, 16, 16>},     // head_dim 256
-    {LQ_KV_BF16, 32, 4, 16, 2, launch_split<uint16_t, 32, 4, 16, 16>},
-    {LQ_KV_BF16, 64, 8, 8, 2, launch_split<uint16_t, 64, 8, 64, 8>},       // head_dim 512
+    {LQ_KV_F32, 16, 2, 32, 2, 4, launch_split<float, 16, 2, 8, 32>},          // head_dim 64
+    {LQ_KV_F32, 16, 4, 32, 2, 4, launch_split<float, 16, 4, 8, 32>},
+    {LQ_KV_F32, 32, 4, 16, 2, 4, launch_split<float, 32, 4, 16, 16>},         // head_dim 128
+    {LQ_KV_BF16, 8, 2, 32, 2, 4, launch_split<uint16_t, 8, 2, 8, 32>},        // head_dim 64
+    {LQ_KV_BF16, 8, 4, 32, 2, 4, launch_split<uint16_t, 8, 4, 8, 32>},
+    {LQ_KV_BF16, 10, 2, 32, 2, 4, launch_split<uint16_t, 10, 2, 8, 32>},      // head_dim 80
+    {LQ_KV_BF16, 10, 4, 32, 2, 4, launch_split<uint16_t, 10, 4, 8, 32>},
+    {LQ_KV_BF16, 16, 2, 32, 2, 4, launch_split<uint16_t, 16, 2, 8, 32>},      // head_dim 128
+    {LQ_KV_BF16, 16, 4, 32, 2, 4, launch_split<uint16_t, 16, 4, 8, 32>},
+    {LQ_KV_BF16, 16, 8, 16, 2, 4, launch_split<uint16_t, 16, 8, 16, 16>},
+    {LQ_KV_BF16, 32, 2, 16, 2, 4, launch_split<uint16_t, 32, 2, 16, 16>},     // head_dim 256
+    {LQ_KV_BF16, 32, 4, 16, 2, 4, launch_split<uint16_t, 32, 4, 16, 16>},
+    {LQ_KV_BF16, 64, 8, 8, 2, 8, launch_split<uint16_t, 64, 8, 64, 8, 2, true, 8>},       // head_dim 512
 };
 
 int ce_of(int32_t dtype) { return dtype == LQ_KV_F32 ? 4 : 8; }
@@ -672,26 +695,28 @@ struct Pick {
     SplitFn fn;
     int tile;
     int wpe;
+    int nw;
 };
 
 Pick pick(int32_t dtype, int64_t hd, int64_t G) {
     const int c = (int)(hd / ce_of(dtype));
     for (const Variant& v : kVariants)
-        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe};
+        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe, v.nw};
     // any head_dim <= 512 and G <= 8: padded loops, one position per K step
-    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2};
-    return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2};
+    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2, 4};
+    return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2, 4};
 }
 
-Plan make_plan(int64_t n_kv, int64_t len, int tile, int wpe) {
+Plan make_plan(int64_t n_kv, int64_t len, const Pick& pk) {
+    const int64_t tile = pk.tile, nw = pk.nw;
     const int64_t tiles = (len + tile - 1) / tile;
-    int64_t ns = ((int64_t)kNumCUs * wpe + n_kv - 1) / n_kv;             // one resident round of workgroups
-    const int64_t by_tiles = (tiles + kWavesPerWG - 1) / kWavesPerWG;   // every wave gets a tile
+    int64_t ns = ((int64_t)kNumCUs * pk.wpe * 4 / nw + n_kv - 1) / n_kv;   // one resident round of workgroups
+    const int64_t by_tiles = (tiles + nw - 1) / nw;                     // every wave gets a tile
     if (ns > by_tiles) ns = by_tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
     int64_t tps = (tiles + ns - 1) / ns;
-    tps = (tps + kWavesPerWG - 1) / kWavesPerWG * kWavesPerWG;        // whole tiles per wave
+    tps = (tps + nw - 1) / nw * nw;                                     // whole tiles per wave
     ns = (tiles + tps - 1) / tps;
     if (ns < 1) ns = 1;
     return Plan{(int)ns, (int)tps};
@@ -708,7 +733,7 @@ bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype) {
 static size_t ws_bytes_for(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t dtype) {
     if (len <= 0 || n_kv <= 0) return 0;
     const Pick pk = pick(dtype, hd, n_q / n_kv);
-    const Plan p = make_plan(n_kv, len, pk.tile, pk.wpe);
+    const Plan p = make_plan(n_kv, len, pk);
     if (p.nsplit == 1) return 0;
     const int64_t slots = n_kv * p.nsplit * (n_q / n_kv);
     return (size_t)(slots * (hd + 2)) * sizeof(float);
@@ -725,7 +750,7 @@ static lq_status launch_common(AttnArgs& a, int64_t n_q, int64_t n_kv, int64_t h
                                void* ws, hipStream_t s, LaunchMarks* marks = nullptr) {
     const int64_t G = n_q / n_kv;
     const Pick pk = pick(kv_dtype, hd, G);
-    const Plan p = make_plan(n_kv, a.len, pk.tile, pk.wpe);
+    const Plan p = make_plan(n_kv, a.len, pk);
     // buffer offsets inside one split stay below 2^31 bytes
     const int64_t es = kv_dtype == LQ_KV_F32 ? 4 : 2;
     if (((int64_t)p.tiles_per_split * pk.tile + 64) * a.pos_stride * es >= (int64_t(1) << 31))

@@ -52,6 +52,7 @@ constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;      // row_ror:8 (within 16 lanes: lane ^ 8)
 
 // Sum over aligned groups of N consecutive lanes (N = 2..64, power of two);
 // every lane of a group receives the group sum.  The mirror steps pair lanes
@@ -91,6 +92,36 @@ __device__ __forceinline__ float group_max(float v) {
         v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     }
     return v;
+}
+
+// Sums each of v[0..7] over the 64 lanes of the wave and leaves the sum of
+// v[h] in the lanes with (lane >> 3) & 7 == h (a reduce-scatter: halves are
+// exchanged across lane bits 5, 4 and 3, then 8-lane groups are summed).
+__device__ __forceinline__ float wave_sum8_scatter(const float (&v)[8]) {
+    const int lane = threadIdx.x & 63;
+    float a[4], b[2];
+    // bit 5: lanes 0-31 keep heads 0-3, lanes 32-63 heads 4-7
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[h]), __float_as_uint(v[h + 4]), false, false);
+        a[h] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // bit 4: keep the first or second pair of the four
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[h]), __float_as_uint(a[h + 2]), false, false);
+        b[h] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // bit 3: keep one of the two; the partner (lane ^ 8) sends the other
+    const bool hi = (lane & 8) != 0;
+    const float send = hi ? b[0] : b[1];
+    const float keep = hi ? b[1] : b[0];
+    float c = keep + dpp<kRowRor8>(send);
+    // bits 0-2
+    c += dpp<kQuadXor1>(c);
+    c += dpp<kQuadXor2>(c);
+    c += dpp<kRowHalfMirror>(c);
+    return c;
 }
 
 // Minimum of an int over the wave (same DPP/permlane steps as group_max<64>).
