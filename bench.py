@@ -144,8 +144,8 @@ def layer_kernels(cfg, nsplit_used):
         ks.append(("attn_combine", "k_attn_combine", 0))
     if cfg["kind"] == 0:
         ks += [("o_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 8 * H),
-               ("gate_up_matvec", "k_mv<NCH=%d,NORM,SWIGLU>" % math.ceil(H / 1024), q8w(2 * I, H) + 8 * H + 4 * I),
-               ("down_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(I / 1024), q8w(H, I) + 4 * I + 8 * H)]
+               ("gate_up_matvec", "k_mv<NCH=%d,NORM,SWIGLU_Q8>" % math.ceil(H / 1024), q8w(2 * I, H) + 8 * H + q8w(1, I)),
+               ("down_matvec", "k_mv<NCH=%d,Q8,RESID>" % math.ceil(I / 1024), q8w(H, I) + q8w(1, I) + 8 * H)]
     else:
         ks += [("o_matvec", "k_mv<NCH=%d,QUANT,STORE>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 4 * H),
                ("post_norm_add", "k_rmsnorm_add", 16 * H)]
@@ -330,7 +330,7 @@ def _kernel_match(name, tag):
     """rocprofv3 kernel names -> the layer's kernel tags."""
     if tag == "gate_up_matvec":
         import re
-        return re.search(r"k_mv<\d+, \d+, 2, 2>", name) is not None     # the RMSNorm + SwiGLU instance
+        return re.search(r"k_mv<\d+, \d+, 2, 3, \d+>", name) is not None     # RMSNorm prologue, SwiGLU + Q8_0 epilogue
     if tag == "copy":
         return "neg" in name.lower()
     raise ValueError(tag)
@@ -360,7 +360,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, command):
     cfg = synthetic.layer_cfg(workload)
     algo = dict((t, b) for t, _, b in layer_kernels(cfg, True))["gate_up_matvec"]
     lines = [
-        f"# HBM traffic of the gate_up matvec (k_mv<NCH, RPW, NORM, SWIGLU>), {workload}",
+        f"# HBM traffic of the gate_up matvec (k_mv<NCH, RPW, NORM, SWIGLU_Q8, WAVES>), {workload}",
         f"command_fetch: {command.replace('WRITE_SIZE', 'FETCH_SIZE')}",
         f"command_write: {command.replace('FETCH_SIZE', 'WRITE_SIZE')}",
         f"source_sha256: {source_hash(KERNEL_SOURCES)}",
