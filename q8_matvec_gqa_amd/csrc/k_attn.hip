@@ -665,6 +665,7 @@ struct Variant {
     int wpe;     // waves per SIMD resident at once
     int nw;      // waves per workgroup
     SplitFn fn;
+    int tpw = 1; // tiles per wave at least (more: the next tile's loads overlap this tile's math)
 };
 
 template <typename KV, int CM, int GM, int NP, int TILE, int WPE = 2, bool EX = true, int NW = 4>
@@ -682,11 +683,11 @@ const Variant kVariants[] = {
     {LQ_KV_BF16, 10, 2, 32, 2, 4, launch_split<uint16_t, 10, 2, 8, 32>},      // head_dim 80
     {LQ_KV_BF16, 10, 4, 32, 2, 4, launch_split<uint16_t, 10, 4, 8, 32>},
     {LQ_KV_BF16, 16, 2, 32, 2, 4, launch_split<uint16_t, 16, 2, 8, 32>},      // head_dim 128
-    {LQ_KV_BF16, 16, 4, 32, 2, 4, launch_split<uint16_t, 16, 4, 8, 32>},
+    {LQ_KV_BF16, 16, 4, 16, 2, 4, launch_split<uint16_t, 16, 4, 8, 16>, 2},
     {LQ_KV_BF16, 16, 8, 16, 2, 4, launch_split<uint16_t, 16, 8, 16, 16>},
-    {LQ_KV_BF16, 32, 2, 16, 2, 4, launch_split<uint16_t, 32, 2, 16, 16>},     // head_dim 256
+    {LQ_KV_BF16, 32, 2, 8, 2, 4, launch_split<uint16_t, 32, 2, 16, 8>},     // head_dim 256
     {LQ_KV_BF16, 32, 4, 16, 2, 4, launch_split<uint16_t, 32, 4, 16, 16>},
-    {LQ_KV_BF16, 64, 8, 8, 2, 8, launch_split<uint16_t, 64, 8, 64, 8, 2, true, 8>},       // head_dim 512
+    {LQ_KV_BF16, 64, 8, 4, 2, 8, launch_split<uint16_t, 64, 8, 64, 4, 2, true, 8>, 2},       // head_dim 512
 };
 
 int ce_of(int32_t dtype) { return dtype == LQ_KV_F32 ? 4 : 8; }
@@ -696,22 +697,23 @@ struct Pick {
     int tile;
     int wpe;
     int nw;
+    int tpw;
 };
 
 Pick pick(int32_t dtype, int64_t hd, int64_t G) {
     const int c = (int)(hd / ce_of(dtype));
     for (const Variant& v : kVariants)
-        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe, v.nw};
+        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe, v.nw, v.tpw};
     // any head_dim <= 512 and G <= 8: padded loops, one position per K step
-    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2, 4};
-    return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2, 4};
+    if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2, 4, 1};
+    return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2, 4, 1};
 }
 
 Plan make_plan(int64_t n_kv, int64_t len, const Pick& pk) {
     const int64_t tile = pk.tile, nw = pk.nw;
     const int64_t tiles = (len + tile - 1) / tile;
     int64_t ns = ((int64_t)kNumCUs * pk.wpe * 4 / nw + n_kv - 1) / n_kv;   // one resident round of workgroups
-    const int64_t by_tiles = (tiles + nw - 1) / nw;                     // every wave gets a tile
+    const int64_t by_tiles = (tiles + nw * pk.tpw - 1) / (nw * pk.tpw);  // every wave gets tpw tiles
     if (ns > by_tiles) ns = by_tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
