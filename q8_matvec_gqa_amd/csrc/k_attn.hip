@@ -259,22 +259,29 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
         voff[c] = (vp < VTP && ch < C) ? (uint32_t)vp * pb + (uint32_t)ch * 16u : kOob;
     }
 
+    // A tile past the split's end (t >= n_tiles) is still issued, at offsets
+    // that are out of range (zeros, no memory access): the loads stay
+    // unconditional, so each wait counts exactly the loads issued before it
+    // (a branch around them would make the compiler wait for all of them).
     auto load_k = [&](int t, int4 (&kr)[KSTEPS][CPL]) {
+        const bool live = t < n_tiles;
         const uint32_t base = (uint32_t)(t * TILE) * pb;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) kr[st][c] = bload16(rk, koff[c] + base + (uint32_t)(st * TP) * pb);
+            for (int c = 0; c < CPL; ++c)
+                kr[st][c] = bload16(rk, live ? koff[c] + base + (uint32_t)(st * TP) * pb : kOob);
     };
     auto load_v = [&](int t, int4 (&vr)[VSTEPS][VCPL]) {
+        const bool live = t < n_tiles;
         const uint32_t base = (uint32_t)(t * TILE) * pb;
 #pragma unroll
         for (int st = 0; st < VSTEPS; ++st) {
             // a last, partial step must not reach into the next tile
-            const bool in = (TILE % VTP == 0) || st * VTP + vp < TILE;
+            const bool in = live && ((TILE % VTP == 0) || st * VTP + vp < TILE);
 #pragma unroll
             for (int c = 0; c < VCPL; ++c)
-                vr[st][c] = bload16(rv, (in ? voff[c] : kOob) + base + (uint32_t)(st * VTP) * pb);
+                vr[st][c] = bload16(rv, in ? voff[c] + base + (uint32_t)(st * VTP) * pb : kOob);
         }
     };
 
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
     // them when they fit in registers), the tile before the items are
     // computed
     constexpr int MAXI = (GM + NW - 1) / NW + 2;
-    constexpr int EARLY = MAXI * 6 * EPL <= 72 ? MAXI : 1;
+    constexpr int EARLY = MAXI * 6 * EPL <= 160 ? MAXI : 1;
     HeadIn<EPL> hin[EARLY];
     HeadSrc srcs[EARLY];
 #pragma unroll
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
                 }
             }
         }
-        if (next < n_tiles) load_k(next, kr);
+        load_k(next, kr);
         if (pt_new >= 0) {
             // the new position: its k row comes from LDS (the cache row was
             // loaded before it was written)
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
                 }
             }
         }
-        if (next < n_tiles) load_v(next, vr);
+        load_v(next, vr);
         wave_lds_sync();                 // this tile's probabilities are read before the next overwrite
     }
 
