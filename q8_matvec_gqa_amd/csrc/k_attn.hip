@@ -33,6 +33,8 @@
 //     that a second kernel rescales and sums over the splits.
 #include <math.h>
 
+#include <type_traits>
+
 #include "lq_device.h"
 #include "lq_internal.h"
 
@@ -174,6 +176,104 @@ __device__ __forceinline__ void head_finish(const HeadIn<EPL>& in, const HeadSrc
     }
 }
 
+// Contiguous form, for head_dim == 64 * EPL: lane l owns elements
+// [l*EPL, (l+1)*EPL), read and written with vector accesses (16-byte aligned
+// rows), and the RoPE partner of each element (i +- head_dim/2) is the same
+// element of lane l ^ 32, fetched with a cross-half lane swap instead of a
+// second load; both halves use the table entries of lane l & 31.
+template <int EPL>
+struct HeadInV {
+    float own[EPL], ga[EPL], cs[EPL], sn[EPL];
+};
+
+template <int N>
+__device__ __forceinline__ void load_run(float (&d)[N], const float* __restrict__ p) {
+    if constexpr (N == 1) {
+        d[0] = p[0];
+    } else if constexpr (N == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        d[0] = v.x; d[1] = v.y;
+    } else {
+        static_assert(N % 4 == 0, "run length");
+#pragma unroll
+        for (int j = 0; j < N; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(p + j);
+            d[j] = v.x; d[j + 1] = v.y; d[j + 2] = v.z; d[j + 3] = v.w;
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_run(float* p, const float (&d)[N]) {
+    if constexpr (N == 1) {
+        p[0] = d[0];
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(d[0], d[1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; j += 4) *reinterpret_cast<float4*>(p + j) = make_float4(d[j], d[j + 1], d[j + 2], d[j + 3]);
+    }
+}
+
+// the value of v held by lane ^ 32
+__device__ __forceinline__ float half_swap(float v, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+template <int EPL>
+__device__ __forceinline__ void head_load_v(HeadInV<EPL>& in, const HeadSrc& h, const float* __restrict__ cs,
+                                            const float* __restrict__ sn, int lane) {
+    const int i0 = lane * EPL, t0 = (lane & 31) * EPL;
+    load_run<EPL>(in.own, h.raw + i0);
+    load_run<EPL>(in.ga, (h.gamma ? h.gamma : h.raw) + i0);
+    load_run<EPL>(in.cs, (h.rope ? cs : h.raw) + t0);
+    load_run<EPL>(in.sn, (h.rope ? sn : h.raw) + t0);
+}
+
+template <typename KV, int EPL>
+__device__ __forceinline__ void head_finish_v(const HeadInV<EPL>& in, const HeadSrc& h, float eps, int lane,
+                                              float* dst, KV* kv_dst) {
+    constexpr int HD = 64 * EPL;
+    const bool wg = h.gamma != nullptr;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) ss += in.own[j] * in.own[j];
+    float rinv = 1.0f;
+    if (h.norm) rinv = 1.0f / sqrtf(wave_sum(ss) / (float)HD + eps);
+    float y[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const float av = in.own[j] * rinv * (wg ? in.ga[j] : 1.0f);
+        y[j] = av;
+        if (h.rope) {
+            const float bv = half_swap(av, lane);
+            y[j] = lane < 32 ? av * in.cs[j] - bv * in.sn[j] : bv * in.sn[j] + av * in.cs[j];
+        }
+        y[j] *= h.scale;
+    }
+    if (kv_dst) {
+        KV* row = kv_dst + lane * EPL;
+        if constexpr (sizeof(KV) == 4) {
+            store_run<EPL>(reinterpret_cast<float*>(row), y);
+        } else {
+            uint32_t b[EPL];
+#pragma unroll
+            for (int j = 0; j < EPL; ++j) {
+                b[j] = f32_to_bf16(y[j]);
+                y[j] = bf16_to_f32(b[j]);
+            }
+            if constexpr (EPL == 1) {
+                row[0] = (KV)b[0];
+            } else {
+#pragma unroll
+                for (int j = 0; j < EPL; j += 2) reinterpret_cast<uint32_t*>(row)[j / 2] = b[j] | (b[j + 1] << 16);
+            }
+        }
+    }
+    store_run<EPL>(dst + lane * EPL, y);
+}
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -286,14 +386,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
     };
 
     // ---- prologue items: the G query heads of this kv head (pre-scaled by
-    // scale*log2(e)), wave w taking heads w, w+4, ...; in the decode layer
-    // they are normalised and rotated here, and the wave whose tiles hold the
-    // new position also builds the new k and v rows and appends them to the
-    // caches (it alone reads them back, from LDS).
-    const int t_new = lp_new >= 0 ? lp_new / TILE : -1;
-    const bool owner = t_new >= 0 && t_new % NW == wave;
+    // scale*log2(e)), then, in the workgroup whose split holds the new
+    // position, its k and v rows: item j goes to wave j % NW.  In the decode
+    // layer they are normalised and rotated here; the new k and v rows are
+    // appended to the caches and kept in LDS, where the wave whose tile holds
+    // the new position reads them back.
+    const bool new_here = lp_new >= 0;
     const int n_qi = wave < G ? (G - wave + NW - 1) / NW : 0;
-    const int n_items = n_qi + (owner ? 2 : 0);
+    const bool has_k = new_here && wave == G % NW, has_v = new_here && wave == (G + 1) % NW;
+    const int n_items = n_qi + (has_k ? 1 : 0) + (has_v ? 1 : 0);
+    // item i of this wave past its query heads: 0 = k, 1 = v
+    auto kv_item = [&](int i) { return (has_k && i == n_qi) ? 0 : 1; };
     auto item_src = [&](int i) -> HeadSrc {
         if (i < n_qi) {
             const float* raw = a.q + (int64_t)(g * G + wave + NW * i) * hd;
@@ -301,31 +404,44 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
             return HeadSrc{raw, a.qk_norm ? a.g_q : nullptr, a.qk_norm != 0, true, a.qscale};
         }
         const float* kraw = a.q + (int64_t)a.n_q * hd + (int64_t)g * hd;
-        if (i == n_qi) return HeadSrc{kraw, a.qk_norm ? a.g_k : nullptr, a.qk_norm != 0, true, 1.0f};
+        if (kv_item(i) == 0) return HeadSrc{kraw, a.qk_norm ? a.g_k : nullptr, a.qk_norm != 0, true, 1.0f};
         return HeadSrc{kraw + (int64_t)a.n_kv * hd, nullptr, a.v_unit_norm != 0, false, 1.0f};
     };
-    auto item_run = [&](int i, const HeadIn<EPL>& in, const HeadSrc& src) {
+    // exact shapes with head_dim == 64 * EPL >= 256 use the contiguous form
+    // (measured: for head_dim 128 the strided form is faster)
+    constexpr bool VEC = EX && HDM == 64 * EPL && EPL >= 4;
+    using HIn = std::conditional_t<VEC, HeadInV<EPL>, HeadIn<EPL>>;
+    auto item_load = [&](HIn& in, const HeadSrc& src) {
+        if constexpr (VEC) head_load_v<EPL>(in, src, a.rope_cos, a.rope_sin, lane);
+        else head_load<EPL>(in, src, a.rope_cos, a.rope_sin, hd, lane);
+    };
+    auto item_fin = [&](const HIn& in, const HeadSrc& src, float* dst, KV* kv) {
+        if constexpr (VEC) head_finish_v<KV, EPL>(in, src, a.eps, lane, dst, kv);
+        else head_finish<KV, EPL>(in, src, hd, a.eps, lane, dst, kv);
+    };
+    auto item_run = [&](int i, const HIn& in, const HeadSrc& src) {
         if (i < n_qi) {
-            head_finish<KV, EPL>(in, src, hd, a.eps, lane, q_lds + (wave + NW * i) * HDM, nullptr);
+            item_fin(in, src, q_lds + (wave + NW * i) * HDM, nullptr);
         } else {
             const int64_t row = (int64_t)g * a.head_stride + pos_new * a.pos_stride;
-            KV* cache = static_cast<KV*>(i == n_qi ? a.kc_w : a.vc_w);
-            head_finish<KV, EPL>(in, src, hd, a.eps, lane, kv_new[i - n_qi], cache + row);
+            const int kv = kv_item(i);
+            KV* cache = static_cast<KV*>(kv == 0 ? a.kc_w : a.vc_w);
+            item_fin(in, src, kv_new[kv], cache + row);
         }
     };
 
     // the items' inputs are read before the wave's first K/V tile (all of
     // them when they fit in registers), the tile before the items are
     // computed
-    constexpr int MAXI = (GM + NW - 1) / NW + 2;
-    constexpr int EARLY = MAXI * 6 * EPL <= 160 ? MAXI : 1;
-    HeadIn<EPL> hin[EARLY];
+    constexpr int MAXI = (GM + 2 + NW - 1) / NW;
+    constexpr int EARLY = MAXI * (VEC ? 4 : 6) * EPL <= (VEC ? 160 : 72) ? MAXI : 1;
+    HIn hin[EARLY];
     HeadSrc srcs[EARLY];
 #pragma unroll
     for (int i = 0; i < EARLY; ++i) {
         if (i < n_items) {
             srcs[i] = item_src(i);
-            head_load<EPL>(hin[i], srcs[i], a.rope_cos, a.rope_sin, hd, lane);
+            item_load(hin[i], srcs[i]);
         }
     }
     __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of the tile's
@@ -339,7 +455,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
         if (i < n_items) item_run(i, hin[i], srcs[i]);
     for (int i = EARLY; i < n_items; ++i) {
         const HeadSrc src = item_src(i);
-        head_load<EPL>(hin[0], src, a.rope_cos, a.rope_sin, hd, lane);
+        item_load(hin[0], src);
         item_run(i, hin[0], src);
     }
     if (!EX) {
@@ -707,10 +823,14 @@ struct Pick {
     int tpw;
 };
 
-Pick pick(int32_t dtype, int64_t hd, int64_t G) {
+// vec_ok: the query rows are 16-byte aligned; exact instances with head_dim
+// 256 or 512 read them with vector loads, so without it the padded instance
+// runs.
+Pick pick(int32_t dtype, int64_t hd, int64_t G, bool vec_ok) {
     const int c = (int)(hd / ce_of(dtype));
-    for (const Variant& v : kVariants)
-        if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe, v.nw, v.tpw};
+    if (vec_ok || !(hd == 256 || hd == 512))
+        for (const Variant& v : kVariants)
+            if (v.dtype == dtype && v.c == c && v.g == G) return Pick{v.fn, v.tile, v.wpe, v.nw, v.tpw};
     // any head_dim <= 512 and G <= 8: padded loops, one position per K step
     if (dtype == LQ_KV_F32) return Pick{launch_split<float, 128, 8, 64, 4, 2, false>, 4, 2, 4, 1};
     return Pick{launch_split<uint16_t, 64, 8, 64, 8, 2, false>, 8, 2, 4, 1};
@@ -741,11 +861,20 @@ bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype) {
 
 static size_t ws_bytes_for(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t dtype) {
     if (len <= 0 || n_kv <= 0) return 0;
-    const Pick pk = pick(dtype, hd, n_q / n_kv);
-    const Plan p = make_plan(n_kv, len, pk);
-    if (p.nsplit == 1) return 0;
-    const int64_t slots = n_kv * p.nsplit * (n_q / n_kv);
-    return (size_t)(slots * (hd + 2)) * sizeof(float);
+    size_t most = 0;
+    for (const bool vec_ok : {true, false}) {
+        const Plan p = make_plan(n_kv, len, pick(dtype, hd, n_q / n_kv, vec_ok));
+        if (p.nsplit == 1) continue;
+        const int64_t slots = n_kv * p.nsplit * (n_q / n_kv);
+        const size_t b = (size_t)(slots * (hd + 2)) * sizeof(float);
+        most = b > most ? b : most;
+    }
+    return most;
+}
+
+int attn_nsplit(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t kv_dtype, bool vec_ok) {
+    if (len <= 0 || n_kv <= 0) return 0;
+    return make_plan(n_kv, len, pick(kv_dtype, hd, n_q / n_kv, vec_ok)).nsplit;
 }
 
 size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len) {
@@ -758,7 +887,7 @@ size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len) 
 static lq_status launch_common(AttnArgs& a, int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype,
                                void* ws, hipStream_t s, LaunchMarks* marks = nullptr) {
     const int64_t G = n_q / n_kv;
-    const Pick pk = pick(kv_dtype, hd, G);
+    const Pick pk = pick(kv_dtype, hd, G, a.fused || reinterpret_cast<uintptr_t>(a.q) % 16 == 0);
     const Plan p = make_plan(n_kv, a.len, pk);
     // buffer offsets inside one split stay below 2^31 bytes
     const int64_t es = kv_dtype == LQ_KV_F32 ? 4 : 2;

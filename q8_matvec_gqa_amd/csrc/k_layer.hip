@@ -136,7 +136,7 @@ using Marks = LaunchMarks;
 
 int kernel_count(const lq_layer_desc* L, int64_t len) {
     // QKV, attention (+ split combine), O, then gate_up and down, or the post-norm add
-    const bool combine = attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, len) > 0;
+    const bool combine = attn_nsplit(L->n_q, L->n_kv, L->head_dim, len, L->kv_dtype, true) > 1;
     return 3 + (combine ? 1 : 0) + (L->kind == LQ_LAYER_PRENORM_FFN ? 2 : 1);
 }
 

@@ -116,6 +116,8 @@ lq_status launch_qkv_post(float* qkv, int64_t n_q, int64_t n_kv, int64_t hd, con
 // ---- launchers (k_attn.hip) ---------------------------------------------------
 bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype);
 size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len);
+// splits the layer's attention uses (1: no combine launch); vec_ok: 16-byte aligned query rows
+int attn_nsplit(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t kv_dtype, bool vec_ok);
 lq_status launch_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd, const void* kc,
                            const void* vc, int32_t kv_dtype, int64_t head_stride,
                            int64_t pos_stride, int64_t start, int64_t len, float scale,

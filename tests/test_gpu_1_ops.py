@@ -188,7 +188,8 @@ def run_attn(q, n_q, n_kv, hd, kc, vc, dtype, hs, ps, max_ctx, start, length, sc
     out = empty(n_q * hd, np.float32)
     need = lq.lq_gqa_decode_attn_workspace_size(n_q, n_kv, hd, length)
     ws = workspace(need)
-    lq.lq_gqa_decode_attn(dev(q), n_q, n_kv, hd, dev(kc), dev(vc), dtype, hs, ps, max_ctx, start, length,
+    qd = q if not isinstance(q, np.ndarray) else dev(q)
+    lq.lq_gqa_decode_attn(qd, n_q, n_kv, hd, dev(kc), dev(vc), dtype, hs, ps, max_ctx, start, length,
                           scale, out, ws, ws.numel())
     sync()
     return host(out)
@@ -234,6 +235,22 @@ def test_attention_strided_layout():
     got = run_attn(q, n_q, n_kv, hd, kc, vc, 1, hd, n_kv * hd, ctx, 200, 1300, 0.1)
     want = oracle.attention(q, n_q, n_kv, hd, kc, vc, 1, hd, n_kv * hd, 200, 1300, 0.1)
     assert_close(got, want, "attention strided")
+
+
+@pytest.mark.parametrize("hd,n_kv,n_q", [(128, 8, 32), (256, 8, 16), (512, 2, 16)])
+def test_attention_unaligned_query(hd, n_kv, n_q):
+    """q 4-byte but not 16-byte aligned: the exact instances read query rows
+    with vector loads, so the padded instance must take the call."""
+    r = rng(91 + hd)
+    ctx = 1200
+    kc = synthetic.kv_cache(r, n_kv, ctx, hd, 1)
+    vc = synthetic.kv_cache(r, n_kv, ctx, hd, 1)
+    q = synthetic.activations(r, n_q * hd)
+    qd = dev(np.concatenate([np.zeros(1, np.float32), q]))[1:]
+    assert qd.data_ptr() % 16 == 4
+    got = run_attn(qd, n_q, n_kv, hd, kc, vc, 1, ctx * hd, hd, ctx, 5, 1190, 0.07)
+    want = oracle.attention(q, n_q, n_kv, hd, kc, vc, 1, ctx * hd, hd, 5, 1190, 0.07)
+    assert_close(got, want, "attention unaligned q")
 
 
 def test_attention_empty_window_writes_zeros():
