@@ -170,31 +170,37 @@ struct RowGroup {
     uint32_t d[RPW][NCH];
 };
 
-// Loads are unconditional, from clamped addresses: rows past the end reload
-// the last row (never stored) and 16-byte slices past the last column reload
-// the row's last slice (their activation slice is zero).  No branches sit
-// between the loads, so nothing forces an early wait on them.
+// Loads are unconditional, from clamped addresses: rows past the end read
+// the first 16 bytes of the matrix in every lane (one cache line, never
+// stored), and 16-byte slices past the last column reload the row's last
+// slice (their activation slice is zero).  No branches sit between the
+// loads, so nothing forces an early wait on them.
 template <int NCH, int RPW, int EPI>
-__device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int lane, RowGroup<NCH, RPW>& G) {
+__device__ __forceinline__ void load_group(const MvArgs& a, int64_t g, int64_t gend, int lane,
+                                           RowGroup<NCH, RPW>& G) {
     const int nb = a.cols >> 5;
+    const bool glive = g < gend;          // groups from gend on belong to no one here
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         // SwiGLU pairs: even i -> gate row, odd i -> the matching up row
         int64_t r;
+        bool live;
         if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) {
-            int64_t o = g * (RPW / 2) + i / 2;
-            if (o >= a.rows) o = a.rows - 1;
+            const int64_t o = g * (RPW / 2) + i / 2;
+            live = glive && o < a.rows;
             r = o + (i & 1) * (int64_t)a.rows;
         } else {
             r = g * RPW + i;
-            if (r >= a.rows) r = a.rows - 1;
+            live = glive && r < a.rows;
         }
+        if (!live) r = 0;
         const int8_t* wr = a.wq + r * a.cols;
         const uint16_t* dr = a.wd + r * nb;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             int off = c * 1024 + lane * 16;
             if (off >= a.cols) off = a.cols - 16;
+            if (!live) off = 0;
             G.w[i][c] = load_stream16(wr + off);
             G.d[i][c] = dr[off >> 5];
         }
@@ -294,17 +300,20 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
     // the Q8 activation that goes to LDS) are issued first, then the first
     // row group's weights: loads retire in order, so the prologue can compute
     // while the weights are in flight.
-    constexpr int BPT = (NCH * 32 + NT - 1) / NT;          // activation blocks per thread
-    constexpr bool EARLY_G = (PRO == PRO_NORM) && BPT == 1;
-    float xf[PRO != PRO_Q8 ? BPT : 1][32];
-    float gf[EARLY_G ? BPT : 1][32];
+    // A float activation is handled in quarter blocks of 8 values: the four
+    // lanes of a quad hold the quarters of one 32-value block.
+    constexpr int QPT = (NCH * 128 + NT - 1) / NT;         // quarter blocks per thread
+    constexpr bool EARLY_G = (PRO == PRO_NORM) && QPT <= 4;
+    const int nqb = 4 * nb;
+    float xf[PRO != PRO_Q8 ? QPT : 1][8];
+    float gf[EARLY_G ? QPT : 1][8];
     if constexpr (PRO != PRO_Q8) {
 #pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-            const int b = threadIdx.x + NT * k;
-            const int bc = b < nb ? b : 0;                // valid address; values dropped below
-            load32(a.x + 32 * bc, xf[k]);
-            if constexpr (EARLY_G) load32((a.gamma ? a.gamma : a.x) + 32 * bc, gf[k]);
+        for (int k = 0; k < QPT; ++k) {
+            const int qb = threadIdx.x + NT * k;
+            const int qc = qb < nqb ? qb : 0;             // valid address; values dropped below
+            load8(a.x + 8 * qc, xf[k]);
+            if constexpr (EARLY_G) load8((a.gamma ? a.gamma : a.x) + 8 * qc, gf[k]);
         }
     } else if constexpr (XL) {
         // codes and scales straight into LDS (global_load_lds: no registers),
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
     }
     __builtin_amdgcn_sched_barrier(0);
     RowGroup<NCH, RPW> A, B;
-    load_group<NCH, RPW, EPI>(a, g, lane, A);            // clamped: waves past the end reload the last group
+    load_group<NCH, RPW, EPI>(a, g, gend, lane, A);      // a wave past the end reads one cache line
 
     XAct<NCH, XL> x;
     x.q_lds = xq_s;
@@ -360,17 +369,17 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < BPT; ++k)
-                if (threadIdx.x + NT * k >= nb)
+            for (int k = 0; k < QPT; ++k)
+                if (threadIdx.x + NT * k >= nqb)
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) xf[k][i] = 0.0f;
+                    for (int i = 0; i < 8; ++i) xf[k][i] = 0.0f;
             float rinv = 1.0f;
             if constexpr (PRO == PRO_NORM) {
                 float ss = 0.0f;
 #pragma unroll
-                for (int k = 0; k < BPT; ++k)
+                for (int k = 0; k < QPT; ++k)
 #pragma unroll
-                    for (int i = 0; i < 32; ++i) ss += xf[k][i] * xf[k][i];
+                    for (int i = 0; i < 8; ++i) ss += xf[k][i] * xf[k][i];
                 ss = wave_sum(ss);
                 if (lane == 0) red[wave] = ss;
                 __syncthreads();
@@ -381,36 +390,39 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             }
             const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
 #pragma unroll
-            for (int k = 0; k < BPT; ++k) {
-                const int b = threadIdx.x + NT * k;
-                if (b < nb) {
-                    float v[32];
+            for (int k = 0; k < QPT; ++k) {
+                // whole quads are in or out together (nqb is a multiple of 4)
+                const int qb = threadIdx.x + NT * k;
+                if (k * NT < nqb) {
+                    float v[8];
                     if constexpr (PRO == PRO_NORM) {
                         if (a.gamma) {
-                            float gm[32];
+                            float gm[8];
                             if constexpr (EARLY_G) {
 #pragma unroll
-                                for (int i = 0; i < 32; ++i) gm[i] = gf[k][i];
+                                for (int i = 0; i < 8; ++i) gm[i] = gf[k][i];
                             } else {
-                                load32(a.gamma + 32 * b, gm);
+                                load8(a.gamma + 8 * (qb < nqb ? qb : 0), gm);
                             }
 #pragma unroll
-                            for (int i = 0; i < 32; ++i) v[i] = (xf[k][i] * rinv) * gm[i];
+                            for (int i = 0; i < 8; ++i) v[i] = (xf[k][i] * rinv) * gm[i];
                         } else {
 #pragma unroll
-                            for (int i = 0; i < 32; ++i) v[i] = xf[k][i] * rinv;
+                            for (int i = 0; i < 8; ++i) v[i] = xf[k][i] * rinv;
                         }
                     } else {
 #pragma unroll
-                        for (int i = 0; i < 32; ++i) v[i] = xf[k][i];
+                        for (int i = 0; i < 8; ++i) v[i] = xf[k][i];
                     }
-                    uint32_t packed[8];
-                    const uint16_t db = quantize_block32_packed(v, packed);
-                    store_codes32(xq_s + 32 * b, packed);
-                    xs_s[b] = db;
-                    if (tap) {
-                        store_codes32(a.tap_q + 32 * b, packed);
-                        a.tap_d[b] = db;
+                    uint32_t packed[2];
+                    const uint16_t db = quantize_quarter8_packed(v, packed);
+                    if (qb < nqb) {
+                        *reinterpret_cast<uint2*>(xq_s + 8 * qb) = make_uint2(packed[0], packed[1]);
+                        if ((qb & 3) == 0) xs_s[qb >> 2] = db;
+                        if (tap) {
+                            *reinterpret_cast<uint2*>(a.tap_q + 8 * qb) = make_uint2(packed[0], packed[1]);
+                            if ((qb & 3) == 0) a.tap_d[qb >> 2] = db;
+                        }
                     }
                 }
             }
@@ -446,14 +458,14 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x, hs);
             break;
         }
-        load_group<NCH, RPW, EPI>(a, g1, lane, B);
+        load_group<NCH, RPW, EPI>(a, g1, gend, lane, B);
         consume_group<NCH, RPW, EPI, XL>(a, g, lane, A, x, hs);
         const int64_t g2 = g1 + gstride;
         if (g2 >= gend) {
             consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x, hs);
             break;
         }
-        load_group<NCH, RPW, EPI>(a, g2, lane, A);
+        load_group<NCH, RPW, EPI>(a, g2, gend, lane, A);
         consume_group<NCH, RPW, EPI, XL>(a, g1, lane, B, x, hs);
         g = g2;
     }
@@ -533,9 +545,9 @@ lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per
     if (a.rows == 0) return LQ_OK;
 #define LQ_PE(P, E) \
     if (pro == P && epi == E) return launch_mv_pe<P, E>(a, s, wg_per_cu, mk);
-    LQ_PE(PRO_Q8, EPI_STORE) LQ_PE(PRO_Q8, EPI_RESID) LQ_PE(PRO_Q8, EPI_SWIGLU)
+    LQ_PE(PRO_Q8, EPI_STORE) LQ_PE(PRO_Q8, EPI_RESID)
     LQ_PE(PRO_QUANT, EPI_STORE) LQ_PE(PRO_QUANT, EPI_RESID)
-    LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU) LQ_PE(PRO_NORM, EPI_SWIGLU_Q8)
+    LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU_Q8)
 #undef LQ_PE
     return fail(LQ_ERR_UNSUPPORTED, "fused matvec: prologue %d / epilogue %d not built", pro, epi);
 }

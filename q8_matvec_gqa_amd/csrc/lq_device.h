@@ -162,6 +162,32 @@ __device__ __forceinline__ uint16_t quantize_block32_packed(const float (&v)[32]
     return f32_to_f16(db);
 }
 
+// The same quantizer with a 32-value block spread over the 4 lanes of a quad
+// (8 values each, lane & 3 = quarter): the block's amax is a quad max, every
+// lane packs its own 8 codes and returns the block's f16 scale.  All four
+// lanes of the quad must be active.
+__device__ __forceinline__ uint16_t quantize_quarter8_packed(const float (&v)[8], uint32_t (&packed)[2]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, dpp<kQuadXor1>(amax));
+    amax = fmaxf(amax, dpp<kQuadXor2>(amax));
+    const float db = amax / 127.0f;
+    const float inv = (db != 0.0f) ? 1.0f / db : 0.0f;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r = roundf(v[4 * w + j] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            word |= ((uint32_t)(int32_t)r & 0xffu) << (8 * j);
+        }
+        packed[w] = word;
+    }
+    return f32_to_f16(db);
+}
+
 __device__ __forceinline__ void store_codes32(int8_t* qs, const uint32_t (&packed)[8]) {
     int4* q4 = reinterpret_cast<int4*>(qs);
     q4[0] = make_int4((int)packed[0], (int)packed[1], (int)packed[2], (int)packed[3]);
@@ -175,6 +201,13 @@ __device__ __forceinline__ void quantize_block32(const float (&v)[32], int8_t* _
     const uint16_t db = quantize_block32_packed(v, packed);
     store_codes32(qs, packed);
     *d = db;
+}
+
+__device__ __forceinline__ void load8(const float* __restrict__ p, float (&v)[8]) {
+    const float4* p4 = reinterpret_cast<const float4*>(p);
+    const float4 a = p4[0], b = p4[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 __device__ __forceinline__ void load32(const float* __restrict__ p, float (&v)[32]) {
