@@ -644,6 +644,53 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
         hM[h] = M;
         hL[h] = L;
     }
+    // A partial result per output element and wave: with 4 position groups
+    // per V step, the wave first sums its groups across lanes (a
+    // reduce-scatter over lane bits 5 and 4), leaving lane (vp, vk) the
+    // values [vp*Q, (vp+1)*Q) of its chunk vk, then writes one [G][hd] slab.
+    constexpr bool RS = VTP == 4 && GM % 4 == 0 && VCPL == 1 && CE == 8;
+    if constexpr (RS) {
+        constexpr int N = GM * CE, Q = N / 4;
+        float hv[N / 2], qv[Q];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float lo = acc[i / CE][0][i % CE], hi = acc[(i + N / 2) / CE][0][(i + N / 2) % CE];
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+            hv[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[i]), __float_as_uint(hv[i + Q]), false,
+                                                            false);
+            qv[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        // qv[i] is element (vp*Q + i) % CE of head (vp*Q + i) / CE, chunk vk
+        static_assert(GM * HDM <= kRedFloats, "combine buffer");
+#pragma unroll
+        for (int i = 0; i < Q; i += 4) {
+            const int h = (vp * Q + i) / CE, e = (vp * Q + i) % CE;
+            *reinterpret_cast<float4*>(&red[wave * kRedFloats + h * HDM + vk * CE + e]) =
+                make_float4(qv[i], qv[i + 1], qv[i + 2], qv[i + 3]);
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < G * hd; idx += NT) {
+            const int h = idx / hd, d = idx - h * hd;
+            float S = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) S += wf[w][h] * red[w * kRedFloats + h * HDM + d];
+            if (a.nsplit == 1) {
+                a.out[(int64_t)(g * G + h) * hd + d] = S / hL[h];
+            } else {
+                const int64_t slot = ((int64_t)g * a.nsplit + split) * G + h;
+                a.part_acc[slot * hd + d] = S;
+                if (d == 0) {
+                    a.part_m[slot] = hM[h];
+                    a.part_l[slot] = hL[h];
+                }
+            }
+        }
+        return;
+    }
     constexpr int per_head = VTP * HDM;
     constexpr int HC = kRedFloats / per_head < GM ? kRedFloats / per_head : GM;
     static_assert(per_head <= kRedFloats, "combine buffer");
