@@ -286,6 +286,40 @@ def measure_moe(name, steps, torch):
             "frac": round(gbs / HBM_PEAK_GBS, 4), "replicas": R, "graph": True}
 
 
+def measure_head(steps, torch):
+    """The output head (final norm, f16 vocab projection, softcap) at the
+    Gemma-4 shape: vocab x hidden f16 weights (1.5 GB, beyond the Infinity
+    Cache) read once per call.  Algorithmic bytes: weights + x + gamma +
+    logits."""
+    import q8_matvec_gqa_amd as lq
+    H = synthetic.HEAD
+    V, D = H["vocab"], H["hidden"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3000)
+    w = (torch.randn(V, D, device="cuda", generator=gen) * 0.02).half().view(torch.int16)
+    x = torch.randn(D, device="cuda", generator=gen)
+    g = 1.0 + 0.1 * torch.randn(D, device="cuda", generator=gen)
+    out = torch.empty(V, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        lq.lq_lm_head_f16(w, V, D, x, 1, g, H["eps"], H["softcap"], out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        lq.lq_lm_head_f16(w, V, D, x, 1, g, H["eps"], H["softcap"], out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = V * D * 2 + D * 8 + V * 4
+    gbs = nbytes / (us * 1e3)
+    log(f"lm_head_v{V}_h{D}: {us:.2f} us/call, {gbs:.1f} GB/s")
+    del w, x, g, out
+    return {"workload": f"lm_head_v{V}_h{D}", "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+            "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "dtype": "f16 weights, f32 math",
+            "softcap": H["softcap"]}
+
+
 def calib_copy(torch, nbytes=1 << 30, reps=3):
     """A plain elementwise copy of known size (reads nbytes, writes nbytes),
     run for the PMC calibration of FETCH_SIZE / WRITE_SIZE."""
@@ -533,6 +567,8 @@ def main():
         for name in synthetic.MOE_WORKLOADS:
             result["moe_block"] = measure_moe(name, max(10, args.steps // 2), torch)
             torch.cuda.empty_cache()
+        result["lm_head"] = measure_head(max(10, args.steps // 2), torch)
+        torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)
     if not args.no_cpu:

@@ -182,6 +182,23 @@ lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t 
                              int64_t start, int64_t len, float scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- output head */
+/* Final norm, vocab projection on f16 weights and logit softcapping
+ * ([CUR] section 3, forward pass steps 4, 5 and 7; section 4,
+ * lm_head_kernel: the projection runs on F16 weights; [TGT] section 3.2:
+ * rms_norm, f16_gemm, softcap; section 3.3: lm_head_f16 [vocab, hidden] f16,
+ * logits [1, vocab] f32), in one launch:
+ *   n = norm ? gamma * x / sqrt(mean(x^2) + eps) : x   (gamma NULL: unit weight)
+ *   logits[r] = sum_c f16(w[r, c]) * n[c]
+ *   if softcap > 0: logits[r] = softcap * tanh(logits[r] / softcap)
+ *   w: device f16 bits [vocab, hidden], row-major, 16-byte aligned.
+ *   x, gamma: device f32 [hidden], 16-byte aligned.  logits: device f32 [vocab].
+ * hidden % 8 == 0 (LQ_ERR_SHAPE) and, in this build, hidden <= 4096
+ * (LQ_ERR_UNSUPPORTED).  vocab == 0 is a no-op.  Float results follow the
+ * library's tolerance (the f16 products are exact; sums are f32). */
+lq_status lq_lm_head_f16(const uint16_t* w, int64_t vocab, int64_t hidden, const float* x, int32_t norm,
+                         const float* gamma, float eps, float softcap, float* logits, void* stream);
+
 /* ---------------------------------------------------------------- MoE */
 /* Router ([TGT] section 3.2: softmax, argsort, gather of the top-k
  * probabilities): per token t, p = softmax(logits[t, :E]); ids[t, s] are

@@ -94,6 +94,7 @@ def _load(path):
     L.orc_silu_mul.argtypes = [_P, _P, _I64, _P]
     L.orc_attention.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64,
                                 _I64, _I64, _D, _P]
+    L.orc_lm_head.argtypes = [_P, _I64, _I64, _P, _I32, _P, _D, _D, _P]
     L.orc_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
     L.orc_moe_block.argtypes = [C.POINTER(OrcMoe), _P, _P, _P, C.POINTER(OrcMoeTrace)]
     L.orc_decode_layer.argtypes = [C.POINTER(OrcLayer), _P, _I64, C.POINTER(OrcLayerTrace)]
@@ -175,6 +176,17 @@ def rmsnorm(x, gamma=None, eps=1e-6):
     y = np.empty_like(x)
     lib().orc_rmsnorm(_ptr(x), x.size, _ptr(g), float(eps), _ptr(y))
     return y
+
+
+def lm_head(w, x, gamma=None, norm=True, eps=1e-6, cap=0.0):
+    """w: uint16 f16 bits [vocab, hidden]; returns f32 logits [vocab]."""
+    w = _c(w, np.uint16)
+    x = _c(x, np.float32)
+    g = None if gamma is None else _c(gamma, np.float32)
+    vocab, hidden = w.shape
+    out = np.empty(vocab, dtype=np.float32)
+    lib().orc_lm_head(_ptr(w), vocab, hidden, _ptr(x), int(bool(norm)), _ptr(g), float(eps), float(cap), _ptr(out))
+    return out
 
 
 def rope_table(max_ctx, hd, theta):

@@ -20,10 +20,12 @@
  *          f64, weighted V) and Supported features (GQA with any ratio).
  *   [TGT]  "Target Inference Architecture: hf2q on mlx-native" -- section 3.2
  *          (decode op list incl. MoE softmax / argsort / gather /
- *          quantized_matmul_id / weighted_sum), section 3.3 (buffer flow:
- *          expert_gate_up_3d [E, 2*I, H], expert_down_3d [E, H, I], KV caches
- *          [1, kv_heads, max_cache, head_dim]), section 6.3 (GGML block
- *          layout, non-zero start offsets).
+ *          quantized_matmul_id / weighted_sum; final rms_norm, f16_gemm
+ *          lm_head and softcap), section 3.3 (buffer flow: expert_gate_up_3d
+ *          [E, 2*I, H], expert_down_3d [E, H, I], KV caches [1, kv_heads,
+ *          max_cache, head_dim], lm_head_f16 [vocab, hidden], logits
+ *          [1, vocab]), section 6.3 (GGML block layout, non-zero start
+ *          offsets).
  * Where the pages leave a step open, the reading taken is stated at the
  * function.
  */
@@ -473,4 +475,35 @@ void orc_decode_layer(const orc_layer* L, float* x, int64_t pos, orc_layer_trace
         memcpy(x, x1, (size_t)H * sizeof(float));
     }
     free(n); free(q8); free(d8); free(qkv); free(att); free(x1); free(tmp);
+}
+
+/* ======================================================================== */
+/* Output head                                                              */
+/* ======================================================================== */
+
+/* Final norm, vocab projection and logit softcapping ([CUR] section 3,
+ * forward pass steps 4, 5 and 7: the final RmsNorm, normed times the
+ * transposed lm_head weight, softcapping as a division, tanh and
+ * multiplication; section 4, lm_head_kernel: the projection runs on F16
+ * weights; [TGT] section 3.2: rms_norm, f16_gemm, softcap; section 3.3:
+ * lm_head_f16 [vocab, hidden] f16, logits [1, vocab] f32).
+ * Readings taken: norm == 0 uses x as given (already normed); the softcap
+ * is cap * tanh(y / cap) and cap <= 0 turns it off. */
+void orc_lm_head(const uint16_t* w, int64_t vocab, int64_t hidden, const float* x, int32_t norm,
+                 const float* gamma, double eps, double cap, float* logits)
+{
+    float* n = (float*)malloc((size_t)hidden * sizeof(float));
+    if (norm) {
+        orc_rmsnorm(x, hidden, gamma, eps, n);
+    } else {
+        for (int64_t c = 0; c < hidden; ++c) n[c] = x[c];
+    }
+    for (int64_t r = 0; r < vocab; ++r) {
+        const uint16_t* row = w + r * hidden;
+        double acc = 0.0;
+        for (int64_t c = 0; c < hidden; ++c) acc += (double)orc_f16_to_f32(row[c]) * (double)n[c];
+        if (cap > 0.0) acc = cap * tanh(acc / cap);
+        logits[r] = (float)acc;
+    }
+    free(n);
 }

@@ -53,6 +53,12 @@ void orc_rope_neox(float* x, int64_t hd, const float* cos_row, const float* sin_
 /* h = silu(g) * u, silu(z) = z / (1 + exp(-z)). */
 void orc_silu_mul(const float* g, const float* u, int64_t n, float* h);
 
+/* ---- output head --------------------------------------------------------- */
+/* n = norm ? rmsnorm(x; gamma, eps) : x;  logits[r] = sum_c f16(w[r,c]) * n[c];
+ * then logits = cap * tanh(logits / cap) when cap > 0. */
+void orc_lm_head(const uint16_t* w, int64_t vocab, int64_t hidden, const float* x, int32_t norm,
+                 const float* gamma, double eps, double cap, float* logits);
+
 /* ---- attention ----------------------------------------------------------- */
 /* For each query head h (kv head g = h / (n_q/n_kv)) attend over cache
  * positions [start, start+len): two-pass softmax in double. out is [n_q, hd]. */

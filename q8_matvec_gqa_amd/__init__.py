@@ -89,6 +89,7 @@ _SIGS = {
     "lq_gqa_decode_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "lq_gqa_decode_attn": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
                                   _F, _P, _P, _SZ, _P]),
+    "lq_lm_head_f16": (_I32, [_P, _I64, _I64, _P, _I32, _P, C.c_float, C.c_float, _P, _P]),
     "lq_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "lq_moe_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lq_moe_q8_matvec_id": (_I32, [_W, _I64, _P, _P, _I32, _P, _I64, _I64, _P, _P, _SZ, _P]),
@@ -225,6 +226,11 @@ def lq_gqa_decode_attn(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_
 
 
 # ---------------------------------------------------------------- MoE
+def lq_lm_head_f16(w, vocab, hidden, x, norm, gamma, eps, softcap, logits, stream=None, check=True):
+    return _check(_lib.lq_lm_head_f16(_ptr(w), vocab, hidden, _ptr(x), int(norm), _ptr(gamma), eps, softcap,
+                                      _ptr(logits), _stream(stream)), check)
+
+
 def lq_moe_route_topk(logits, T, E, k, ids, w, stream=None, check=True):
     return _check(_lib.lq_moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)), check)
 

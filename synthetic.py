@@ -15,6 +15,8 @@ Distributions (the five workloads below):
     the top 16 bits of the float32 draw (a truncation, which is a way of
     drawing bf16 values, not the path's f32->bf16 rounding).
   * MoE router logits: N(0, 1) float32.
+  * output head (f16 weights): N(0, 0.02) cast to IEEE f16; its input is
+    N(0, 1) float32 and its norm weight N(1, 0.1).
 Draw order per layer: x, g_in, W_qkv, g_q, g_k, W_o, g_post, [W_gate_up,
 W_down], K cache, V cache.  MoE: x, logits, W_gate_up (all experts),
 W_down (all experts).
@@ -58,6 +60,15 @@ def q8_weight(rng, rows, cols):
     qs = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
     d = (np.abs(rng.normal(0.0, 0.02, size=(rows, cols // 32))) / 127.0)
     return qs, d.astype(np.float16).view(np.uint16)
+
+
+# The output head of the Gemma-4 shape the pages quote (vocab 262144, hidden 2816).
+HEAD = dict(vocab=262144, hidden=2816, eps=1e-6, softcap=30.0)
+
+
+def f16_weight(rng, rows, cols, std=0.02):
+    """f16 bits [rows, cols]: N(0, std) cast to IEEE binary16 by numpy."""
+    return (rng.standard_normal((rows, cols)) * std).astype(np.float16).view(np.uint16)
 
 
 def activations(rng, *shape):

@@ -77,6 +77,15 @@ def test_matvec_validation():
     assert st(lq.lq_q8_block_dots, w, A, None) == lq.LQ_ERR_NULL
 
 
+def test_lm_head_validation():
+    assert st(lq.lq_lm_head_f16, A, 10, 36, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_lm_head_f16, A, 10, 8192, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_lm_head_f16, None, 10, 64, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_lm_head_f16, A + 4, 10, 64, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_lm_head_f16, A, 10, 64, A, 1, A + 8, 1e-6, 0.0, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_lm_head_f16, None, 0, 64, None, 1, None, 1e-6, 0.0, None) == lq.LQ_OK   # empty: no launch
+
+
 def test_norm_rope_kv_validation():
     assert st(lq.lq_rmsnorm_rope, A, 4, 63, 63, None, 1e-6, None, None, 0, 0) == lq.LQ_ERR_SHAPE
     assert st(lq.lq_rmsnorm_rope, A, 4, 1024, 1024, None, 1e-6, None, None, 0, 0) == lq.LQ_ERR_UNSUPPORTED

@@ -272,6 +272,49 @@ def test_attention_deterministic():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------ output head
+@pytest.mark.parametrize("vocab,hidden,norm,cap", [
+    (1000, 2816, True, 30.0),    # the Gemma-4 head width, ragged row count
+    (777, 64, True, 0.0),        # one chunk per lane, no softcap
+    (513, 520, False, 0.0),      # 65 chunks: the second step has one live lane
+    (300, 4096, True, 5.0),      # widest supported row, a cap that bites
+    (1, 8, True, 30.0),          # a single row of one chunk
+])
+def test_lm_head(vocab, hidden, norm, cap):
+    r = rng(vocab + hidden)
+    w = synthetic.f16_weight(r, vocab, hidden, 0.05)
+    x = synthetic.activations(r, hidden)
+    g = synthetic.gamma(r, hidden)
+    out = empty(vocab, np.float32)
+    lq.lq_lm_head_f16(dev(w), vocab, hidden, dev(x), int(norm), dev(g), 1e-6, cap, out)
+    sync()
+    want = oracle.lm_head(w, x, g, norm=norm, eps=1e-6, cap=cap)
+    assert_close(host(out), want, "lm_head")
+
+
+@pytest.mark.gpu
+def test_lm_head_full_size_sampled():
+    """The 262144 x 2816 head at full size (weights drawn on the GPU), checked
+    on 256 sampled rows against the oracle."""
+    torch = torch_mod()
+    H = synthetic.HEAD
+    V, D = H["vocab"], H["hidden"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    w = (torch.randn(V, D, device="cuda", generator=gen) * 0.02).half().view(torch.int16)
+    x = torch.randn(D, device="cuda", generator=gen)
+    g = 1.0 + 0.1 * torch.randn(D, device="cuda", generator=gen)
+    out = torch.empty(V, dtype=torch.float32, device="cuda")
+    lq.lq_lm_head_f16(w, V, D, x, 1, g, H["eps"], H["softcap"], out)
+    sync()
+    idx = np.sort(np.random.default_rng(5).choice(V, 256, replace=False))
+    rows = w[torch.from_numpy(idx).cuda()].cpu().numpy().view(np.uint16)
+    want = oracle.lm_head(rows, x.cpu().numpy(), g.cpu().numpy(), norm=True, eps=H["eps"], cap=H["softcap"])
+    assert_close(host(out)[idx], want, "lm_head full size")
+    del w
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ MoE pieces
 def test_moe_route():
     r = rng(21)

@@ -22,11 +22,15 @@ ALL_PINS = [
     pins.pin_quantize_golden, pins.pin_quantize_invariants, pins.pin_block_dots, pins.pin_matvec,
     pins.pin_rmsnorm, pins.pin_rope, pins.pin_silu, pins.pin_attention, pins.pin_moe_route,
     pins.pin_moe_block, lambda: pins.pin_layer(0, 1), lambda: pins.pin_layer(1, 1),
-    lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16,
+    lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head,
 ]
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("head_no_norm", "        orc_rmsnorm(x, hidden, gamma, eps, n);", "        for (int64_t c = 0; c < hidden; ++c) n[c] = x[c];"),
+    ("head_transposed", "acc += (double)orc_f16_to_f32(row[c]) * (double)n[c];",
+     "acc += (double)orc_f16_to_f32(w[c * vocab + r < vocab * hidden ? c * vocab + r : 0]) * (double)n[c];"),
+    ("head_cap_no_divide", "if (cap > 0.0) acc = cap * tanh(acc / cap);", "if (cap > 0.0) acc = cap * tanh(acc);"),
     ("round_half_even", "float r = roundf(v);", "float r = rintf(v);"),
     ("scale_over_128", "float db = amax / 127.0f;", "float db = amax / 128.0f;"),
     ("no_clamp_and_trunc", "float r = roundf(v);", "float r = truncf(v);"),

@@ -244,6 +244,48 @@ def pin_silu():
     assert abs(h[3] - 30.0) < 1e-6                                 # silu(z) -> z
 
 
+def pin_lm_head():
+    rng = np.random.default_rng(7)
+    vocab, hidden = 48, 96
+    wf = (rng.standard_normal((vocab, hidden)) * 0.05).astype(np.float16)
+    w = wf.view(np.uint16)
+    x = rng.standard_normal(hidden).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(hidden)).astype(np.float32)
+    # no norm, no cap: numpy's own f16 decode and an f64 product
+    want = wf.astype(np.float64) @ x.astype(np.float64)
+    got = oracle.lm_head(w, x, norm=False)
+    assert np.allclose(got, want, rtol=1e-6, atol=1e-30)
+    # one-hot input: a single term, n_c = gamma_c * s / sqrt(s^2 / hidden + eps)
+    c, sv, eps = 17, 3.0, 1e-6
+    e = np.zeros(hidden, np.float32)
+    e[c] = sv
+    nc = np.float32(gamma[c] * sv / math.sqrt(sv * sv / hidden + eps))
+    got = oracle.lm_head(w, e, gamma, norm=True, eps=eps)
+    assert np.allclose(got, wf[:, c].astype(np.float64) * float(nc), rtol=1e-6)
+    # the norm: a constant input and an all-ones weight give hidden * c / sqrt(c^2 + eps)
+    ones = np.full((3, hidden), 1.0, np.float16).view(np.uint16)
+    got = oracle.lm_head(ones, np.full(hidden, 0.5, np.float32), None, norm=True, eps=eps)
+    assert np.allclose(got, hidden * 0.5 / math.sqrt(0.25 + eps), rtol=1e-6)
+    # softcap: cap * tanh(y / cap); cap * atanh(1/2) maps to cap / 2, large values saturate
+    cap = 30.0
+    big = np.zeros((4, hidden), np.float16)
+    big[0, 0] = cap * math.atanh(0.5) / 1.0
+    big[1, 0] = 2000.0
+    big[2, 0] = -2000.0
+    big[3, 0] = 0.01
+    one = np.zeros(hidden, np.float32)
+    one[0] = 1.0
+    got = oracle.lm_head(big.view(np.uint16), one, norm=False, cap=cap).astype(np.float64)
+    y0 = float(big[0, 0])
+    assert abs(got[0] - cap * math.tanh(y0 / cap)) < 1e-5 and abs(got[0] - cap / 2) < 0.02
+    assert abs(got[1] - cap) < 1e-5 and abs(got[2] + cap) < 1e-5
+    assert abs(got[3] - float(big[3, 0])) < 1e-7
+
+
+def test_lm_head():
+    pin_lm_head()
+
+
 def test_rmsnorm():
     pin_rmsnorm()
 
