@@ -263,6 +263,11 @@ lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const float* logits
                                         -> norm -> gate_up -> SwiGLU -> down + x1 */
 #define LQ_LAYER_ATTN_POSTNORM   1   /* Gemma attention block: ... -> attn -> O -> norm -> + x */
 
+/* FFN gate activation of LQ_LAYER_PRENORM_FFN: h = act(gate) * up. */
+#define LQ_ACT_SILU        0   /* SwiGLU: silu(z) = z / (1 + exp(-z)) */
+#define LQ_ACT_GELU_TANH   1   /* GeGLU, the Gemma MLP gate ([TGT] section 3.2 lists gelu in the
+                                  decode op list): 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+
 typedef struct lq_layer_desc {
     int64_t hidden, n_q, n_kv, head_dim;
     int64_t ffn;              /* used by LQ_LAYER_PRENORM_FFN */
@@ -282,6 +287,10 @@ typedef struct lq_layer_desc {
     const float *g_post;      /* [hidden] post-attention norm */
     void *k_cache, *v_cache;  /* [n_kv, max_ctx, head_dim], contiguous */
     const float *rope_cos, *rope_sin;   /* [max_ctx, head_dim/2] */
+    int32_t ffn_act;          /* LQ_ACT_SILU (0) or LQ_ACT_GELU_TANH */
+    float attn_softcap;       /* > 0: each scaled score s becomes cap * tanh(s / cap) before the softmax
+                                 (the optional Gemma score softcap of [ENG] BLAS-Fused Attention);
+                                 0: none */
 } lq_layer_desc;
 
 /* Optional device buffers for the layer's intermediates; read them after

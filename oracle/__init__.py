@@ -32,6 +32,7 @@ class OrcLayer(C.Structure):
         ("gu_qs", _P), ("gu_d", _P), ("dn_qs", _P), ("dn_d", _P),
         ("g_in", _P), ("g_q", _P), ("g_k", _P), ("g_post", _P),
         ("k_cache", _P), ("v_cache", _P), ("rope_cos", _P), ("rope_sin", _P),
+        ("ffn_act", _I32), ("attn_softcap", _D),
     ]
 
 
@@ -92,8 +93,9 @@ def _load(path):
     L.orc_rope_table.argtypes = [_I64, _I64, _D, _P, _P]
     L.orc_rope_neox.argtypes = [_P, _I64, _P, _P]
     L.orc_silu_mul.argtypes = [_P, _P, _I64, _P]
+    L.orc_gelu_mul.argtypes = [_P, _P, _I64, _P]
     L.orc_attention.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64,
-                                _I64, _I64, _D, _P]
+                                _I64, _I64, _D, _D, _P]
     L.orc_lm_head.argtypes = [_P, _I64, _I64, _P, _I32, _P, _D, _D, _P]
     L.orc_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
     L.orc_moe_block.argtypes = [C.POINTER(OrcMoe), _P, _P, _P, C.POINTER(OrcMoeTrace)]
@@ -210,8 +212,16 @@ def silu_mul(g, u):
     return h
 
 
+def gelu_mul(g, u):
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    h = np.empty_like(g)
+    lib().orc_gelu_mul(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
 def attention(q, n_q, n_kv, hd, k_cache, v_cache, kv_dtype, head_stride, pos_stride,
-              start, length, scale):
+              start, length, scale, softcap=0.0):
     """kv_dtype 0: caches are float32 arrays; 1: caches are uint16 bf16 bit patterns."""
     q = _c(q, np.float32)
     kd = np.float32 if kv_dtype == 0 else np.uint16
@@ -219,7 +229,7 @@ def attention(q, n_q, n_kv, hd, k_cache, v_cache, kv_dtype, head_stride, pos_str
     v_cache = _c(v_cache, kd)
     out = np.empty(n_q * hd, dtype=np.float32)
     lib().orc_attention(_ptr(q), n_q, n_kv, hd, _ptr(k_cache), _ptr(v_cache), kv_dtype,
-                        head_stride, pos_stride, start, length, float(scale), _ptr(out))
+                        head_stride, pos_stride, start, length, float(scale), float(softcap), _ptr(out))
     return out
 
 
@@ -294,7 +304,8 @@ def decode_layer(cfg, w, x, pos, k_cache, v_cache, trace=False):
         g_in=P("g_in", np.float32), g_q=P("g_q", np.float32),
         g_k=P("g_k", np.float32), g_post=P("g_post", np.float32),
         k_cache=_ptr(kc), v_cache=_ptr(vc),
-        rope_cos=P("rope_cos", np.float32), rope_sin=P("rope_sin", np.float32))
+        rope_cos=P("rope_cos", np.float32), rope_sin=P("rope_sin", np.float32),
+        ffn_act=cfg.get("ffn_act", 0), attn_softcap=cfg.get("attn_softcap", 0.0))
     tr = OrcLayerTrace()
     arrays = {}
     if trace:

@@ -241,6 +241,20 @@ void orc_silu_mul(const float* g, const float* u, int64_t n, float* h)
     }
 }
 
+/* GeGLU gate: gelu(gate) * up with the tanh form of GELU ([TGT] section 3.2
+ * lists gelu among the decode ops; the Gemma MLP gates with it).  Reading
+ * taken: the tanh approximation 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715
+ * z^3))), the form Gemma-family MLPs use; the pages name no variant. */
+void orc_gelu_mul(const float* g, const float* u, int64_t n, float* h)
+{
+    const double k = sqrt(2.0 / acos(-1.0));   /* sqrt(2 / pi) */
+    for (int64_t i = 0; i < n; ++i) {
+        double z = (double)g[i];
+        double gz = 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z)));
+        h[i] = (float)(gz * (double)u[i]);
+    }
+}
+
 /* ======================================================================== */
 /* Attention                                                                */
 /* ======================================================================== */
@@ -254,7 +268,7 @@ void orc_silu_mul(const float* g, const float* u, int64_t n, float* h)
 void orc_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd,
                    const void* k_cache, const void* v_cache, int32_t kv_dtype,
                    int64_t head_stride, int64_t pos_stride,
-                   int64_t start, int64_t len, double scale, float* out)
+                   int64_t start, int64_t len, double scale, double softcap, float* out)
 {
     int64_t G = n_q / n_kv;
     double* s = (double*)malloc((size_t)(len > 0 ? len : 1) * sizeof(double));
@@ -269,6 +283,9 @@ void orc_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd,
             for (int64_t d = 0; d < hd; ++d)
                 acc += (double)qh[d] * kv_elem(k_cache, kv_dtype, base + d);
             s[j] = scale * acc;
+            /* optional score softcap ([ENG] BLAS-Fused Attention: the Gemma
+             * tanh(score / cap) * cap after the scaling) */
+            if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);
             if (s[j] > m) m = s[j];
         }
         double z = 0.0;
@@ -441,7 +458,7 @@ void orc_decode_layer(const orc_layer* L, float* x, int64_t pos, orc_layer_trace
     int64_t start = 0;
     if (L->window > 0 && pos - L->window + 1 > 0) start = pos - L->window + 1;
     orc_attention(q, nq, nkv, hd, L->k_cache, L->v_cache, L->kv_dtype, hs, hd,
-                  start, pos - start + 1, L->attn_scale, att);
+                  start, pos - start + 1, L->attn_scale, L->attn_softcap, att);
     if (tr && tr->attn) memcpy(tr->attn, att, (size_t)qd * sizeof(float));
 
     orc_q8_quantize(att, qd, q8, d8);
@@ -465,7 +482,8 @@ void orc_decode_layer(const orc_layer* L, float* x, int64_t pos, orc_layer_trace
         if (tr && tr->nd) memcpy(tr->nd, d8, (size_t)(H / 32) * sizeof(uint16_t));
         orc_q8_matvec(L->gu_qs, L->gu_d, 2 * I, H, q8, d8, NULL, gu);
         if (tr && tr->gu) memcpy(tr->gu, gu, (size_t)(2 * I) * sizeof(float));
-        orc_silu_mul(gu, gu + I, I, tmp);
+        if (L->ffn_act == 1) orc_gelu_mul(gu, gu + I, I, tmp);
+        else orc_silu_mul(gu, gu + I, I, tmp);
         orc_q8_quantize(tmp, I, q8, d8);
         if (tr && tr->hq) memcpy(tr->hq, q8, (size_t)I);
         if (tr && tr->hd) memcpy(tr->hd, d8, (size_t)(I / 32) * sizeof(uint16_t));

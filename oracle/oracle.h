@@ -52,6 +52,8 @@ void orc_rope_table(int64_t max_ctx, int64_t hd, double theta, float* cos_t, flo
 void orc_rope_neox(float* x, int64_t hd, const float* cos_row, const float* sin_row);
 /* h = silu(g) * u, silu(z) = z / (1 + exp(-z)). */
 void orc_silu_mul(const float* g, const float* u, int64_t n, float* h);
+/* h = gelu(g) * u, gelu(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))). */
+void orc_gelu_mul(const float* g, const float* u, int64_t n, float* h);
 
 /* ---- output head --------------------------------------------------------- */
 /* n = norm ? rmsnorm(x; gamma, eps) : x;  logits[r] = sum_c f16(w[r,c]) * n[c];
@@ -61,11 +63,12 @@ void orc_lm_head(const uint16_t* w, int64_t vocab, int64_t hidden, const float* 
 
 /* ---- attention ----------------------------------------------------------- */
 /* For each query head h (kv head g = h / (n_q/n_kv)) attend over cache
- * positions [start, start+len): two-pass softmax in double. out is [n_q, hd]. */
+ * positions [start, start+len): two-pass softmax in double, scores optionally
+ * soft-capped (softcap > 0: s -> softcap * tanh(s / softcap)). out is [n_q, hd]. */
 void orc_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd,
                    const void* k_cache, const void* v_cache, int32_t kv_dtype,
                    int64_t head_stride, int64_t pos_stride,
-                   int64_t start, int64_t len, double scale, float* out);
+                   int64_t start, int64_t len, double scale, double softcap, float* out);
 
 /* ---- MoE ----------------------------------------------------------------- */
 /* Per token: softmax over E logits, the k largest (ties: lower expert id),
@@ -106,6 +109,8 @@ typedef struct orc_layer {
     const float *g_in, *g_q, *g_k, *g_post;      /* norm weights */
     void *k_cache, *v_cache;                     /* [n_kv, max_ctx, hd], updated at pos */
     const float *rope_cos, *rope_sin;            /* [max_ctx, hd/2] */
+    int32_t ffn_act;                             /* 0 silu(gate) * up; 1 gelu_tanh(gate) * up */
+    double attn_softcap;                         /* > 0: scores become cap * tanh(s / cap) */
 } orc_layer;
 
 typedef struct orc_layer_trace {    /* every pointer may be NULL */

@@ -29,6 +29,7 @@ _lib = C.CDLL(LIB_PATH)
 LQ_OK, LQ_ERR_NULL, LQ_ERR_SHAPE, LQ_ERR_ALIGN, LQ_ERR_WORKSPACE, LQ_ERR_HIP, LQ_ERR_UNSUPPORTED = range(7)
 LQ_KV_F32, LQ_KV_BF16 = 0, 1
 LQ_LAYER_PRENORM_FFN, LQ_LAYER_ATTN_POSTNORM = 0, 1
+LQ_ACT_SILU, LQ_ACT_GELU_TANH = 0, 1
 
 _P = C.c_void_p
 _I64 = C.c_int64
@@ -65,6 +66,7 @@ class lq_layer_desc(C.Structure):
         ("w_down", lq_q8_weight),
         ("g_in", _P), ("g_q", _P), ("g_k", _P), ("g_post", _P),
         ("k_cache", _P), ("v_cache", _P), ("rope_cos", _P), ("rope_sin", _P),
+        ("ffn_act", _I32), ("attn_softcap", _F),
     ]
 
 

@@ -84,6 +84,7 @@ struct AttnArgs {
     int hd, G, n_q, n_kv, nsplit, tiles_per_split;
     int fused, qk_norm, v_unit_norm;
     float qscale;            // scale * log2(e)
+    float cap2;              // score softcap times log2(e) (scores are kept in the log2 domain); 0: none
     float eps;
 };
 
@@ -272,6 +273,14 @@ __device__ __forceinline__ void head_finish_v(const HeadInV<EPL>& in, const Head
         }
     }
     store_run<EPL>(dst + lane * EPL, y);
+}
+
+// Optional score softcap ("Inference Engine" (larql), BLAS-Fused Attention:
+// the Gemma cap * tanh(score / cap) after the scaling), applied in the log2
+// domain the kernel keeps its scores in: with c2 = cap * log2(e),
+// c2 * tanh(u / c2) is log2(e) times the capped natural score.
+__device__ __forceinline__ float soft_cap(float u, float c2) {
+    return c2 > 0.0f ? c2 * tanhf(u / c2) : u;
 }
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
@@ -516,13 +525,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
             if constexpr (NP == 64 && GM == 8) {
                 // one position per step: reduce-scatter, lane group h holds head h
                 const float sum = wave_sum8_scatter(part);
-                if ((lane & 7) == 0) sc[wave][st][(lane >> 3) & 7] = sum;
+                if ((lane & 7) == 0) sc[wave][st][(lane >> 3) & 7] = soft_cap(sum, a.cap2);
             } else {
 #pragma unroll
                 for (int h = 0; h < GM; ++h) part[h] = group_sum<NP>(part[h]);
                 if (kk == 0) {
 #pragma unroll
-                    for (int h = 0; h < GM; ++h) sc[wave][st * TP + kp][h] = part[h];
+                    for (int h = 0; h < GM; ++h) sc[wave][st * TP + kp][h] = soft_cap(part[h], a.cap2);
                 }
             }
         }
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
             for (int h = 0; h < GM; ++h) sn[h] = wave_sum(sn[h]);
             if (lane == 0) {
 #pragma unroll
-                for (int h = 0; h < GM; ++h) sc[wave][pt_new][h] = sn[h];
+                for (int h = 0; h < GM; ++h) sc[wave][pt_new][h] = soft_cap(sn[h], a.cap2);
             }
         }
         wave_lds_sync();
@@ -980,9 +989,10 @@ lq_status launch_attention_fused(const float* qkv, int64_t n_q, int64_t n_kv, in
                                  const float* g_k, int32_t qk_norm, int32_t v_unit_norm, float eps,
                                  const float* rope_cos_row, const float* rope_sin_row, void* kc, void* vc,
                                  int32_t kv_dtype, int64_t head_stride, int64_t pos_stride, int64_t start,
-                                 int64_t len, float scale, float* out, void* ws, hipStream_t s,
+                                 int64_t len, float scale, float softcap, float* out, void* ws, hipStream_t s,
                                  LaunchMarks* marks) {
     AttnArgs a{};
+    a.cap2 = softcap > 0.0f ? softcap * kLog2e : 0.0f;
     a.q = qkv; a.kc = kc; a.kc_w = kc; a.vc_w = vc; a.out = out;
     a.g_q = g_q; a.g_k = g_k; a.rope_cos = rope_cos_row; a.rope_sin = rope_sin_row;
     a.head_stride = head_stride; a.pos_stride = pos_stride; a.start = start; a.len = len;

@@ -9,6 +9,7 @@
 // mlx-native", section 3.2 and design principle P2: one commit per forward
 // pass).  Every intermediate lives in the caller's workspace (INV-8: no
 // allocation in the forward pass), or in a caller tap buffer.
+#include <math.h>
 #include "lq_device.h"
 #include "lq_internal.h"
 
@@ -75,6 +76,10 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
         return fail(LQ_ERR_SHAPE, "%s: pos=%lld max_ctx=%lld window=%lld", fn, (long long)pos,
                     (long long)L->max_ctx, (long long)L->window);
     if (!(L->eps >= 0.0f)) return fail(LQ_ERR_SHAPE, "%s: eps must be >= 0", fn);
+    if (L->ffn_act != LQ_ACT_SILU && L->ffn_act != LQ_ACT_GELU_TANH)
+        return fail(LQ_ERR_SHAPE, "%s: ffn_act %d", fn, L->ffn_act);
+    if (!(L->attn_softcap >= 0.0f) || L->attn_softcap == INFINITY)
+        return fail(LQ_ERR_SHAPE, "%s: attn_softcap must be finite and >= 0", fn);
     if (!weight_is(L->w_qkv, nq * hd + 2 * nkv * hd, H) || !weight_is(L->w_o, H, nq * hd))
         return fail(LQ_ERR_SHAPE, "%s: w_qkv must be [%lld, %lld] and w_o [%lld, %lld]", fn,
                     (long long)(nq * hd + 2 * nkv * hd), (long long)H, (long long)H, (long long)(nq * hd));
@@ -199,7 +204,8 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
     const int64_t half = hd / 2;
     if ((st = launch_attention_fused(b.qkv, nq, nkv, hd, L->g_q, L->g_k, L->qk_norm, L->v_unit_norm, L->eps,
                                      L->rope_cos + pos * half, L->rope_sin + pos * half, L->k_cache, L->v_cache,
-                                     L->kv_dtype, head_stride, pos_stride, start, len, L->attn_scale, b.attn,
+                                     L->kv_dtype, head_stride, pos_stride, start, len, L->attn_scale,
+                                     L->attn_softcap, b.attn,
                                      b.attn_ws, s, &mk)) != LQ_OK)
         return st;
     // O projection, quantizing the attention output in-kernel
@@ -218,7 +224,7 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
     const int64_t I = L->ffn;
     m = MvArgs{};
     m.wq = L->w_gate_up.qs; m.wd = L->w_gate_up.d; m.rows = (int)I; m.cols = (int)H;
-    m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = T.h; m.yq = b.hq; m.yd = b.hd;
+    m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = T.h; m.yq = b.hq; m.yd = b.hd; m.act = L->ffn_act;
     m.tap_q = T.nq; m.tap_d = T.nd;
     if ((st = launch_mv(m, PRO_NORM, EPI_SWIGLU_Q8, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
     // down projection on the Q8_0 h, plus the residual

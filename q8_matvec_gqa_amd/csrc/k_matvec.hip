@@ -228,6 +228,13 @@ struct XAct {
     }
 };
 
+// SwiGLU gate silu(z) = z / (1 + exp(-z)), or the GeGLU gate with the tanh
+// form of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float gate_act(float z, int act) {
+    if (act == LQ_ACT_GELU_TANH) return 0.5f * z * (1.0f + tanhf(0.7978845608028654f * (z + 0.044715f * z * z * z)));
+    return z / (1.0f + expf(-z));
+}
+
 template <int NCH, int RPW, int EPI, bool XL>
 __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int lane, const RowGroup<NCH, RPW>& G,
                                               const XAct<NCH, XL>& x, float* hs) {
@@ -254,7 +261,7 @@ __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int la
             const int64_t r = g * (RPW / 2) + j;
             if (r < a.rows) {
                 const float gt = acc[2 * j], up = acc[2 * j + 1];
-                const float h = (gt / (1.0f + expf(-gt))) * up;
+                const float h = gate_act(gt, a.act) * up;
                 if constexpr (EPI == EPI_SWIGLU_Q8) {
                     hs[r & 31] = h;               // the workgroup's 32-value block, quantized at the end
                     if (a.y) a.y[r] = h;

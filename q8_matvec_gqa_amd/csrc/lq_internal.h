@@ -93,6 +93,7 @@ struct MvArgs {
     uint16_t* yd;
     int8_t* tap_q;       // optional: workgroup 0 writes the Q8_0 input it built
     uint16_t* tap_d;
+    int act;             // EPI_SWIGLU*: gate activation, LQ_ACT_SILU or LQ_ACT_GELU_TANH
 };
 lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per_cu,
                     LaunchMarks* mk = nullptr);
@@ -129,7 +130,7 @@ lq_status launch_attention_fused(const float* qkv, int64_t n_q, int64_t n_kv, in
                                  const float* g_k, int32_t qk_norm, int32_t v_unit_norm, float eps,
                                  const float* rope_cos_row, const float* rope_sin_row, void* kc, void* vc,
                                  int32_t kv_dtype, int64_t head_stride, int64_t pos_stride, int64_t start,
-                                 int64_t len, float scale, float* out, void* ws, hipStream_t s,
+                                 int64_t len, float scale, float softcap, float* out, void* ws, hipStream_t s,
                                  LaunchMarks* marks = nullptr);
 
 // ---- launchers (k_moe.hip) ----------------------------------------------------

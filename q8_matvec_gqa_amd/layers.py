@@ -41,7 +41,8 @@ class DeviceLayer:
             g_in=t["g_in"].data_ptr(), g_q=t["g_q"].data_ptr(), g_k=t["g_k"].data_ptr(),
             g_post=t["g_post"].data_ptr(), k_cache=t["k_cache"].data_ptr(),
             v_cache=t["v_cache"].data_ptr(), rope_cos=t["rope_cos"].data_ptr(),
-            rope_sin=t["rope_sin"].data_ptr())
+            rope_sin=t["rope_sin"].data_ptr(), ffn_act=cfg.get("ffn_act", 0),
+            attn_softcap=cfg.get("attn_softcap", 0.0))
         self.ws_bytes = lq_decode_layer_workspace_size(self.desc)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
 

@@ -30,12 +30,28 @@ def oracle_cfg(cfg):
 
 @pytest.mark.parametrize("name", LAYERS)
 def test_layer_teacher_forced(name):
+    run_teacher_forced(name)
+
+
+# the Gemma fidelity options: GeGLU gate (tanh GELU) and the attention score softcap
+@pytest.mark.parametrize("name,act,cap", [
+    ("tiny_h1024", 1, 0.0),
+    ("qwen3_4b_like_h2560", 1, 1.5),
+    ("gemma4_sliding_h2816", 0, 1.5),
+    ("gemma4_global_h2816", 0, 3.0),
+])
+def test_layer_variants_teacher_forced(name, act, cap):
+    run_teacher_forced(name, act, cap)
+
+
+def run_teacher_forced(name, act=0, cap=0.0):
     torch = torch_mod()
     cfg, w = synthetic.layer_inputs(name, seed=0)
+    cfg = dict(cfg, ffn_act=act, attn_softcap=cap)
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
     pos, kind = cfg["pos"], cfg["kind"]
     qd, kvd = nq * hd, nkv * hd
-    print(f"[layer] {name} pos={pos}", flush=True)
+    print(f"[layer] {name} pos={pos} act={act} softcap={cap}", flush=True)
     L = DeviceLayer(cfg, w, torch)
     taps, bufs = L.make_taps()
     x = dev(w["x"])
@@ -79,7 +95,7 @@ def test_layer_teacher_forced(name):
     # 4. attention from the oracle's q (of the GPU's projection) and the GPU's caches
     start = max(0, pos - cfg["window"] + 1) if cfg["window"] else 0
     att = oracle.attention(post[:qd], nq, nkv, hd, kc_gpu, vc_gpu, cfg["kv_dtype"],
-                           cfg["max_ctx"] * hd, hd, start, pos - start + 1, cfg["attn_scale"])
+                           cfg["max_ctx"] * hd, hd, start, pos - start + 1, cfg["attn_scale"], softcap=cap)
     assert_close(T["attn"], att, "attention")
     # 5. quantize of the attention output: identical float input -> bit-exact
     aq, ad = oracle.q8_quantize(T["attn"])
@@ -89,7 +105,8 @@ def test_layer_teacher_forced(name):
         assert_close(T["x1"], oracle.q8_matvec(w["o_qs"], w["o_d"], T["aq"], T["ad"], residual=w["x"]), "x1")
         flips += assert_q8_near(T["nq"], T["nd"], oracle.rmsnorm(T["x1"], w["g_post"], eps), "post norm Q8")
         gu = oracle.q8_matvec(w["gu_qs"], w["gu_d"], T["nq"], T["nd"])
-        assert_close(T["h"], oracle.silu_mul(gu[:I], gu[I:]), "silu(gate) * up")
+        gate = oracle.gelu_mul if act == 1 else oracle.silu_mul
+        assert_close(T["h"], gate(gu[:I], gu[I:]), "act(gate) * up")
         hq, hd_ = oracle.q8_quantize(T["h"])                 # identical float input -> bit-exact
         assert np.array_equal(T["hq"], hq) and np.array_equal(T["hd"], hd_)
         assert_close(out_gpu, oracle.q8_matvec(w["dn_qs"], w["dn_d"], T["hq"], T["hd"], residual=T["x1"]),

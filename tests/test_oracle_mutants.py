@@ -22,11 +22,17 @@ ALL_PINS = [
     pins.pin_quantize_golden, pins.pin_quantize_invariants, pins.pin_block_dots, pins.pin_matvec,
     pins.pin_rmsnorm, pins.pin_rope, pins.pin_silu, pins.pin_attention, pins.pin_moe_route,
     pins.pin_moe_block, lambda: pins.pin_layer(0, 1), lambda: pins.pin_layer(1, 1),
-    lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head,
+    lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head, pins.pin_gelu,
+    pins.pin_attention_softcap,
 ]
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("gelu_coefficient", "0.044715 * z * z * z", "0.44715 * z * z * z"),
+    ("gelu_no_half", "double gz = 0.5 * z *", "double gz = 1.0 * z *"),
+    ("attn_cap_missing", "if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);", "(void)softcap;"),
+    ("attn_cap_no_divide", "if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);",
+     "if (softcap > 0.0) s[j] = softcap * tanh(s[j]);"),
     ("head_no_norm", "        orc_rmsnorm(x, hidden, gamma, eps, n);", "        for (int64_t c = 0; c < hidden; ++c) n[c] = x[c];"),
     ("head_transposed", "acc += (double)orc_f16_to_f32(row[c]) * (double)n[c];",
      "acc += (double)orc_f16_to_f32(w[c * vocab + r < vocab * hidden ? c * vocab + r : 0]) * (double)n[c];"),

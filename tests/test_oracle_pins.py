@@ -286,6 +286,55 @@ def test_lm_head():
     pin_lm_head()
 
 
+def pin_gelu():
+    z = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.5, -2.5, 10.0, -10.0, 0.03], np.float32)
+    one = np.ones_like(z)
+    h = oracle.gelu_mul(z, one).astype(np.float64)
+    hn = oracle.gelu_mul(-z, one).astype(np.float64)
+    assert h[0] == 0.0
+    # the tanh form is odd around z/2: gelu(z) - gelu(-z) = z exactly
+    assert np.allclose(h - hn, z.astype(np.float64), rtol=1e-6, atol=1e-7)
+    # and it approximates z * Phi(z) (the normal CDF) to well under 1e-3
+    exact = z.astype(np.float64) * scipy.special.ndtr(z.astype(np.float64))
+    assert np.max(np.abs(h - exact)) < 1e-3
+    assert abs(h[7] - 10.0) < 1e-6 and abs(h[8]) < 1e-6
+    # the up factor multiplies
+    u = np.full_like(z, -3.0)
+    assert np.allclose(oracle.gelu_mul(z, u), -3.0 * h, rtol=1e-6)
+
+
+def pin_attention_softcap():
+    # one head, two positions whose scaled scores (100 and 200) both saturate a
+    # cap of 2: the capped scores are equal, so the output is the mean of V
+    hd = 4
+    q = np.array([1.0, 0.0, 0.0, 0.0], np.float32)
+    k = np.zeros((1, 2, hd), np.float32)
+    k[0, 0, 0], k[0, 1, 0] = 100.0, 200.0
+    v = np.zeros((1, 2, hd), np.float32)
+    v[0, 0] = [1.0, 2.0, 3.0, 4.0]
+    v[0, 1] = [5.0, -6.0, 7.0, 0.5]
+    capped = oracle.attention(q, 1, 1, hd, k, v, 0, 2 * hd, hd, 0, 2, 1.0, softcap=2.0)
+    assert np.allclose(capped, (v[0, 0] + v[0, 1]) / 2, rtol=1e-6)
+    plain = oracle.attention(q, 1, 1, hd, k, v, 0, 2 * hd, hd, 0, 2, 1.0)
+    assert np.allclose(plain, v[0, 1], rtol=1e-6)
+    # a very large cap changes nothing at ordinary scores
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal(2 * 16).astype(np.float32)
+    kc = rng.standard_normal((1, 40, 16)).astype(np.float32)
+    vc = rng.standard_normal((1, 40, 16)).astype(np.float32)
+    a = oracle.attention(q, 2, 1, 16, kc, vc, 0, 40 * 16, 16, 0, 40, 0.25)
+    b = oracle.attention(q, 2, 1, 16, kc, vc, 0, 40 * 16, 16, 0, 40, 0.25, softcap=1e12)
+    assert np.allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+def test_gelu():
+    pin_gelu()
+
+
+def test_attention_softcap():
+    pin_attention_softcap()
+
+
 def test_rmsnorm():
     pin_rmsnorm()
 
