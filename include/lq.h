@@ -241,6 +241,8 @@ typedef struct lq_moe_desc {
     int64_t hidden, ffn, n_experts, top_k;
     lq_q8_weight w_gate_up;   /* one expert: rows 2*ffn (gate rows, then up rows), cols hidden */
     lq_q8_weight w_down;      /* one expert: rows hidden, cols ffn */
+    const float* expert_scale;  /* device f32 [n_experts], or NULL (all 1): per-expert output scale
+                                   ([TGT] section 3.2: gather of per_expert_scale, weight * scale) */
 } lq_moe_desc;
 
 /* Optional device buffers; a non-NULL tap replaces the workspace buffer for

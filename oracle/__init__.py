@@ -44,7 +44,7 @@ class OrcLayerTrace(C.Structure):
 class OrcMoe(C.Structure):
     _fields_ = [
         ("hidden", _I64), ("ffn", _I64), ("n_experts", _I64), ("top_k", _I64), ("tokens", _I64),
-        ("gu_qs", _P), ("gu_d", _P), ("dn_qs", _P), ("dn_d", _P),
+        ("gu_qs", _P), ("gu_d", _P), ("dn_qs", _P), ("dn_d", _P), ("expert_scale", _P),
     ]
 
 
@@ -243,13 +243,15 @@ def moe_route(logits, k):
     return ids, w
 
 
-def moe_block(hidden, ffn, n_experts, top_k, gu_qs, gu_d, dn_qs, dn_d, x, logits, trace=False):
+def moe_block(hidden, ffn, n_experts, top_k, gu_qs, gu_d, dn_qs, dn_d, x, logits, trace=False,
+              expert_scale=None):
     x = _c(x, np.float32)
     logits = _c(logits, np.float32)
     T = x.shape[0]
     gu_qs = _c(gu_qs, np.int8); gu_d = _c(gu_d, np.uint16)
     dn_qs = _c(dn_qs, np.int8); dn_d = _c(dn_d, np.uint16)
-    m = OrcMoe(hidden, ffn, n_experts, top_k, T, _ptr(gu_qs), _ptr(gu_d), _ptr(dn_qs), _ptr(dn_d))
+    es = None if expert_scale is None else _c(expert_scale, np.float32)
+    m = OrcMoe(hidden, ffn, n_experts, top_k, T, _ptr(gu_qs), _ptr(gu_d), _ptr(dn_qs), _ptr(dn_d), _ptr(es))
     out = np.empty((T, hidden), dtype=np.float32)
     tr = OrcMoeTrace()
     arrays = {}

@@ -378,7 +378,11 @@ void orc_moe_block(const orc_moe* m, const float* x, const float* logits, float*
             if (tr && tr->hq) memcpy(tr->hq + slot * I, hq, (size_t)I);
             if (tr && tr->hd) memcpy(tr->hd + slot * (I / 32), hd, (size_t)(I / 32) * sizeof(uint16_t));
             if (tr && tr->y2) memcpy(tr->y2 + slot * H, y2, (size_t)H * sizeof(float));
-            for (int64_t j = 0; j < H; ++j) acc[j] += (double)w[slot] * (double)y2[j];
+            /* per-expert output scale ([TGT] section 3.2: gather of
+             * per_expert_scale, then weight * scale) */
+            double ws = (double)w[slot];
+            if (m->expert_scale) ws *= (double)m->expert_scale[e];
+            for (int64_t j = 0; j < H; ++j) acc[j] += ws * (double)y2[j];
         }
         for (int64_t j = 0; j < H; ++j) out[t * H + j] = (float)acc[j];
     }

@@ -80,6 +80,7 @@ typedef struct orc_moe {
     int64_t hidden, ffn, n_experts, top_k, tokens;
     const int8_t* gu_qs;  const uint16_t* gu_d;    /* [E, 2*ffn, hidden] */
     const int8_t* dn_qs;  const uint16_t* dn_d;    /* [E, hidden, ffn]   */
+    const float* expert_scale;                     /* [E] or NULL (all 1) */
 } orc_moe;
 
 typedef struct orc_moe_trace {       /* every pointer may be NULL */

@@ -50,7 +50,7 @@ class lq_q8_weight(C.Structure):
 
 class lq_moe_desc(C.Structure):
     _fields_ = [("hidden", _I64), ("ffn", _I64), ("n_experts", _I64), ("top_k", _I64),
-                ("w_gate_up", lq_q8_weight), ("w_down", lq_q8_weight)]
+                ("w_gate_up", lq_q8_weight), ("w_down", lq_q8_weight), ("expert_scale", _P)]
 
 
 class lq_moe_taps(C.Structure):

@@ -415,14 +415,26 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_moe_gu_swiglu_q8(const int8_t
     }
 }
 
+// out[t] = sum_s w[t,s] * scale[ids[t,s]] * y[t,s] in slot order; without a
+// scale table (escale NULL) every scale is 1, and ids past the table (the
+// skipped invalid ids, whose y rows are zero) also count 1.
 __global__ __launch_bounds__(256) void k_moe_weighted_sum(const float* __restrict__ y,
                                                           const float* __restrict__ w, int64_t T,
-                                                          int k, int64_t rows, float* __restrict__ out) {
+                                                          int k, int64_t rows, const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ escale, int E,
+                                                          float* __restrict__ out) {
     const int64_t n = T * rows;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         const int64_t t = i / rows, r = i - t * rows;
         float acc = 0.0f;
-        for (int s = 0; s < k; ++s) acc = fmaf(w[t * k + s], y[(t * k + s) * rows + r], acc);
+        for (int s = 0; s < k; ++s) {
+            float ws = w[t * k + s];
+            if (escale) {
+                const int e = ids[t * k + s];
+                if (e >= 0 && e < E) ws *= escale[e];
+            }
+            acc = fmaf(ws, y[(t * k + s) * rows + r], acc);
+        }
         out[i] = acc;
     }
 }
@@ -507,12 +519,13 @@ lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t row
 }
 
 lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
-                                  float* out, hipStream_t s) {
+                                  const int32_t* ids, const float* escale, int64_t E, float* out, hipStream_t s) {
     const int64_t n = T * rows;
     if (n == 0) return LQ_OK;
     int64_t grid = (n + 255) / 256;
     if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL(k_moe_weighted_sum, dim3((unsigned)grid), dim3(256), 0, s, y, w, T, (int)k, rows, out);
+    hipLaunchKernelGGL(k_moe_weighted_sum, dim3((unsigned)grid), dim3(256), 0, s, y, w, T, (int)k, rows, ids, escale,
+                       (int)E, out);
     return check_launch("moe_weighted_sum");
 }
 
@@ -579,7 +592,7 @@ extern "C" lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t
     if (!y || !w || !out) return fail(LQ_ERR_NULL, "lq_moe_weighted_sum: NULL pointer");
     if (!aligned(y, 4) || !aligned(w, 4) || !aligned(out, 4))
         return fail(LQ_ERR_ALIGN, "lq_moe_weighted_sum: misaligned pointer");
-    return launch_moe_weighted_sum(y, w, T, k, rows, out, as_stream(stream));
+    return launch_moe_weighted_sum(y, w, T, k, rows, nullptr, nullptr, 0, out, as_stream(stream));
 }
 
 // ---- whole block ---------------------------------------------------------------
@@ -646,7 +659,7 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
     if (T == 0) return LQ_OK;
     if (!x || !logits || !out) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
-    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(out, 4))
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(out, 4) || !aligned(m->expert_scale, 4))
         return fail(LQ_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
     const size_t need = moe_layout(m, T, nullptr, nullptr).total;
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
@@ -671,5 +684,5 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     }
     if ((st = launch_id_gathered(m->w_down.qs, m->w_down.d, H, I, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK)
         return st;
-    return launch_moe_weighted_sum(b.y2, b.w, T, k, H, out, s);
+    return launch_moe_weighted_sum(b.y2, b.w, T, k, H, b.ids, m->expert_scale, m->n_experts, out, s);
 }

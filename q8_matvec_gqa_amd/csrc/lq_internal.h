@@ -141,7 +141,8 @@ lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t row
                                int64_t n_experts, const int8_t* xq, const uint16_t* xd,
                                int32_t x_per_slot, const int32_t* ids, int64_t T, int64_t k,
                                float* y, void* ws, hipStream_t s);
-lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k,
-                                  int64_t rows, float* out, hipStream_t s);
+// out[t] = sum_s w[t,s] * escale[ids[t,s]] * y[t,s] (escale NULL: scale 1; ids, E only read with escale)
+lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
+                                  const int32_t* ids, const float* escale, int64_t E, float* out, hipStream_t s);
 
 }  // namespace lq

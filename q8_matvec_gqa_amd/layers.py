@@ -68,11 +68,12 @@ class DeviceMoe:
     def __init__(self, cfg, w, torch):
         self.cfg, self.torch = cfg, torch
         H, I, E, k = cfg["hidden"], cfg["ffn"], cfg["n_experts"], cfg["top_k"]
-        self.t = {n: _dev(w[n], torch) for n in ("gu_qs", "gu_d", "dn_qs", "dn_d")}
+        self.t = {n: _dev(w[n], torch) for n in ("gu_qs", "gu_d", "dn_qs", "dn_d", "expert_scale") if n in w}
         t = self.t
         self.desc = lq_moe_desc(H, I, E, k,
                                    lq_q8_weight(t["gu_qs"].data_ptr(), t["gu_d"].data_ptr(), 2 * I, H),
-                                   lq_q8_weight(t["dn_qs"].data_ptr(), t["dn_d"].data_ptr(), H, I))
+                                   lq_q8_weight(t["dn_qs"].data_ptr(), t["dn_d"].data_ptr(), H, I),
+                                   expert_scale=None if t.get("expert_scale") is None else t["expert_scale"].data_ptr())
         self.ws_bytes = lq_moe_block_workspace_size(self.desc, cfg["tokens"])
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
 

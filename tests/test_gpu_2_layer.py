@@ -194,12 +194,16 @@ def test_layer_positions_sliding(pos):
     assert_close(host(bufs["attn"]), att, f"attention at pos {pos}")
 
 
-def test_moe_block_teacher_forced():
+@pytest.mark.parametrize("scaled", [False, True])
+def test_moe_block_teacher_forced(scaled):
     torch = torch_mod()
     name = list(synthetic.MOE_WORKLOADS)[0]
     cfg, w = synthetic.moe_inputs(name, seed=0)
     T_, H, I, E, k = cfg["tokens"], cfg["hidden"], cfg["ffn"], cfg["n_experts"], cfg["top_k"]
-    print(f"[moe] {name}", flush=True)
+    escale = synthetic.gamma(np.random.default_rng(77), E) if scaled else None
+    if scaled:
+        w = dict(w, expert_scale=escale)
+    print(f"[moe] {name} per-expert scale={scaled}", flush=True)
     M = DeviceMoe(cfg, w, torch)
     taps, bufs = M.make_taps()
     x, logits = dev(w["x"]), dev(w["logits"])
@@ -225,10 +229,14 @@ def test_moe_block_teacher_forced():
             assert_close(y1[t, s], oracle.q8_matvec(w["gu_qs"][e], w["gu_d"][e], xq[t], xd[t]), f"y1 {t},{s}")
             flips += assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1[t, s, :I], y1[t, s, I:]), f"h {t},{s}")
             assert_close(y2[t, s], oracle.q8_matvec(w["dn_qs"][e], w["dn_d"][e], hq[t, s], hd[t, s]), f"y2 {t},{s}")
-    want = np.einsum("ts,tsh->th", G["w"].reshape(T_, k).astype(np.float64), y2.astype(np.float64))
+    ws = G["w"].reshape(T_, k).astype(np.float64)
+    if scaled:
+        ws = ws * escale[ids].astype(np.float64)
+    want = np.einsum("ts,tsh->th", ws, y2.astype(np.float64))
     got = host(out).reshape(T_, H)
     assert_close(got, want, "weighted sum")
-    ref = oracle.moe_block(H, I, E, k, w["gu_qs"], w["gu_d"], w["dn_qs"], w["dn_d"], w["x"], w["logits"])
+    ref = oracle.moe_block(H, I, E, k, w["gu_qs"], w["gu_d"], w["dn_qs"], w["dn_d"], w["x"], w["logits"],
+                           expert_scale=escale)
     touched = len(np.unique(ids))
     if flips == 0:
         err = assert_close(got, ref, "free-running MoE block")

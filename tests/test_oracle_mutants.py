@@ -28,6 +28,9 @@ ALL_PINS = [
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("moe_scale_ignored", "if (m->expert_scale) ws *= (double)m->expert_scale[e];", "(void)e;"),
+    ("moe_scale_by_slot", "if (m->expert_scale) ws *= (double)m->expert_scale[e];",
+     "if (m->expert_scale) ws *= (double)m->expert_scale[s];"),
     ("gelu_coefficient", "0.044715 * z * z * z", "0.44715 * z * z * z"),
     ("gelu_no_half", "double gz = 0.5 * z *", "double gz = 1.0 * z *"),
     ("attn_cap_missing", "if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);", "(void)softcap;"),
@@ -66,7 +69,7 @@ MUTANTS = [
     ("attn_start_ignored", "int64_t base = g * head_stride + (start + j) * pos_stride;\n            double acc",
      "int64_t base = g * head_stride + j * pos_stride;\n            double acc"),
     ("route_tie_high_id", "if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
-    ("moe_unweighted", "acc[j] += (double)w[slot] * (double)y2[j];", "acc[j] += (double)y2[j];"),
+    ("moe_unweighted", "double ws = (double)w[slot];", "double ws = 1.0;"),
     ("layer_gate_up_swapped", "orc_silu_mul(gu, gu + I, I, tmp);", "orc_silu_mul(gu + I, gu, I, tmp);"),
     ("layer_window_off_by_one", "if (L->window > 0 && pos - L->window + 1 > 0) start = pos - L->window + 1;",
      "if (L->window > 0 && pos - L->window > 0) start = pos - L->window;"),

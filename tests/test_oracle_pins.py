@@ -468,6 +468,18 @@ def pin_moe_block():
             assert np.allclose(tr["y2"][t, s], y2, rtol=1e-6, atol=1e-7)
             acc += tr["w"][t, s] * y2
         assert np.allclose(out[t], acc, rtol=1e-6, atol=1e-6)
+    # per-expert output scale: all 2 doubles the block exactly; a one-hot table
+    # keeps only the slots routed to that expert
+    out2 = oracle.moe_block(H, I, E, k, gq, gd, dq, dd, x, logits, expert_scale=np.full(E, 2.0, np.float32))
+    assert np.array_equal(out2, 2.0 * out)
+    e1 = int(tr["ids"][0, 0])
+    one = np.zeros(E, np.float32)
+    one[e1] = 1.5
+    out1 = oracle.moe_block(H, I, E, k, gq, gd, dq, dd, x, logits, expert_scale=one)
+    for t in range(T):
+        want = sum(1.5 * float(tr["w"][t, s]) * tr["y2"][t, s].astype(np.float64)
+                   for s in range(k) if tr["ids"][t, s] == e1) + np.zeros(H)
+        assert np.allclose(out1[t], want, rtol=1e-6, atol=1e-7)
     # one expert, k = 1, weight 1: the block is the plain two-matvec FFN
     out1, tr1 = oracle.moe_block(H, I, 1, 1, gq[:1], gd[:1], dq[:1], dd[:1], x, logits[:, :1], trace=True)
     assert np.allclose(tr1["w"], 1.0)
