@@ -93,6 +93,15 @@ lq_status lq_q8_pack_ggml(const void* blocks, int64_t rows, int64_t cols,
 lq_status lq_rope_table(int64_t max_ctx, int64_t head_dim, double theta,
                         float* cos_out, float* sin_out);
 
+/* The same table with per-pair frequency factors (the Gemma global layers'
+ * rope_freqs vector of [CUR] section 2, step 3, item 4, a frequency mask of
+ * head_dim/2 entries; sliding and global layers also use their own theta,
+ * item 5, which is a second table): angle = pos * theta^(-2i/head_dim) /
+ * freq_factors[i].  A factor of +inf leaves pair i unrotated.  freq_factors:
+ * HOST f32 [head_dim/2], every entry > 0, or NULL (all 1).  HOST memory. */
+lq_status lq_rope_table_freqs(int64_t max_ctx, int64_t head_dim, double theta, const float* freq_factors,
+                              float* cos_out, float* sin_out);
+
 /* ---------------------------------------------------------------- Q8_0 */
 /* Quantize n_rows independent vectors of n floats (n % 32 == 0) to Q8_0:
  * per 32-block d = amax/127 (float), codes = round-half-away(x * (1/d))

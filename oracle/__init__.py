@@ -91,6 +91,7 @@ def _load(path):
     L.orc_q8_matvec.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P]
     L.orc_rmsnorm.argtypes = [_P, _I64, _P, _D, _P]
     L.orc_rope_table.argtypes = [_I64, _I64, _D, _P, _P]
+    L.orc_rope_table_freqs.argtypes = [_I64, _I64, _D, _P, _P, _P]
     L.orc_rope_neox.argtypes = [_P, _I64, _P, _P]
     L.orc_silu_mul.argtypes = [_P, _P, _I64, _P]
     L.orc_gelu_mul.argtypes = [_P, _P, _I64, _P]
@@ -195,6 +196,14 @@ def rope_table(max_ctx, hd, theta):
     c = np.empty((max_ctx, hd // 2), dtype=np.float32)
     s = np.empty((max_ctx, hd // 2), dtype=np.float32)
     lib().orc_rope_table(max_ctx, hd, float(theta), _ptr(c), _ptr(s))
+    return c, s
+
+
+def rope_table_freqs(max_ctx, hd, theta, factors):
+    f = None if factors is None else _c(factors, np.float32)
+    c = np.empty((max_ctx, hd // 2), dtype=np.float32)
+    s = np.empty((max_ctx, hd // 2), dtype=np.float32)
+    lib().orc_rope_table_freqs(max_ctx, hd, float(theta), _ptr(f), _ptr(c), _ptr(s))
     return c, s
 
 

@@ -207,10 +207,21 @@ void orc_rmsnorm(const float* x, int64_t n, const float* gamma, double eps, floa
  * stored as float. */
 void orc_rope_table(int64_t max_ctx, int64_t hd, double theta, float* cos_t, float* sin_t)
 {
+    orc_rope_table_freqs(max_ctx, hd, theta, NULL, cos_t, sin_t);
+}
+
+/* The table with per-pair frequency factors ([CUR] section 2, step 3: the
+ * global layers' rope_freqs vector, a frequency mask over the head_dim/2
+ * pairs).  Reading taken: each factor divides its pair's frequency (so +inf
+ * leaves the pair unrotated). */
+void orc_rope_table_freqs(int64_t max_ctx, int64_t hd, double theta, const float* factors,
+                          float* cos_t, float* sin_t)
+{
     int64_t half = hd / 2;
     for (int64_t p = 0; p < max_ctx; ++p)
         for (int64_t i = 0; i < half; ++i) {
             double inv_freq = pow(theta, -2.0 * (double)i / (double)hd);
+            if (factors) inv_freq = inv_freq / (double)factors[i];
             double a = (double)p * inv_freq;
             cos_t[p * half + i] = (float)cos(a);
             sin_t[p * half + i] = (float)sin(a);

@@ -48,6 +48,9 @@ void orc_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t c
 void orc_rmsnorm(const float* x, int64_t n, const float* gamma, double eps, float* y);
 /* cos/sin tables [max_ctx, hd/2]: angle(pos, i) = pos * theta^(-2i/hd). */
 void orc_rope_table(int64_t max_ctx, int64_t hd, double theta, float* cos_t, float* sin_t);
+/* ... with angle / factors[i] (factors NULL: all 1). */
+void orc_rope_table_freqs(int64_t max_ctx, int64_t hd, double theta, const float* factors,
+                          float* cos_t, float* sin_t);
 /* NeoX rotation of one head in place: pairs (i, i + hd/2). */
 void orc_rope_neox(float* x, int64_t hd, const float* cos_row, const float* sin_row);
 /* h = silu(g) * u, silu(z) = z / (1 + exp(-z)). */

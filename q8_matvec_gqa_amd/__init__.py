@@ -91,6 +91,7 @@ _SIGS = {
     "lq_gqa_decode_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "lq_gqa_decode_attn": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
                                   _F, _P, _P, _SZ, _P]),
+    "lq_rope_table_freqs": (_I32, [_I64, _I64, C.c_double, _P, _P, _P]),
     "lq_lm_head_f16": (_I32, [_P, _I64, _I64, _P, _I32, _P, C.c_float, C.c_float, _P, _P]),
     "lq_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "lq_moe_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -175,6 +176,11 @@ def lq_q8_pack_ggml(blocks, rows, cols, qs, d, check=True):
 
 def lq_rope_table(max_ctx, head_dim, theta, cos_out, sin_out, check=True):
     return _check(_lib.lq_rope_table(max_ctx, head_dim, theta, _ptr(cos_out), _ptr(sin_out)), check)
+
+
+def lq_rope_table_freqs(max_ctx, head_dim, theta, freq_factors, cos_out, sin_out, check=True):
+    return _check(_lib.lq_rope_table_freqs(max_ctx, head_dim, theta, _ptr(freq_factors), _ptr(cos_out),
+                                           _ptr(sin_out)), check)
 
 
 # ---------------------------------------------------------------- Q8_0

@@ -74,17 +74,22 @@ extern "C" lq_status lq_q8_pack_ggml(const void* blocks, int64_t rows, int64_t c
     return LQ_OK;
 }
 
-extern "C" lq_status lq_rope_table(int64_t max_ctx, int64_t head_dim, double theta, float* cos_out,
-                                   float* sin_out) {
+extern "C" lq_status lq_rope_table_freqs(int64_t max_ctx, int64_t head_dim, double theta,
+                                         const float* freq_factors, float* cos_out, float* sin_out) {
     if (max_ctx < 0 || head_dim <= 0 || head_dim % 2 || !(theta > 0.0))
         return fail(LQ_ERR_SHAPE, "lq_rope_table: max_ctx=%lld head_dim=%lld theta=%g",
                     (long long)max_ctx, (long long)head_dim, theta);
+    const int64_t half = head_dim / 2;
+    if (freq_factors)
+        for (int64_t i = 0; i < half; ++i)
+            if (!(freq_factors[i] > 0.0f))
+                return fail(LQ_ERR_SHAPE, "lq_rope_table_freqs: freq_factors[%lld] must be > 0", (long long)i);
     if (max_ctx == 0) return LQ_OK;
     if (!cos_out || !sin_out) return fail(LQ_ERR_NULL, "lq_rope_table: NULL output");
-    const int64_t half = head_dim / 2;
     const double lt = log2(theta);
     for (int64_t i = 0; i < half; ++i) {
-        const double freq = exp2(-(2.0 * (double)i / (double)head_dim) * lt);
+        double freq = exp2(-(2.0 * (double)i / (double)head_dim) * lt);
+        if (freq_factors) freq /= (double)freq_factors[i];
         for (int64_t p = 0; p < max_ctx; ++p) {
             const double a = (double)p * freq;
             cos_out[p * half + i] = (float)cos(a);
@@ -92,4 +97,9 @@ extern "C" lq_status lq_rope_table(int64_t max_ctx, int64_t head_dim, double the
         }
     }
     return LQ_OK;
+}
+
+extern "C" lq_status lq_rope_table(int64_t max_ctx, int64_t head_dim, double theta, float* cos_out,
+                                   float* sin_out) {
+    return lq_rope_table_freqs(max_ctx, head_dim, theta, nullptr, cos_out, sin_out);
 }

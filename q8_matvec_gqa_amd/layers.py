@@ -5,7 +5,7 @@ import numpy as np
 
 from . import (lq_decode_layer, lq_decode_layer_workspace_size, lq_layer_desc, lq_layer_taps,
                lq_moe_block, lq_moe_block_workspace_size, lq_moe_desc, lq_moe_taps, lq_q8_weight,
-               lq_rope_table, q8_weight)
+               lq_rope_table, lq_rope_table_freqs, q8_weight)
 
 
 def _dev(a, torch):
@@ -27,7 +27,11 @@ class DeviceLayer:
         self.t = {k: _dev(v, torch) for k, v in w.items() if k != "x"}
         c = np.zeros((cfg["max_ctx"], hd // 2), np.float32)
         s = np.zeros((cfg["max_ctx"], hd // 2), np.float32)
-        lq_rope_table(cfg["max_ctx"], hd, cfg["theta"], c, s)
+        if cfg.get("rope_freqs") is not None:
+            lq_rope_table_freqs(cfg["max_ctx"], hd, cfg["theta"], np.ascontiguousarray(cfg["rope_freqs"], np.float32),
+                                c, s)
+        else:
+            lq_rope_table(cfg["max_ctx"], hd, cfg["theta"], c, s)
         self.t["rope_cos"], self.t["rope_sin"] = _dev(c, torch), _dev(s, torch)
         t = self.t
         W = lambda name: q8_weight(t[name + "_qs"], t[name + "_d"])

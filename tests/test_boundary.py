@@ -204,3 +204,22 @@ def test_rope_table_host(hd):
     assert np.abs(c.astype(np.float64) - oc).max() <= 2 ** -23
     assert np.abs(s.astype(np.float64) - os_).max() <= 2 ** -23
     assert lq.lq_rope_table(ctx, 63, theta, c, s, check=False) == lq.LQ_ERR_SHAPE
+
+
+def test_rope_table_freqs_host():
+    """The frequency-factor table (host helper) against the oracle's, with a
+    mask that leaves the upper pairs unrotated."""
+    ctx, hd, theta = 4096, 512, 1e6
+    f = np.ones(hd // 2, np.float32)
+    f[64:] = np.inf
+    f[10] = 4.0
+    c = np.zeros((ctx, hd // 2), np.float32)
+    s = np.zeros((ctx, hd // 2), np.float32)
+    lq.lq_rope_table_freqs(ctx, hd, theta, f, c, s)
+    oc, os_ = oracle.rope_table_freqs(ctx, hd, theta, f)
+    assert np.abs(c.astype(np.float64) - oc).max() <= 2 ** -23
+    assert np.abs(s.astype(np.float64) - os_).max() <= 2 ** -23
+    assert np.all(c[:, 64:] == 1.0) and np.all(s[:, 64:] == 0.0)
+    bad = f.copy()
+    bad[3] = 0.0
+    assert lq.lq_rope_table_freqs(ctx, hd, theta, bad, c, s, check=False) == lq.LQ_ERR_SHAPE

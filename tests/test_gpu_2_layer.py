@@ -44,10 +44,19 @@ def test_layer_variants_teacher_forced(name, act, cap):
     run_teacher_forced(name, act, cap)
 
 
-def run_teacher_forced(name, act=0, cap=0.0):
+def test_layer_rope_freqs_teacher_forced():
+    """Gemma global layer with a RoPE frequency mask: the first 64 of the 256
+    pairs rotate (one at a quarter of its frequency), the rest do not."""
+    f = np.ones(256, np.float32)
+    f[64:] = np.inf
+    f[7] = 4.0
+    run_teacher_forced("gemma4_global_h2816", freqs=f)
+
+
+def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
     torch = torch_mod()
     cfg, w = synthetic.layer_inputs(name, seed=0)
-    cfg = dict(cfg, ffn_act=act, attn_softcap=cap)
+    cfg = dict(cfg, ffn_act=act, attn_softcap=cap, rope_freqs=freqs)
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
     pos, kind = cfg["pos"], cfg["kind"]
     qd, kvd = nq * hd, nkv * hd
@@ -65,7 +74,10 @@ def run_teacher_forced(name, act=0, cap=0.0):
     kc_gpu = host(L.t["k_cache"], kv_np)
     vc_gpu = host(L.t["v_cache"], kv_np)
     out_gpu = host(x)
-    oc, os_ = oracle.rope_table(cfg["max_ctx"], hd, cfg["theta"])
+    if freqs is None:
+        oc, os_ = oracle.rope_table(cfg["max_ctx"], hd, cfg["theta"])
+    else:
+        oc, os_ = oracle.rope_table_freqs(cfg["max_ctx"], hd, cfg["theta"], freqs)
     eps = cfg["eps"]
     flips = 0
 

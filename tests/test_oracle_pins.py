@@ -335,6 +335,26 @@ def test_attention_softcap():
     pin_attention_softcap()
 
 
+def pin_rope_freqs():
+    hd, theta, ctx = 32, 1e4, 40
+    c0, s0 = oracle.rope_table(ctx, hd, theta)
+    c1, s1 = oracle.rope_table_freqs(ctx, hd, theta, np.ones(hd // 2, np.float32))
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    # a factor of 2 halves every angle: position p reads like position p/2
+    c2, s2 = oracle.rope_table_freqs(ctx, hd, theta, np.full(hd // 2, 2.0, np.float32))
+    assert np.array_equal(c2[0::2][:ctx // 2], c0[:ctx // 2]) and np.array_equal(s2[0::2][:ctx // 2], s0[:ctx // 2])
+    # an infinite factor leaves the pair unrotated; the others are untouched
+    f = np.ones(hd // 2, np.float32)
+    f[5:] = np.inf
+    c3, s3 = oracle.rope_table_freqs(ctx, hd, theta, f)
+    assert np.all(c3[:, 5:] == 1.0) and np.all(s3[:, 5:] == 0.0)
+    assert np.array_equal(c3[:, :5], c0[:, :5]) and np.array_equal(s3[:, :5], s0[:, :5])
+
+
+def test_rope_freqs():
+    pin_rope_freqs()
+
+
 def test_rmsnorm():
     pin_rmsnorm()
 
