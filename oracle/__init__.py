@@ -89,6 +89,7 @@ def _load(path):
     L.orc_q8_quantize.argtypes = [_P, _I64, _P, _P]
     L.orc_q8_block_dots.argtypes = [_P, _I64, _I64, _P, _P]
     L.orc_q8_matvec.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P]
+    L.orc_q8_matmul.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P]
     L.orc_rmsnorm.argtypes = [_P, _I64, _P, _D, _P]
     L.orc_rope_table.argtypes = [_I64, _I64, _D, _P, _P]
     L.orc_rope_table_freqs.argtypes = [_I64, _I64, _D, _P, _P, _P]
@@ -169,6 +170,20 @@ def q8_matvec(wq, wd, xq, xd, residual=None):
     res = None if residual is None else _c(residual, np.float32)
     y = np.empty(rows, dtype=np.float32)
     lib().orc_q8_matvec(_ptr(wq), _ptr(wd), rows, cols, _ptr(xq), _ptr(xd), _ptr(res), _ptr(y))
+    return y
+
+
+def q8_matmul(wq, wd, xq, xd, residual=None):
+    """xq [T, cols] int8, xd [T, cols/32] f16 bits -> y [T, rows]."""
+    wq = _c(wq, np.int8)
+    wd = _c(wd, np.uint16)
+    xq = _c(xq, np.int8)
+    xd = _c(xd, np.uint16)
+    rows, cols = wq.shape
+    T = xq.shape[0]
+    res = None if residual is None else _c(residual, np.float32)
+    y = np.empty((T, rows), dtype=np.float32)
+    lib().orc_q8_matmul(_ptr(wq), _ptr(wd), rows, cols, _ptr(xq), _ptr(xd), T, _ptr(res), _ptr(y))
     return y
 
 

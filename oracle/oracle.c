@@ -185,6 +185,16 @@ void orc_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t c
     }
 }
 
+/* The same product for T tokens ([LAT] Current Design, applied row by row of
+ * a token batch): y[t] = W x[t] (+ residual[t]), one matvec per token. */
+void orc_q8_matmul(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                   const int8_t* xq, const uint16_t* xd, int64_t T, const float* residual, float* y)
+{
+    for (int64_t t = 0; t < T; ++t)
+        orc_q8_matvec(wq, wd, rows, cols, xq + t * cols, xd + t * (cols / 32),
+                      residual ? residual + t * rows : NULL, y + t * rows);
+}
+
 /* ======================================================================== */
 /* Norms, RoPE, activation                                                  */
 /* ======================================================================== */

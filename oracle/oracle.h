@@ -43,6 +43,10 @@ void orc_q8_block_dots(const int8_t* wq, int64_t rows, int64_t cols,
 void orc_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
                    const int8_t* xq, const uint16_t* xd, const float* residual, float* y);
 
+/* y[t] = W x[t] (+ residual[t]) for t < T: x [T, cols], y [T, rows]. */
+void orc_q8_matmul(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
+                   const int8_t* xq, const uint16_t* xd, int64_t T, const float* residual, float* y);
+
 /* ---- norms, RoPE, activation --------------------------------------------- */
 /* y = gamma * x / sqrt(mean(x^2) + eps); gamma == NULL means unit weight. */
 void orc_rmsnorm(const float* x, int64_t n, const float* gamma, double eps, float* y);

@@ -23,11 +23,13 @@ ALL_PINS = [
     pins.pin_rmsnorm, pins.pin_rope, pins.pin_silu, pins.pin_attention, pins.pin_moe_route,
     pins.pin_moe_block, lambda: pins.pin_layer(0, 1), lambda: pins.pin_layer(1, 1),
     lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head, pins.pin_gelu,
-    pins.pin_attention_softcap, pins.pin_rope_freqs,
+    pins.pin_attention_softcap, pins.pin_rope_freqs, pins.pin_matmul,
 ]
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("matmul_token_stride", "orc_q8_matvec(wq, wd, rows, cols, xq + t * cols, xd + t * (cols / 32),",
+     "orc_q8_matvec(wq, wd, rows, cols, xq + t, xd + t * (cols / 32),"),
     ("rope_factor_multiplies", "if (factors) inv_freq = inv_freq / (double)factors[i];",
      "if (factors) inv_freq = inv_freq * (double)factors[i];"),
     ("moe_scale_ignored", "if (m->expert_scale) ws *= (double)m->expert_scale[e];", "(void)e;"),

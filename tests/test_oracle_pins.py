@@ -355,6 +355,28 @@ def test_rope_freqs():
     pin_rope_freqs()
 
 
+def pin_matmul():
+    rng = np.random.default_rng(12)
+    T, rows, cols = 5, 40, 96
+    wq, wd = synthetic.q8_weight(rng, rows, cols)
+    xq = rng.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = (np.abs(rng.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
+    res = rng.standard_normal((T, rows)).astype(np.float32)
+
+    def deq(q, d):
+        return q.astype(np.float64) * np.repeat(d.view(np.float16).astype(np.float64), 32, axis=-1)
+
+    want = deq(xq, xd) @ deq(wq, wd).T + res.astype(np.float64)
+    got = oracle.q8_matmul(wq, wd, xq, xd, residual=res)
+    assert got.shape == (T, rows)
+    assert np.allclose(got, want, rtol=1e-6, atol=1e-6)
+    assert oracle.q8_matmul(wq, wd, xq[:0], xd[:0]).shape == (0, rows)
+
+
+def test_matmul():
+    pin_matmul()
+
+
 def test_rmsnorm():
     pin_rmsnorm()
 
