@@ -286,6 +286,62 @@ def measure_moe(name, steps, torch):
             "frac": round(gbs / HBM_PEAK_GBS, 4), "replicas": R, "graph": True}
 
 
+def measure_matmul(T, steps, torch):
+    """The multi-token Q8_0 matmul (int8 MFMA) on the 8B-like layer's four
+    projections for a batch of T tokens, over R distinct replicas of the
+    weights (>= 2 GB, beyond the Infinity Cache).  Algorithmic bytes per call:
+    weights + T rows of Q8_0 input + T rows of f32 output."""
+    import q8_matvec_gqa_amd as lq
+    cfg = synthetic.layer_cfg("qwen3_8b_like_h4096")
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    shapes = {"qkv": (nq * hd + 2 * nkv * hd, H), "o": (H, nq * hd), "gate_up": (2 * I, H), "down": (H, I)}
+    per_rep = sum(r * c * 34 // 32 for r, c in shapes.values())
+    R = max(2, math.ceil(2e9 / per_rep))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4000)
+    reps = []
+    for _ in range(R):
+        ws = {}
+        for k, (r, c) in shapes.items():
+            qs = torch.randint(-127, 128, (r, c), dtype=torch.int8, device="cuda", generator=gen)
+            d = (torch.randn(r, c // 32, device="cuda", generator=gen).abs() * (0.02 / 127)).half().view(torch.int16)
+            ws[k] = (lq.q8_weight(qs, d), qs, d)
+        reps.append(ws)
+    xs = {}
+    for k, (r, c) in shapes.items():
+        xs[k] = (torch.randint(-127, 128, (T, c), dtype=torch.int8, device="cuda", generator=gen),
+                 (torch.rand(T, c // 32, device="cuda", generator=gen) * 0.05).half().view(torch.int16),
+                 torch.empty(T, r, device="cuda"))
+    stream = torch.cuda.current_stream()
+    nws = max(lq.lq_q8_matmul_workspace_size(r, c, T) for r, c in shapes.values())
+    work = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
+    res = {}
+    total_us = 0.0
+    for k, (r, c) in shapes.items():
+        xq, xd, y = xs[k]
+        for ws in reps[:2]:
+            lq.lq_q8_matmul(ws[k][0], xq, xd, T, None, y, work, nws, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            for ws in reps:
+                lq.lq_q8_matmul(ws[k][0], xq, xd, T, None, y, work, nws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (steps * R)
+        nbytes = r * c * 34 // 32 + T * c * 34 // 32 + T * r * 4
+        res[k] = {"rows": r, "cols": c, "us": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
+                  "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4),
+                  "TOPs": round(2.0 * T * r * c / (us * 1e-6) / 1e12, 1)}
+        total_us += us
+        log(f"q8_matmul T={T} {k:8s} {r}x{c}: {us:.2f} us, {res[k]['GBps']:.1f} GB/s, {res[k]['TOPs']:.1f} TOP/s")
+    del reps, xs, work
+    return {"workload": f"q8_matmul_t{T}_qwen3_8b_like_h4096", "tokens": T, "replicas": R,
+            "us_four_projections": round(total_us, 3), "us_per_token_four_projections": round(total_us / T, 3),
+            "per_matrix": res, "mfma": "v_mfma_i32_32x32x32_i8"}
+
+
 def measure_head(steps, torch):
     """The output head (final norm, f16 vocab projection, softcap) at the
     Gemma-4 shape: vocab x hidden f16 weights (1.5 GB, beyond the Infinity
@@ -568,6 +624,8 @@ def main():
             result["moe_block"] = measure_moe(name, max(10, args.steps // 2), torch)
             torch.cuda.empty_cache()
         result["lm_head"] = measure_head(max(10, args.steps // 2), torch)
+        torch.cuda.empty_cache()
+        result["q8_matmul"] = measure_matmul(32, max(5, args.steps // 10), torch)
         torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)

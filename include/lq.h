@@ -141,6 +141,27 @@ lq_status lq_q8_matvec(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t
 lq_status lq_q8_block_dots(const lq_q8_weight* w, const int8_t* x_qs, int32_t* dots,
                            void* stream);
 
+/* Multi-token Q8_0 matmul: the decode matvec for T tokens at once (prefill,
+ * batched decode), each weight byte read once per 32 tokens ([LAT] Current
+ * Design: int8 weights times int8 activations with int32 accumulation, one
+ * f16 scale per 32 values):
+ *   y[t, r] = residual[t, r] + sum_b f16(d_w[r,b]) * f16(x_d[t,b]) * dot_b(W[r], X[t])
+ * with dot_b the exact int32 dot of block b.  Runs on int8 MFMA; the float
+ * sum is in an unspecified but fixed order (results do not vary from run to
+ * run).
+ *   w: as for lq_q8_matvec, cols <= 16384 (LQ_ERR_UNSUPPORTED beyond).
+ *   x_qs: device int8 [T, cols], 16-byte aligned; x_d: device f16 bits [T, cols/32].
+ *   residual: device f32 [T, rows] or NULL; y: device f32 [T, rows]; y may
+ *   alias residual.
+ *   workspace: device memory of lq_q8_matmul_workspace_size(rows, cols, T)
+ *   bytes (4-byte aligned; may be NULL when that size is 0), holding partial
+ *   sums when a short weight splits its blocks over several workgroups.
+ * T == 0 or rows == 0 is a no-op. */
+size_t lq_q8_matmul_workspace_size(int64_t rows, int64_t cols, int64_t T);
+lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d, int64_t T,
+                       const float* residual, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* ---------------------------------------------------------------- norm + RoPE */
 /* In place, for each of n_heads heads of head_dim floats starting at
  * x + h*head_stride ([LAT] Current Design: fused_qk_norm_rope; [CUR]

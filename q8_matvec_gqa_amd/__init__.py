@@ -92,6 +92,8 @@ _SIGS = {
     "lq_gqa_decode_attn": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
                                   _F, _P, _P, _SZ, _P]),
     "lq_rope_table_freqs": (_I32, [_I64, _I64, C.c_double, _P, _P, _P]),
+    "lq_q8_matmul_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lq_q8_matmul": (_I32, [_W, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
     "lq_lm_head_f16": (_I32, [_P, _I64, _I64, _P, _I32, _P, C.c_float, C.c_float, _P, _P]),
     "lq_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "lq_moe_workspace_size": (_SZ, [_I64, _I64, _I64]),
@@ -234,6 +236,15 @@ def lq_gqa_decode_attn(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_
 
 
 # ---------------------------------------------------------------- MoE
+def lq_q8_matmul_workspace_size(rows, cols, T):
+    return _lib.lq_q8_matmul_workspace_size(rows, cols, T)
+
+
+def lq_q8_matmul(w, x_qs, x_d, T, residual, y, workspace, workspace_bytes, stream=None, check=True):
+    return _check(_lib.lq_q8_matmul(_ref(w), _ptr(x_qs), _ptr(x_d), T, _ptr(residual), _ptr(y), _ptr(workspace),
+                                    workspace_bytes, _stream(stream)), check)
+
+
 def lq_lm_head_f16(w, vocab, hidden, x, norm, gamma, eps, softcap, logits, stream=None, check=True):
     return _check(_lib.lq_lm_head_f16(_ptr(w), vocab, hidden, _ptr(x), int(norm), _ptr(gamma), eps, softcap,
                                       _ptr(logits), _stream(stream)), check)

@@ -1,0 +1,285 @@
+// k_matmul.hip -- multi-token Q8_0 matmul on gfx950 int8 MFMA.
+//
+// What it computes ("Design: lattice-inference", Current Design: the Q8_0
+// path multiplies int8 weights by int8 activations with int32 accumulation,
+// one scale per 32 values; the same product as the decode matvec, for T
+// tokens at once, as in prefill or batched decode):
+//     Y[t, r] = sum_b f16(dW[r, b]) * f16(dX[t, b]) * sum_{i<32} W[r, 32b+i] * X[t, 32b+i]
+//     (+ residual[t, r])
+//
+// With T >= 16-32 tokens every weight byte feeds T multiply-adds, so the
+// block dots form a dense int8 contraction: v_mfma_i32_32x32x32_i8 computes a
+// 32-token x 32-row tile of one 32-value block (K = 32 is exactly one Q8_0
+// block, so each MFMA result is one block dot per (token, row) and takes its
+// two scales before the next block is added).
+//
+// Memory mapping.  The MFMA operands span 32 rows (lane l holds 16 bytes of
+// row l % 32), but reading them that way sends every load instruction to 32
+// rows cols bytes apart, and the weight and scale streams then crawl.  So a
+// workgroup (4 waves, 32 rows) reads each batch of 16 blocks -- 512
+// contiguous bytes of every row of W and X, and the matching runs of both
+// scale arrays -- with row-contiguous 16-byte loads, stages them in padded
+// LDS tiles (the 16-byte pad puts the 8 rows one b128 read phase touches on
+// distinct banks), and each wave runs the MFMAs of a quarter of the batch's
+// blocks from LDS.  The next batch's loads are in flight while the current
+// one is computed.  The waves' partial tiles are summed in LDS in a fixed
+// order.  Few row tiles (a short weight) split the blocks over several
+// workgroups per tile; each writes its partial tile to the workspace and an
+// ordered reduce launch adds them (and the residual), so results do not
+// depend on timing.
+#include "lq_device.h"
+#include "lq_internal.h"
+
+namespace lq {
+
+namespace {
+
+typedef int v4i_mm __attribute__((ext_vector_type(4)));
+typedef int v16i_mm __attribute__((ext_vector_type(16)));
+typedef float v16f_mm __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h_mm __attribute__((ext_vector_type(8)));
+
+constexpr int kMmTok = 32;                  // tokens per launch (MFMA M); the host loops over chunks
+constexpr int kMmKB = 16;                   // Q8_0 blocks per batch: 512 bytes of every row
+constexpr int kMmRB = kMmKB * 32 + 16;      // LDS row stride in bytes (16-byte pad)
+constexpr int kMmSS = 34;                   // LDS stride of one block's 32 f16 scales
+constexpr int kMmNT = 256;                  // 4 waves
+constexpr int kMmMaxBlocks = 512;           // cols <= 16384
+constexpr int kMmTargetWG = kNumCUs * 3;    // workgroups a launch aims for (3 fit per CU)
+constexpr int kMmMaxSplit = 8;              // workgroups per row tile at most
+
+struct MmArgs {
+    const int8_t* wq;
+    const uint16_t* wd;
+    int rows, cols;
+    const int8_t* xq;       // [T, cols]
+    const uint16_t* xd;     // [T, cols/32]
+    int T;                  // <= 32
+    const float* res;       // [T, ld] or NULL (ks == 1 only)
+    float* y;               // [T, ld] (ks == 1 only)
+    int64_t ld;             // row stride of res / y (elements)
+    float* part;            // ks > 1: [ks][kMmTok][rows] partial sums
+    int ks, bpw;            // workgroups per row tile, blocks per workgroup
+};
+
+// One batch in registers, per thread: kMmNL 16-byte chunks of W and of X,
+// kMmNS weight and activation scales.
+constexpr int kMmCPR = 2 * kMmKB;                  // 16-byte chunks per row and batch
+constexpr int kMmNL = 32 * kMmCPR / kMmNT;         // chunk loads per thread and matrix
+constexpr int kMmNS = 32 * kMmKB / kMmNT;          // scales per thread and matrix
+struct MmStage {
+    int4 w[kMmNL], x[kMmNL];
+    uint32_t dw[kMmNS], dx[kMmNS];
+};
+
+// Loads of the batch [bs, be) (be - bs <= kMmKB blocks).  Load j of thread
+// tid takes chunk idx % kMmCPR of row idx / kMmCPR (idx = tid + 256j), so
+// each wave instruction reads whole contiguous row runs; scales likewise
+// (consecutive lanes read one row's consecutive scales).  Chunks of blocks
+// past be, rows past the matrix and tokens past T read valid memory (block
+// 0, the last row, the last token) and are zeroed through their scales or
+// never stored.
+__device__ __forceinline__ void mm_load(const MmArgs& a, int row0, int bs, int be, int tid, MmStage& S) {
+    const int nb = a.cols >> 5;
+    const int c = tid % kMmCPR;
+    const int64_t coff = bs + (c >> 1) < be ? (int64_t)bs * 32 + 16 * c : 16 * (c & 1);
+#pragma unroll
+    for (int j = 0; j < kMmNL; ++j) {
+        const int r = (tid + kMmNT * j) / kMmCPR;
+        const int row = row0 + r < a.rows ? row0 + r : a.rows - 1;
+        const int tok = r < a.T ? r : a.T - 1;
+        S.w[j] = load_stream16(a.wq + (int64_t)row * a.cols + coff);
+        S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)tok * a.cols + coff);
+    }
+#pragma unroll
+    for (int i = 0; i < kMmNS; ++i) {
+        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
+        const int b = bs + u < be ? bs + u : 0;
+        const int row = row0 + rr < a.rows ? row0 + rr : a.rows - 1;
+        const int tok = rr < a.T ? rr : a.T - 1;
+        S.dw[i] = a.wd[(int64_t)row * nb + b];
+        S.dx[i] = a.xd[(int64_t)tok * nb + b];
+    }
+}
+
+// LDS: W tile [32 rows][kMmRB], X tile [32 tokens][kMmRB], scales as f16
+// bits [block][kMmSS] (row or token fastest), zero for blocks past be and
+// tokens past T.
+__device__ __forceinline__ void mm_store(const MmArgs& a, int bs, int be, int tid, const MmStage& S, int8_t* wl,
+                                         int8_t* xl, uint16_t* dwl, uint16_t* dxl) {
+    const int c = tid % kMmCPR;
+#pragma unroll
+    for (int j = 0; j < kMmNL; ++j) {
+        const int r = (tid + kMmNT * j) / kMmCPR;
+        *reinterpret_cast<int4*>(wl + r * kMmRB + 16 * c) = S.w[j];
+        *reinterpret_cast<int4*>(xl + r * kMmRB + 16 * c) = S.x[j];
+    }
+#pragma unroll
+    for (int i = 0; i < kMmNS; ++i) {
+        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
+        const bool uv = bs + u < be;
+        dwl[u * kMmSS + rr] = uv ? (uint16_t)S.dw[i] : (uint16_t)0;
+        dxl[u * kMmSS + rr] = (uv && rr < a.T) ? (uint16_t)S.dx[i] : (uint16_t)0;
+    }
+}
+
+__global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
+    __shared__ __attribute__((aligned(16))) int8_t wl[32 * kMmRB];
+    __shared__ __attribute__((aligned(16))) int8_t xl[32 * kMmRB];
+    __shared__ __attribute__((aligned(16))) uint16_t dwl[kMmKB * kMmSS];
+    __shared__ __attribute__((aligned(16))) uint16_t dxl[kMmKB * kMmSS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, half = lane >> 5;
+    const int nb = a.cols >> 5;
+    const int split = blockIdx.x % a.ks, row0 = (blockIdx.x / a.ks) * 32;
+    const int b0 = split * a.bpw, b1 = b0 + a.bpw < nb ? b0 + a.bpw : nb;   // host: b0 < b1
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    MmStage S;
+    mm_load(a, row0, b0, b0 + kMmKB < b1 ? b0 + kMmKB : b1, tid, S);
+    for (int bs = b0; bs < b1; bs += kMmKB) {
+        const int be = bs + kMmKB < b1 ? bs + kMmKB : b1;
+        if (bs > b0) __syncthreads();        // every wave is done with the previous batch
+        mm_store(a, bs, be, tid, S, wl, xl, dwl, dxl);
+        __syncthreads();
+        if (be < b1) mm_load(a, row0, be, be + kMmKB < b1 ? be + kMmKB : b1, tid, S);
+        // this wave's blocks of the batch: wave, wave + 4, wave + 8, ...; per
+        // block an int8 MFMA (the block dots) and an f16 MFMA whose only
+        // nonzero k term forms the scale products f16(dX[t]) * f16(dW[r])
+        // (exact in f32) in the same tile layout.  Lane holds tokens
+        // 8*(i/4) + 4*half + i%4 of row n.
+#pragma unroll
+        for (int k = 0; k < kMmKB / 4; ++k) {
+            const int u = wave + 4 * k;
+            const v4i_mm A = *reinterpret_cast<const v4i_mm*>(xl + n * kMmRB + 32 * u + 16 * half);
+            const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + n * kMmRB + 32 * u + 16 * half);
+            const int xs = dxl[u * kMmSS + n], ws = dwl[u * kMmSS + n];
+            const v16i_mm c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
+            const v4i_mm As = {half ? 0 : xs, 0, 0, 0}, Bs = {half ? 0 : ws, 0, 0, 0};
+            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h_mm, As),
+                                                                      __builtin_bit_cast(v8h_mm, Bs), v16f_mm{}, 0,
+                                                                      0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
+        }
+    }
+    // the 4 waves' partial tiles, summed in wave order; thread = (token, row)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(wl);     // [4][32 tokens][32 rows]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave * 1024 + (8 * (r / 4) + 4 * half + (r & 3)) * 32 + n] = acc[r];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = tid + kMmNT * k, t = i >> 5, row = row0 + (i & 31);
+        if (t < a.T && row < a.rows) {
+            const float s = ((red[i] + red[1024 + i]) + red[2048 + i]) + red[3072 + i];
+            if (a.ks == 1) {
+                const int64_t o = (int64_t)t * a.ld + row;
+                a.y[o] = a.res ? a.res[o] + s : s;
+            } else {
+                a.part[((int64_t)split * kMmTok + t) * a.rows + row] = s;
+            }
+        }
+    }
+}
+
+// y[t, r] = residual[t, r] + sum over the splits in order; V consecutive
+// rows per thread (V = 4 needs rows % 4 == 0), every split's load issued
+// before the sum.
+template <int V>
+__global__ __launch_bounds__(256) void k_q8_matmul_reduce(const float* __restrict__ part, int ks, int T, int rows,
+                                                          const float* res, float* y, int64_t ld) {
+    typedef float vf __attribute__((ext_vector_type(V)));
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    if (i >= (int64_t)T * rows) return;
+    const int t = (int)(i / rows), r = (int)(i % rows);
+    vf p[kMmMaxSplit];
+#pragma unroll
+    for (int k = 0; k < kMmMaxSplit; ++k)
+        p[k] = k < ks ? *reinterpret_cast<const vf*>(part + ((int64_t)k * kMmTok + t) * rows + r) : vf{};
+    vf s = p[0];
+#pragma unroll
+    for (int k = 1; k < kMmMaxSplit; ++k) s += p[k];
+    const int64_t o = (int64_t)t * ld + r;
+    if (res) s += *reinterpret_cast<const vf*>(res + o);
+    *reinterpret_cast<vf*>(y + o) = s;
+}
+
+// Workgroups per row tile and blocks per workgroup: a short weight splits
+// its blocks (in whole batches, at most kMmMaxSplit ways) so that the grid
+// fills but does not exceed one resident round.
+void mm_plan(int64_t rows, int64_t cols, int* ks, int* bpw) {
+    const int64_t tiles = (rows + 31) / 32, nb = cols / 32;
+    int best_k = 1;
+    int64_t best_b = nb;
+    for (int k = 2; k <= kMmMaxSplit; ++k) {
+        int64_t b = (nb + k - 1) / k;
+        if (nb > kMmKB) b = (b + kMmKB - 1) / kMmKB * kMmKB;
+        const int64_t kk = (nb + b - 1) / b;
+        if (tiles * kk > kMmTargetWG) break;
+        if (kk > best_k) best_k = (int)kk, best_b = b;
+    }
+    *bpw = (int)best_b;
+    *ks = best_k;
+}
+
+}  // namespace
+
+}  // namespace lq
+
+using namespace lq;
+
+extern "C" size_t lq_q8_matmul_workspace_size(int64_t rows, int64_t cols, int64_t T) {
+    if (rows <= 0 || cols <= 0 || T <= 0 || cols % 32 || cols > 32 * kMmMaxBlocks) return 0;
+    int ks, bpw;
+    mm_plan(rows, cols, &ks, &bpw);
+    return ks > 1 ? (size_t)ks * kMmTok * (size_t)rows * sizeof(float) : 0;
+}
+
+extern "C" lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d, int64_t T,
+                                  const float* residual, float* y, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    const char* fn = "lq_q8_matmul";
+    lq_status st = check_weight(w, fn);
+    if (st != LQ_OK) return st;
+    if (T < 0) return fail(LQ_ERR_SHAPE, "%s: T=%lld", fn, (long long)T);
+    if (w->cols > 32 * kMmMaxBlocks || w->rows > 0x7fffffffLL)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: cols=%lld rows=%lld (cols <= %d)", fn, (long long)w->cols,
+                    (long long)w->rows, 32 * kMmMaxBlocks);
+    if (T == 0 || w->rows == 0) return LQ_OK;
+    if (!x_qs || !x_d || !y) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(x_qs, 16) || !aligned(x_d, 2) || !aligned(y, 4) || (residual && !aligned(residual, 4)))
+        return fail(LQ_ERR_ALIGN, "%s: x_qs must be 16-byte aligned", fn);
+    const size_t need = lq_q8_matmul_workspace_size(w->rows, w->cols, T);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 4)))
+        return fail(LQ_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+    const hipStream_t s = as_stream(stream);
+    const int64_t rows = w->rows, cols = w->cols, nb = cols / 32;
+    int ks, bpw;
+    mm_plan(rows, cols, &ks, &bpw);
+    const unsigned grid = (unsigned)(((rows + 31) / 32) * ks);
+    for (int64_t t0 = 0; t0 < T; t0 += kMmTok) {
+        const int Tc = (int)(T - t0 < kMmTok ? T - t0 : kMmTok);
+        const float* res = residual ? residual + t0 * rows : nullptr;
+        MmArgs a{w->qs, w->d, (int)rows, (int)cols, x_qs + t0 * cols, x_d + t0 * nb, Tc, res, y + t0 * rows, rows,
+                 static_cast<float*>(workspace), ks, bpw};
+        hipLaunchKernelGGL(k_q8_matmul, dim3(grid), dim3(kMmNT), 0, s, a);
+        if (ks > 1) {
+            const int64_t n = (int64_t)Tc * rows;
+            const bool v4 = rows % 4 == 0 && aligned(y, 16) && (!residual || aligned(residual, 16)) &&
+                            aligned(workspace, 16);
+            if (v4)
+                hipLaunchKernelGGL(k_q8_matmul_reduce<4>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                                   static_cast<const float*>(workspace), ks, Tc, (int)rows, res, y + t0 * rows, rows);
+            else
+                hipLaunchKernelGGL(k_q8_matmul_reduce<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                                   static_cast<const float*>(workspace), ks, Tc, (int)rows, res, y + t0 * rows, rows);
+        }
+        st = check_launch(fn);
+        if (st != LQ_OK) return st;
+    }
+    return LQ_OK;
+}

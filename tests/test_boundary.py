@@ -77,6 +77,25 @@ def test_matvec_validation():
     assert st(lq.lq_q8_block_dots, w, A, None) == lq.LQ_ERR_NULL
 
 
+def test_matmul_validation_and_workspace():
+    w = lq.lq_q8_weight(A, A, 4096, 4096)
+    need = lq.lq_q8_matmul_workspace_size(4096, 4096, 32)
+    # a short weight splits its blocks: one f32 partial tile per split, reused per 32-token chunk
+    assert need > 0 and need % (32 * 4096 * 4) == 0
+    assert lq.lq_q8_matmul_workspace_size(4096, 4096, 1000) == need
+    assert lq.lq_q8_matmul_workspace_size(24576, 4096, 32) == 0       # enough row tiles: no split
+    assert lq.lq_q8_matmul_workspace_size(4096, 4096, 0) == 0
+    assert lq.lq_q8_matmul_workspace_size(4096, 48, 8) == 0
+    assert st(lq.lq_q8_matmul, w, A, A, -1, None, A, A, need) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q8_matmul, lq.lq_q8_weight(A, A, 10, 32 * 513), A, A, 4, None, A, A, 1 << 20) == \
+        lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_q8_matmul, w, None, A, 4, None, A, A, need) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q8_matmul, w, A + 4, A, 4, None, A, A, need) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q8_matmul, w, A, A, 4, None, A, None, need) == lq.LQ_ERR_WORKSPACE
+    assert st(lq.lq_q8_matmul, w, A, A, 4, None, A, A, need - 4) == lq.LQ_ERR_WORKSPACE
+    assert st(lq.lq_q8_matmul, w, None, None, 0, None, None, None, 0) == lq.LQ_OK     # T == 0: no launch
+
+
 def test_lm_head_validation():
     assert st(lq.lq_lm_head_f16, A, 10, 36, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_SHAPE
     assert st(lq.lq_lm_head_f16, A, 10, 8192, A, 1, A, 1e-6, 0.0, A) == lq.LQ_ERR_UNSUPPORTED

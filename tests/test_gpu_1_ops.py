@@ -272,6 +272,121 @@ def test_attention_deterministic():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------ multi-token matmul
+def run_matmul(W, rows, cols, xq, xd, T, res, y):
+    nws = lq.lq_q8_matmul_workspace_size(rows, cols, T)
+    ws = empty(max(nws // 4, 1), np.float32)
+    lq.lq_q8_matmul(W, xq, xd, T, res, y, ws, nws)
+    sync()
+
+
+@pytest.mark.parametrize("T,rows,cols", [
+    (32, 4096, 4096),     # a batch of 32 on the 8B-like O projection
+    (1, 96, 64),          # one token, two blocks
+    (17, 1000, 1024),     # ragged tokens and rows
+    (45, 300, 2816),      # two token chunks (32 + 13), Gemma width
+    (33, 64, 16384),      # widest rows
+    (16, 6144, 4096),     # 8B-like QKV, half a tile of tokens
+    (32, 24576, 4096),    # 8B-like gate_up (no block split)
+    (8, 4096, 12288),     # 8B-like down (block split over 6 workgroups)
+    (32, 33, 32),         # one block, a one-row ragged tile
+])
+def test_q8_matmul(T, rows, cols):
+    r = rng(T * 7 + rows + cols)
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = (np.abs(r.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
+    res = synthetic.activations(r, T, rows)
+    y = empty(T * rows, np.float32)
+    run_matmul(lq.q8_weight(dev(wq), dev(wd)), rows, cols, dev(xq), dev(xd), T, dev(res), y)
+    want = oracle.q8_matmul(wq, wd, xq, xd, residual=res)
+    assert_close(host(y).reshape(T, rows), want, "q8 matmul")
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 4096), (24576, 1024)])
+def test_q8_matmul_in_place_and_repeatable(rows, cols):
+    """y aliasing the residual (the residual-add form of a projection) gives
+    the same as separate buffers, and two runs agree bit for bit (the split
+    partials are summed in a fixed order)."""
+    r = rng(rows + 3 * cols)
+    T = 20
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = (np.abs(r.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
+    res = synthetic.activations(r, T, rows)
+    W = lq.q8_weight(dev(wq), dev(wd))
+    y1 = empty(T * rows, np.float32)
+    run_matmul(W, rows, cols, dev(xq), dev(xd), T, dev(res), y1)
+    y2 = dev(res)
+    run_matmul(W, rows, cols, dev(xq), dev(xd), T, y2, y2)
+    assert np.array_equal(host(y1).reshape(T, rows), host(y2).reshape(T, rows))
+    assert_close(host(y1).reshape(T, rows), oracle.q8_matmul(wq, wd, xq, xd, residual=res), "q8 matmul")
+
+
+def test_q8_matmul_subnormal_scales():
+    """Q8_0 scales are f16 including its subnormals: blocks whose weight or
+    activation scale is subnormal (or zero) keep their exact products, with
+    no flush to zero.  Rows 0-63 have only subnormal weight scales, tokens
+    0-7 only subnormal activation scales; each region is checked with an
+    absolute floor far below its own magnitude."""
+    r = rng(77)
+    T, rows, cols = 32, 256, 1024
+    nb = cols // 32
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    wsub = r.integers(1, 1024, (rows, nb)).astype(np.uint16)                     # f16 subnormal bit patterns
+    wd = np.where(r.random((rows, nb)) < 0.5, wsub, wd).astype(np.uint16)
+    wd[:64] = wsub[:64]
+    wd[:, 3] = 0                                                                  # a zero scale
+    xsub = r.integers(1, 1024, (T, nb)).astype(np.uint16)
+    xd = (np.abs(r.standard_normal((T, nb))) * 0.05).astype(np.float16).view(np.uint16)
+    xd = np.where(r.random((T, nb)) < 0.5, xsub, xd).astype(np.uint16)
+    xd[:8] = xsub[:8]
+    y = empty(T * rows, np.float32)
+    run_matmul(lq.q8_weight(dev(wq), dev(wd)), rows, cols, dev(xq), dev(xd), T, None, y)
+    got = host(y).reshape(T, rows)
+    want = oracle.q8_matmul(wq, wd, xq, xd)
+    assert_close(got, want, "q8 matmul, mixed scales")
+    both = np.abs(want[:8, :64]).mean()
+    assert 1e-6 < both < 1e-3
+    assert_close(got[:8, :64], want[:8, :64], "subnormal x subnormal", atol=both * 1e-5)
+    assert_close(got[8:, :64], want[8:, :64], "subnormal weight scales", atol=np.abs(want[8:, :64]).mean() * 1e-5)
+    assert_close(got[:8, 64:], want[:8, 64:], "subnormal activation scales", atol=np.abs(want[:8, 64:]).mean() * 1e-5)
+
+
+def test_q8_matmul_workspace_checked():
+    r = rng(5)
+    rows, cols, T = 4096, 4096, 4
+    need = lq.lq_q8_matmul_workspace_size(rows, cols, T)
+    assert need > 0
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = np.ones((T, cols // 32), np.float16).view(np.uint16)
+    y = empty(T * rows, np.float32)
+    ws = empty(need // 4, np.float32)
+    st = lq.lq_q8_matmul(lq.q8_weight(dev(wq), dev(wd)), dev(xq), dev(xd), T, None, y, ws, need - 4, check=False)
+    assert st == lq.LQ_ERR_WORKSPACE
+
+
+def test_q8_matmul_matches_matvec_rows():
+    """Every token row of the MFMA matmul equals the decode matvec of that
+    token to the float tolerance (same block dots, different combine order)."""
+    r = rng(404)
+    T, rows, cols = 24, 512, 2048
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = (np.abs(r.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
+    W = lq.q8_weight(dev(wq), dev(wd))
+    y = empty(T * rows, np.float32)
+    run_matmul(W, rows, cols, dev(xq), dev(xd), T, None, y)
+    Y = host(y).reshape(T, rows)
+    for t in (0, 5, 23):
+        yt = empty(rows, np.float32)
+        lq.lq_q8_matvec(W, dev(xq[t]), dev(xd[t]), None, yt)
+        sync()
+        assert_close(Y[t], host(yt), f"token {t}")
+
+
 # ------------------------------------------------------------------ output head
 @pytest.mark.parametrize("vocab,hidden,norm,cap", [
     (1000, 2816, True, 30.0),    # the Gemma-4 head width, ragged row count
