@@ -90,6 +90,10 @@ def _load(path):
     L.orc_q8_block_dots.argtypes = [_P, _I64, _I64, _P, _P]
     L.orc_q8_matvec.argtypes = [_P, _P, _I64, _I64, _P, _P, _P, _P]
     L.orc_q8_matmul.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P]
+    L.orc_q4_0_dequant.argtypes = [_P, _I64, _P]
+    L.orc_q6_k_dequant.argtypes = [_P, _I64, _P]
+    L.orc_q4_0_matvec.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
+    L.orc_q6_k_matvec.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
     L.orc_rmsnorm.argtypes = [_P, _I64, _P, _D, _P]
     L.orc_rope_table.argtypes = [_I64, _I64, _D, _P, _P]
     L.orc_rope_table_freqs.argtypes = [_I64, _I64, _D, _P, _P, _P]
@@ -184,6 +188,33 @@ def q8_matmul(wq, wd, xq, xd, residual=None):
     res = None if residual is None else _c(residual, np.float32)
     y = np.empty((T, rows), dtype=np.float32)
     lib().orc_q8_matmul(_ptr(wq), _ptr(wd), rows, cols, _ptr(xq), _ptr(xd), T, _ptr(res), _ptr(y))
+    return y
+
+
+# ---------------------------------------------------------------- other GGML formats
+_QK = {"q4_0": (32, 18), "q6_k": (256, 210)}   # values and bytes per GGML block
+
+
+def q_dequant(fmt, blocks, n):
+    """GGML blocks (uint8, n values' worth) -> float64 values."""
+    per, nbytes = _QK[fmt]
+    blocks = _c(blocks, np.uint8)
+    assert n % per == 0 and blocks.size == n // per * nbytes
+    w = np.empty(n, dtype=np.float64)
+    getattr(lib(), f"orc_{fmt}_dequant")(_ptr(blocks), n, _ptr(w))
+    return w
+
+
+def q_matvec(fmt, blocks, rows, cols, xq, xd, residual=None):
+    """Q4_0 / Q6_K weight (GGML blocks, row-major) times a Q8_0 activation."""
+    per, nbytes = _QK[fmt]
+    blocks = _c(blocks, np.uint8)
+    assert cols % per == 0 and blocks.size == rows * (cols // per) * nbytes
+    xq = _c(xq, np.int8)
+    xd = _c(xd, np.uint16)
+    res = None if residual is None else _c(residual, np.float32)
+    y = np.empty(rows, dtype=np.float32)
+    getattr(lib(), f"orc_{fmt}_matvec")(_ptr(blocks), rows, cols, _ptr(xq), _ptr(xd), _ptr(res), _ptr(y))
     return y
 
 

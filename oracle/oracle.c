@@ -196,6 +196,118 @@ void orc_q8_matmul(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t c
 }
 
 /* ======================================================================== */
+/* Other GGML weight formats against Q8_0 activations                       */
+/* ======================================================================== */
+
+/* [CUR] section 4 (the MoE kernel of the current path runs on Q6_K weights)
+ * and [TGT] section 8 (Q1: candle keeps GGML block order) name GGML's Q4_0
+ * and Q6_K beside Q8_0 without their bit layouts.  The layouts here are
+ * GGML's published block definitions as this oracle reads them (blocks in
+ * order, f16 little-endian):
+ *   Q4_0: 18 bytes per 32 values: f16 d, then 16 code bytes.  Byte j holds
+ *         value j in its low nibble and value j+16 in its high nibble;
+ *         w = d * (n - 8).
+ *   Q6_K: 210 bytes per 256 values: ql[128], qh[64], int8 sc[16], f16 d.
+ *         Value i, with h = i/128, g = (i%128)/32, l = i%32, takes its low 4
+ *         bits from ql[64h + 32(g%2) + l] (the low nibble for g < 2, the high
+ *         one for g >= 2) and its high 2 bits from bits 2g and 2g+1 of
+ *         qh[32h + l]; w = d * sc[i/16] * (q - 32).
+ * The product with a Q8_0 activation takes the int8 x int8 path of [LAT]
+ * Current Design: exact int32 dots over each run of values that share their
+ * scales (a Q4_0 block; 16 values of Q6_K, which sit inside one activation
+ * block), times those scales. */
+static void q4_0_codes(const uint8_t* blk, int8_t* q, double* d)
+{
+    *d = (double)orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    for (int j = 0; j < 16; ++j) {
+        q[j] = (int8_t)((blk[2 + j] & 0x0F) - 8);
+        q[j + 16] = (int8_t)((blk[2 + j] >> 4) - 8);
+    }
+}
+
+static void q6_k_codes(const uint8_t* blk, int8_t* q, double* d, int8_t* sc)
+{
+    const uint8_t* ql = blk;
+    const uint8_t* qh = blk + 128;
+    for (int k = 0; k < 16; ++k) sc[k] = (int8_t)blk[192 + k];
+    *d = (double)orc_f16_to_f32((uint16_t)(blk[208] | (blk[209] << 8)));
+    for (int i = 0; i < 256; ++i) {
+        const int h = i / 128, g = (i % 128) / 32, l = i % 32;
+        const uint8_t lb = ql[64 * h + 32 * (g % 2) + l];
+        const int lo = g < 2 ? (lb & 0x0F) : (lb >> 4);
+        const int hi = (qh[32 * h + l] >> (2 * g)) & 3;
+        q[i] = (int8_t)((lo | (hi << 4)) - 32);
+    }
+}
+
+/* Dequantized values (for pins): n values from consecutive blocks. */
+void orc_q4_0_dequant(const uint8_t* blocks, int64_t n, double* w)
+{
+    int8_t q[32];
+    double d;
+    for (int64_t b = 0; b < n / 32; ++b) {
+        q4_0_codes(blocks + 18 * b, q, &d);
+        for (int i = 0; i < 32; ++i) w[32 * b + i] = d * (double)q[i];
+    }
+}
+
+void orc_q6_k_dequant(const uint8_t* blocks, int64_t n, double* w)
+{
+    int8_t q[256], sc[16];
+    double d;
+    for (int64_t b = 0; b < n / 256; ++b) {
+        q6_k_codes(blocks + 210 * b, q, &d, sc);
+        for (int i = 0; i < 256; ++i) w[256 * b + i] = d * (double)sc[i / 16] * (double)q[i];
+    }
+}
+
+/* y[r] = residual[r] + sum over blocks of d_w * d_x * dot (Q4_0 weights,
+ * row-major GGML blocks [rows, cols/32]); double, in block order. */
+void orc_q4_0_matvec(const uint8_t* blocks, int64_t rows, int64_t cols, const int8_t* xq,
+                     const uint16_t* xd, const float* residual, float* y)
+{
+    const int64_t nb = cols / 32;
+    int8_t q[32];
+    double d;
+    for (int64_t r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            q4_0_codes(blocks + 18 * (r * nb + b), q, &d);
+            int32_t dot = 0;
+            for (int i = 0; i < 32; ++i) dot += (int32_t)q[i] * (int32_t)xq[32 * b + i];
+            acc += d * (double)orc_f16_to_f32(xd[b]) * (double)dot;
+        }
+        if (residual) acc += (double)residual[r];
+        y[r] = (float)acc;
+    }
+}
+
+/* The same for Q6_K weights (GGML blocks [rows, cols/256]): one int32 dot
+ * per 16 values, times d * sc and the scale of the activation block that
+ * holds them. */
+void orc_q6_k_matvec(const uint8_t* blocks, int64_t rows, int64_t cols, const int8_t* xq,
+                     const uint16_t* xd, const float* residual, float* y)
+{
+    const int64_t nsb = cols / 256;
+    int8_t q[256], sc[16];
+    double d;
+    for (int64_t r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < nsb; ++b) {
+            q6_k_codes(blocks + 210 * (r * nsb + b), q, &d, sc);
+            for (int k = 0; k < 16; ++k) {
+                const int64_t c0 = 256 * b + 16 * k;
+                int32_t dot = 0;
+                for (int i = 0; i < 16; ++i) dot += (int32_t)q[16 * k + i] * (int32_t)xq[c0 + i];
+                acc += d * (double)sc[k] * (double)orc_f16_to_f32(xd[c0 / 32]) * (double)dot;
+            }
+        }
+        if (residual) acc += (double)residual[r];
+        y[r] = (float)acc;
+    }
+}
+
+/* ======================================================================== */
 /* Norms, RoPE, activation                                                  */
 /* ======================================================================== */
 

@@ -47,6 +47,14 @@ void orc_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t c
 void orc_q8_matmul(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
                    const int8_t* xq, const uint16_t* xd, int64_t T, const float* residual, float* y);
 
+/* ---- other GGML weight formats (GGML blocks, row-major) ------------------ */
+void orc_q4_0_dequant(const uint8_t* blocks, int64_t n, double* w);
+void orc_q6_k_dequant(const uint8_t* blocks, int64_t n, double* w);
+void orc_q4_0_matvec(const uint8_t* blocks, int64_t rows, int64_t cols, const int8_t* xq,
+                     const uint16_t* xd, const float* residual, float* y);
+void orc_q6_k_matvec(const uint8_t* blocks, int64_t rows, int64_t cols, const int8_t* xq,
+                     const uint16_t* xd, const float* residual, float* y);
+
 /* ---- norms, RoPE, activation --------------------------------------------- */
 /* y = gamma * x / sqrt(mean(x^2) + eps); gamma == NULL means unit weight. */
 void orc_rmsnorm(const float* x, int64_t n, const float* gamma, double eps, float* y);

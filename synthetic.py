@@ -62,6 +62,33 @@ def q8_weight(rng, rows, cols):
     return qs, d.astype(np.float16).view(np.uint16)
 
 
+def q4_0_blocks(rng, rows, cols):
+    """GGML Q4_0 blocks uint8 [rows, cols/32, 18]: f16 scale bytes (little
+    endian; |N(0, 0.02)|/8, so d*(n-8) spreads like the Q8_0 weights) then 16
+    random code bytes."""
+    nb = cols // 32
+    blk = np.empty((rows, nb, 18), np.uint8)
+    d = (np.abs(rng.normal(0.0, 0.02, size=(rows, nb))) / 8.0).astype(np.float16).view(np.uint16)
+    blk[..., 0] = d & 0xFF
+    blk[..., 1] = d >> 8
+    blk[..., 2:] = rng.integers(0, 256, size=(rows, nb, 16), dtype=np.uint8)
+    return blk
+
+
+def q6_k_blocks(rng, rows, cols):
+    """GGML Q6_K blocks uint8 [rows, cols/256, 210]: 192 random bytes of
+    low/high code bits, 16 random int8 sub-scales (the full range), then the
+    f16 super-scale bytes (|N(0, 1)| * 2e-5, so weights spread about 0.02;
+    many are f16-subnormal)."""
+    nsb = cols // 256
+    blk = np.empty((rows, nsb, 210), np.uint8)
+    blk[..., :208] = rng.integers(0, 256, size=(rows, nsb, 208), dtype=np.uint8)
+    d = (np.abs(rng.normal(0.0, 1.0, size=(rows, nsb))) * 2e-5).astype(np.float16).view(np.uint16)
+    blk[..., 208] = d & 0xFF
+    blk[..., 209] = d >> 8
+    return blk
+
+
 # The output head of the Gemma-4 shape the pages quote (vocab 262144, hidden 2816).
 HEAD = dict(vocab=262144, hidden=2816, eps=1e-6, softcap=30.0)
 

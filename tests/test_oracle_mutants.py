@@ -23,11 +23,24 @@ ALL_PINS = [
     pins.pin_rmsnorm, pins.pin_rope, pins.pin_silu, pins.pin_attention, pins.pin_moe_route,
     pins.pin_moe_block, lambda: pins.pin_layer(0, 1), lambda: pins.pin_layer(1, 1),
     lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head, pins.pin_gelu,
-    pins.pin_attention_softcap, pins.pin_rope_freqs, pins.pin_matmul,
+    pins.pin_attention_softcap, pins.pin_rope_freqs, pins.pin_matmul, pins.pin_q4_0, pins.pin_q6_k,
 ]
 
 # (name, text in oracle.c, replacement)
 MUTANTS = [
+    ("q4_high_nibble_dropped", "q[j + 16] = (int8_t)((blk[2 + j] >> 4) - 8);",
+     "q[j + 16] = (int8_t)((blk[2 + j] & 0x0F) - 8);"),
+    ("q4_offset", "q[j] = (int8_t)((blk[2 + j] & 0x0F) - 8);", "q[j] = (int8_t)((blk[2 + j] & 0x0F) - 7);"),
+    ("q6_qh_shift", "const int hi = (qh[32 * h + l] >> (2 * g)) & 3;", "const int hi = (qh[32 * h + l] >> g) & 3;"),
+    ("q6_ql_half", "const uint8_t lb = ql[64 * h + 32 * (g % 2) + l];",
+     "const uint8_t lb = ql[64 * h + 32 * (g / 2) + l];"),
+    ("q6_offset", "q[i] = (int8_t)((lo | (hi << 4)) - 32);", "q[i] = (int8_t)((lo | (hi << 4)) - 31);"),
+    ("q6_scale_by_32", "w[256 * b + i] = d * (double)sc[i / 16] * (double)q[i];",
+     "w[256 * b + i] = d * (double)sc[i / 32] * (double)q[i];"),
+    ("q6_matvec_scale", "acc += d * (double)sc[k] * (double)orc_f16_to_f32(xd[c0 / 32]) * (double)dot;",
+     "acc += d * (double)sc[k / 2] * (double)orc_f16_to_f32(xd[c0 / 32]) * (double)dot;"),
+    ("q6_matvec_act_block", "acc += d * (double)sc[k] * (double)orc_f16_to_f32(xd[c0 / 32]) * (double)dot;",
+     "acc += d * (double)sc[k] * (double)orc_f16_to_f32(xd[(256 * b) / 32]) * (double)dot;"),
     ("matmul_token_stride", "orc_q8_matvec(wq, wd, rows, cols, xq + t * cols, xd + t * (cols / 32),",
      "orc_q8_matvec(wq, wd, rows, cols, xq + t, xd + t * (cols / 32),"),
     ("rope_factor_multiplies", "if (factors) inv_freq = inv_freq / (double)factors[i];",

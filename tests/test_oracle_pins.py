@@ -377,6 +377,108 @@ def test_matmul():
     pin_matmul()
 
 
+def pin_q4_0():
+    # layout: d = 1, byte j = j | (15 - j) << 4 -> values j - 8 (j < 16) in the
+    # low nibbles, then 7 - (j - 16) in the high ones (value j + 16 of byte j)
+    blk = np.zeros(18, np.uint8)
+    blk[0:2] = [0x00, 0x3C]                       # f16 1.0
+    blk[2:] = [j | ((15 - j) << 4) for j in range(16)]
+    want = np.array([j - 8 for j in range(16)] + [7 - j for j in range(16)], np.float64)
+    assert np.array_equal(oracle.q_dequant("q4_0", blk, 32), want)
+    # the scale multiplies: f16 0.5, and the smallest subnormal 2^-24
+    blk[0:2] = [0x00, 0x38]
+    assert np.array_equal(oracle.q_dequant("q4_0", blk, 32), 0.5 * want)
+    blk[0:2] = [0x01, 0x00]
+    assert np.array_equal(oracle.q_dequant("q4_0", blk, 32), 2.0 ** -24 * want)
+    # the matvec equals the pinned Q8_0 matvec of the same codes (n - 8 as int8)
+    rng = np.random.default_rng(31)
+    rows, cols = 12, 160
+    b = synthetic.q4_0_blocks(rng, rows, cols)
+    code = b[..., 2:]
+    q8 = np.concatenate([(code & 15).astype(np.int16) - 8, (code >> 4).astype(np.int16) - 8], axis=-1)
+    q8 = q8.reshape(rows, cols).astype(np.int8)
+    d = (b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8))
+    xq = rng.integers(-127, 128, cols).astype(np.int8)
+    xd = (np.abs(rng.standard_normal(cols // 32)) * 0.05).astype(np.float16).view(np.uint16)
+    res = rng.standard_normal(rows).astype(np.float32)
+    got = oracle.q_matvec("q4_0", b, rows, cols, xq, xd, residual=res)
+    assert np.array_equal(got, oracle.q8_matvec(q8, d, xq, xd, residual=res))
+
+
+def _q6_block(d_bits=0x3C00):
+    blk = np.zeros(210, np.uint8)
+    blk[192:208] = 1
+    blk[208:210] = [d_bits & 0xFF, d_bits >> 8]
+    return blk
+
+
+def pin_q6_k():
+    # all code bits zero: q = 0 - 32 everywhere
+    blk = _q6_block()
+    assert np.array_equal(oracle.q_dequant("q6_k", blk, 256), np.full(256, -32.0))
+    # hand-placed bits, values derived from the layout statement:
+    #   ql[0] = 0x5A: low nibble 10 -> value 0, high nibble 5 -> value 64
+    #   qh[0] = 0b11100100: bit pairs 0,1,2,3 -> values 0, 32, 64, 96
+    #   ql[32] = 0x0C: low nibble 12 -> value 32 (high nibble 0 -> value 96)
+    #   second half: ql[64 + 5] = 0xF3 -> value 128 + 5 (3) and 128 + 69 (15);
+    #   qh[32 + 5] = 0b00000010 -> value 128 + 5 gets high bits 2
+    blk[0] = 0x5A
+    blk[128] = 0b11100100
+    blk[32] = 0x0C
+    blk[64 + 5] = 0xF3
+    blk[128 + 32 + 5] = 0b00000010
+    w = oracle.q_dequant("q6_k", blk, 256)
+    want = np.full(256, -32.0)
+    want[0] = 10 + (0 << 4) - 32
+    want[32] = 12 + (1 << 4) - 32
+    want[64] = 5 + (2 << 4) - 32
+    want[96] = 0 + (3 << 4) - 32
+    want[128 + 5] = 3 + (2 << 4) - 32
+    want[128 + 69] = 15 - 32
+    assert np.array_equal(w, want)
+    # sub-scales run in value order, 16 values each; d multiplies
+    blk = _q6_block(0x3800)                        # d = 0.5
+    blk[192:208] = np.arange(16, dtype=np.int8).view(np.uint8) - 7
+    w = oracle.q_dequant("q6_k", blk, 256)
+    assert np.array_equal(w, 0.5 * np.repeat(np.arange(16) - 7.0, 16) * -32.0)
+    # every stored code bit reaches exactly one value, and each value gets
+    # six distinct bit weights (1, 2, 4, 8 from ql, 16, 32 from qh)
+    base = oracle.q_dequant("q6_k", _q6_block(), 256)
+    seen = np.zeros((256, 6), int)
+    for byte in range(192):
+        for bit in range(8):
+            blk = _q6_block()
+            blk[byte] = 1 << bit
+            diff = oracle.q_dequant("q6_k", blk, 256) - base
+            hit = np.nonzero(diff)[0]
+            assert hit.size == 1, (byte, bit)
+            k = int(round(np.log2(diff[hit[0]])))
+            assert diff[hit[0]] == 2.0 ** k and 0 <= k < 6
+            seen[hit[0], k] += 1
+    assert np.array_equal(seen, np.ones((256, 6), int))
+    # the matvec is the int8 path: per 16 values an exact dot, times d * sc
+    # and the activation block's scale; equal to the f64 dot of the values
+    rng = np.random.default_rng(32)
+    rows, cols = 6, 512
+    b = synthetic.q6_k_blocks(rng, rows, cols)
+    xq = rng.integers(-127, 128, cols).astype(np.int8)
+    xd = (np.abs(rng.standard_normal(cols // 32)) * 0.05).astype(np.float16).view(np.uint16)
+    x = xq.astype(np.float64) * np.repeat(xd.view(np.float16).astype(np.float64), 32)
+    W = oracle.q_dequant("q6_k", b, rows * cols).reshape(rows, cols)
+    got = oracle.q_matvec("q6_k", b, rows, cols, xq, xd)
+    assert np.allclose(got, W @ x, rtol=1e-6, atol=1e-9)
+    got = oracle.q_matvec("q6_k", b, rows, cols, xq, xd, residual=np.ones(rows, np.float32))
+    assert np.allclose(got, W @ x + 1.0, rtol=1e-6, atol=1e-9)
+
+
+def test_q4_0():
+    pin_q4_0()
+
+
+def test_q6_k():
+    pin_q6_k()
+
+
 def test_rmsnorm():
     pin_rmsnorm()
 
