@@ -286,6 +286,33 @@ def measure_moe(name, steps, torch):
             "frac": round(gbs / HBM_PEAK_GBS, 4), "replicas": R, "graph": True}
 
 
+def graph_us(torch, calls, steps):
+    """calls(stream) issues one round of launches; it is run once eagerly,
+    captured as a HIP graph on a side stream and replayed `steps` times, so
+    no host launch overhead is timed.  Returns microseconds per replay."""
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        calls(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            calls(stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
 def measure_matmul(T, steps, torch):
     """The multi-token Q8_0 matmul (int8 MFMA) on the 8B-like layer's four
     projections for a batch of T tokens, over R distinct replicas of the
@@ -312,24 +339,18 @@ def measure_matmul(T, steps, torch):
         xs[k] = (torch.randint(-127, 128, (T, c), dtype=torch.int8, device="cuda", generator=gen),
                  (torch.rand(T, c // 32, device="cuda", generator=gen) * 0.05).half().view(torch.int16),
                  torch.empty(T, r, device="cuda"))
-    stream = torch.cuda.current_stream()
     nws = max(lq.lq_q8_matmul_workspace_size(r, c, T) for r, c in shapes.values())
     work = torch.empty(max(nws, 4), dtype=torch.uint8, device="cuda")
     res = {}
     total_us = 0.0
     for k, (r, c) in shapes.items():
         xq, xd, y = xs[k]
-        for ws in reps[:2]:
-            lq.lq_q8_matmul(ws[k][0], xq, xd, T, None, y, work, nws, stream=stream)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
+
+        def calls(stream):
             for ws in reps:
                 lq.lq_q8_matmul(ws[k][0], xq, xd, T, None, y, work, nws, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (steps * R)
+
+        us = graph_us(torch, calls, steps) / R
         nbytes = r * c * 34 // 32 + T * c * 34 // 32 + T * r * 4
         res[k] = {"rows": r, "cols": c, "us": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
                   "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4),
@@ -340,6 +361,64 @@ def measure_matmul(T, steps, torch):
     return {"workload": f"q8_matmul_t{T}_qwen3_8b_like_h4096", "tokens": T, "replicas": R,
             "us_four_projections": round(total_us, 3), "us_per_token_four_projections": round(total_us / T, 3),
             "per_matrix": res, "mfma": "v_mfma_i32_32x32x32_i8"}
+
+
+def measure_ggml_formats(steps, torch):
+    """The Q4_0 and Q6_K weight matvecs (Q8_0 activation) on the 8B-like
+    layer's four projection shapes, one token, over R distinct weight
+    replicas (>= 2 GB, beyond the Infinity Cache).  Algorithmic bytes per
+    call: the format's weight bytes (Q4_0 18 and Q6_K 210 per 32 / 256
+    values) + the Q8_0 input + the f32 output."""
+    import q8_matvec_gqa_amd as lq
+    cfg = synthetic.layer_cfg("qwen3_8b_like_h4096")
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    shapes = {"qkv": (nq * hd + 2 * nkv * hd, H), "o": (H, nq * hd), "gate_up": (2 * I, H), "down": (H, I)}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5000)
+    out = {}
+    for fmt, bpv in (("q4_0", 18 / 32), ("q6_k", 210 / 256)):
+        per_rep = sum(r * c * bpv for r, c in shapes.values())
+        R = max(2, math.ceil(2e9 / per_rep))
+
+        def rbytes(*shape):
+            return torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=gen)
+
+        def f16(shape, scale):
+            return (torch.randn(shape, device="cuda", generator=gen).abs() * scale).half().view(torch.int16)
+
+        reps = []
+        for _ in range(R):
+            ws = {}
+            for k, (r, c) in shapes.items():
+                if fmt == "q4_0":
+                    ws[k] = lq.q4_0_weight(rbytes(r, c // 2), f16((r, c // 32), 0.02 / 8), r, c)
+                else:
+                    ws[k] = lq.q6_k_weight(rbytes(r, c // 2), rbytes(r, c // 4), rbytes(r, c // 16).view(torch.int8),
+                                           f16((r, c // 256), 2e-5), r, c)
+            reps.append(ws)
+        call = lq.lq_q4_0_matvec if fmt == "q4_0" else lq.lq_q6_k_matvec
+        res = {}
+        total = 0.0
+        for k, (r, c) in shapes.items():
+            xq = torch.randint(-127, 128, (c,), dtype=torch.int8, device="cuda", generator=gen)
+            xd = (torch.rand(c // 32, device="cuda", generator=gen) * 0.05).half().view(torch.int16)
+            y = torch.empty(r, device="cuda")
+
+            def calls(stream):
+                for ws in reps:
+                    call(ws[k], xq, xd, None, y, stream=stream)
+
+            us = graph_us(torch, calls, steps) / R
+            nbytes = r * c * bpv + c * 34 / 32 + 4 * r
+            res[k] = {"rows": r, "cols": c, "us": round(us, 3), "GBps": round(nbytes / (us * 1e3), 1),
+                      "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4)}
+            total += us
+            log(f"{fmt}_matvec {k:8s} {r}x{c}: {us:.2f} us, {res[k]['GBps']:.1f} GB/s")
+        out[fmt] = {"workload": f"{fmt}_matvec_qwen3_8b_like_h4096", "replicas": R,
+                    "us_four_projections": round(total, 3), "per_matrix": res}
+        del reps
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_head(steps, torch):
@@ -626,6 +705,8 @@ def main():
         result["lm_head"] = measure_head(max(10, args.steps // 2), torch)
         torch.cuda.empty_cache()
         result["q8_matmul"] = measure_matmul(32, max(5, args.steps // 10), torch)
+        torch.cuda.empty_cache()
+        result["ggml_formats"] = measure_ggml_formats(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)

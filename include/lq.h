@@ -75,6 +75,37 @@ typedef struct lq_q8_weight {
     int64_t cols;
 } lq_q8_weight;
 
+/* Other GGML weight formats ([CUR] section 4: the current path's MoE kernel
+ * runs on Q6_K weights; [TGT] section 8, Q1: GGML block order).  Device
+ * layout, SoA (lq_q4_0_pack_ggml / lq_q6_k_pack_ggml convert GGML blocks):
+ *   Q4_0: qs  uint8 [rows, cols/2]: each 32-value block's 16 code bytes in
+ *             GGML order (byte j: value j in the low nibble, value j+16 in
+ *             the high nibble), 16-byte aligned;
+ *         d   f16 bits [rows, cols/32].     w = d * (n - 8).
+ *   Q6_K: ql  uint8 [rows, cols/2] and qh uint8 [rows, cols/4] (the low 4
+ *             and high 2 code bits, each 256-value super-block's bytes in
+ *             GGML order), both 16-byte aligned;
+ *         sc  int8 [rows, cols/16] (one scale per 16 values), 8-byte aligned;
+ *         d   f16 bits [rows, cols/256].   w = d * sc[i/16] * (q - 32),
+ *         where value i (h = i/128, g = (i%128)/32, l = i%32) takes its low
+ *         bits from ql[64h + 32(g%2) + l] (low nibble for g < 2, high for
+ *         g >= 2) and its high bits from bits 2g, 2g+1 of qh[32h + l]. */
+typedef struct lq_q4_0_weight {
+    const uint8_t*  qs;
+    const uint16_t* d;
+    int64_t rows;
+    int64_t cols;
+} lq_q4_0_weight;
+
+typedef struct lq_q6_k_weight {
+    const uint8_t*  ql;
+    const uint8_t*  qh;
+    const int8_t*   sc;
+    const uint16_t* d;
+    int64_t rows;
+    int64_t cols;
+} lq_q6_k_weight;
+
 /* ---------------------------------------------------------------- misc */
 int32_t     lq_version(void);
 const char* lq_status_string(lq_status s);
@@ -86,6 +117,15 @@ const char* lq_last_error(void);
  * [rows, cols/32].  All pointers are HOST memory.  cols % 32 == 0. */
 lq_status lq_q8_pack_ggml(const void* blocks, int64_t rows, int64_t cols,
                           int8_t* qs, uint16_t* d);
+
+/* Host-only helpers: GGML Q4_0 blocks (18 bytes per 32 values: f16 d, 16
+ * code bytes) and Q6_K blocks (210 bytes per 256 values: ql[128], qh[64],
+ * int8 sc[16], f16 d) of a [rows, cols] matrix, row-major, into the SoA
+ * arrays above.  All pointers are HOST memory.  cols % 32 (Q4_0) or % 256
+ * (Q6_K) == 0. */
+lq_status lq_q4_0_pack_ggml(const void* blocks, int64_t rows, int64_t cols, uint8_t* qs, uint16_t* d);
+lq_status lq_q6_k_pack_ggml(const void* blocks, int64_t rows, int64_t cols, uint8_t* ql, uint8_t* qh,
+                            int8_t* sc, uint16_t* d);
 
 /* Host-only helper: RoPE cos/sin tables [max_ctx, head_dim/2] for angle
  * pos * theta^(-2i/head_dim), computed in double and stored as float
@@ -140,6 +180,21 @@ lq_status lq_q8_matvec(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t
  * to dots (device int32 [rows, cols/32]), computed by the same device code. */
 lq_status lq_q8_block_dots(const lq_q8_weight* w, const int8_t* x_qs, int32_t* dots,
                            void* stream);
+
+/* Q4_0 and Q6_K weight matvecs against a Q8_0 activation, on the int8 x
+ * int8 path of [LAT] Current Design: an exact int32 dot over each run of
+ * values that share their scales (a Q4_0 block; 16 Q6_K values, which lie in
+ * one activation block), then
+ *   Q4_0: y[r] = residual[r] + sum_b d[r,b] * f16(x_d[b]) * dot
+ *   Q6_K: y[r] = residual[r] + sum_k d[r,k/16] * sc[r,k] * f16(x_d[k/2]) * dot
+ * with the float sum in an unspecified order.  Weights as above, cols <=
+ * 16384 (LQ_ERR_UNSUPPORTED beyond).  x_qs: device int8 [cols], 16-byte
+ * aligned; x_d: device f16 bits [cols/32]; y, residual: device f32 [rows]
+ * (residual may be NULL and may alias y).  rows == 0 is a no-op. */
+lq_status lq_q4_0_matvec(const lq_q4_0_weight* w, const int8_t* x_qs, const uint16_t* x_d,
+                         const float* residual, float* y, void* stream);
+lq_status lq_q6_k_matvec(const lq_q6_k_weight* w, const int8_t* x_qs, const uint16_t* x_d,
+                         const float* residual, float* y, void* stream);
 
 /* Multi-token Q8_0 matmul: the decode matvec for T tokens at once (prefill,
  * batched decode), each weight byte read once per 32 tokens ([LAT] Current

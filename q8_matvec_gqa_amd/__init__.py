@@ -48,6 +48,14 @@ class lq_q8_weight(C.Structure):
     _fields_ = [("qs", _P), ("d", _P), ("rows", _I64), ("cols", _I64)]
 
 
+class lq_q4_0_weight(C.Structure):
+    _fields_ = [("qs", _P), ("d", _P), ("rows", _I64), ("cols", _I64)]
+
+
+class lq_q6_k_weight(C.Structure):
+    _fields_ = [("ql", _P), ("qh", _P), ("sc", _P), ("d", _P), ("rows", _I64), ("cols", _I64)]
+
+
 class lq_moe_desc(C.Structure):
     _fields_ = [("hidden", _I64), ("ffn", _I64), ("n_experts", _I64), ("top_k", _I64),
                 ("w_gate_up", lq_q8_weight), ("w_down", lq_q8_weight), ("expert_scale", _P)]
@@ -80,11 +88,15 @@ _SIGS = {
     "lq_status_string": (C.c_char_p, [_I32]),
     "lq_last_error": (C.c_char_p, []),
     "lq_q8_pack_ggml": (_I32, [_P, _I64, _I64, _P, _P]),
+    "lq_q4_0_pack_ggml": (_I32, [_P, _I64, _I64, _P, _P]),
+    "lq_q6_k_pack_ggml": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
     "lq_rope_table": (_I32, [_I64, _I64, C.c_double, _P, _P]),
     "lq_q8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "lq_rmsnorm_q8": (_I32, [_P, _I64, _I64, _P, _F, _P, _P, _P]),
     "lq_swiglu_q8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "lq_q8_matvec": (_I32, [_W, _P, _P, _P, _P, _P]),
+    "lq_q4_0_matvec": (_I32, [C.POINTER(lq_q4_0_weight), _P, _P, _P, _P, _P]),
+    "lq_q6_k_matvec": (_I32, [C.POINTER(lq_q6_k_weight), _P, _P, _P, _P, _P]),
     "lq_q8_block_dots": (_I32, [_W, _P, _P, _P]),
     "lq_rmsnorm_rope": (_I32, [_P, _I64, _I64, _I64, _P, _F, _P, _P, _I64, _I64, _P]),
     "lq_kv_append": (_I32, [_P, _P, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
@@ -176,6 +188,28 @@ def lq_q8_pack_ggml(blocks, rows, cols, qs, d, check=True):
     return _check(_lib.lq_q8_pack_ggml(_ptr(blocks), rows, cols, _ptr(qs), _ptr(d)), check)
 
 
+def lq_q4_0_pack_ggml(blocks, rows, cols, qs, d, check=True):
+    return _check(_lib.lq_q4_0_pack_ggml(_ptr(blocks), rows, cols, _ptr(qs), _ptr(d)), check)
+
+
+def lq_q6_k_pack_ggml(blocks, rows, cols, ql, qh, sc, d, check=True):
+    return _check(_lib.lq_q6_k_pack_ggml(_ptr(blocks), rows, cols, _ptr(ql), _ptr(qh), _ptr(sc), _ptr(d)), check)
+
+
+def q4_0_weight(qs, d, rows, cols):
+    """lq_q4_0_weight over device arrays qs [rows, cols/2] and d [rows, cols/32]."""
+    w = lq_q4_0_weight(_ptr(qs), _ptr(d), rows, cols)
+    w._keep = (qs, d)
+    return w
+
+
+def q6_k_weight(ql, qh, sc, d, rows, cols):
+    """lq_q6_k_weight over device arrays ql, qh, sc and d (see include/lq.h)."""
+    w = lq_q6_k_weight(_ptr(ql), _ptr(qh), _ptr(sc), _ptr(d), rows, cols)
+    w._keep = (ql, qh, sc, d)
+    return w
+
+
 def lq_rope_table(max_ctx, head_dim, theta, cos_out, sin_out, check=True):
     return _check(_lib.lq_rope_table(max_ctx, head_dim, theta, _ptr(cos_out), _ptr(sin_out)), check)
 
@@ -202,6 +236,16 @@ def lq_swiglu_q8(gate_up, n_rows, ffn, qs, d, stream=None, check=True):
 def lq_q8_matvec(w, x_qs, x_d, residual, y, stream=None, check=True):
     return _check(_lib.lq_q8_matvec(_ref(w), _ptr(x_qs), _ptr(x_d), _ptr(residual), _ptr(y),
                                     _stream(stream)), check)
+
+
+def lq_q4_0_matvec(w, x_qs, x_d, residual, y, stream=None, check=True):
+    return _check(_lib.lq_q4_0_matvec(_ref(w), _ptr(x_qs), _ptr(x_d), _ptr(residual), _ptr(y), _stream(stream)),
+                  check)
+
+
+def lq_q6_k_matvec(w, x_qs, x_d, residual, y, stream=None, check=True):
+    return _check(_lib.lq_q6_k_matvec(_ref(w), _ptr(x_qs), _ptr(x_d), _ptr(residual), _ptr(y), _stream(stream)),
+                  check)
 
 
 def lq_q8_block_dots(w, x_qs, dots, stream=None, check=True):

@@ -74,6 +74,40 @@ extern "C" lq_status lq_q8_pack_ggml(const void* blocks, int64_t rows, int64_t c
     return LQ_OK;
 }
 
+extern "C" lq_status lq_q4_0_pack_ggml(const void* blocks, int64_t rows, int64_t cols, uint8_t* qs,
+                                       uint16_t* d) {
+    if (rows < 0 || cols <= 0 || cols % 32)
+        return fail(LQ_ERR_SHAPE, "lq_q4_0_pack_ggml: rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    if (rows == 0) return LQ_OK;
+    if (!blocks || !qs || !d) return fail(LQ_ERR_NULL, "lq_q4_0_pack_ggml: NULL pointer");
+    const uint8_t* src = static_cast<const uint8_t*>(blocks);
+    const int64_t nb = rows * (cols / 32);
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = src + 18 * b;
+        d[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+        memcpy(qs + 16 * b, blk + 2, 16);
+    }
+    return LQ_OK;
+}
+
+extern "C" lq_status lq_q6_k_pack_ggml(const void* blocks, int64_t rows, int64_t cols, uint8_t* ql, uint8_t* qh,
+                                       int8_t* sc, uint16_t* d) {
+    if (rows < 0 || cols <= 0 || cols % 256)
+        return fail(LQ_ERR_SHAPE, "lq_q6_k_pack_ggml: rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    if (rows == 0) return LQ_OK;
+    if (!blocks || !ql || !qh || !sc || !d) return fail(LQ_ERR_NULL, "lq_q6_k_pack_ggml: NULL pointer");
+    const uint8_t* src = static_cast<const uint8_t*>(blocks);
+    const int64_t nb = rows * (cols / 256);
+    for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = src + 210 * b;
+        memcpy(ql + 128 * b, blk, 128);
+        memcpy(qh + 64 * b, blk + 128, 64);
+        memcpy(sc + 16 * b, blk + 192, 16);
+        d[b] = (uint16_t)(blk[208] | (blk[209] << 8));
+    }
+    return LQ_OK;
+}
+
 extern "C" lq_status lq_rope_table_freqs(int64_t max_ctx, int64_t head_dim, double theta,
                                          const float* freq_factors, float* cos_out, float* sin_out) {
     if (max_ctx < 0 || head_dim <= 0 || head_dim % 2 || !(theta > 0.0))

@@ -77,6 +77,55 @@ def test_matvec_validation():
     assert st(lq.lq_q8_block_dots, w, A, None) == lq.LQ_ERR_NULL
 
 
+def test_ggml_format_validation():
+    w4 = lq.lq_q4_0_weight(A, A, 10, 64)
+    assert st(lq.lq_q4_0_matvec, None, A, A, None, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q4_0_matvec, lq.lq_q4_0_weight(A, A, 10, 48), A, A, None, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q4_0_matvec, lq.lq_q4_0_weight(A, A, 10, 16384 + 32), A, A, None, A) == lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_q4_0_matvec, lq.lq_q4_0_weight(A + 8, A, 10, 64), A, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q4_0_matvec, lq.lq_q4_0_weight(None, A, 10, 64), A, A, None, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q4_0_matvec, w4, A + 1, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q4_0_matvec, w4, A, A, None, None) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q4_0_matvec, lq.lq_q4_0_weight(None, None, 0, 64), None, None, None, None) == lq.LQ_OK
+    w6 = lq.lq_q6_k_weight(A, A, A, A, 10, 512)
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(A, A, A, A, 10, 384), A, A, None, A) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(A, A, A, A, 10, 16384 + 256), A, A, None, A) == \
+        lq.LQ_ERR_UNSUPPORTED
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(A, A + 8, A, A, 10, 512), A, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(A, A, A + 4, A, 10, 512), A, A, None, A) == lq.LQ_ERR_ALIGN
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(A, A, None, A, 10, 512), A, A, None, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q6_k_matvec, w6, A, None, None, A) == lq.LQ_ERR_NULL
+    assert st(lq.lq_q6_k_matvec, lq.lq_q6_k_weight(None, None, None, None, 0, 256), None, None, None, None) == \
+        lq.LQ_OK
+
+
+def test_ggml_format_pack_host():
+    """The pack helpers move every GGML block field to its SoA array (host
+    memory only), and reject bad shapes."""
+    import synthetic
+    rng = np.random.default_rng(9)
+    rows, cols = 5, 512
+    b4 = synthetic.q4_0_blocks(rng, rows, cols)
+    qs = np.zeros((rows, cols // 2), np.uint8)
+    d = np.zeros((rows, cols // 32), np.uint16)
+    lq.lq_q4_0_pack_ggml(b4, rows, cols, qs, d)
+    assert np.array_equal(qs.reshape(rows, cols // 32, 16), b4[..., 2:])
+    assert np.array_equal(d, b4[..., 0].astype(np.uint16) | (b4[..., 1].astype(np.uint16) << 8))
+    b6 = synthetic.q6_k_blocks(rng, rows, cols)
+    ql = np.zeros((rows, cols // 2), np.uint8)
+    qh = np.zeros((rows, cols // 4), np.uint8)
+    sc = np.zeros((rows, cols // 16), np.int8)
+    d6 = np.zeros((rows, cols // 256), np.uint16)
+    lq.lq_q6_k_pack_ggml(b6, rows, cols, ql, qh, sc, d6)
+    assert np.array_equal(ql.reshape(rows, cols // 256, 128), b6[..., :128])
+    assert np.array_equal(qh.reshape(rows, cols // 256, 64), b6[..., 128:192])
+    assert np.array_equal(sc.view(np.uint8).reshape(rows, cols // 256, 16), b6[..., 192:208])
+    assert np.array_equal(d6, b6[..., 208].astype(np.uint16) | (b6[..., 209].astype(np.uint16) << 8))
+    assert lq.lq_q4_0_pack_ggml(b4, rows, 48, qs, d, check=False) == lq.LQ_ERR_SHAPE
+    assert lq.lq_q6_k_pack_ggml(b6, rows, 384, ql, qh, sc, d6, check=False) == lq.LQ_ERR_SHAPE
+    assert lq.lq_q6_k_pack_ggml(None, rows, 512, ql, qh, sc, d6, check=False) == lq.LQ_ERR_NULL
+
+
 def test_matmul_validation_and_workspace():
     w = lq.lq_q8_weight(A, A, 4096, 4096)
     need = lq.lq_q8_matmul_workspace_size(4096, 4096, 32)

@@ -387,6 +387,90 @@ def test_q8_matmul_matches_matvec_rows():
         assert_close(Y[t], host(yt), f"token {t}")
 
 
+# ------------------------------------------------------------------ Q4_0 / Q6_K weights
+def ggml_weight(fmt, r, rows, cols):
+    """Random GGML blocks, packed on the host by the library's helper and
+    uploaded: (blocks, lq weight struct)."""
+    if fmt == "q4_0":
+        b = synthetic.q4_0_blocks(r, rows, cols)
+        qs = np.zeros((rows, cols // 2), np.uint8)
+        d = np.zeros((rows, cols // 32), np.uint16)
+        lq.lq_q4_0_pack_ggml(b, rows, cols, qs, d)
+        return b, lq.q4_0_weight(dev(qs), dev(d), rows, cols)
+    b = synthetic.q6_k_blocks(r, rows, cols)
+    ql = np.zeros((rows, cols // 2), np.uint8)
+    qh = np.zeros((rows, cols // 4), np.uint8)
+    sc = np.zeros((rows, cols // 16), np.int8)
+    d = np.zeros((rows, cols // 256), np.uint16)
+    lq.lq_q6_k_pack_ggml(b, rows, cols, ql, qh, sc, d)
+    return b, lq.q6_k_weight(dev(ql), dev(qh), dev(sc), dev(d), rows, cols)
+
+
+def run_qk(fmt, W, xq, xd, res, y):
+    (lq.lq_q4_0_matvec if fmt == "q4_0" else lq.lq_q6_k_matvec)(W, xq, xd, res, y)
+    sync()
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [
+    ("q4_0", 4096, 4096),      # the 8B-like O projection
+    ("q4_0", 24576, 4096),     # 8B-like gate_up
+    ("q4_0", 4096, 12288),     # 8B-like down (6 steps per row)
+    ("q4_0", 1000, 2816),      # Gemma width, ragged rows, a partial step
+    ("q4_0", 33, 32),          # one block
+    ("q4_0", 5, 16384),        # widest rows (8 steps)
+    ("q6_k", 4096, 4096),
+    ("q6_k", 24576, 4096),
+    ("q6_k", 4096, 12288),     # 3 steps, one row per wave
+    ("q6_k", 1000, 2816),      # 11 super-blocks: 44 of 64 lanes
+    ("q6_k", 7, 256),          # one super-block
+    ("q6_k", 9, 16384),        # widest rows (4 steps)
+])
+def test_ggml_format_matvec(fmt, rows, cols):
+    r = rng(rows * 3 + cols + len(fmt))
+    b, W = ggml_weight(fmt, r, rows, cols)
+    xq = r.integers(-127, 128, cols).astype(np.int8)
+    xd = (np.abs(r.standard_normal(cols // 32)) * 0.05).astype(np.float16).view(np.uint16)
+    res = synthetic.activations(r, rows)
+    y = empty(rows, np.float32)
+    run_qk(fmt, W, dev(xq), dev(xd), dev(res), y)
+    assert_close(host(y), oracle.q_matvec(fmt, b, rows, cols, xq, xd, residual=res), f"{fmt} matvec")
+    # no residual, and the residual aliasing y
+    run_qk(fmt, W, dev(xq), dev(xd), None, y)
+    want = oracle.q_matvec(fmt, b, rows, cols, xq, xd)
+    assert_close(host(y), want, f"{fmt} matvec, no residual")
+    y2 = dev(res)
+    run_qk(fmt, W, dev(xq), dev(xd), y2, y2)
+    assert_close(host(y2), want + res, f"{fmt} matvec, in place")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q6_k"])
+def test_ggml_format_extreme_codes(fmt):
+    """All-extreme codes (nibble 0 and 15; 6-bit 0 and 63), int8 sub-scales
+    at -128 and 127 and +-127 activations: the int32 dots and the offsets
+    at their limits."""
+    r = rng(11 if fmt == "q4_0" else 12)
+    rows, cols = 64, 2048
+    b, _ = ggml_weight(fmt, r, rows, cols)
+    if fmt == "q4_0":
+        b[..., 2:] = np.where(r.random(b[..., 2:].shape) < 0.5, 0x00, 0xFF)
+        qs = np.ascontiguousarray(b[..., 2:]).reshape(rows, cols // 2)
+        d = b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8)
+        W = lq.q4_0_weight(dev(qs), dev(d), rows, cols)
+    else:
+        b[..., :192] = np.where(r.random(b[..., :192].shape) < 0.5, 0x00, 0xFF)
+        b[..., 192:208] = np.where(r.random(b[..., 192:208].shape) < 0.5, 0x80, 0x7F)
+        ql = np.ascontiguousarray(b[..., :128]).reshape(rows, cols // 2)
+        qh = np.ascontiguousarray(b[..., 128:192]).reshape(rows, cols // 4)
+        sc = np.ascontiguousarray(b[..., 192:208]).view(np.int8).reshape(rows, cols // 16)
+        d = b[..., 208].astype(np.uint16) | (b[..., 209].astype(np.uint16) << 8)
+        W = lq.q6_k_weight(dev(ql), dev(qh), dev(sc), dev(d), rows, cols)
+    xq = np.where(r.random(cols) < 0.5, -127, 127).astype(np.int8)
+    xd = np.full(cols // 32, 0x2C00, np.uint16)       # f16 1/16
+    y = empty(rows, np.float32)
+    run_qk(fmt, W, dev(xq), dev(xd), None, y)
+    assert_close(host(y), oracle.q_matvec(fmt, b, rows, cols, xq, xd), f"{fmt} extremes")
+
+
 # ------------------------------------------------------------------ output head
 @pytest.mark.parametrize("vocab,hidden,norm,cap", [
     (1000, 2816, True, 30.0),    # the Gemma-4 head width, ragged row count
