@@ -50,9 +50,10 @@ struct HeadRows {
     int4 w[kHeadRPW][ST];
 };
 
-// Unconditional loads: chunks past the row's end and rows past the end read
-// the first 16 bytes of the matrix (one cache line; their n values are zero
-// or the row is never stored).
+// Unconditional loads: chunks past the row's end read the row's last chunk
+// (the same 16 bytes a live lane reads, so the request merges with it; their
+// n values are zero) and rows past the end read the first 16 bytes of the
+// matrix (never stored).
 template <int ST>
 __device__ __forceinline__ void head_load(const HeadArgs& a, int64_t grp, int lane, int c16, HeadRows<ST>& R) {
 #pragma unroll
@@ -62,7 +63,7 @@ __device__ __forceinline__ void head_load(const HeadArgs& a, int64_t grp, int la
 #pragma unroll
         for (int st = 0; st < ST; ++st) {
             const int ch = st * kWave + lane;
-            const int64_t off = (live && ch < c16) ? r * a.hidden + 8 * ch : 0;
+            const int64_t off = live ? r * a.hidden + 8 * (ch < c16 ? ch : c16 - 1) : 0;
             R.w[i][st] = load_stream16(a.w + off);
         }
     }
@@ -107,14 +108,19 @@ __global__ __launch_bounds__(kHeadWaves * 64, 2) void k_lm_head(HeadArgs a) {
 
     // prologue loads first (x and gamma, 16 bytes per thread and step), then
     // the first row group's weights
+    // (threads past the vector issue no load: every workgroup reads x, and
+    // clamped duplicates would pile onto one cache line)
     constexpr int XP = (kHeadMaxHidden / 4 + NT - 1) / NT;
     float4 xv[XP], gv[XP];
 #pragma unroll
     for (int k = 0; k < XP; ++k) {
         const int i4 = threadIdx.x + NT * k;
-        const int ic = i4 < n4 ? i4 : 0;
-        xv[k] = reinterpret_cast<const float4*>(a.x)[ic];
-        gv[k] = a.gamma ? reinterpret_cast<const float4*>(a.gamma)[ic] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        xv[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        gv[k] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if (i4 < n4) {
+            xv[k] = reinterpret_cast<const float4*>(a.x)[i4];
+            if (a.gamma) gv[k] = reinterpret_cast<const float4*>(a.gamma)[i4];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     HeadRows<ST> A, B;

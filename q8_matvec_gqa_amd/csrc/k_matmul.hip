@@ -76,9 +76,10 @@ struct MmStage {
 // tid takes chunk idx % kMmCPR of row idx / kMmCPR (idx = tid + 256j), so
 // each wave instruction reads whole contiguous row runs; scales likewise
 // (consecutive lanes read one row's consecutive scales).  Chunks of blocks
-// past be, rows past the matrix and tokens past T read valid memory (block
-// 0, the last row, the last token) and are zeroed through their scales or
-// never stored.
+// past be and rows past the matrix read valid memory of their own row (block
+// 0, the last row) and are zeroed through their scales or never stored.
+// Tokens past T load nothing (every workgroup reads X, so clamped duplicates
+// would pile onto a few cache lines): their LDS rows and scales are zero.
 __device__ __forceinline__ void mm_load(const MmArgs& a, int row0, int bs, int be, int tid, MmStage& S) {
     const int nb = a.cols >> 5;
     const int c = tid % kMmCPR;
@@ -87,18 +88,18 @@ __device__ __forceinline__ void mm_load(const MmArgs& a, int row0, int bs, int b
     for (int j = 0; j < kMmNL; ++j) {
         const int r = (tid + kMmNT * j) / kMmCPR;
         const int row = row0 + r < a.rows ? row0 + r : a.rows - 1;
-        const int tok = r < a.T ? r : a.T - 1;
         S.w[j] = load_stream16(a.wq + (int64_t)row * a.cols + coff);
-        S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)tok * a.cols + coff);
+        S.x[j] = make_int4(0, 0, 0, 0);
+        if (r < a.T) S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)r * a.cols + coff);
     }
 #pragma unroll
     for (int i = 0; i < kMmNS; ++i) {
         const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
         const int b = bs + u < be ? bs + u : 0;
         const int row = row0 + rr < a.rows ? row0 + rr : a.rows - 1;
-        const int tok = rr < a.T ? rr : a.T - 1;
         S.dw[i] = a.wd[(int64_t)row * nb + b];
-        S.dx[i] = a.xd[(int64_t)tok * nb + b];
+        S.dx[i] = 0;
+        if (rr < a.T) S.dx[i] = a.xd[(int64_t)rr * nb + b];
     }
 }
 
