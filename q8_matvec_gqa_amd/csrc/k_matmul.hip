@@ -138,14 +138,28 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
     float acc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    // Batches in a rotated order: tile t starts at batch t mod nbt, so the
+    // workgroups that run side by side read different parts of X (every
+    // workgroup reads all of X; in lockstep they would all hit the same few
+    // cache lines at once).  The order is fixed per tile (deterministic).
+    const int nbt = (b1 - b0 + kMmKB - 1) / kMmKB;
+    const int rot = (int)((blockIdx.x / a.ks) % nbt);
     MmStage S;
-    mm_load(a, row0, b0, b0 + kMmKB < b1 ? b0 + kMmKB : b1, tid, S);
-    for (int bs = b0; bs < b1; bs += kMmKB) {
-        const int be = bs + kMmKB < b1 ? bs + kMmKB : b1;
-        if (bs > b0) __syncthreads();        // every wave is done with the previous batch
+    {
+        const int bs = b0 + kMmKB * rot;
+        mm_load(a, row0, bs, bs + kMmKB < b1 ? bs + kMmKB : b1, tid, S);
+    }
+    for (int i = 0; i < nbt; ++i) {
+        const int j = i + rot < nbt ? i + rot : i + rot - nbt;
+        const int bs = b0 + kMmKB * j, be = bs + kMmKB < b1 ? bs + kMmKB : b1;
+        if (i > 0) __syncthreads();          // every wave is done with the previous batch
         mm_store(a, bs, be, tid, S, wl, xl, dwl, dxl);
         __syncthreads();
-        if (be < b1) mm_load(a, row0, be, be + kMmKB < b1 ? be + kMmKB : b1, tid, S);
+        if (i + 1 < nbt) {
+            const int jn = j + 1 < nbt ? j + 1 : 0;
+            const int bn = b0 + kMmKB * jn;
+            mm_load(a, row0, bn, bn + kMmKB < b1 ? bn + kMmKB : b1, tid, S);
+        }
         // this wave's blocks of the batch: wave, wave + 4, wave + 8, ...; per
         // block an int8 MFMA (the block dots) and an f16 MFMA whose only
         // nonzero k term forms the scale products f16(dX[t]) * f16(dW[r])
