@@ -421,6 +421,64 @@ def measure_ggml_formats(steps, torch):
     return out
 
 
+def measure_moe_formats(steps, torch):
+    """The index-driven matvec on Q6_K and Q4_0 experts at the MoE workload
+    (16 tokens, top-8 of 128 experts): the gate/up projection [2*ffn, hidden]
+    per expert, ids from a softmax top-k of N(0,1) logits, R replicas of all
+    experts (>= 1.5 GB).  Algorithmic bytes: the touched experts' weights in
+    the format, plus the per-token Q8_0 input and the f32 output."""
+    import q8_matvec_gqa_amd as lq
+    c = dict(synthetic.MOE_WORKLOADS["moe_e128_top8_t16"])
+    H, I, E, T, k = c["hidden"], c["ffn"], c["n_experts"], c["tokens"], c["top_k"]
+    rows, cols = 2 * I, H
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6000)
+    out = {}
+    for fmt, bpv in (("q6_k", 210 / 256), ("q4_0", 18 / 32)):
+        expert_bytes = rows * cols * bpv
+        R = max(2, math.ceil(1.5e9 / (E * expert_bytes)))
+
+        def rbytes(*shape):
+            return torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=gen)
+
+        def f16(shape, scale):
+            return (torch.randn(shape, device="cuda", generator=gen).abs() * scale).half().view(torch.int16)
+
+        reps = []
+        for _ in range(R):
+            n = E * rows
+            if fmt == "q4_0":
+                W = lq.q4_0_weight(rbytes(n, cols // 2), f16((n, cols // 32), 0.02 / 8), rows, cols)
+            else:
+                W = lq.q6_k_weight(rbytes(n, cols // 2), rbytes(n, cols // 4), rbytes(n, cols // 16).view(torch.int8),
+                                   f16((n, cols // 256), 2e-5), rows, cols)
+            logits = torch.randn(T, E, device="cuda", generator=gen)
+            ids = torch.topk(torch.softmax(logits.double(), dim=1), k, dim=1).indices.to(torch.int32).contiguous()
+            reps.append((W, ids, int(torch.unique(ids).numel())))
+        xq = torch.randint(-127, 128, (T, cols), dtype=torch.int8, device="cuda", generator=gen)
+        xd = (torch.rand(T, cols // 32, device="cuda", generator=gen) * 0.05).half().view(torch.int16)
+        y = torch.empty(T * k, rows, device="cuda")
+        nws = lq.lq_moe_workspace_size(T, k, E)
+        work = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        call = lq.lq_moe_q4_0_matvec_id if fmt == "q4_0" else lq.lq_moe_q6_k_matvec_id
+
+        def calls(stream):
+            for W, ids, _ in reps:
+                call(W, E, xq, xd, 0, ids, T, k, y, work, nws, stream=stream)
+
+        us = graph_us(torch, calls, steps) / R
+        touched = sum(t for _, _, t in reps) / R
+        nbytes = touched * expert_bytes + T * cols * 34 / 32 + T * k * rows * 4
+        out[fmt] = {"workload": f"moe_e128_top8_t16_gate_up_{fmt}", "replicas": R, "us": round(us, 3),
+                    "touched_experts": round(touched, 1), "GBps": round(nbytes / (us * 1e3), 1),
+                    "frac": round(nbytes / (us * 1e3) / HBM_PEAK_GBS, 4)}
+        log(f"moe {fmt} gate/up id-matvec {rows}x{cols} x {E} experts: {us:.2f} us, "
+            f"{touched:.1f} touched, {out[fmt]['GBps']:.1f} GB/s")
+        del reps, work
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_head(steps, torch):
     """The output head (final norm, f16 vocab projection, softcap) at the
     Gemma-4 shape: vocab x hidden f16 weights (1.5 GB, beyond the Infinity
@@ -707,6 +765,8 @@ def main():
         result["q8_matmul"] = measure_matmul(32, max(5, args.steps // 10), torch)
         torch.cuda.empty_cache()
         result["ggml_formats"] = measure_ggml_formats(max(5, args.steps // 5), torch)
+        torch.cuda.empty_cache()
+        result["moe_ggml_formats"] = measure_moe_formats(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)

@@ -313,6 +313,19 @@ lq_status lq_moe_q8_matvec_id(const lq_q8_weight* w, int64_t n_experts,
                               const int32_t* ids, int64_t T, int64_t k, float* y,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same index-driven matvec with Q4_0 or Q6_K expert weights (the
+ * current path's MoE kernel runs on Q6_K, [CUR] section 4), on the int8
+ * path of lq_q4_0_matvec / lq_q6_k_matvec.  w describes ONE expert (rows,
+ * cols); the arrays hold n_experts experts back to back, expert e's row r
+ * being row e*rows + r of each array.  cols <= 8192; ids, workspace, x and
+ * y as for lq_moe_q8_matvec_id. */
+lq_status lq_moe_q4_0_matvec_id(const lq_q4_0_weight* w, int64_t n_experts, const int8_t* x_qs,
+                                const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                int64_t k, float* y, void* workspace, size_t workspace_bytes, void* stream);
+lq_status lq_moe_q6_k_matvec_id(const lq_q6_k_weight* w, int64_t n_experts, const int8_t* x_qs,
+                                const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                int64_t k, float* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Weighted sum over slots ([TGT] section 3.2 weighted_sum):
  * out[t, r] = sum_{s<k} w[t, s] * y[t, s, r], slots summed in order s = 0..k-1.
  * y: device f32 [T, k, rows]; w: device f32 [T, k]; out: device f32 [T, rows]. */

@@ -110,6 +110,10 @@ _SIGS = {
     "lq_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "lq_moe_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lq_moe_q8_matvec_id": (_I32, [_W, _I64, _P, _P, _I32, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "lq_moe_q4_0_matvec_id": (_I32, [C.POINTER(lq_q4_0_weight), _I64, _P, _P, _I32, _P, _I64, _I64, _P, _P, _SZ,
+                                      _P]),
+    "lq_moe_q6_k_matvec_id": (_I32, [C.POINTER(lq_q6_k_weight), _I64, _P, _P, _I32, _P, _I64, _I64, _P, _P, _SZ,
+                                      _P]),
     "lq_moe_weighted_sum": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
     "lq_moe_block_workspace_size": (_SZ, [C.POINTER(lq_moe_desc), _I64]),
     "lq_moe_block": (_I32, [C.POINTER(lq_moe_desc), _P, _P, _I64, _P, C.POINTER(lq_moe_taps), _P, _SZ,
@@ -307,6 +311,18 @@ def lq_moe_q8_matvec_id(w, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y, works
     return _check(_lib.lq_moe_q8_matvec_id(_ref(w), n_experts, _ptr(x_qs), _ptr(x_d), x_per_slot, _ptr(ids),
                                            T, k, _ptr(y), _ptr(workspace), workspace_bytes,
                                            _stream(stream)), check)
+
+
+def lq_moe_q4_0_matvec_id(w, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y, workspace, workspace_bytes,
+                          stream=None, check=True):
+    return _check(_lib.lq_moe_q4_0_matvec_id(_ref(w), n_experts, _ptr(x_qs), _ptr(x_d), x_per_slot, _ptr(ids), T, k,
+                                             _ptr(y), _ptr(workspace), workspace_bytes, _stream(stream)), check)
+
+
+def lq_moe_q6_k_matvec_id(w, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y, workspace, workspace_bytes,
+                          stream=None, check=True):
+    return _check(_lib.lq_moe_q6_k_matvec_id(_ref(w), n_experts, _ptr(x_qs), _ptr(x_d), x_per_slot, _ptr(ids), T, k,
+                                             _ptr(y), _ptr(workspace), workspace_bytes, _stream(stream)), check)
 
 
 def lq_moe_weighted_sum(y, w, T, k, rows, out, stream=None, check=True):

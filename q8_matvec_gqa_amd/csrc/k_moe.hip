@@ -18,6 +18,7 @@
 
 #include "lq_device.h"
 #include "lq_internal.h"
+#include "lq_qk.h"
 
 namespace lq {
 
@@ -319,6 +320,58 @@ __global__ __launch_bounds__(256) void k_moe_matvec_id(const int8_t* __restrict_
     }
 }
 
+// ---- index-driven Q4_0 / Q6_K matvec -------------------------------------------
+// The MoE kernel of the current path runs on Q6_K expert weights ("Current
+// Inference Path -- Architecture Map", section 4).  Same decomposition as
+// k_moe_matvec_id: blockIdx.x = active-expert index * rowblocks + row block;
+// each wave holds the units (lq_qk.h) of RPW rows of its expert in VGPRs and
+// applies them to every listed slot, reading the slot's Q8_0 activation from
+// memory.  Experts are stacked: expert e's row r is row e*rows + r of the
+// arrays.  Dead units and rows read the expert's first unit (never used).
+template <int FMT, int ST, int RPW>
+__global__ __launch_bounds__(256) void k_moe_qk_matvec_id(QkMat m, int rows, int cols, const int8_t* __restrict__ xq,
+                                                          const uint16_t* __restrict__ xd, int x_per_slot, int k,
+                                                          const int32_t* __restrict__ wsbase, int E, int rowblocks,
+                                                          float* __restrict__ y) {
+    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
+    const int ai = blockIdx.x / rowblocks, rb = blockIdx.x - ai * rowblocks;
+    if (ai >= *ws.n_active()) return;
+    const int e = ws.active()[ai];
+    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r0 = (rb * 4 + wave) * RPW;
+    if (r0 >= rows) return;
+    const int units = qk_units<FMT>(cols);
+    const int64_t er = (int64_t)e * rows;
+    QkUnit<FMT> U[RPW][ST];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+            const int r = r0 + i, u = st * 64 + lane;
+            const bool live = r < rows && u < units;
+            qk_load_unit(m, cols, er + (live ? r : 0), live ? u : 0, U[i][st]);
+        }
+    for (int si = s0; si < s1; ++si) {
+        const int slot = ws.slots()[si];
+        const int64_t xrow = x_per_slot ? slot : slot / k;
+        const int8_t* xr = xq + xrow * cols;
+        const uint16_t* xdr = xd + xrow * (cols >> 5);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+                const int u = st * 64 + lane;
+                if (u < units) acc += qk_unit_dot_h(U[i][st], u, xr, xdr);
+            }
+            acc = wave_sum(acc);
+            const int r = r0 + i;
+            if (lane == 0 && r < rows) y[(int64_t)slot * rows + r] = acc;
+        }
+    }
+}
+
 // ---- gate/up id-matvec with SwiGLU and the Q8_0 of h in the epilogue --------
 // blockIdx.x = active-expert index * (ffn/32) + h block.  A workgroup of 16
 // waves owns one 32-value block of h for its expert: wave w holds the gate
@@ -518,6 +571,35 @@ lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t row
     return launch_id_gathered(wq, wd, rows, cols, n_experts, xq, xd, x_per_slot, k, ws, y, s);
 }
 
+template <int FMT, int ST, int RPW>
+static void launch_qk_id_st(hipStream_t s, const QkMat& m, int rows, int cols, int E, const int8_t* xq,
+                            const uint16_t* xd, int x_per_slot, int k, const int32_t* ws, float* y) {
+    const int rowblocks = (rows + 4 * RPW - 1) / (4 * RPW);
+    hipLaunchKernelGGL((k_moe_qk_matvec_id<FMT, ST, RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, m, rows,
+                       cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
+}
+
+// steps per row: Q4_0 up to 4, Q6_K up to 2 (cols <= 8192)
+template <int FMT>
+static lq_status launch_moe_qk_matvec_id(const QkMat& m, int64_t rows, int64_t cols, int64_t E, const int8_t* xq,
+                                         const uint16_t* xd, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                         int64_t k, float* y, void* ws, hipStream_t s) {
+    lq_status st = launch_gather(ids, T * k, E, ws, y, rows, nullptr, 0, s);
+    if (st != LQ_OK) return st;
+    const int32_t* w32 = static_cast<const int32_t*>(ws);
+    switch ((qk_units<FMT>((int)cols) + 63) / 64) {
+        case 1: launch_qk_id_st<FMT, 1, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
+        case 2: launch_qk_id_st<FMT, 2, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
+        default:
+            if constexpr (FMT == QK_Q4_0) {
+                launch_qk_id_st<FMT, 4, 1>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y);
+                break;
+            }
+            return fail(LQ_ERR_UNSUPPORTED, "moe matvec: cols > 8192");
+    }
+    return check_launch("moe_qk_matvec_id");
+}
+
 lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
                                   const int32_t* ids, const float* escale, int64_t E, float* out, hipStream_t s) {
     const int64_t n = T * rows;
@@ -581,6 +663,63 @@ extern "C" lq_status lq_moe_q8_matvec_id(const lq_q8_weight* w, int64_t n_expert
         return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
     return launch_moe_matvec_id(w->qs, w->d, w->rows, w->cols, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y,
                                 workspace, as_stream(stream));
+}
+
+// Shared argument checks of the Q4_0 / Q6_K id-matvecs (per = values per
+// block of the format).
+static lq_status check_moe_qk(const char* fn, int64_t rows, int64_t cols, int per, int64_t n_experts,
+                              const int8_t* x_qs, const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids,
+                              int64_t T, int64_t k, float* y, void* workspace, size_t workspace_bytes) {
+    if (rows < 0 || cols <= 0 || cols % per)
+        return fail(LQ_ERR_SHAPE, "%s: rows=%lld cols=%lld (cols %% %d == 0)", fn, (long long)rows, (long long)cols,
+                    per);
+    if (n_experts <= 0 || n_experts > kMoeMaxExperts)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: n_experts=%lld (1..%d)", fn, (long long)n_experts, kMoeMaxExperts);
+    if (cols > 8192 || rows > 0x7fffffffLL / 4)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: expert rows=%lld cols=%lld too large", fn, (long long)rows,
+                    (long long)cols);
+    if (T < 0 || k <= 0 || (x_per_slot != 0 && x_per_slot != 1))
+        return fail(LQ_ERR_SHAPE, "%s: T=%lld k=%lld x_per_slot=%d", fn, (long long)T, (long long)k, x_per_slot);
+    if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
+    if (T == 0 || rows == 0) return LQ_OK;
+    if (!x_qs || !x_d || !ids || !y) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(x_qs, 16) || !aligned(x_d, 2) || !aligned(ids, 4) || !aligned(y, 4))
+        return fail(LQ_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const size_t need = moe_ws_bytes(T, k, n_experts);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+        return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, workspace_bytes);
+    return LQ_OK;
+}
+
+extern "C" lq_status lq_moe_q4_0_matvec_id(const lq_q4_0_weight* w, int64_t n_experts, const int8_t* x_qs,
+                                           const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                           int64_t k, float* y, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+    const char* fn = "lq_moe_q4_0_matvec_id";
+    if (!w) return fail(LQ_ERR_NULL, "%s: NULL weight", fn);
+    lq_status st = check_moe_qk(fn, w->rows, w->cols, 32, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y, workspace,
+                                workspace_bytes);
+    if (st != LQ_OK || T == 0 || w->rows == 0) return st;
+    if (!w->qs || !w->d) return fail(LQ_ERR_NULL, "%s: NULL weight array", fn);
+    if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return fail(LQ_ERR_ALIGN, "%s: qs must be 16-byte aligned", fn);
+    return launch_moe_qk_matvec_id<QK_Q4_0>(QkMat{w->qs, nullptr, nullptr, w->d}, w->rows, w->cols, n_experts, x_qs,
+                                            x_d, x_per_slot, ids, T, k, y, workspace, as_stream(stream));
+}
+
+extern "C" lq_status lq_moe_q6_k_matvec_id(const lq_q6_k_weight* w, int64_t n_experts, const int8_t* x_qs,
+                                           const uint16_t* x_d, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                           int64_t k, float* y, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+    const char* fn = "lq_moe_q6_k_matvec_id";
+    if (!w) return fail(LQ_ERR_NULL, "%s: NULL weight", fn);
+    lq_status st = check_moe_qk(fn, w->rows, w->cols, 256, n_experts, x_qs, x_d, x_per_slot, ids, T, k, y,
+                                workspace, workspace_bytes);
+    if (st != LQ_OK || T == 0 || w->rows == 0) return st;
+    if (!w->ql || !w->qh || !w->sc || !w->d) return fail(LQ_ERR_NULL, "%s: NULL weight array", fn);
+    if (!aligned(w->ql, 16) || !aligned(w->qh, 16) || !aligned(w->sc, 8) || !aligned(w->d, 2))
+        return fail(LQ_ERR_ALIGN, "%s: ql and qh must be 16-byte aligned, sc 8-byte aligned", fn);
+    return launch_moe_qk_matvec_id<QK_Q6_K>(QkMat{w->ql, w->qh, w->sc, w->d}, w->rows, w->cols, n_experts, x_qs,
+                                            x_d, x_per_slot, ids, T, k, y, workspace, as_stream(stream));
 }
 
 extern "C" lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,

@@ -17,19 +17,16 @@
 //         d f16 [rows][cols/256], each 256-value super-block's arrays in GGML
 //         order.
 //
-// Mapping onto CDNA4.  A lane owns one unit of a row per step: a Q4_0 block
-// (one 16-byte load: 32 values) or a quarter of a Q6_K super-block (two
-// 16-byte ql loads and one qh load: the 64 values l..l+15 of each 32-value
-// quarter of one 128-value half).  Codes become signed int8 in registers
-// -- per byte (n | 0x80) - 8 (or q - 32 for Q6_K), then ^ 0x80, which never
-// borrows across bytes -- and v_dot4_i32_i8 against the activation codes in
-// LDS gives the exact int32 dots.  A wave owns RPW rows per group; row
+// Mapping onto CDNA4.  A lane owns one unit of a row per step (lq_qk.h: a
+// Q4_0 block or a quarter of a Q6_K super-block) and its exact int32 dots
+// with the activation codes in LDS.  A wave owns RPW rows per group; row
 // groups are double-buffered (the next group's loads in flight while the
 // current one is consumed) and a DPP wave sum finishes each row.  Every
 // workgroup copies the activation into LDS first; its loads go out before
 // the first weights.
 #include "lq_device.h"
 #include "lq_internal.h"
+#include "lq_qk.h"
 
 namespace lq {
 
@@ -39,13 +36,8 @@ constexpr int kQkWaves = 8;
 constexpr int kQkNT = kQkWaves * 64;
 constexpr int kQkMaxCols = 16384;
 
-enum { QK_Q4_0 = 0, QK_Q6_K = 1 };
-
 struct QkArgs {
-    const uint8_t* q0;      // Q4_0 qs / Q6_K ql
-    const uint8_t* q1;      // Q6_K qh
-    const int8_t* sc;       // Q6_K sub-scales
-    const uint16_t* d;      // Q4_0 block scales / Q6_K super-scales
+    QkMat m;
     int rows, cols;
     const int8_t* xq;       // [cols]
     const uint16_t* xd;     // [cols/32]
@@ -53,100 +45,11 @@ struct QkArgs {
     float* y;               // [rows]
 };
 
-template <int FMT>
-struct QkUnit;
-template <>
-struct QkUnit<QK_Q4_0> {
-    int4 q;
-    uint32_t d;
-};
-template <>
-struct QkUnit<QK_Q6_K> {
-    int4 l0, l1, h;
-    uint2 sc;
-    uint32_t d;
-};
-
-template <int FMT>
-__host__ __device__ __forceinline__ int qk_units(int cols) { return FMT == QK_Q4_0 ? cols >> 5 : cols >> 6; }
-
-// Loads of unit u of a row.  Dead units and rows read the first bytes of
+// Loads of unit u of a row; dead units and rows read the first bytes of
 // row 0 (never used).
-__device__ __forceinline__ void qk_load(const QkArgs& a, int row, int u, bool live, QkUnit<QK_Q4_0>& U) {
-    const int64_t r = live ? row : 0;
-    const int uu = live ? u : 0;
-    U.q = load_stream16(a.q0 + r * (a.cols >> 1) + 16 * uu);
-    U.d = a.d[r * (a.cols >> 5) + uu];
-}
-__device__ __forceinline__ void qk_load(const QkArgs& a, int row, int u, bool live, QkUnit<QK_Q6_K>& U) {
-    const int64_t r = live ? row : 0;
-    const int uu = live ? u : 0;
-    const int sb = uu >> 2, h = (uu >> 1) & 1, p = uu & 1;
-    const uint8_t* ql = a.q0 + r * (a.cols >> 1) + sb * 128 + h * 64 + p * 16;
-    U.l0 = load_stream16(ql);
-    U.l1 = load_stream16(ql + 32);
-    U.h = load_stream16(a.q1 + r * (a.cols >> 2) + sb * 64 + h * 32 + p * 16);
-    U.sc = *reinterpret_cast<const uint2*>(a.sc + r * (a.cols >> 4) + sb * 16 + h * 8);
-    U.d = a.d[r * (a.cols >> 8) + sb];
-}
-
-// signed int8 from 4 packed unsigned bytes minus an offset (< 0x80) without
-// borrows between bytes
-template <uint32_t OFF>
-__device__ __forceinline__ int sub_bytes(uint32_t v) {
-    return (int)(((v | 0x80808080u) - OFF) ^ 0x80808080u);
-}
-
-__device__ __forceinline__ int dot16(const int (&w)[4], const int4 x) {
-    int s = __builtin_amdgcn_sdot4(w[0], x.x, 0, false);
-    s = __builtin_amdgcn_sdot4(w[1], x.y, s, false);
-    s = __builtin_amdgcn_sdot4(w[2], x.z, s, false);
-    return __builtin_amdgcn_sdot4(w[3], x.w, s, false);
-}
-
-// Contribution of unit u (live) to its row, in f32.  xl: activation codes in
-// LDS, xs: activation scales in LDS (f32).
-__device__ __forceinline__ float qk_unit_dot(const QkUnit<QK_Q4_0>& U, int u, const int8_t* xl, const float* xs) {
-    const int4 x0 = *reinterpret_cast<const int4*>(xl + 32 * u);
-    const int4 x1 = *reinterpret_cast<const int4*>(xl + 32 * u + 16);
-    const uint32_t q[4] = {(uint32_t)U.q.x, (uint32_t)U.q.y, (uint32_t)U.q.z, (uint32_t)U.q.w};
-    int lo[4], hi[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo[i] = sub_bytes<0x08080808u>(q[i] & 0x0F0F0F0Fu);
-        hi[i] = sub_bytes<0x08080808u>((q[i] >> 4) & 0x0F0F0F0Fu);
-    }
-    const int dot = dot16(hi, x1) + dot16(lo, x0);
-    return (f16_to_f32(U.d) * xs[u]) * (float)dot;
-}
-__device__ __forceinline__ float qk_unit_dot(const QkUnit<QK_Q6_K>& U, int u, const int8_t* xl, const float* xs) {
-    const int sb = u >> 2, h = (u >> 1) & 1, p = u & 1;
-    const int v0 = sb * 256 + h * 128 + p * 16;        // value of group 0, lane's first
-    const uint32_t L0[4] = {(uint32_t)U.l0.x, (uint32_t)U.l0.y, (uint32_t)U.l0.z, (uint32_t)U.l0.w};
-    const uint32_t L1[4] = {(uint32_t)U.l1.x, (uint32_t)U.l1.y, (uint32_t)U.l1.z, (uint32_t)U.l1.w};
-    const uint32_t H[4] = {(uint32_t)U.h.x, (uint32_t)U.h.y, (uint32_t)U.h.z, (uint32_t)U.h.w};
-    int g0[4], g1[4], g2[4], g3[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        g0[i] = sub_bytes<0x20202020u>((L0[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u));
-        g1[i] = sub_bytes<0x20202020u>((L1[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u));
-        g2[i] = sub_bytes<0x20202020u>(((L0[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u));
-        g3[i] = sub_bytes<0x20202020u>(((L1[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
-    }
-    const int d0 = dot16(g0, *reinterpret_cast<const int4*>(xl + v0));
-    const int d1 = dot16(g1, *reinterpret_cast<const int4*>(xl + v0 + 32));
-    const int d2 = dot16(g2, *reinterpret_cast<const int4*>(xl + v0 + 64));
-    const int d3 = dot16(g3, *reinterpret_cast<const int4*>(xl + v0 + 96));
-    // sub-scale of group g: byte p + 2g of the half's 8 scales
-    const uint32_t s01 = p ? U.sc.x >> 8 : U.sc.x, s23 = p ? U.sc.y >> 8 : U.sc.y;
-    const float c0 = (float)(int8_t)(s01 & 0xFF), c1 = (float)(int8_t)((s01 >> 16) & 0xFF);
-    const float c2 = (float)(int8_t)(s23 & 0xFF), c3 = (float)(int8_t)((s23 >> 16) & 0xFF);
-    const float* xsv = xs + (v0 >> 5);
-    float s = (c0 * xsv[0]) * (float)d0;
-    s = fmaf(c1 * xsv[1], (float)d1, s);
-    s = fmaf(c2 * xsv[2], (float)d2, s);
-    s = fmaf(c3 * xsv[3], (float)d3, s);
-    return f16_to_f32(U.d) * s;
+template <int FMT>
+__device__ __forceinline__ void qk_load(const QkArgs& a, int row, int u, bool live, QkUnit<FMT>& U) {
+    qk_load_unit(a.m, a.cols, live ? row : 0, live ? u : 0, U);
 }
 
 template <int FMT, int ST, int RPW>
@@ -304,7 +207,7 @@ extern "C" lq_status lq_q4_0_matvec(const lq_q4_0_weight* w, const int8_t* x_qs,
     if (st != LQ_OK || w->rows == 0) return st;
     if (!w->qs || !w->d) return fail(LQ_ERR_NULL, "%s: NULL weight array", fn);
     if (!aligned(w->qs, 16) || !aligned(w->d, 2)) return fail(LQ_ERR_ALIGN, "%s: qs must be 16-byte aligned", fn);
-    const QkArgs a{w->qs, nullptr, nullptr, w->d, (int)w->rows, (int)w->cols, x_qs, x_d, residual, y};
+    const QkArgs a{QkMat{w->qs, nullptr, nullptr, w->d}, (int)w->rows, (int)w->cols, x_qs, x_d, residual, y};
     dispatch_qk<QK_Q4_0>(a, as_stream(stream));
     return check_launch(fn);
 }
@@ -318,7 +221,7 @@ extern "C" lq_status lq_q6_k_matvec(const lq_q6_k_weight* w, const int8_t* x_qs,
     if (!w->ql || !w->qh || !w->sc || !w->d) return fail(LQ_ERR_NULL, "%s: NULL weight array", fn);
     if (!aligned(w->ql, 16) || !aligned(w->qh, 16) || !aligned(w->sc, 8) || !aligned(w->d, 2))
         return fail(LQ_ERR_ALIGN, "%s: ql and qh must be 16-byte aligned, sc 8-byte aligned", fn);
-    const QkArgs a{w->ql, w->qh, w->sc, w->d, (int)w->rows, (int)w->cols, x_qs, x_d, residual, y};
+    const QkArgs a{QkMat{w->ql, w->qh, w->sc, w->d}, (int)w->rows, (int)w->cols, x_qs, x_d, residual, y};
     dispatch_qk<QK_Q6_K>(a, as_stream(stream));
     return check_launch(fn);
 }

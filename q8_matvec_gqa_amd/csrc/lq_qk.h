@@ -1,0 +1,174 @@
+// lq_qk.h -- device decode of Q4_0 and Q6_K weight units, shared by the
+// dense matvec (k_qk.hip) and the index-driven MoE matvec (k_moe.hip).
+//
+// Layouts (SoA per matrix; GGML block order inside each array, as GGML's
+// Q4_0 / Q6_K blocks define it -- formats named in "Current Inference Path --
+// Architecture Map", section 4, and "Target Inference Architecture: hf2q on
+// mlx-native", section 8, Q1):
+//   Q4_0: qs [rows][cols/2], byte j of a 32-value block holds value j (low
+//         nibble) and value j+16 (high nibble); d f16 [rows][cols/32].
+//   Q6_K: ql [rows][cols/2], qh [rows][cols/4], sc int8 [rows][cols/16],
+//         d f16 [rows][cols/256]; value i of a 256-value super-block (h =
+//         i/128, g = (i%128)/32, l = i%32) has its low 4 bits in
+//         ql[64h + 32(g%2) + l] (low nibble for g < 2, high for g >= 2) and its
+//         high 2 bits at bits 2g, 2g+1 of qh[32h + l]; scale sc[i/16].
+//
+// A lane's unit: a Q4_0 block (32 values, one 16-byte load), or a quarter of
+// a Q6_K super-block: the 16 positions l = 16p..16p+15 of each 32-value
+// quarter g of half h (two 16-byte ql loads, one qh load; 64 values in four
+// groups of 16 at value offsets v0 + 32g).  Codes become signed int8 in
+// registers -- per byte (n | 0x80) - offset, then ^ 0x80, which never borrows
+// across bytes -- for exact v_dot4_i32_i8 dots with Q8_0 activation codes.
+#pragma once
+#include "lq_device.h"
+
+namespace lq {
+
+enum { QK_Q4_0 = 0, QK_Q6_K = 1 };
+
+template <int FMT>
+struct QkUnit;
+template <>
+struct QkUnit<QK_Q4_0> {
+    int4 q;
+    uint32_t d;
+};
+template <>
+struct QkUnit<QK_Q6_K> {
+    int4 l0, l1, h;
+    uint2 sc;
+    uint32_t d;
+};
+
+// One matrix's arrays (Q4_0 uses q0 = qs and d).
+struct QkMat {
+    const uint8_t* q0;      // Q4_0 qs / Q6_K ql
+    const uint8_t* q1;      // Q6_K qh
+    const int8_t* sc;       // Q6_K sub-scales
+    const uint16_t* d;      // Q4_0 block scales / Q6_K super-scales
+};
+
+template <int FMT>
+__host__ __device__ __forceinline__ int qk_units(int cols) { return FMT == QK_Q4_0 ? cols >> 5 : cols >> 6; }
+
+// Loads of unit u of row r.
+__device__ __forceinline__ void qk_load_unit(const QkMat& m, int cols, int64_t r, int u, QkUnit<QK_Q4_0>& U) {
+    U.q = load_stream16(m.q0 + r * (cols >> 1) + 16 * u);
+    U.d = m.d[r * (cols >> 5) + u];
+}
+__device__ __forceinline__ void qk_load_unit(const QkMat& m, int cols, int64_t r, int u, QkUnit<QK_Q6_K>& U) {
+    const int sb = u >> 2, h = (u >> 1) & 1, p = u & 1;
+    const uint8_t* ql = m.q0 + r * (cols >> 1) + sb * 128 + h * 64 + p * 16;
+    U.l0 = load_stream16(ql);
+    U.l1 = load_stream16(ql + 32);
+    U.h = load_stream16(m.q1 + r * (cols >> 2) + sb * 64 + h * 32 + p * 16);
+    U.sc = *reinterpret_cast<const uint2*>(m.sc + r * (cols >> 4) + sb * 16 + h * 8);
+    U.d = m.d[r * (cols >> 8) + sb];
+}
+
+template <uint32_t OFF>
+__device__ __forceinline__ int qk_sub_bytes(uint32_t v) {
+    return (int)(((v | 0x80808080u) - OFF) ^ 0x80808080u);
+}
+
+__device__ __forceinline__ int qk_dot16(const int (&w)[4], const int4 x) {
+    int s = __builtin_amdgcn_sdot4(w[0], x.x, 0, false);
+    s = __builtin_amdgcn_sdot4(w[1], x.y, s, false);
+    s = __builtin_amdgcn_sdot4(w[2], x.z, s, false);
+    return __builtin_amdgcn_sdot4(w[3], x.w, s, false);
+}
+
+// Q4_0: the exact int32 dot of the block with activation codes x_lo (values
+// 0..15 of the block) and x_hi (values 16..31).
+__device__ __forceinline__ int qk4_dot(const QkUnit<QK_Q4_0>& U, const int4 x_lo, const int4 x_hi) {
+    const uint32_t q[4] = {(uint32_t)U.q.x, (uint32_t)U.q.y, (uint32_t)U.q.z, (uint32_t)U.q.w};
+    int lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = qk_sub_bytes<0x08080808u>(q[i] & 0x0F0F0F0Fu);
+        hi[i] = qk_sub_bytes<0x08080808u>((q[i] >> 4) & 0x0F0F0F0Fu);
+    }
+    return qk_dot16(hi, x_hi) + qk_dot16(lo, x_lo);
+}
+
+// Q6_K: first value of unit u's group 0 (groups g at + 32g, 16 values each;
+// each group lies in the Q8_0 activation block (v0 >> 5) + g).
+__device__ __forceinline__ int qk6_v0(int u) { return (u >> 2) * 256 + ((u >> 1) & 1) * 128 + (u & 1) * 16; }
+
+// Q6_K: the four groups' exact int32 dots with activation codes x[g].
+__device__ __forceinline__ void qk6_dots(const QkUnit<QK_Q6_K>& U, const int4 (&x)[4], int (&dots)[4]) {
+    const uint32_t L0[4] = {(uint32_t)U.l0.x, (uint32_t)U.l0.y, (uint32_t)U.l0.z, (uint32_t)U.l0.w};
+    const uint32_t L1[4] = {(uint32_t)U.l1.x, (uint32_t)U.l1.y, (uint32_t)U.l1.z, (uint32_t)U.l1.w};
+    const uint32_t H[4] = {(uint32_t)U.h.x, (uint32_t)U.h.y, (uint32_t)U.h.z, (uint32_t)U.h.w};
+    int g0[4], g1[4], g2[4], g3[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        g0[i] = qk_sub_bytes<0x20202020u>((L0[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u));
+        g1[i] = qk_sub_bytes<0x20202020u>((L1[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u));
+        g2[i] = qk_sub_bytes<0x20202020u>(((L0[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u));
+        g3[i] = qk_sub_bytes<0x20202020u>(((L1[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
+    }
+    dots[0] = qk_dot16(g0, x[0]);
+    dots[1] = qk_dot16(g1, x[1]);
+    dots[2] = qk_dot16(g2, x[2]);
+    dots[3] = qk_dot16(g3, x[3]);
+}
+
+// Q6_K: the sub-scales of unit u's four groups (byte p + 2g of the half's 8).
+__device__ __forceinline__ void qk6_subscales(const QkUnit<QK_Q6_K>& U, int u, float (&c)[4]) {
+    const int p = u & 1;
+    const uint32_t s01 = p ? U.sc.x >> 8 : U.sc.x, s23 = p ? U.sc.y >> 8 : U.sc.y;
+    c[0] = (float)(int8_t)(s01 & 0xFF);
+    c[1] = (float)(int8_t)((s01 >> 16) & 0xFF);
+    c[2] = (float)(int8_t)(s23 & 0xFF);
+    c[3] = (float)(int8_t)((s23 >> 16) & 0xFF);
+}
+
+// A unit's contribution to its row: activation codes xq and f32 scales xs
+// (per Q8_0 block) of the same row, from LDS or global memory.
+__device__ __forceinline__ float qk_unit_dot(const QkUnit<QK_Q4_0>& U, int u, const int8_t* xq, const float* xs) {
+    const int dot = qk4_dot(U, *reinterpret_cast<const int4*>(xq + 32 * u),
+                            *reinterpret_cast<const int4*>(xq + 32 * u + 16));
+    return (f16_to_f32(U.d) * xs[u]) * (float)dot;
+}
+__device__ __forceinline__ float qk_unit_dot(const QkUnit<QK_Q6_K>& U, int u, const int8_t* xq, const float* xs) {
+    const int v0 = qk6_v0(u);
+    const int4 x[4] = {*reinterpret_cast<const int4*>(xq + v0), *reinterpret_cast<const int4*>(xq + v0 + 32),
+                       *reinterpret_cast<const int4*>(xq + v0 + 64), *reinterpret_cast<const int4*>(xq + v0 + 96)};
+    int dots[4];
+    qk6_dots(U, x, dots);
+    float c[4];
+    qk6_subscales(U, u, c);
+    const float* xsv = xs + (v0 >> 5);
+    float s = (c[0] * xsv[0]) * (float)dots[0];
+    s = fmaf(c[1] * xsv[1], (float)dots[1], s);
+    s = fmaf(c[2] * xsv[2], (float)dots[2], s);
+    s = fmaf(c[3] * xsv[3], (float)dots[3], s);
+    return f16_to_f32(U.d) * s;
+}
+
+// The same with the activation scales as f16 bits in global memory.
+__device__ __forceinline__ float qk_unit_dot_h(const QkUnit<QK_Q4_0>& U, int u, const int8_t* xq,
+                                               const uint16_t* xd) {
+    const int dot = qk4_dot(U, *reinterpret_cast<const int4*>(xq + 32 * u),
+                            *reinterpret_cast<const int4*>(xq + 32 * u + 16));
+    return (f16_to_f32(U.d) * f16_to_f32(xd[u])) * (float)dot;
+}
+__device__ __forceinline__ float qk_unit_dot_h(const QkUnit<QK_Q6_K>& U, int u, const int8_t* xq,
+                                               const uint16_t* xd) {
+    const int v0 = qk6_v0(u);
+    const int4 x[4] = {*reinterpret_cast<const int4*>(xq + v0), *reinterpret_cast<const int4*>(xq + v0 + 32),
+                       *reinterpret_cast<const int4*>(xq + v0 + 64), *reinterpret_cast<const int4*>(xq + v0 + 96)};
+    int dots[4];
+    qk6_dots(U, x, dots);
+    float c[4];
+    qk6_subscales(U, u, c);
+    const uint16_t* xdv = xd + (v0 >> 5);
+    float s = (c[0] * f16_to_f32(xdv[0])) * (float)dots[0];
+    s = fmaf(c[1] * f16_to_f32(xdv[1]), (float)dots[1], s);
+    s = fmaf(c[2] * f16_to_f32(xdv[2]), (float)dots[2], s);
+    s = fmaf(c[3] * f16_to_f32(xdv[3]), (float)dots[3], s);
+    return f16_to_f32(U.d) * s;
+}
+
+}  // namespace lq

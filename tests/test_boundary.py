@@ -99,6 +99,24 @@ def test_ggml_format_validation():
         lq.LQ_OK
 
 
+def test_moe_ggml_format_validation():
+    w4 = lq.lq_q4_0_weight(A, A, 64, 704)
+    w6 = lq.lq_q6_k_weight(A, A, A, A, 64, 512)
+    for fn, w in ((lq.lq_moe_q4_0_matvec_id, w4), (lq.lq_moe_q6_k_matvec_id, w6)):
+        assert st(fn, None, 8, A, A, 0, A, 4, 2, A, A, 1 << 20) == lq.LQ_ERR_NULL
+        assert st(fn, w, 0, A, A, 0, A, 4, 2, A, A, 1 << 20) == lq.LQ_ERR_UNSUPPORTED
+        assert st(fn, w, 8, A, A, 2, A, 4, 2, A, A, 1 << 20) == lq.LQ_ERR_SHAPE
+        assert st(fn, w, 8, A + 4, A, 0, A, 4, 2, A, A, 1 << 20) == lq.LQ_ERR_ALIGN
+        assert st(fn, w, 8, A, A, 0, A, 4, 2, A, None, 0) == lq.LQ_ERR_WORKSPACE
+        assert st(fn, w, 8, A, A, 0, A, 0, 2, A, None, 0) == lq.LQ_OK          # T == 0: no launch
+    assert st(lq.lq_moe_q4_0_matvec_id, lq.lq_q4_0_weight(A, A, 64, 48), 8, A, A, 0, A, 4, 2, A, A, 1 << 20) == \
+        lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_q6_k_matvec_id, lq.lq_q6_k_weight(A, A, A, A, 64, 704), 8, A, A, 0, A, 4, 2, A, A,
+              1 << 20) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_q6_k_matvec_id, lq.lq_q6_k_weight(A, A, A, A, 64, 8192 + 256), 8, A, A, 0, A, 4, 2, A, A,
+              1 << 20) == lq.LQ_ERR_UNSUPPORTED
+
+
 def test_ggml_format_pack_host():
     """The pack helpers move every GGML block field to its SoA array (host
     memory only), and reject bad shapes."""

@@ -471,6 +471,46 @@ def test_ggml_format_extreme_codes(fmt):
     assert_close(host(y), oracle.q_matvec(fmt, b, rows, cols, xq, xd), f"{fmt} extremes")
 
 
+@pytest.mark.parametrize("fmt,E,rows,cols,T,k", [
+    ("q4_0", 12, 200, 704, 5, 3),
+    ("q6_k", 12, 200, 512, 5, 3),
+    ("q6_k", 128, 1408, 2816, 16, 8),    # the MoE workload's gate/up on Q6_K experts
+    ("q4_0", 128, 2816, 704, 16, 8),     # its down projection on Q4_0 experts
+    ("q4_0", 4, 64, 8192, 3, 2),         # widest rows (4 steps per lane)
+    ("q6_k", 4, 33, 8192, 3, 2),         # Q6_K widest (2 steps), ragged row blocks
+])
+def test_moe_ggml_format_matvec_id(fmt, E, rows, cols, T, k):
+    """The index-driven matvec on Q4_0 / Q6_K experts: every valid (t, s) equals
+    the pinned oracle matvec of its expert; invalid ids give zeros."""
+    r = rng(E + rows + cols + T)
+    b, W = ggml_weight(fmt, r, E * rows, cols)
+    W.rows = rows                                         # the struct describes one expert
+    x = synthetic.activations(r, T * k, cols)
+    xq, xd = oracle.q8_quantize(x)
+    ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[0, 0] = 99
+    if T > 2:
+        ids[1, 0] = ids[2, 1] = ids[0, 1]                  # an expert with several slots
+    call = lq.lq_moe_q4_0_matvec_id if fmt == "q4_0" else lq.lq_moe_q6_k_matvec_id
+    y = dev(np.full((T * k, rows), 5.0, np.float32))
+    ws = workspace(lq.lq_moe_workspace_size(T, k, E))
+    for per_slot in (1, 0):
+        xq_use = xq if per_slot else np.ascontiguousarray(xq[::k])
+        xd_use = xd if per_slot else np.ascontiguousarray(xd[::k])
+        call(W, E, dev(xq_use), dev(xd_use), per_slot, dev(ids), T, k, y, ws, ws.numel())
+        sync()
+        got = host(y).reshape(T, k, rows)
+        for t in range(T):
+            for s in range(k):
+                e = ids[t, s]
+                xi = t * k + s if per_slot else t
+                if 0 <= e < E:
+                    ref = oracle.q_matvec(fmt, b[e * rows:(e + 1) * rows], rows, cols, xq_use[xi], xd_use[xi])
+                    assert_close(got[t, s], ref, f"{fmt} slot {t},{s}")
+                else:
+                    assert np.all(got[t, s] == 0)
+
+
 # ------------------------------------------------------------------ output head
 @pytest.mark.parametrize("vocab,hidden,norm,cap", [
     (1000, 2816, True, 30.0),    # the Gemma-4 head width, ragged row count
