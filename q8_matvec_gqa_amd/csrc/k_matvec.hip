@@ -21,6 +21,8 @@
 //     exact in f32; even lanes accumulate dot * (d_w * d_x).
 //   * A wave keeps RPW rows of loads in flight, then reduces each row with a
 //     DPP / permlane wave sum.  The grid is sized so every CU gets many waves.
+#include <atomic>
+
 #include "lq_device.h"
 #include "lq_internal.h"
 
@@ -517,11 +519,15 @@ static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchM
     constexpr int OUT = SW ? RPW / 2 : RPW;
     constexpr int WAVES = MvWaves<NCH, PRO, EPI>::value;
     auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
-    static int resident = -1;     // workgroups per CU this instance can keep resident
+    // workgroups per CU this instance can keep resident (queried once; the
+    // value is the same for every caller, so concurrent first calls agree)
+    static std::atomic<int> resident_cache{-1};
+    int resident = resident_cache.load(std::memory_order_relaxed);
     if (resident < 0) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WAVES * 64, 0) != hipSuccess || n < 1) n = 1;
         resident = n;
+        resident_cache.store(n, std::memory_order_relaxed);
     }
     const int cap_wg = wg_per_cu * 4 / WAVES > 0 ? wg_per_cu * 4 / WAVES : 1;
     const int per_cu = resident < cap_wg ? resident : cap_wg;
