@@ -24,6 +24,8 @@
 // current one is consumed) and a DPP wave sum finishes each row.  Every
 // workgroup copies the activation into LDS first; its loads go out before
 // the first weights.
+#include <atomic>
+
 #include "lq_device.h"
 #include "lq_internal.h"
 #include "lq_qk.h"
@@ -148,8 +150,19 @@ __global__ __launch_bounds__(kQkNT, 2) void k_qk_mv(QkArgs a) {
 
 template <int FMT, int ST, int RPW>
 void launch_qk(const QkArgs& a, hipStream_t s) {
+    // one resident round: workgroups per CU as the occupancy query reports
+    // for this instance (1 or 2, by its register count), queried once
+    static std::atomic<int> resident_cache{-1};
+    int resident = resident_cache.load(std::memory_order_relaxed);
+    if (resident < 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_qk_mv<FMT, ST, RPW>, kQkNT, 0) != hipSuccess || n < 1)
+            n = 1;
+        resident = n < 2 ? n : 2;
+        resident_cache.store(resident, std::memory_order_relaxed);
+    }
     const int64_t groups = (a.rows + RPW - 1) / RPW;
-    const int64_t waves = (int64_t)kNumCUs * 2 * kQkWaves;     // one resident round: 2 workgroups per CU
+    const int64_t waves = (int64_t)kNumCUs * resident * kQkWaves;
     const int64_t iters = (groups + waves - 1) / waves;
     int64_t grid = (groups + kQkWaves * iters - 1) / (kQkWaves * iters);
     if (grid < 1) grid = 1;
