@@ -40,13 +40,13 @@ typedef float v16f_mm __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h_mm __attribute__((ext_vector_type(8)));
 
 constexpr int kMmTok = 32;                  // tokens per launch (MFMA M); the host loops over chunks
-constexpr int kMmKB = 16;                   // Q8_0 blocks per batch: 512 bytes of every row
+constexpr int kMmKB = 8;                    // Q8_0 blocks per batch: 256 bytes of every row
 constexpr int kMmRB = kMmKB * 32 + 16;      // LDS row stride in bytes (16-byte pad)
 constexpr int kMmSS = 34;                   // LDS stride of one block's 32 f16 scales
 constexpr int kMmNT = 256;                  // 4 waves
 constexpr int kMmMaxBlocks = 512;           // cols <= 16384
 constexpr int kMmTargetWG = kNumCUs * 3;    // workgroups a launch aims for (3 fit per CU)
-constexpr int kMmMaxSplit = 8;              // workgroups per row tile at most
+constexpr int kMmMaxSplit = 4;              // workgroups per row tile at most
 
 struct MmArgs {
     const int8_t* wq;
@@ -125,8 +125,9 @@ __device__ __forceinline__ void mm_store(const MmArgs& a, int bs, int be, int ti
 }
 
 __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
-    __shared__ __attribute__((aligned(16))) int8_t wl[32 * kMmRB];
-    __shared__ __attribute__((aligned(16))) int8_t xl[32 * kMmRB];
+    __shared__ __attribute__((aligned(16))) int8_t tiles[2 * 32 * kMmRB];   // W tile, then X tile
+    int8_t* const wl = tiles;
+    int8_t* const xl = tiles + 32 * kMmRB;
     __shared__ __attribute__((aligned(16))) uint16_t dwl[kMmKB * kMmSS];
     __shared__ __attribute__((aligned(16))) uint16_t dxl[kMmKB * kMmSS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -142,29 +143,21 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
     // workgroups that run side by side read different parts of X (every
     // workgroup reads all of X; in lockstep they would all hit the same few
     // cache lines at once).  The order is fixed per tile (deterministic).
+    // Two batches are in flight in registers (P, Q): batch i + 2 is requested
+    // as soon as batch i sits in LDS, so the loads never pause while a batch
+    // is stored and computed.
     const int nbt = (b1 - b0 + kMmKB - 1) / kMmKB;
     const int rot = (int)((blockIdx.x / a.ks) % nbt);
-    MmStage S;
-    {
-        const int bs = b0 + kMmKB * rot;
-        mm_load(a, row0, bs, bs + kMmKB < b1 ? bs + kMmKB : b1, tid, S);
-    }
-    for (int i = 0; i < nbt; ++i) {
+    auto batch_start = [&](int i) {
         const int j = i + rot < nbt ? i + rot : i + rot - nbt;
-        const int bs = b0 + kMmKB * j, be = bs + kMmKB < b1 ? bs + kMmKB : b1;
-        if (i > 0) __syncthreads();          // every wave is done with the previous batch
-        mm_store(a, bs, be, tid, S, wl, xl, dwl, dxl);
-        __syncthreads();
-        if (i + 1 < nbt) {
-            const int jn = j + 1 < nbt ? j + 1 : 0;
-            const int bn = b0 + kMmKB * jn;
-            mm_load(a, row0, bn, bn + kMmKB < b1 ? bn + kMmKB : b1, tid, S);
-        }
-        // this wave's blocks of the batch: wave, wave + 4, wave + 8, ...; per
-        // block an int8 MFMA (the block dots) and an f16 MFMA whose only
-        // nonzero k term forms the scale products f16(dX[t]) * f16(dW[r])
-        // (exact in f32) in the same tile layout.  Lane holds tokens
-        // 8*(i/4) + 4*half + i%4 of row n.
+        return b0 + kMmKB * j;
+    };
+    auto batch_end = [&](int bs) { return bs + kMmKB < b1 ? bs + kMmKB : b1; };
+    // this wave's blocks of the batch: wave, wave + 4, ...; per block an int8
+    // MFMA (the block dots) and an f16 MFMA whose only nonzero k term forms
+    // the scale products f16(dX[t]) * f16(dW[r]) (exact in f32) in the same
+    // tile layout.  Lane holds tokens 8*(i/4) + 4*half + i%4 of row n.
+    auto compute = [&]() {
 #pragma unroll
         for (int k = 0; k < kMmKB / 4; ++k) {
             const int u = wave + 4 * k;
@@ -179,10 +172,35 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
+    };
+    auto step = [&](int i, MmStage& S) {
+        const int bs = batch_start(i), be = batch_end(bs);
+        if (i > 0) __syncthreads();          // every wave is done with the previous batch
+        mm_store(a, bs, be, tid, S, wl, xl, dwl, dxl);
+        __syncthreads();
+        if (i + 2 < nbt) {
+            const int bn = batch_start(i + 2);
+            mm_load(a, row0, bn, batch_end(bn), tid, S);
+        }
+        compute();
+    };
+    MmStage P, Q;
+    {
+        const int bs = batch_start(0);
+        mm_load(a, row0, bs, batch_end(bs), tid, P);
+    }
+    if (nbt > 1) {
+        const int bs = batch_start(1);
+        mm_load(a, row0, bs, batch_end(bs), tid, Q);
+    }
+    for (int i = 0; i < nbt; i += 2) {
+        step(i, P);
+        if (i + 1 < nbt) step(i + 1, Q);
     }
     // the 4 waves' partial tiles, summed in wave order; thread = (token, row)
     __syncthreads();
-    float* red = reinterpret_cast<float*>(wl);     // [4][32 tokens][32 rows]
+    static_assert(4 * 1024 * sizeof(float) <= sizeof(tiles), "partial tiles fit the W and X tiles");
+    float* red = reinterpret_cast<float*>(tiles);  // [4][32 tokens][32 rows]
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[wave * 1024 + (8 * (r / 4) + 4 * half + (r & 3)) * 32 + n] = acc[r];
     __syncthreads();
