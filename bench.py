@@ -764,6 +764,8 @@ def main():
         torch.cuda.empty_cache()
         result["q8_matmul"] = measure_matmul(32, max(5, args.steps // 10), torch)
         torch.cuda.empty_cache()
+        result["q8_matmul_prefill"] = measure_matmul(512, max(3, args.steps // 20), torch)
+        torch.cuda.empty_cache()
         result["ggml_formats"] = measure_ggml_formats(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
         result["moe_ggml_formats"] = measure_moe_formats(max(5, args.steps // 5), torch)

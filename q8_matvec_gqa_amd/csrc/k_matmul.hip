@@ -54,12 +54,13 @@ struct MmArgs {
     int rows, cols;
     const int8_t* xq;       // [T, cols]
     const uint16_t* xd;     // [T, cols/32]
-    int T;                  // <= 32
+    int T;                  // tokens (the kernel narrows it to its 32-token chunk)
     const float* res;       // [T, ld] or NULL (ks == 1 only)
     float* y;               // [T, ld] (ks == 1 only)
     int64_t ld;             // row stride of res / y (elements)
     float* part;            // ks > 1: [ks][kMmTok][rows] partial sums
     int ks, bpw;            // workgroups per row tile, blocks per workgroup
+    int tiles, nchunk;      // row tiles; 32-token chunks (nchunk > 1 needs ks == 1)
 };
 
 // One batch in registers, per thread: kMmNL 16-byte chunks of W and of X,
@@ -124,7 +125,7 @@ __device__ __forceinline__ void mm_store(const MmArgs& a, int bs, int be, int ti
     }
 }
 
-__global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
+__global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs args) {
     __shared__ __attribute__((aligned(16))) int8_t tiles[2 * 32 * kMmRB];   // W tile, then X tile
     int8_t* const wl = tiles;
     int8_t* const xl = tiles + 32 * kMmRB;
@@ -132,8 +133,30 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t dxl[kMmKB * kMmSS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, half = lane >> 5;
+    // Which row tile, block split and token chunk.  With several chunks the
+    // workgroups of one tile's chunks sit next to each other in dispatch
+    // order on one XCD (workgroups go round-robin over the 8 XCDs), so the
+    // tile's weight rows, read by all of them at about the same time, come
+    // from that XCD's L2 after the first read.
+    MmArgs a = args;
+    int tile, split = 0;
+    if (a.nchunk == 1) {
+        tile = blockIdx.x / a.ks;
+        split = blockIdx.x % a.ks;
+    } else {
+        const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+        const int chunk = q % a.nchunk;
+        tile = 8 * (q / a.nchunk) + x;
+        if (tile >= a.tiles) return;          // padding of the grid to whole XCD rounds
+        const int64_t t0 = (int64_t)chunk * kMmTok;
+        a.xq += t0 * a.cols;
+        a.xd += t0 * (a.cols >> 5);
+        if (a.res) a.res += t0 * a.ld;
+        a.y += t0 * a.ld;
+        a.T = a.T - (int)t0 < kMmTok ? a.T - (int)t0 : kMmTok;
+    }
+    const int row0 = tile * 32;
     const int nb = a.cols >> 5;
-    const int split = blockIdx.x % a.ks, row0 = (blockIdx.x / a.ks) * 32;
     const int b0 = split * a.bpw, b1 = b0 + a.bpw < nb ? b0 + a.bpw : nb;   // host: b0 < b1
 
     float acc[16];
@@ -147,7 +170,7 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs a) {
     // as soon as batch i sits in LDS, so the loads never pause while a batch
     // is stored and computed.
     const int nbt = (b1 - b0 + kMmKB - 1) / kMmKB;
-    const int rot = (int)((blockIdx.x / a.ks) % nbt);
+    const int rot = tile % nbt;
     auto batch_start = [&](int i) {
         const int j = i + rot < nbt ? i + rot : i + rot - nbt;
         return b0 + kMmKB * j;
@@ -243,9 +266,15 @@ __global__ __launch_bounds__(256) void k_q8_matmul_reduce(const float* __restric
 
 // Workgroups per row tile and blocks per workgroup: a short weight splits
 // its blocks (in whole batches, at most kMmMaxSplit ways) so that the grid
-// fills but does not exceed one resident round.
-void mm_plan(int64_t rows, int64_t cols, int* ks, int* bpw) {
+// fills but does not exceed one resident round.  More than 32 tokens fill
+// the grid with token chunks instead: no split.
+void mm_plan(int64_t rows, int64_t cols, int64_t T, int* ks, int* bpw) {
     const int64_t tiles = (rows + 31) / 32, nb = cols / 32;
+    if (T > kMmTok) {
+        *ks = 1;
+        *bpw = (int)nb;
+        return;
+    }
     int best_k = 1;
     int64_t best_b = nb;
     for (int k = 2; k <= kMmMaxSplit; ++k) {
@@ -268,7 +297,7 @@ using namespace lq;
 extern "C" size_t lq_q8_matmul_workspace_size(int64_t rows, int64_t cols, int64_t T) {
     if (rows <= 0 || cols <= 0 || T <= 0 || cols % 32 || cols > 32 * kMmMaxBlocks) return 0;
     int ks, bpw;
-    mm_plan(rows, cols, &ks, &bpw);
+    mm_plan(rows, cols, T, &ks, &bpw);
     return ks > 1 ? (size_t)ks * kMmTok * (size_t)rows * sizeof(float) : 0;
 }
 
@@ -292,27 +321,25 @@ extern "C" lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, con
     const hipStream_t s = as_stream(stream);
     const int64_t rows = w->rows, cols = w->cols, nb = cols / 32;
     int ks, bpw;
-    mm_plan(rows, cols, &ks, &bpw);
-    const unsigned grid = (unsigned)(((rows + 31) / 32) * ks);
-    for (int64_t t0 = 0; t0 < T; t0 += kMmTok) {
-        const int Tc = (int)(T - t0 < kMmTok ? T - t0 : kMmTok);
-        const float* res = residual ? residual + t0 * rows : nullptr;
-        MmArgs a{w->qs, w->d, (int)rows, (int)cols, x_qs + t0 * cols, x_d + t0 * nb, Tc, res, y + t0 * rows, rows,
-                 static_cast<float*>(workspace), ks, bpw};
-        hipLaunchKernelGGL(k_q8_matmul, dim3(grid), dim3(kMmNT), 0, s, a);
-        if (ks > 1) {
-            const int64_t n = (int64_t)Tc * rows;
-            const bool v4 = rows % 4 == 0 && aligned(y, 16) && (!residual || aligned(residual, 16)) &&
-                            aligned(workspace, 16);
-            if (v4)
-                hipLaunchKernelGGL(k_q8_matmul_reduce<4>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                                   static_cast<const float*>(workspace), ks, Tc, (int)rows, res, y + t0 * rows, rows);
-            else
-                hipLaunchKernelGGL(k_q8_matmul_reduce<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                                   static_cast<const float*>(workspace), ks, Tc, (int)rows, res, y + t0 * rows, rows);
-        }
-        st = check_launch(fn);
-        if (st != LQ_OK) return st;
+    mm_plan(rows, cols, T, &ks, &bpw);
+    const int64_t tiles = (rows + 31) / 32, nchunk = (T + kMmTok - 1) / kMmTok;
+    const int64_t grid = nchunk == 1 ? tiles * ks : 8 * nchunk * ((tiles + 7) / 8);
+    if (grid > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)T);
+    MmArgs a{w->qs, w->d, (int)rows, (int)cols, x_qs, x_d, (int)T, residual, y, rows,
+             static_cast<float*>(workspace), ks, bpw, (int)tiles, (int)nchunk};
+    hipLaunchKernelGGL(k_q8_matmul, dim3((unsigned)grid), dim3(kMmNT), 0, s, a);
+    if (ks > 1) {                                  // T <= 32: one chunk
+        const int64_t n = T * rows;
+        const bool v4 = rows % 4 == 0 && aligned(y, 16) && (!residual || aligned(residual, 16)) &&
+                        aligned(workspace, 16);
+        if (v4)
+            hipLaunchKernelGGL(k_q8_matmul_reduce<4>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                               static_cast<const float*>(workspace), ks, (int)T, (int)rows, residual, y, rows);
+        else
+            hipLaunchKernelGGL(k_q8_matmul_reduce<1>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                               static_cast<const float*>(workspace), ks, (int)T, (int)rows, residual, y, rows);
     }
+    st = check_launch(fn);
+    if (st != LQ_OK) return st;
     return LQ_OK;
 }

@@ -290,6 +290,8 @@ def run_matmul(W, rows, cols, xq, xd, T, res, y):
     (32, 24576, 4096),    # 8B-like gate_up (no block split)
     (8, 4096, 12288),     # 8B-like down (block split over 6 workgroups)
     (32, 33, 32),         # one block, a one-row ragged tile
+    (200, 1000, 2048),    # prefill-like: 7 token chunks in one launch (6 full + 8 tokens), ragged rows
+    (512, 256, 1024),     # 16 chunks over 8 row tiles
 ])
 def test_q8_matmul(T, rows, cols):
     r = rng(T * 7 + rows + cols)
