@@ -242,6 +242,146 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs args) {
     }
 }
 
+// ---- wide tiles for longer token batches (prefill) ----------------------------
+// With more than 32 tokens a workgroup owns 64 rows x 64 tokens: each batch
+// of W and X rows staged in LDS feeds two row tiles and two token tiles, so
+// every staged byte serves twice the MFMAs of the 32 x 32 tile.  Wave w
+// owns output sub-tile (rows 32*(w&1).., tokens 32*(w>>1)..) over all the
+// batch's blocks: no cross-wave reduction.  Same loads (row-contiguous, two
+// batches in flight in registers), rotated batch order and scale MFMA as
+// the 32 x 32 kernel.
+constexpr int kMwR = 64, kMwT = 64;
+constexpr int kMwNL = kMwR * kMmCPR / kMmNT;     // W (and X) 16-byte chunks per thread and batch
+constexpr int kMwNS = kMwR * kMmKB / kMmNT;      // W (and X) scales per thread and batch
+constexpr int kMwSS = 66;                        // LDS stride of one block's 64 f16 scales
+
+struct MwStage {
+    int4 w[kMwNL], x[kMwNL];
+    uint32_t dw[kMwNS], dx[kMwNS];
+};
+
+__device__ __forceinline__ void mw_load(const MmArgs& a, int row0, int t0, int Tc, int bs, int be, int tid,
+                                        MwStage& S) {
+    const int nb = a.cols >> 5;
+    const int c = tid % kMmCPR;
+    const int64_t coff = bs + (c >> 1) < be ? (int64_t)bs * 32 + 16 * c : 16 * (c & 1);
+#pragma unroll
+    for (int j = 0; j < kMwNL; ++j) {
+        const int r = (tid + kMmNT * j) / kMmCPR;
+        const int row = row0 + r < a.rows ? row0 + r : a.rows - 1;
+        S.w[j] = load_stream16(a.wq + (int64_t)row * a.cols + coff);
+        S.x[j] = make_int4(0, 0, 0, 0);
+        if (r < Tc) S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)(t0 + r) * a.cols + coff);
+    }
+#pragma unroll
+    for (int i = 0; i < kMwNS; ++i) {
+        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
+        const int b = bs + u < be ? bs + u : 0;
+        const int row = row0 + rr < a.rows ? row0 + rr : a.rows - 1;
+        S.dw[i] = a.wd[(int64_t)row * nb + b];
+        S.dx[i] = 0;
+        if (rr < Tc) S.dx[i] = a.xd[(int64_t)(t0 + rr) * nb + b];
+    }
+}
+
+__device__ __forceinline__ void mw_store(int Tc, int bs, int be, int tid, const MwStage& S, int8_t* wl, int8_t* xl,
+                                         uint16_t* dwl, uint16_t* dxl) {
+    const int c = tid % kMmCPR;
+#pragma unroll
+    for (int j = 0; j < kMwNL; ++j) {
+        const int r = (tid + kMmNT * j) / kMmCPR;
+        *reinterpret_cast<int4*>(wl + r * kMmRB + 16 * c) = S.w[j];
+        *reinterpret_cast<int4*>(xl + r * kMmRB + 16 * c) = S.x[j];
+    }
+#pragma unroll
+    for (int i = 0; i < kMwNS; ++i) {
+        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
+        const bool uv = bs + u < be;
+        dwl[u * kMwSS + rr] = uv ? (uint16_t)S.dw[i] : (uint16_t)0;
+        dxl[u * kMwSS + rr] = (uv && rr < Tc) ? (uint16_t)S.dx[i] : (uint16_t)0;
+    }
+}
+
+// grid: 8 * nchunk * ceil(tiles / 8) over 64-row tiles and 64-token chunks,
+// a tile's chunks adjacent on one XCD
+__global__ __launch_bounds__(kMmNT, 2) void k_q8_matmul_wide(MmArgs a) {
+    __shared__ __attribute__((aligned(16))) int8_t wl[kMwR * kMmRB];
+    __shared__ __attribute__((aligned(16))) int8_t xl[kMwT * kMmRB];
+    __shared__ __attribute__((aligned(16))) uint16_t dwl[kMmKB * kMwSS];
+    __shared__ __attribute__((aligned(16))) uint16_t dxl[kMmKB * kMwSS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, half = lane >> 5;
+    const int x8 = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int chunk = q % a.nchunk, tile = 8 * (q / a.nchunk) + x8;
+    if (tile >= a.tiles) return;                  // padding of the grid to whole XCD rounds
+    const int row0 = tile * kMwR, t0 = chunk * kMwT;
+    const int Tc = a.T - t0 < kMwT ? a.T - t0 : kMwT;
+    const int nb = a.cols >> 5;
+    const int rt = wave & 1, tt = wave >> 1;      // this wave's output sub-tile
+
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const int nbt = (nb + kMmKB - 1) / kMmKB;
+    const int rot = tile % nbt;
+    auto batch_start = [&](int i) {
+        const int j = i + rot < nbt ? i + rot : i + rot - nbt;
+        return kMmKB * j;
+    };
+    auto batch_end = [&](int bs) { return bs + kMmKB < nb ? bs + kMmKB : nb; };
+    auto compute = [&]() {
+#pragma unroll
+        for (int u = 0; u < kMmKB; ++u) {
+            const v4i_mm A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
+            const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
+            const int xs = dxl[u * kMwSS + tt * 32 + n], ws = dwl[u * kMwSS + rt * 32 + n];
+            const v16i_mm c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
+            const v4i_mm As = {half ? 0 : xs, 0, 0, 0}, Bs = {half ? 0 : ws, 0, 0, 0};
+            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h_mm, As),
+                                                                      __builtin_bit_cast(v8h_mm, Bs), v16f_mm{}, 0,
+                                                                      0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
+        }
+    };
+    auto step = [&](int i, MwStage& S) {
+        const int bs = batch_start(i), be = batch_end(bs);
+        if (i > 0) __syncthreads();
+        mw_store(Tc, bs, be, tid, S, wl, xl, dwl, dxl);
+        __syncthreads();
+        if (i + 2 < nbt) {
+            const int bn = batch_start(i + 2);
+            mw_load(a, row0, t0, Tc, bn, batch_end(bn), tid, S);
+        }
+        compute();
+    };
+    MwStage P, Q;
+    {
+        const int bs = batch_start(0);
+        mw_load(a, row0, t0, Tc, bs, batch_end(bs), tid, P);
+    }
+    if (nbt > 1) {
+        const int bs = batch_start(1);
+        mw_load(a, row0, t0, Tc, bs, batch_end(bs), tid, Q);
+    }
+    for (int i = 0; i < nbt; i += 2) {
+        step(i, P);
+        if (i + 1 < nbt) step(i + 1, Q);
+    }
+    // lane holds tokens 8*(r/4) + 4*half + r%4 of row n of the sub-tile
+    const int row = row0 + rt * 32 + n;
+    if (row < a.rows) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = tt * 32 + 8 * (r / 4) + 4 * half + (r & 3);
+            if (t < Tc) {
+                const int64_t o = (int64_t)(t0 + t) * a.ld + row;
+                a.y[o] = a.res ? a.res[o] + acc[r] : acc[r];
+            }
+        }
+    }
+}
+
 // y[t, r] = residual[t, r] + sum over the splits in order; V consecutive
 // rows per thread (V = 4 needs rows % 4 == 0), every split's load issued
 // before the sum.
@@ -322,6 +462,19 @@ extern "C" lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, con
     const int64_t rows = w->rows, cols = w->cols, nb = cols / 32;
     int ks, bpw;
     mm_plan(rows, cols, T, &ks, &bpw);
+    // 64 x 64 tiles once they fill a resident round (2 per CU); fewer of them
+    // leave CUs idle, and the 32 x 32 tiles (every 32-token chunk in one
+    // launch) do better there
+    const int64_t wtiles = (rows + kMwR - 1) / kMwR, wchunks = (T + kMwT - 1) / kMwT;
+    if (T > kMmTok && wtiles * wchunks >= 2 * kNumCUs) {
+        const int64_t tiles = wtiles, nchunk = wchunks;
+        const int64_t grid = 8 * nchunk * ((tiles + 7) / 8);
+        if (grid > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)T);
+        MmArgs a{w->qs, w->d, (int)rows, (int)cols, x_qs, x_d, (int)T, residual, y, rows, nullptr, 1, (int)nb,
+                 (int)tiles, (int)nchunk};
+        hipLaunchKernelGGL(k_q8_matmul_wide, dim3((unsigned)grid), dim3(kMmNT), 0, s, a);
+        return check_launch(fn);
+    }
     const int64_t tiles = (rows + 31) / 32, nchunk = (T + kMmTok - 1) / kMmTok;
     const int64_t grid = nchunk == 1 ? tiles * ks : 8 * nchunk * ((tiles + 7) / 8);
     if (grid > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "%s: T=%lld too large", fn, (long long)T);

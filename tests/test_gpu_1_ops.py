@@ -292,6 +292,8 @@ def run_matmul(W, rows, cols, xq, xd, T, res, y):
     (32, 33, 32),         # one block, a one-row ragged tile
     (200, 1000, 2048),    # prefill-like: 7 token chunks in one launch (6 full + 8 tokens), ragged rows
     (512, 256, 1024),     # 16 chunks over 8 row tiles
+    (512, 4096, 256),     # 64 x 64 tiles (512 of them), one batch
+    (1000, 2050, 512),    # 64 x 64 tiles with ragged rows and tokens, two batches
 ])
 def test_q8_matmul(T, rows, cols):
     r = rng(T * 7 + rows + cols)
