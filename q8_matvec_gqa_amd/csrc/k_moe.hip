@@ -47,15 +47,23 @@ size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts) {
 // Softmax over the token's E logits, then the k largest (ties: lower id);
 // the weights are the probabilities themselves.  Lane 0 writes id and weight
 // of each pick to ids/w and, when sids is given, the id to sids (LDS).
-__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k, int lane,
-                                            int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
-    constexpr int PER = 16;   // E <= 1024
+// PER logits per lane (E <= 64 * PER): the instance for the smallest PER
+// that holds E runs (routing is VALU work on one workgroup in k_moe_prep).
+template <int PER>
+__device__ __forceinline__ void route_token_p(const float* __restrict__ lt, int E, int k, int lane,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
     float v[PER];
     float mx = -INFINITY;
+    // straight-line loads (a clamped index, then a select): a load under a
+    // branch per element would wait for each one in turn
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? lt[e] : -INFINITY;
+        v[i] = lt[e < E ? e : E - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = lane + 64 * i < E ? v[i] : -INFINITY;
         mx = fmaxf(mx, v[i]);
     }
     mx = wave_max(mx);
@@ -90,6 +98,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lt, int E,
         for (int i = 0; i < PER; ++i)
             if (lane + 64 * i == bi) v[i] = __int_as_float(0xff800001u);
     }
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ lt, int E, int k, int lane,
+                                            int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
+    if (E <= 64) route_token_p<1>(lt, E, k, lane, ids, w, sids);
+    else if (E <= 128) route_token_p<2>(lt, E, k, lane, ids, w, sids);
+    else if (E <= 256) route_token_p<4>(lt, E, k, lane, ids, w, sids);
+    else if (E <= 512) route_token_p<8>(lt, E, k, lane, ids, w, sids);
+    else route_token_p<16>(lt, E, k, lane, ids, w, sids);   // E <= 1024
 }
 
 __global__ __launch_bounds__(64) void k_moe_route(const float* __restrict__ logits, int E, int k,
