@@ -197,9 +197,8 @@ lq_status lq_q6_k_matvec(const lq_q6_k_weight* w, const int8_t* x_qs, const uint
                          const float* residual, float* y, void* stream);
 
 /* Multi-token Q8_0 matmul: the decode matvec for T tokens at once (prefill,
- * batched decode), each weight byte read once per 32 tokens ([LAT] Current
- * Design: int8 weights times int8 activations with int32 accumulation, one
- * f16 scale per 32 values):
+ * batched decode) in one launch ([LAT] Current Design: int8 weights times
+ * int8 activations with int32 accumulation, one f16 scale per 32 values):
  *   y[t, r] = residual[t, r] + sum_b f16(d_w[r,b]) * f16(x_d[t,b]) * dot_b(W[r], X[t])
  * with dot_b the exact int32 dot of block b.  Runs on int8 MFMA; the float
  * sum is in an unspecified but fixed order (results do not vary from run to
@@ -210,8 +209,10 @@ lq_status lq_q6_k_matvec(const lq_q6_k_weight* w, const int8_t* x_qs, const uint
  *   alias residual.
  *   workspace: device memory of lq_q8_matmul_workspace_size(rows, cols, T)
  *   bytes (4-byte aligned; may be NULL when that size is 0), holding partial
- *   sums when a short weight splits its blocks over several workgroups.
- * T == 0 or rows == 0 is a no-op. */
+ *   sums when a short weight splits its blocks over several workgroups
+ *   (T <= 32 only; the size is 0 for more tokens).
+ * T == 0 or rows == 0 is a no-op; T above 2^31 / 32 tokens per call is
+ * LQ_ERR_UNSUPPORTED. */
 size_t lq_q8_matmul_workspace_size(int64_t rows, int64_t cols, int64_t T);
 lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d, int64_t T,
                        const float* residual, float* y, void* workspace, size_t workspace_bytes,
