@@ -211,8 +211,8 @@ lq_status lq_q6_k_matvec(const lq_q6_k_weight* w, const int8_t* x_qs, const uint
  *   bytes (4-byte aligned; may be NULL when that size is 0), holding partial
  *   sums when a short weight splits its blocks over several workgroups
  *   (T <= 32 only; the size is 0 for more tokens).
- * T == 0 or rows == 0 is a no-op; T above 2^31 / 32 tokens per call is
- * LQ_ERR_UNSUPPORTED. */
+ * T == 0 or rows == 0 is a no-op; T >= 2^31, or a launch of 2^31 or more
+ * workgroups, is LQ_ERR_UNSUPPORTED. */
 size_t lq_q8_matmul_workspace_size(int64_t rows, int64_t cols, int64_t T);
 lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d, int64_t T,
                        const float* residual, float* y, void* workspace, size_t workspace_bytes,

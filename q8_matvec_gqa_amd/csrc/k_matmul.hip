@@ -448,6 +448,7 @@ extern "C" lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, con
     lq_status st = check_weight(w, fn);
     if (st != LQ_OK) return st;
     if (T < 0) return fail(LQ_ERR_SHAPE, "%s: T=%lld", fn, (long long)T);
+    if (T > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "%s: T=%lld (< 2^31)", fn, (long long)T);
     if (w->cols > 32 * kMmMaxBlocks || w->rows > 0x7fffffffLL)
         return fail(LQ_ERR_UNSUPPORTED, "%s: cols=%lld rows=%lld (cols <= %d)", fn, (long long)w->cols,
                     (long long)w->rows, 32 * kMmMaxBlocks);

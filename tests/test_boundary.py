@@ -154,6 +154,7 @@ def test_matmul_validation_and_workspace():
     assert lq.lq_q8_matmul_workspace_size(4096, 4096, 0) == 0
     assert lq.lq_q8_matmul_workspace_size(4096, 48, 8) == 0
     assert st(lq.lq_q8_matmul, w, A, A, -1, None, A, A, need) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_q8_matmul, w, A, A, 1 << 31, None, A, A, need) == lq.LQ_ERR_UNSUPPORTED
     assert st(lq.lq_q8_matmul, lq.lq_q8_weight(A, A, 10, 32 * 513), A, A, 4, None, A, A, 1 << 20) == \
         lq.LQ_ERR_UNSUPPORTED
     assert st(lq.lq_q8_matmul, w, None, A, 4, None, A, A, need) == lq.LQ_ERR_NULL
