@@ -307,6 +307,21 @@ def test_q8_matmul(T, rows, cols):
     assert_close(host(y).reshape(T, rows), want, "q8 matmul")
 
 
+def test_q8_matmul_prefill_full_size_sampled():
+    """The bench's prefill launch (512 tokens on the 8B-like gate_up weight,
+    64 x 64 tiles): sampled tokens against the oracle matvec of each."""
+    r = rng(512)
+    T, rows, cols = 512, 24576, 4096
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
+    xd = (np.abs(r.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
+    y = empty(T * rows, np.float32)
+    run_matmul(lq.q8_weight(dev(wq), dev(wd)), rows, cols, dev(xq), dev(xd), T, None, y)
+    Y = host(y).reshape(T, rows)
+    for t in (0, 63, 64, 300, 511):
+        assert_close(Y[t], oracle.q8_matvec(wq, wd, xq[t], xd[t]), f"token {t}")
+
+
 @pytest.mark.parametrize("rows,cols", [(4096, 4096), (24576, 1024)])
 def test_q8_matmul_in_place_and_repeatable(rows, cols):
     """y aliasing the residual (the residual-add form of a projection) gives
