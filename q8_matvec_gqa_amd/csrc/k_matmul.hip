@@ -38,6 +38,8 @@ typedef int v4i_mm __attribute__((ext_vector_type(4)));
 typedef int v16i_mm __attribute__((ext_vector_type(16)));
 typedef float v16f_mm __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h_mm __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h_mm __attribute__((ext_vector_type(4)));
+typedef int v2i_mm __attribute__((ext_vector_type(2)));
 
 constexpr int kMmTok = 32;                  // tokens per launch (MFMA M); the host loops over chunks
 constexpr int kMmKB = 8;                    // Q8_0 blocks per batch: 256 bytes of every row
@@ -247,9 +249,10 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs args) {
 // of W and X rows staged in LDS feeds two row tiles and two token tiles, so
 // every staged byte serves twice the MFMAs of the 32 x 32 tile.  Wave w
 // owns output sub-tile (rows 32*(w&1).., tokens 32*(w>>1)..) over all the
-// batch's blocks: no cross-wave reduction.  Same loads (row-contiguous, two
-// batches in flight in registers), rotated batch order and scale MFMA as
-// the 32 x 32 kernel.
+// batch's blocks: no cross-wave reduction.  Same row-contiguous loads and
+// rotated batch order as the 32 x 32 kernel, but one batch in flight in
+// registers (three workgroups per CU hide the latency better than a second
+// batch in one) and the smaller scale MFMA.
 constexpr int kMwR = 64, kMwT = 64;
 constexpr int kMwNL = kMwR * kMmCPR / kMmNT;     // W (and X) 16-byte chunks per thread and batch
 constexpr int kMwNS = kMwR * kMmKB / kMmNT;      // W (and X) scales per thread and batch
@@ -304,7 +307,7 @@ __device__ __forceinline__ void mw_store(int Tc, int bs, int be, int tid, const 
 
 // grid: 8 * nchunk * ceil(tiles / 8) over 64-row tiles and 64-token chunks,
 // a tile's chunks adjacent on one XCD
-__global__ __launch_bounds__(kMmNT, 2) void k_q8_matmul_wide(MmArgs a) {
+__global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul_wide(MmArgs a) {
     __shared__ __attribute__((aligned(16))) int8_t wl[kMwR * kMmRB];
     __shared__ __attribute__((aligned(16))) int8_t xl[kMwT * kMmRB];
     __shared__ __attribute__((aligned(16))) uint16_t dwl[kMmKB * kMwSS];
@@ -329,17 +332,24 @@ __global__ __launch_bounds__(kMmNT, 2) void k_q8_matmul_wide(MmArgs a) {
         return kMmKB * j;
     };
     auto batch_end = [&](int bs) { return bs + kMmKB < nb ? bs + kMmKB : nb; };
+    // block u: the block dots (i8 MFMA) and the scale products from the
+    // smallest f16 MFMA (32x32x8: two-register operands, half the cycles of
+    // the 32x32x16 one), its only nonzero k term f16(dX[t]) * f16(dW[r])
+    auto mma = [&](int u, v16i_mm& c, v16f_mm& sc) {
+        const v4i_mm A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
+        const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
+        const int xs = dxl[u * kMwSS + tt * 32 + n], ws = dwl[u * kMwSS + rt * 32 + n];
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
+        const v2i_mm As = {half ? 0 : xs, 0}, Bs = {half ? 0 : ws, 0};
+        sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_mm, As), __builtin_bit_cast(v4h_mm, Bs),
+                                                  v16f_mm{}, 0, 0, 0);
+    };
     auto compute = [&]() {
 #pragma unroll
         for (int u = 0; u < kMmKB; ++u) {
-            const v4i_mm A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
-            const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
-            const int xs = dxl[u * kMwSS + tt * 32 + n], ws = dwl[u * kMwSS + rt * 32 + n];
-            const v16i_mm c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
-            const v4i_mm As = {half ? 0 : xs, 0, 0, 0}, Bs = {half ? 0 : ws, 0, 0, 0};
-            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h_mm, As),
-                                                                      __builtin_bit_cast(v8h_mm, Bs), v16f_mm{}, 0,
-                                                                      0, 0);
+            v16i_mm c;
+            v16f_mm sc;
+            mma(u, c, sc);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
@@ -349,25 +359,20 @@ __global__ __launch_bounds__(kMmNT, 2) void k_q8_matmul_wide(MmArgs a) {
         if (i > 0) __syncthreads();
         mw_store(Tc, bs, be, tid, S, wl, xl, dwl, dxl);
         __syncthreads();
-        if (i + 2 < nbt) {
-            const int bn = batch_start(i + 2);
+        if (i + 1 < nbt) {
+            const int bn = batch_start(i + 1);
             mw_load(a, row0, t0, Tc, bn, batch_end(bn), tid, S);
         }
         compute();
     };
-    MwStage P, Q;
+    // one batch in flight in registers (the next batch's loads overlap this
+    // batch's math): 156 VGPRs, three workgroups per CU
+    MwStage P;
     {
         const int bs = batch_start(0);
         mw_load(a, row0, t0, Tc, bs, batch_end(bs), tid, P);
     }
-    if (nbt > 1) {
-        const int bs = batch_start(1);
-        mw_load(a, row0, t0, Tc, bs, batch_end(bs), tid, Q);
-    }
-    for (int i = 0; i < nbt; i += 2) {
-        step(i, P);
-        if (i + 1 < nbt) step(i + 1, Q);
-    }
+    for (int i = 0; i < nbt; ++i) step(i, P);
     // lane holds tokens 8*(r/4) + 4*half + r%4 of row n of the sub-tile
     const int row = row0 + rt * 32 + n;
     if (row < a.rows) {
@@ -463,7 +468,7 @@ extern "C" lq_status lq_q8_matmul(const lq_q8_weight* w, const int8_t* x_qs, con
     const int64_t rows = w->rows, cols = w->cols, nb = cols / 32;
     int ks, bpw;
     mm_plan(rows, cols, T, &ks, &bpw);
-    // 64 x 64 tiles once they fill a resident round (2 per CU); fewer of them
+    // 64 x 64 tiles once they fill two workgroups per CU; fewer of them
     // leave CUs idle, and the 32 x 32 tiles (every 32-token chunk in one
     // launch) do better there
     const int64_t wtiles = (rows + kMwR - 1) / kMwR, wchunks = (T + kMwT - 1) / kMwT;
