@@ -294,6 +294,7 @@ def run_matmul(W, rows, cols, xq, xd, T, res, y):
     (512, 256, 1024),     # 16 chunks over 8 row tiles
     (512, 4096, 256),     # 64 x 64 tiles (512 of them), one batch
     (1000, 2050, 512),    # 64 x 64 tiles with ragged rows and tokens, two batches
+    (520, 3650, 352),     # 64 x 64 tiles, ragged rows and tokens, a partial last batch (8 + 3 blocks)
 ])
 def test_q8_matmul(T, rows, cols):
     r = rng(T * 7 + rows + cols)
