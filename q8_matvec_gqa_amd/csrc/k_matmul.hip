@@ -190,10 +190,9 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs args) {
             const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + n * kMmRB + 32 * u + 16 * half);
             const int xs = dxl[u * kMmSS + n], ws = dwl[u * kMmSS + n];
             const v16i_mm c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
-            const v4i_mm As = {half ? 0 : xs, 0, 0, 0}, Bs = {half ? 0 : ws, 0, 0, 0};
-            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h_mm, As),
-                                                                      __builtin_bit_cast(v8h_mm, Bs), v16f_mm{}, 0,
-                                                                      0, 0);
+            const v2i_mm As = {half ? 0 : xs, 0}, Bs = {half ? 0 : ws, 0};
+            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_mm, As),
+                                                                    __builtin_bit_cast(v4h_mm, Bs), v16f_mm{}, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
