@@ -56,7 +56,7 @@ typedef int32_t lq_status;
 #define LQ_ERR_ALIGN        3   /* a pointer or stride breaks the alignment below */
 #define LQ_ERR_WORKSPACE    4   /* workspace NULL or smaller than the query says */
 #define LQ_ERR_HIP          5   /* the HIP runtime reported an error on launch */
-#define LQ_ERR_UNSUPPORTED  6   /* valid by definition, outside this build's kernels */
+#define LQ_ERR_UNSUPPORTED  6   /* valid by definition, outside what the library's kernels cover */
 
 #define LQ_KV_F32   0
 #define LQ_KV_BF16  1
@@ -257,8 +257,8 @@ lq_status lq_kv_append(const float* k, const float* v, int64_t n_kv, int64_t hea
  *   caches: device f32 or bf16 (kv_dtype), 16-byte aligned, with
  *   head_stride and pos_stride multiples of 16 bytes; max_ctx is the number
  *   of positions allocated per head: start + len <= max_ctx.
- * Shapes: n_q % n_kv == 0 (INV-3), head_dim % 4 == 0 (INV-2); this build
- * also needs head_dim % 8 == 0 for bf16, head_dim <= 512 and
+ * Shapes: n_q % n_kv == 0 (INV-3), head_dim % 4 == 0 (INV-2); the kernels
+ * also need head_dim % 8 == 0 for bf16, head_dim <= 512 and
  * n_q / n_kv <= 8 (else LQ_ERR_UNSUPPORTED).  len == 0 writes zeros. */
 size_t lq_gqa_decode_attn_workspace_size(int64_t n_q, int64_t n_kv, int64_t head_dim,
                                          int64_t len);
@@ -279,7 +279,7 @@ lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t 
  *   if softcap > 0: logits[r] = softcap * tanh(logits[r] / softcap)
  *   w: device f16 bits [vocab, hidden], row-major, 16-byte aligned.
  *   x, gamma: device f32 [hidden], 16-byte aligned.  logits: device f32 [vocab].
- * hidden % 8 == 0 (LQ_ERR_SHAPE) and, in this build, hidden <= 4096
+ * hidden % 8 == 0 (LQ_ERR_SHAPE) and, for the kernel as written, hidden <= 4096
  * (LQ_ERR_UNSUPPORTED).  vocab == 0 is a no-op.  Float results follow the
  * library's tolerance (the f16 products are exact; sums are f32). */
 lq_status lq_lm_head_f16(const uint16_t* w, int64_t vocab, int64_t hidden, const float* x, int32_t norm,
@@ -419,7 +419,7 @@ typedef struct lq_layer_taps {
  * (device f32 [hidden]) is updated in place; k and v of the token are
  * written into the caches at pos (pos < max_ctx); attention covers the
  * window ending at pos.  taps may be NULL.
- * This build's kernels need head_dim % 8 == 0 (<= 512), hidden, n_q*head_dim
+ * The kernels need head_dim % 8 == 0 (<= 512), hidden, n_q*head_dim
  * and ffn <= 16384, and 16-byte aligned x, norm weights, RoPE tables and
  * caches (LQ_ERR_UNSUPPORTED / LQ_ERR_ALIGN otherwise). */
 size_t lq_decode_layer_workspace_size(const lq_layer_desc* L);

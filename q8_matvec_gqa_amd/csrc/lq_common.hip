@@ -50,7 +50,7 @@ extern "C" const char* lq_status_string(lq_status s) {
         case LQ_ERR_ALIGN: return "misaligned pointer or stride";
         case LQ_ERR_WORKSPACE: return "workspace missing or too small";
         case LQ_ERR_HIP: return "HIP runtime error";
-        case LQ_ERR_UNSUPPORTED: return "unsupported by this build";
+        case LQ_ERR_UNSUPPORTED: return "unsupported by the library's kernels";
         default: return "unknown status";
     }
 }
