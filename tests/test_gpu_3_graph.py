@@ -95,20 +95,23 @@ def test_moe_block_graph_replays():
         assert np.array_equal(host(out), want), f"replay {i}"
 
 
-def test_matmul_graph_replays():
-    """The split matmul (partials in the workspace, then the ordered reduce)
-    in a graph, residual aliasing y: each replay adds W x to the result of
-    the previous one, as the eager calls do."""
+@pytest.mark.parametrize("T,rows,cols", [
+    (32, 4096, 4096),     # split blocks: partials in the workspace, then the ordered reduce
+    (512, 4096, 1024),    # 64 x 64 tiles, no workspace
+])
+def test_matmul_graph_replays(T, rows, cols):
+    """The matmul in a graph, residual aliasing y: each replay adds W x to
+    the result of the previous one, as the eager calls do."""
     torch = torch_mod()
+    print(f"[graph] matmul T={T} {rows}x{cols}", flush=True)
     r = np.random.default_rng(8)
-    T, rows, cols = 32, 4096, 4096
     wq, wd = synthetic.q8_weight(r, rows, cols)
     xq = r.integers(-127, 128, (T, cols)).astype(np.int8)
     xd = (np.abs(r.standard_normal((T, cols // 32))) * 0.05).astype(np.float16).view(np.uint16)
     y0 = synthetic.activations(r, T, rows)
     W = lq.q8_weight(dev(wq), dev(wd))
     nws = lq.lq_q8_matmul_workspace_size(rows, cols, T)
-    assert nws > 0
+    assert (nws > 0) == (T <= 32)
     ws = workspace(nws)
     xqd, xdd = dev(xq), dev(xd)
     y = dev(y0)
