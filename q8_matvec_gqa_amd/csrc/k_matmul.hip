@@ -84,25 +84,30 @@ struct MmStage {
 // Tokens past T load nothing (every workgroup reads X, so clamped duplicates
 // would pile onto a few cache lines): their LDS rows and scales are zero.
 __device__ __forceinline__ void mm_load(const MmArgs& a, int row0, int bs, int be, int tid, MmStage& S) {
+    // a tile base (wave-uniform) plus a 32-bit offset inside the tile: the
+    // loads take the scalar-base form, with no 64-bit arithmetic per lane
     const int nb = a.cols >> 5;
     const int c = tid % kMmCPR;
-    const int64_t coff = bs + (c >> 1) < be ? (int64_t)bs * 32 + 16 * c : 16 * (c & 1);
+    const uint32_t coff = bs + (c >> 1) < be ? (uint32_t)bs * 32u + 16u * c : 16u * (c & 1);
+    const int rlast = a.rows - 1 - row0;                  // last row of the tile that exists
+    const int8_t* wt = a.wq + (int64_t)row0 * a.cols;
 #pragma unroll
     for (int j = 0; j < kMmNL; ++j) {
         const int r = (tid + kMmNT * j) / kMmCPR;
-        const int row = row0 + r < a.rows ? row0 + r : a.rows - 1;
-        S.w[j] = load_stream16(a.wq + (int64_t)row * a.cols + coff);
+        const uint32_t wr = (uint32_t)(r < rlast ? r : rlast) * (uint32_t)a.cols;
+        S.w[j] = load_stream16(wt + (wr + coff));
         S.x[j] = make_int4(0, 0, 0, 0);
-        if (r < a.T) S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)r * a.cols + coff);
+        if (r < a.T) S.x[j] = *reinterpret_cast<const int4*>(a.xq + ((uint32_t)r * (uint32_t)a.cols + coff));
     }
+    const char* wdt = reinterpret_cast<const char*>(a.wd + (int64_t)row0 * nb);
+    const char* xdt = reinterpret_cast<const char*>(a.xd);
 #pragma unroll
     for (int i = 0; i < kMmNS; ++i) {
         const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
-        const int b = bs + u < be ? bs + u : 0;
-        const int row = row0 + rr < a.rows ? row0 + rr : a.rows - 1;
-        S.dw[i] = a.wd[(int64_t)row * nb + b];
+        const uint32_t b = bs + u < be ? (uint32_t)(bs + u) : 0u;
+        S.dw[i] = *reinterpret_cast<const uint16_t*>(wdt + 2u * ((uint32_t)(rr < rlast ? rr : rlast) * (uint32_t)nb + b));
         S.dx[i] = 0;
-        if (rr < a.T) S.dx[i] = a.xd[(int64_t)rr * nb + b];
+        if (rr < a.T) S.dx[i] = *reinterpret_cast<const uint16_t*>(xdt + 2u * ((uint32_t)rr * (uint32_t)nb + b));
     }
 }
 
@@ -262,27 +267,35 @@ struct MwStage {
     uint32_t dw[kMwNS], dx[kMwNS];
 };
 
+// Addresses are a tile base (wave-uniform, 64-bit) plus a 32-bit offset
+// inside the tile (64 rows of at most 16 KB), so the loads take the
+// scalar-base form and need no 64-bit address arithmetic per lane.
 __device__ __forceinline__ void mw_load(const MmArgs& a, int row0, int t0, int Tc, int bs, int be, int tid,
                                         MwStage& S) {
     const int nb = a.cols >> 5;
     const int c = tid % kMmCPR;
-    const int64_t coff = bs + (c >> 1) < be ? (int64_t)bs * 32 + 16 * c : 16 * (c & 1);
+    const uint32_t coff = bs + (c >> 1) < be ? (uint32_t)bs * 32u + 16u * c : 16u * (c & 1);
+    const int rlast = a.rows - 1 - row0;                  // last row of the tile that exists
+    const int8_t* wt = a.wq + (int64_t)row0 * a.cols;
+    const int8_t* xt = a.xq + (int64_t)t0 * a.cols;
 #pragma unroll
     for (int j = 0; j < kMwNL; ++j) {
         const int r = (tid + kMmNT * j) / kMmCPR;
-        const int row = row0 + r < a.rows ? row0 + r : a.rows - 1;
-        S.w[j] = load_stream16(a.wq + (int64_t)row * a.cols + coff);
+        const uint32_t wr = (uint32_t)(r < rlast ? r : rlast) * (uint32_t)a.cols;
+        S.w[j] = load_stream16(wt + (wr + coff));
         S.x[j] = make_int4(0, 0, 0, 0);
-        if (r < Tc) S.x[j] = *reinterpret_cast<const int4*>(a.xq + (int64_t)(t0 + r) * a.cols + coff);
+        if (r < Tc) S.x[j] = *reinterpret_cast<const int4*>(xt + ((uint32_t)r * (uint32_t)a.cols + coff));
     }
+    const char* wdt = reinterpret_cast<const char*>(a.wd + (int64_t)row0 * nb);
+    const char* xdt = reinterpret_cast<const char*>(a.xd + (int64_t)t0 * nb);
 #pragma unroll
     for (int i = 0; i < kMwNS; ++i) {
         const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
-        const int b = bs + u < be ? bs + u : 0;
-        const int row = row0 + rr < a.rows ? row0 + rr : a.rows - 1;
-        S.dw[i] = a.wd[(int64_t)row * nb + b];
+        const uint32_t b = bs + u < be ? (uint32_t)(bs + u) : 0u;
+        const uint32_t wo = 2u * ((uint32_t)(rr < rlast ? rr : rlast) * (uint32_t)nb + b);
+        S.dw[i] = *reinterpret_cast<const uint16_t*>(wdt + wo);
         S.dx[i] = 0;
-        if (rr < Tc) S.dx[i] = a.xd[(int64_t)(t0 + rr) * nb + b];
+        if (rr < Tc) S.dx[i] = *reinterpret_cast<const uint16_t*>(xdt + 2u * ((uint32_t)rr * (uint32_t)nb + b));
     }
 }
 
