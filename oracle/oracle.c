@@ -28,6 +28,15 @@
  *          offsets).
  * Where the pages leave a step open, the reading taken is stated at the
  * function.
+ *
+ * Pins (tests/test_oracle_pins.py) tie every function to something other
+ * than itself, with two limits:
+ *   orc_decode_layer -- parity unpinned as a whole: it is checked against an
+ *          independent composition of its pinned stages, and no external
+ *          value for a whole layer exists.
+ *   orc_q6_k_dequant / orc_q6_k_matvec -- parity unpinned against GGML
+ *          itself: the element order is pinned to the layout as read from
+ *          the pages (no GGML fixture is available offline).
  */
 #include "oracle.h"
 
