@@ -1,0 +1,46 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the algorithmic
+byte model behind every GB/s figure, and the kernel-name matching used to
+read rocprofv3 output."""
+import os
+import subprocess
+import sys
+
+import bench
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_headline_byte_model():
+    """The 8B-like layer's bytes, written out from the storage formats:
+    Q8_0 weights at 34 bytes per 32 values, f32 activations, bf16 K and V
+    read once over the 8192 positions attended."""
+    cfg = synthetic.layer_cfg(synthetic.HEADLINE)
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    assert (H, nq, nkv, hd, I, cfg["pos"] + 1) == (4096, 32, 8, 128, 12288, 8192)
+    names = {tag: b for tag, _, b in bench.layer_kernels(cfg, True)}
+    q8 = lambda r, c: r * c * 34 // 32
+    # gate_up: the weight pair, x and gamma in (f32), the Q8_0 of h out
+    assert names["gate_up_matvec"] == q8(2 * I, H) + 4 * H + 4 * H + q8(1, I) == 107000576
+    # down: the weight, the Q8_0 of h in, residual in and x out (f32)
+    assert names["down_matvec"] == q8(H, I) + q8(1, I) + 4 * H + 4 * H
+    # attention: K and V once, q in and the output (f32), plus the projection read back
+    kv = 2 * nkv * 8192 * hd * 2
+    assert names["attn_split"] == kv + 4 * nq * hd * 2 + 4 * (nq * hd + 2 * nkv * hd)
+    mv, at = bench.layer_bytes(cfg)
+    assert at == kv + 4 * nq * hd * 2
+    assert mv + at == 238765568
+
+
+def test_rocprof_kernel_name_matching():
+    gate_up = "void lq::k_mv<4, 2, 2, 3, 4>(lq::MvArgs)"
+    qkv = "void lq::k_mv<4, 2, 2, 0, 8>(lq::MvArgs)"
+    assert bench._kernel_match(gate_up, "gate_up_matvec")
+    assert not bench._kernel_match(qkv, "gate_up_matvec")
