@@ -210,6 +210,7 @@ ATTN_CASES = [
     (8, 2, 96, 0, 700, 100, 555),         # f32, head_dim 96 (generic)
     (8, 2, 512, 0, 200, 0, 200),          # f32, head_dim 512 (two chunks per lane in V)
     (4, 4, 8, 1, 130, 0, 130),            # head_dim 8: one 16-byte chunk per row
+    (32, 8, 128, 1, 65536, 0, 65536),     # long context: 64 splits of 1024 positions (16 tiles per wave)
 ]
 
 
