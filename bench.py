@@ -513,6 +513,40 @@ def measure_head(steps, torch):
             "softcap": H["softcap"]}
 
 
+def measure_attn_context(steps, torch, ctx=65536):
+    """GQA decode attention alone (split kernel + combine) with the 8B-like
+    heads at a long bf16 context, where every wave streams 16 tiles: the
+    regime in which the split kernel is bound by HBM rather than by latency.
+    Two K/V cache pairs alternate (2 x 268 MB, beyond the Infinity Cache).
+    Algorithmic bytes: K and V once, q in, the output out."""
+    import q8_matvec_gqa_amd as lq
+    n_q, n_kv, hd = 32, 8, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4000)
+    pairs = [tuple((torch.randn(n_kv * ctx * hd, device="cuda", generator=gen) * 0.5).bfloat16().view(torch.int16)
+                   for _ in range(2)) for _ in range(2)]
+    q = torch.randn(n_q * hd, device="cuda", generator=gen)
+    out = torch.empty(n_q * hd, dtype=torch.float32, device="cuda")
+    nws = lq.lq_gqa_decode_attn_workspace_size(n_q, n_kv, hd, ctx)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / math.sqrt(hd)
+
+    def calls(stream):
+        for k, v in pairs:
+            lq.lq_gqa_decode_attn(q, n_q, n_kv, hd, k, v, 1, ctx * hd, hd, ctx, 0, ctx, scale, out, ws, nws,
+                                  stream=stream)
+
+    us = graph_us(torch, calls, steps) / len(pairs)
+    nbytes = attn_bytes(n_q, n_kv, hd, ctx, 2)
+    gbs = nbytes / (us * 1e3)
+    log(f"attention n_q {n_q} n_kv {n_kv} hd {hd} bf16 x {ctx} positions: {us:.2f} us/call, {gbs:.1f} GB/s")
+    del pairs, q, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"gqa_attn_q{n_q}_kv{n_kv}_hd{hd}_bf16_ctx{ctx}", "kernel": "k_attn_split+k_attn_combine",
+            "us_per_call": round(us, 3), "bytes_per_call": nbytes, "GBps": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def calib_copy(torch, nbytes=1 << 30, reps=3):
     """A plain elementwise copy of known size (reads nbytes, writes nbytes),
     run for the PMC calibration of FETCH_SIZE / WRITE_SIZE."""
@@ -765,6 +799,7 @@ def main():
         result["q8_matmul"] = measure_matmul(32, max(5, args.steps // 10), torch)
         torch.cuda.empty_cache()
         result["q8_matmul_prefill"] = measure_matmul(512, max(3, args.steps // 20), torch)
+        result["attn_long_context"] = measure_attn_context(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
         result["ggml_formats"] = measure_ggml_formats(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
