@@ -359,6 +359,36 @@ lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const float* logits
                        float* out, const lq_moe_taps* taps,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same MoE block with Q4_0 or Q6_K expert weights (the current path's
+ * MoE runs Q6_K experts through the index-driven matvec, [CUR] section 4;
+ * [TGT] section 3.2 lists the same block op by op): route -> Q8(x) ->
+ * gate_up id-matvec -> SwiGLU + Q8 -> down id-matvec -> weighted sum, with
+ * the id-matvecs of lq_moe_q4_0_matvec_id / lq_moe_q6_k_matvec_id.
+ * gate_up_format and down_format are LQ_FMT_Q4_0 or LQ_FMT_Q6_K and name
+ * which of the two weight descriptors of each matrix is used (the other is
+ * ignored); each describes ONE expert as in lq_moe_q4_0_matvec_id: gate_up
+ * rows 2*ffn (gate rows, then up rows) by hidden columns, down rows hidden by
+ * ffn columns, the experts back to back.  hidden and ffn <= 8192 and
+ * multiples of 32 (Q4_0) or 256 (Q6_K) where they are a weight's columns.
+ * Taps, workspace, expert_scale and errors as for lq_moe_block; the y1 tap
+ * holds the gate_up outputs before SwiGLU. */
+#define LQ_FMT_Q4_0  0
+#define LQ_FMT_Q6_K  1
+typedef struct lq_moe_ggml_desc {
+    int64_t hidden, ffn, n_experts, top_k;
+    int32_t gate_up_format, down_format;
+    lq_q4_0_weight gate_up_q4_0;
+    lq_q6_k_weight gate_up_q6_k;
+    lq_q4_0_weight down_q4_0;
+    lq_q6_k_weight down_q6_k;
+    const float* expert_scale;  /* device f32 [n_experts], or NULL (all 1) */
+} lq_moe_ggml_desc;
+
+size_t lq_moe_block_ggml_workspace_size(const lq_moe_ggml_desc* m, int64_t T);
+lq_status lq_moe_block_ggml(const lq_moe_ggml_desc* m, const float* x, const float* logits, int64_t T,
+                            float* out, const lq_moe_taps* taps,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- decode layer */
 #define LQ_LAYER_PRENORM_FFN     0   /* x -> norm -> QKV -> qk-norm/RoPE -> KV append -> attn -> O + x
                                         -> norm -> gate_up -> SwiGLU -> down + x1 */

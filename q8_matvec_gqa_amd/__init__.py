@@ -65,6 +65,16 @@ class lq_moe_taps(C.Structure):
     _fields_ = [(n, _P) for n in ("ids", "w", "xq", "xd", "y1", "hq", "hd", "y2")]
 
 
+LQ_FMT_Q4_0, LQ_FMT_Q6_K = 0, 1
+
+
+class lq_moe_ggml_desc(C.Structure):
+    _fields_ = [("hidden", _I64), ("ffn", _I64), ("n_experts", _I64), ("top_k", _I64),
+                ("gate_up_format", _I32), ("down_format", _I32),
+                ("gate_up_q4_0", lq_q4_0_weight), ("gate_up_q6_k", lq_q6_k_weight),
+                ("down_q4_0", lq_q4_0_weight), ("down_q6_k", lq_q6_k_weight), ("expert_scale", _P)]
+
+
 class lq_layer_desc(C.Structure):
     _fields_ = [
         ("hidden", _I64), ("n_q", _I64), ("n_kv", _I64), ("head_dim", _I64), ("ffn", _I64),
@@ -115,6 +125,9 @@ _SIGS = {
     "lq_moe_q6_k_matvec_id": (_I32, [C.POINTER(lq_q6_k_weight), _I64, _P, _P, _I32, _P, _I64, _I64, _P, _P, _SZ,
                                       _P]),
     "lq_moe_weighted_sum": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "lq_moe_block_ggml_workspace_size": (_SZ, [C.POINTER(lq_moe_ggml_desc), _I64]),
+    "lq_moe_block_ggml": (_I32, [C.POINTER(lq_moe_ggml_desc), _P, _P, _I64, _P, C.POINTER(lq_moe_taps), _P, _SZ,
+                                 _P]),
     "lq_moe_block_workspace_size": (_SZ, [C.POINTER(lq_moe_desc), _I64]),
     "lq_moe_block": (_I32, [C.POINTER(lq_moe_desc), _P, _P, _I64, _P, C.POINTER(lq_moe_taps), _P, _SZ,
                             _P]),
@@ -336,6 +349,15 @@ def lq_moe_block_workspace_size(desc, T):
 def lq_moe_block(desc, x, logits, T, out, taps, workspace, workspace_bytes, stream=None, check=True):
     return _check(_lib.lq_moe_block(_ref(desc), _ptr(x), _ptr(logits), T, _ptr(out), _ref(taps),
                                     _ptr(workspace), workspace_bytes, _stream(stream)), check)
+
+
+def lq_moe_block_ggml_workspace_size(desc, T):
+    return _lib.lq_moe_block_ggml_workspace_size(_ref(desc), T)
+
+
+def lq_moe_block_ggml(desc, x, logits, T, out, taps, workspace, workspace_bytes, stream=None, check=True):
+    return _check(_lib.lq_moe_block_ggml(_ref(desc), _ptr(x), _ptr(logits), T, _ptr(out), _ref(taps),
+                                         _ptr(workspace), workspace_bytes, _stream(stream)), check)
 
 
 # ---------------------------------------------------------------- layer

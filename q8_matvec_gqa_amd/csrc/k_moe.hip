@@ -596,13 +596,12 @@ static void launch_qk_id_st(hipStream_t s, const QkMat& m, int rows, int cols, i
                        cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
 }
 
-// steps per row: Q4_0 up to 4, Q6_K up to 2 (cols <= 8192)
+// The id-matvec on an already gathered workspace.  Steps per row: Q4_0 up
+// to 4, Q6_K up to 2 (cols <= 8192).
 template <int FMT>
-static lq_status launch_moe_qk_matvec_id(const QkMat& m, int64_t rows, int64_t cols, int64_t E, const int8_t* xq,
-                                         const uint16_t* xd, int32_t x_per_slot, const int32_t* ids, int64_t T,
-                                         int64_t k, float* y, void* ws, hipStream_t s) {
-    lq_status st = launch_gather(ids, T * k, E, ws, y, rows, nullptr, 0, s);
-    if (st != LQ_OK) return st;
+static lq_status launch_qk_id_gathered(const QkMat& m, int64_t rows, int64_t cols, int64_t E, const int8_t* xq,
+                                       const uint16_t* xd, int32_t x_per_slot, int64_t k, const void* ws, float* y,
+                                       hipStream_t s) {
     const int32_t* w32 = static_cast<const int32_t*>(ws);
     switch ((qk_units<FMT>((int)cols) + 63) / 64) {
         case 1: launch_qk_id_st<FMT, 1, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
@@ -615,6 +614,15 @@ static lq_status launch_moe_qk_matvec_id(const QkMat& m, int64_t rows, int64_t c
             return fail(LQ_ERR_UNSUPPORTED, "moe matvec: cols > 8192");
     }
     return check_launch("moe_qk_matvec_id");
+}
+
+template <int FMT>
+static lq_status launch_moe_qk_matvec_id(const QkMat& m, int64_t rows, int64_t cols, int64_t E, const int8_t* xq,
+                                         const uint16_t* xd, int32_t x_per_slot, const int32_t* ids, int64_t T,
+                                         int64_t k, float* y, void* ws, hipStream_t s) {
+    lq_status st = launch_gather(ids, T * k, E, ws, y, rows, nullptr, 0, s);
+    if (st != LQ_OK) return st;
+    return launch_qk_id_gathered<FMT>(m, rows, cols, E, xq, xd, x_per_slot, k, ws, y, s);
 }
 
 lq_status launch_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t k, int64_t rows,
@@ -840,5 +848,96 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     }
     if ((st = launch_id_gathered(m->w_down.qs, m->w_down.d, H, I, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK)
         return st;
+    return launch_moe_weighted_sum(b.y2, b.w, T, k, H, b.ids, m->expert_scale, m->n_experts, out, s);
+}
+
+// ---- whole block, GGML-format experts ------------------------------------------
+namespace {
+struct GgmlMat {
+    QkMat m;
+    int fmt;
+    int64_t rows, cols;
+};
+
+lq_status ggml_mat(const char* fn, const char* what, int32_t fmt, const lq_q4_0_weight& q4,
+                   const lq_q6_k_weight& q6, int64_t rows, int64_t cols, GgmlMat* out) {
+    if (fmt == LQ_FMT_Q4_0) {
+        if (q4.rows != rows || q4.cols != cols || cols % 32)
+            return fail(LQ_ERR_SHAPE, "%s: %s Q4_0 weight is %lld x %lld, need %lld x %lld (cols %% 32 == 0)", fn,
+                        what, (long long)q4.rows, (long long)q4.cols, (long long)rows, (long long)cols);
+        if (!q4.qs || !q4.d) return fail(LQ_ERR_NULL, "%s: %s: NULL weight array", fn, what);
+        if (!aligned(q4.qs, 16) || !aligned(q4.d, 2)) return fail(LQ_ERR_ALIGN, "%s: %s: qs must be 16-byte aligned", fn, what);
+        *out = GgmlMat{QkMat{q4.qs, nullptr, nullptr, q4.d}, QK_Q4_0, rows, cols};
+        return LQ_OK;
+    }
+    if (fmt == LQ_FMT_Q6_K) {
+        if (q6.rows != rows || q6.cols != cols || cols % 256)
+            return fail(LQ_ERR_SHAPE, "%s: %s Q6_K weight is %lld x %lld, need %lld x %lld (cols %% 256 == 0)", fn,
+                        what, (long long)q6.rows, (long long)q6.cols, (long long)rows, (long long)cols);
+        if (!q6.ql || !q6.qh || !q6.sc || !q6.d) return fail(LQ_ERR_NULL, "%s: %s: NULL weight array", fn, what);
+        if (!aligned(q6.ql, 16) || !aligned(q6.qh, 16) || !aligned(q6.sc, 8) || !aligned(q6.d, 2))
+            return fail(LQ_ERR_ALIGN, "%s: %s: ql and qh must be 16-byte aligned, sc 8-byte aligned", fn, what);
+        *out = GgmlMat{QkMat{q6.ql, q6.qh, q6.sc, q6.d}, QK_Q6_K, rows, cols};
+        return LQ_OK;
+    }
+    return fail(LQ_ERR_SHAPE, "%s: %s format %d (LQ_FMT_Q4_0 or LQ_FMT_Q6_K)", fn, what, (int)fmt);
+}
+
+lq_status launch_ggml_id(const GgmlMat& g, int64_t E, const int8_t* xq, const uint16_t* xd, int32_t x_per_slot,
+                         int64_t k, const void* ws, float* y, hipStream_t s) {
+    if (g.fmt == QK_Q4_0) return launch_qk_id_gathered<QK_Q4_0>(g.m, g.rows, g.cols, E, xq, xd, x_per_slot, k, ws, y, s);
+    return launch_qk_id_gathered<QK_Q6_K>(g.m, g.rows, g.cols, E, xq, xd, x_per_slot, k, ws, y, s);
+}
+
+// the buffers are those of the Q8_0 block of the same sizes
+lq_moe_desc as_q8_desc(const lq_moe_ggml_desc* m) {
+    lq_moe_desc d{};
+    d.hidden = m->hidden; d.ffn = m->ffn; d.n_experts = m->n_experts; d.top_k = m->top_k;
+    d.expert_scale = m->expert_scale;
+    return d;
+}
+}  // namespace
+
+extern "C" size_t lq_moe_block_ggml_workspace_size(const lq_moe_ggml_desc* m, int64_t T) {
+    if (!m || T < 0 || m->top_k <= 0 || m->n_experts <= 0) return 0;
+    const lq_moe_desc d = as_q8_desc(m);
+    return moe_layout(&d, T, nullptr, nullptr).total;
+}
+
+extern "C" lq_status lq_moe_block_ggml(const lq_moe_ggml_desc* m, const float* x, const float* logits, int64_t T,
+                                       float* out, const lq_moe_taps* taps, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    const char* fn = "lq_moe_block_ggml";
+    if (!m) return fail(LQ_ERR_NULL, "%s: descriptor is NULL", fn);
+    const int64_t H = m->hidden, I = m->ffn, E = m->n_experts, k = m->top_k;
+    if (T < 0 || H <= 0 || I <= 0 || H % 32 || I % 32 || k <= 0 || k > E)
+        return fail(LQ_ERR_SHAPE, "%s: T=%lld hidden=%lld ffn=%lld E=%lld k=%lld", fn, (long long)T, (long long)H,
+                    (long long)I, (long long)E, (long long)k);
+    GgmlMat gu{}, dn{};
+    lq_status st = ggml_mat(fn, "gate_up", m->gate_up_format, m->gate_up_q4_0, m->gate_up_q6_k, 2 * I, H, &gu);
+    if (st == LQ_OK) st = ggml_mat(fn, "down", m->down_format, m->down_q4_0, m->down_q6_k, H, I, &dn);
+    if (st != LQ_OK) return st;
+    if (H > 8192 || I > 8192 || E > kMoeMaxExperts || k > 32 || 2 * I * E > 0x7fffffffLL || H * E > 0x7fffffffLL)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: hidden and ffn <= 8192, E <= %d, k <= 32", fn, kMoeMaxExperts);
+    if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
+    if (T == 0) return LQ_OK;
+    if (!x || !logits || !out) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (!aligned(x, 16) || !aligned(logits, 4) || !aligned(out, 4) || !aligned(m->expert_scale, 4))
+        return fail(LQ_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+    const lq_moe_desc d = as_q8_desc(m);
+    const size_t need = moe_layout(&d, T, nullptr, nullptr).total;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-byte aligned), got %zu", fn, need,
+                    workspace_bytes);
+    MoeBuffers b = moe_layout(&d, T, static_cast<char*>(workspace), taps);
+    hipStream_t s = as_stream(stream);
+    const int64_t S = T * k;
+    const int64_t prep_grid = 1 + (T * (H / 32) + kPrepQuantBlocks - 1) / kPrepQuantBlocks;
+    hipLaunchKernelGGL(k_moe_prep, dim3((unsigned)prep_grid), dim3(kGatherThreads), 0, s, logits, x, (int)T, (int)E,
+                       (int)k, (int)H, b.ids, b.w, static_cast<int32_t*>(b.gather), b.xq, b.xd, b.y1, 2 * I, b.y2, H);
+    if ((st = check_launch("moe_prep")) != LQ_OK) return st;
+    if ((st = launch_ggml_id(gu, E, b.xq, b.xd, 0, k, b.gather, b.y1, s)) != LQ_OK) return st;
+    if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
+    if ((st = launch_ggml_id(dn, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK) return st;
     return launch_moe_weighted_sum(b.y2, b.w, T, k, H, b.ids, m->expert_scale, m->n_experts, out, s);
 }

@@ -228,6 +228,30 @@ def test_moe_validation():
     assert st(lq.lq_moe_block, bad, A, A, 16, A, None, A, need) == lq.LQ_ERR_SHAPE
 
 
+def test_moe_block_ggml_validation():
+    H, I, E, k = 2816, 704, 128, 8
+    gu6, dn4 = lq.lq_q6_k_weight(A, A, A, A, 2 * I, H), lq.lq_q4_0_weight(A, A, H, I)
+
+    def desc(gf=lq.LQ_FMT_Q6_K, df=lq.LQ_FMT_Q4_0, gu=gu6, dn=dn4, dn6=lq.lq_q6_k_weight()):
+        return lq.lq_moe_ggml_desc(H, I, E, k, gf, df, gate_up_q6_k=gu, down_q4_0=dn, down_q6_k=dn6)
+
+    d = desc()
+    need = lq.lq_moe_block_ggml_workspace_size(d, 16)
+    assert need == lq.lq_moe_block_workspace_size(
+        lq.lq_moe_desc(H, I, E, k, lq.lq_q8_weight(A, A, 2 * I, H), lq.lq_q8_weight(A, A, H, I)), 16)
+    assert st(lq.lq_moe_block_ggml, None, A, A, 16, A, None, A, need) == lq.LQ_ERR_NULL
+    assert st(lq.lq_moe_block_ggml, d, A, A, 16, A, None, A, need - 1) == lq.LQ_ERR_WORKSPACE
+    assert st(lq.lq_moe_block_ggml, d, A, A, 0, A, None, A, need) == lq.LQ_OK          # T == 0: no launch
+    assert st(lq.lq_moe_block_ggml, desc(gf=7), A, A, 16, A, None, A, need) == lq.LQ_ERR_SHAPE
+    # Q6_K down would need ffn % 256 == 0 (704 is not); a wrong row count
+    assert st(lq.lq_moe_block_ggml, desc(df=lq.LQ_FMT_Q6_K, dn6=lq.lq_q6_k_weight(A, A, A, A, H, I)), A, A, 16, A,
+              None, A, need) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_block_ggml, desc(gu=lq.lq_q6_k_weight(A, A, A, A, 2 * I - 1, H)), A, A, 16, A, None, A,
+              need) == lq.LQ_ERR_SHAPE
+    assert st(lq.lq_moe_block_ggml, desc(dn=lq.lq_q4_0_weight(A + 4, A, H, I)), A, A, 16, A, None, A,
+              need) == lq.LQ_ERR_ALIGN
+
+
 def _layer_desc(**over):
     H, nq, nkv, hd, I, ctx = 4096, 32, 8, 128, 12288, 8192
     d = lq.lq_layer_desc(

@@ -255,3 +255,81 @@ def test_moe_block_teacher_forced(scaled):
         print(f"[moe] free-running max rel err {err:.2e}; {touched} experts touched", flush=True)
     else:
         print(f"[moe] {flips} code flips at rounding boundaries; {touched} experts touched", flush=True)
+
+
+def _ggml_experts(fmt, r, rows, cols, E):
+    """E experts of random GGML blocks ([E*rows] rows), packed by the
+    library's host helper and uploaded; the struct describes one expert."""
+    if fmt == "q4_0":
+        b = synthetic.q4_0_blocks(r, E * rows, cols)
+        qs = np.zeros((E * rows, cols // 2), np.uint8)
+        d = np.zeros((E * rows, cols // 32), np.uint16)
+        lq.lq_q4_0_pack_ggml(b, E * rows, cols, qs, d)
+        return b, lq.q4_0_weight(dev(qs), dev(d), rows, cols)
+    b = synthetic.q6_k_blocks(r, E * rows, cols)
+    ql = np.zeros((E * rows, cols // 2), np.uint8)
+    qh = np.zeros((E * rows, cols // 4), np.uint8)
+    sc = np.zeros((E * rows, cols // 16), np.int8)
+    d = np.zeros((E * rows, cols // 256), np.uint16)
+    lq.lq_q6_k_pack_ggml(b, E * rows, cols, ql, qh, sc, d)
+    return b, lq.q6_k_weight(dev(ql), dev(qh), dev(sc), dev(d), rows, cols)
+
+
+@pytest.mark.parametrize("gu_fmt,dn_fmt,small", [
+    ("q6_k", "q4_0", False),     # the MoE workload at full size, with the pages' formats (Q6_K gate/up, Q4_0 down)
+    ("q4_0", "q6_k", True),      # the other pairing: 16 experts, 5 tokens, top-4, hidden 512, ffn 256
+])
+def test_moe_block_ggml_teacher_forced(gu_fmt, dn_fmt, small):
+    """The MoE block on GGML-format experts: routing, Q8(x), each slot's
+    gate_up and down id-matvec against the pinned oracle matvec of its
+    expert fed the GPU's own inputs, the Q8_0 of h near the oracle's, and the
+    weighted sum."""
+    torch = torch_mod()
+    r = np.random.default_rng(31 if small else 32)
+    if small:
+        T_, H, I, E, k = 5, 512, 256, 16, 4
+        x = synthetic.activations(r, T_, H)
+        logits = r.standard_normal((T_, E)).astype(np.float32)
+    else:
+        name = list(synthetic.MOE_WORKLOADS)[0]
+        cfg, w = synthetic.moe_inputs(name, seed=6)
+        T_, H, I, E, k = cfg["tokens"], cfg["hidden"], cfg["ffn"], cfg["n_experts"], cfg["top_k"]
+        x, logits = w["x"], w["logits"]
+    print(f"[moe ggml] gate_up {gu_fmt}, down {dn_fmt}, T={T_} H={H} I={I} E={E} k={k}", flush=True)
+    bgu, Wgu = _ggml_experts(gu_fmt, r, 2 * I, H, E)
+    bdn, Wdn = _ggml_experts(dn_fmt, r, H, I, E)
+    fmt = {"q4_0": lq.LQ_FMT_Q4_0, "q6_k": lq.LQ_FMT_Q6_K}
+    d = lq.lq_moe_ggml_desc(H, I, E, k, fmt[gu_fmt], fmt[dn_fmt])
+    setattr(d, "gate_up_" + gu_fmt, Wgu)
+    setattr(d, "down_" + dn_fmt, Wdn)
+    e = lambda n, dt: torch.empty(n, dtype=dt, device="cuda")
+    bufs = dict(ids=e(T_ * k, torch.int32), w=e(T_ * k, torch.float32), xq=e(T_ * H, torch.int8),
+                xd=e(T_ * H // 32, torch.int16), y1=e(T_ * k * 2 * I, torch.float32), hq=e(T_ * k * I, torch.int8),
+                hd=e(T_ * k * I // 32, torch.int16), y2=e(T_ * k * H, torch.float32))
+    taps = lq.lq_moe_taps(**{n: v.data_ptr() for n, v in bufs.items()})
+    nws = lq.lq_moe_block_ggml_workspace_size(d, T_)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    out = torch.empty(T_ * H, dtype=torch.float32, device="cuda")
+    lq.lq_moe_block_ggml(d, dev(x), dev(logits), T_, out, taps, ws, nws)
+    sync()
+    G = {n: host(v) for n, v in bufs.items()}
+    G["xd"], G["hd"] = G["xd"].view(np.uint16), G["hd"].view(np.uint16)
+    ids = G["ids"].reshape(T_, k)
+    rid, rw = oracle.moe_route(logits, k)
+    assert np.array_equal(ids, rid)
+    assert_close(G["w"].reshape(T_, k), rw, "route weights")
+    xq, xd = oracle.q8_quantize(x)
+    assert np.array_equal(G["xq"].reshape(T_, H), xq) and np.array_equal(G["xd"].reshape(T_, H // 32), xd)
+    y1 = G["y1"].reshape(T_, k, 2 * I)
+    hq, hd = G["hq"].reshape(T_, k, I), G["hd"].reshape(T_, k, I // 32)
+    y2 = G["y2"].reshape(T_, k, H)
+    for t in range(T_):
+        for s in range(k):
+            ex = ids[t, s]
+            assert_close(y1[t, s], oracle.q_matvec(gu_fmt, bgu[ex * 2 * I:(ex + 1) * 2 * I], 2 * I, H, xq[t], xd[t]),
+                         f"y1 {t},{s}")
+            assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1[t, s, :I], y1[t, s, I:]), f"h {t},{s}")
+            assert_close(y2[t, s], oracle.q_matvec(dn_fmt, bdn[ex * H:(ex + 1) * H], H, I, hq[t, s], hd[t, s]),
+                         f"y2 {t},{s}")
+    want = np.einsum("ts,tsh->th", G["w"].reshape(T_, k).astype(np.float64), y2.astype(np.float64))
+    assert_close(host(out).reshape(T_, H), want, "weighted sum")
