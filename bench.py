@@ -479,6 +479,59 @@ def measure_moe_formats(steps, torch):
     return out
 
 
+def measure_moe_block_ggml(steps, torch):
+    """The whole MoE block (lq_moe_block_ggml) on the pages' expert formats,
+    Q6_K gate/up and Q4_0 down, at the MoE workload (16 tokens, top-8 of 128
+    experts), R replicas of all experts (>= 1.5 GB) with their own logits.
+    Algorithmic bytes: the touched experts' gate/up and down weights in their
+    formats, plus x, logits and the output (f32)."""
+    import q8_matvec_gqa_amd as lq
+    c = dict(synthetic.MOE_WORKLOADS["moe_e128_top8_t16"])
+    H, I, E, T, k = c["hidden"], c["ffn"], c["n_experts"], c["tokens"], c["top_k"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7000)
+
+    def rbytes(*shape):
+        return torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=gen)
+
+    def f16(shape, scale):
+        return (torch.randn(shape, device="cuda", generator=gen).abs() * scale).half().view(torch.int16)
+
+    expert_bytes = 2 * I * H * 210 / 256 + H * I * 18 / 32
+    R = max(2, math.ceil(1.5e9 / (E * expert_bytes)))
+    reps = []
+    for _ in range(R):
+        n = E * 2 * I
+        gu = lq.q6_k_weight(rbytes(n, H // 2), rbytes(n, H // 4), rbytes(n, H // 16).view(torch.int8),
+                            f16((n, H // 256), 2e-5), 2 * I, H)
+        dn = lq.q4_0_weight(rbytes(E * H, I // 2), f16((E * H, I // 32), 0.02 / 8), H, I)
+        d = lq.lq_moe_ggml_desc(H, I, E, k, lq.LQ_FMT_Q6_K, lq.LQ_FMT_Q4_0, gate_up_q6_k=gu, down_q4_0=dn)
+        d._keep = (gu, dn)
+        logits = torch.randn(T, E, device="cuda", generator=gen)
+        touched = int(torch.unique(torch.topk(logits, k, dim=1).indices).numel())
+        reps.append((d, logits, touched))
+    x = torch.randn(T, H, device="cuda", generator=gen)
+    out = torch.empty(T, H, device="cuda")
+    nws = lq.lq_moe_block_ggml_workspace_size(reps[0][0], T)
+    work = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def calls(stream):
+        for d, logits, _ in reps:
+            lq.lq_moe_block_ggml(d, x, logits, T, out, None, work, nws, stream=stream)
+
+    us = graph_us(torch, calls, steps) / R
+    touched = sum(t for _, _, t in reps) / R
+    nbytes = touched * expert_bytes + T * H * 4 * 2 + T * E * 4
+    gbs = nbytes / (us * 1e3)
+    log(f"moe block q6_k gate/up + q4_0 down, 128 experts, 16 tokens: {us:.2f} us/block, {touched:.1f} touched, "
+        f"{gbs:.1f} GB/s")
+    del reps, work
+    torch.cuda.empty_cache()
+    return {"workload": "moe_e128_top8_t16_q6_k_gate_up_q4_0_down", "replicas": R, "us_per_block": round(us, 3),
+            "us_per_token": round(us / T, 3), "touched_experts": round(touched, 1), "GBps": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def measure_head(steps, torch):
     """The output head (final norm, f16 vocab projection, softcap) at the
     Gemma-4 shape: vocab x hidden f16 weights (1.5 GB, beyond the Infinity
@@ -804,6 +857,7 @@ def main():
         result["ggml_formats"] = measure_ggml_formats(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
         result["moe_ggml_formats"] = measure_moe_formats(max(5, args.steps // 5), torch)
+        result["moe_block_ggml"] = measure_moe_block_ggml(max(5, args.steps // 5), torch)
         torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)
