@@ -176,10 +176,29 @@ lq_status lq_swiglu_q8(const float* gate_up, int64_t n_rows, int64_t ffn,
 lq_status lq_q8_matvec(const lq_q8_weight* w, const int8_t* x_qs, const uint16_t* x_d,
                        const float* residual, float* y, void* stream);
 
-/* Test tap: the int32 block dots dot[r,b] that lq_q8_matvec forms, written
- * to dots (device int32 [rows, cols/32]), computed by the same device code. */
+/* Test tap: the int32 block dots dot[r,b] of the Q8_0 matvec ([LAT] Current
+ * Design: int8 x int8 products summed into int32 per block), written to dots
+ * (device int32 [rows, cols/32]).  For cols <= 16384 they come from the
+ * fused matvec kernel that lq_q8_matvec and lq_decode_layer run (same
+ * weight loads, lane-to-slice mapping and block-dot routine, with an
+ * epilogue that stores the dots instead of y); for longer rows from the
+ * kernel lq_q8_matvec runs there.  x_qs: device int8 [cols], 16-byte
+ * aligned.  No scales are read: the dots do not depend on them. */
 lq_status lq_q8_block_dots(const lq_q8_weight* w, const int8_t* x_qs, int32_t* dots,
                            void* stream);
+
+/* Test tap: the same block dots when the fused matvec builds its Q8_0 input
+ * in-kernel from a float vector, as the decode layer's projections do
+ * ([CUR] section 4: rms_norm F=2 weighted, F=1 unit): norm == 0 quantizes
+ * x as lq_q8_quantize_act; norm == 1 first applies y = gamma * x /
+ * sqrt(mean(x^2) + eps) (gamma NULL: unit weight), as lq_rmsnorm_q8.
+ * The Q8_0 input the kernel built is written to x_qs_out (device int8
+ * [cols], 8-byte aligned) and x_d_out (device f16 bits [cols/32]), so the
+ * dots can be checked against it.  x, gamma: device f32 [cols], 16-byte
+ * aligned.  cols <= 16384 (LQ_ERR_UNSUPPORTED beyond). */
+lq_status lq_q8_block_dots_f32(const lq_q8_weight* w, const float* x, int32_t norm, const float* gamma,
+                               float eps, int32_t* dots, int8_t* x_qs_out, uint16_t* x_d_out,
+                               void* stream);
 
 /* Q4_0 and Q6_K weight matvecs against a Q8_0 activation, on the int8 x
  * int8 path of [LAT] Current Design: an exact int32 dot over each run of
@@ -335,7 +354,9 @@ lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t T, int64_t
 
 /* Whole MoE FFN block for T tokens ([CUR] section 3 item i, fused path):
  * route -> Q8(x) -> gate_up id-matvec -> SwiGLU + Q8 -> down id-matvec ->
- * weighted sum.  No host synchronization. */
+ * weighted sum.  No host synchronization.  n_experts <= 1024 and
+ * top_k <= 32 (the router's limits, as lq_moe_route_topk), T * top_k <=
+ * 8192; LQ_ERR_UNSUPPORTED beyond. */
 typedef struct lq_moe_desc {
     int64_t hidden, ffn, n_experts, top_k;
     lq_q8_weight w_gate_up;   /* one expert: rows 2*ffn (gate rows, then up rows), cols hidden */
@@ -442,6 +463,10 @@ typedef struct lq_layer_taps {
     int8_t* nq; uint16_t* nd;  /* Q8 of the post-attention norm (PRENORM_FFN) */
     float* h;                  /* silu(gate) * up [ffn] */
     int8_t* hq; uint16_t* hd;  /* Q8 of h */
+    float* qkv_post;           /* q and k after the per-head norm and RoPE, v after its optional
+                                  unit norm, as f32 before the attention scale and before the
+                                  conversion to the cache dtype [n_q*hd + 2*n_kv*hd]: the cache
+                                  rows written at pos are exactly cvt(k), cvt(v) of these */
 } lq_layer_taps;
 
 /* One decode token through one layer ([CUR] section 3 sequence; [TGT]

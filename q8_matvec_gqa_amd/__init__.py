@@ -89,7 +89,8 @@ class lq_layer_desc(C.Structure):
 
 
 class lq_layer_taps(C.Structure):
-    _fields_ = [(n, _P) for n in ("xq", "xd", "qkv", "attn", "aq", "ad", "x1", "nq", "nd", "h", "hq", "hd")]
+    _fields_ = [(n, _P) for n in ("xq", "xd", "qkv", "attn", "aq", "ad", "x1", "nq", "nd", "h", "hq", "hd",
+                                  "qkv_post")]
 
 
 _W = C.POINTER(lq_q8_weight)
@@ -108,6 +109,7 @@ _SIGS = {
     "lq_q4_0_matvec": (_I32, [C.POINTER(lq_q4_0_weight), _P, _P, _P, _P, _P]),
     "lq_q6_k_matvec": (_I32, [C.POINTER(lq_q6_k_weight), _P, _P, _P, _P, _P]),
     "lq_q8_block_dots": (_I32, [_W, _P, _P, _P]),
+    "lq_q8_block_dots_f32": (_I32, [_W, _P, _I32, _P, _F, _P, _P, _P, _P]),
     "lq_rmsnorm_rope": (_I32, [_P, _I64, _I64, _I64, _P, _F, _P, _P, _I64, _I64, _P]),
     "lq_kv_append": (_I32, [_P, _P, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _P]),
     "lq_gqa_decode_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
@@ -267,6 +269,11 @@ def lq_q6_k_matvec(w, x_qs, x_d, residual, y, stream=None, check=True):
 
 def lq_q8_block_dots(w, x_qs, dots, stream=None, check=True):
     return _check(_lib.lq_q8_block_dots(_ref(w), _ptr(x_qs), _ptr(dots), _stream(stream)), check)
+
+
+def lq_q8_block_dots_f32(w, x, norm, gamma, eps, dots, x_qs_out, x_d_out, stream=None, check=True):
+    return _check(_lib.lq_q8_block_dots_f32(_ref(w), _ptr(x), int(norm), _ptr(gamma), eps, _ptr(dots),
+                                            _ptr(x_qs_out), _ptr(x_d_out), _stream(stream)), check)
 
 
 # ---------------------------------------------------------------- norm / RoPE / KV

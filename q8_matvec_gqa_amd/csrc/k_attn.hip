@@ -86,6 +86,8 @@ struct AttnArgs {
     float qscale;            // scale * log2(e)
     float cap2;              // score softcap times log2(e) (scores are kept in the log2 domain); 0: none
     float eps;
+    float* tap_post;         // fused prologue, optional: q, k, v heads after norm / RoPE, before the
+                             // attention scale and the cache conversion [n_q*hd + 2*n_kv*hd]
 };
 
 }  // namespace
@@ -140,7 +142,7 @@ __device__ __forceinline__ void head_load(HeadIn<EPL>& in, const HeadSrc& h, con
 // row), and dst then holds the stored value.
 template <typename KV, int EPL>
 __device__ __forceinline__ void head_finish(const HeadIn<EPL>& in, const HeadSrc& h, int hd, float eps, int lane,
-                                            float* dst, KV* kv_dst) {
+                                            float* dst, KV* kv_dst, float* tap) {
     const int half = hd >> 1;
     const bool wg = h.gamma != nullptr;
     float own[EPL];
@@ -162,6 +164,7 @@ __device__ __forceinline__ void head_finish(const HeadIn<EPL>& in, const HeadSrc
                 const float bv = in.par[j] * rinv * (wg ? in.gb[j] : 1.0f);
                 y = i < half ? av * in.cs[j] - bv * in.sn[j] : bv * in.sn[j] + av * in.cs[j];
             }
+            if (tap) tap[i] = y;
             y *= h.scale;
             if (kv_dst) {
                 if constexpr (sizeof(KV) == 4) {
@@ -234,7 +237,7 @@ __device__ __forceinline__ void head_load_v(HeadInV<EPL>& in, const HeadSrc& h, 
 
 template <typename KV, int EPL>
 __device__ __forceinline__ void head_finish_v(const HeadInV<EPL>& in, const HeadSrc& h, float eps, int lane,
-                                              float* dst, KV* kv_dst) {
+                                              float* dst, KV* kv_dst, float* tap) {
     constexpr int HD = 64 * EPL;
     const bool wg = h.gamma != nullptr;
     float ss = 0.0f;
@@ -251,8 +254,10 @@ __device__ __forceinline__ void head_finish_v(const HeadInV<EPL>& in, const Head
             const float bv = half_swap(av, lane);
             y[j] = lane < 32 ? av * in.cs[j] - bv * in.sn[j] : bv * in.sn[j] + av * in.cs[j];
         }
-        y[j] *= h.scale;
     }
+    if (tap) store_run<EPL>(tap + lane * EPL, y);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) y[j] *= h.scale;
     if (kv_dst) {
         KV* row = kv_dst + lane * EPL;
         if constexpr (sizeof(KV) == 4) {
@@ -424,18 +429,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
         if constexpr (VEC) head_load_v<EPL>(in, src, a.rope_cos, a.rope_sin, lane);
         else head_load<EPL>(in, src, a.rope_cos, a.rope_sin, hd, lane);
     };
-    auto item_fin = [&](const HIn& in, const HeadSrc& src, float* dst, KV* kv) {
-        if constexpr (VEC) head_finish_v<KV, EPL>(in, src, a.eps, lane, dst, kv);
-        else head_finish<KV, EPL>(in, src, hd, a.eps, lane, dst, kv);
+    auto item_fin = [&](const HIn& in, const HeadSrc& src, float* dst, KV* kv, float* tap) {
+        if constexpr (VEC) head_finish_v<KV, EPL>(in, src, a.eps, lane, dst, kv, tap);
+        else head_finish<KV, EPL>(in, src, hd, a.eps, lane, dst, kv, tap);
     };
+    // the optional tap of the prologue's results: the query heads from split
+    // 0 of each kv head, k and v from the workgroup that appends them
     auto item_run = [&](int i, const HIn& in, const HeadSrc& src) {
         if (i < n_qi) {
-            item_fin(in, src, q_lds + (wave + NW * i) * HDM, nullptr);
+            const int h = wave + NW * i;
+            float* tap = (a.tap_post && split == 0) ? a.tap_post + (int64_t)(g * G + h) * hd : nullptr;
+            item_fin(in, src, q_lds + h * HDM, nullptr, tap);
         } else {
             const int64_t row = (int64_t)g * a.head_stride + pos_new * a.pos_stride;
             const int kv = kv_item(i);
             KV* cache = static_cast<KV*>(kv == 0 ? a.kc_w : a.vc_w);
-            item_fin(in, src, kv_new[kv], cache + row);
+            float* tap = a.tap_post ? a.tap_post + (int64_t)(a.n_q + kv * a.n_kv + g) * hd : nullptr;
+            item_fin(in, src, kv_new[kv], cache + row, tap);
         }
     };
 
@@ -990,8 +1000,9 @@ lq_status launch_attention_fused(const float* qkv, int64_t n_q, int64_t n_kv, in
                                  const float* rope_cos_row, const float* rope_sin_row, void* kc, void* vc,
                                  int32_t kv_dtype, int64_t head_stride, int64_t pos_stride, int64_t start,
                                  int64_t len, float scale, float softcap, float* out, void* ws, hipStream_t s,
-                                 LaunchMarks* marks) {
+                                 LaunchMarks* marks, float* tap_post) {
     AttnArgs a{};
+    a.tap_post = tap_post;
     a.cap2 = softcap > 0.0f ? softcap * kLog2e : 0.0f;
     a.q = qkv; a.kc = kc; a.kc_w = kc; a.vc_w = vc; a.out = out;
     a.g_q = g_q; a.g_k = g_k; a.rope_cos = rope_cos_row; a.rope_sin = rope_sin_row;
@@ -1011,12 +1022,10 @@ extern "C" size_t lq_gqa_decode_attn_workspace_size(int64_t n_q, int64_t n_kv, i
     return attn_workspace_bytes(n_q, n_kv, head_dim, len);
 }
 
-extern "C" lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
-                                        const void* k_cache, const void* v_cache, int32_t kv_dtype,
-                                        int64_t head_stride, int64_t pos_stride, int64_t max_ctx,
-                                        int64_t start, int64_t len, float scale, float* out,
-                                        void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "lq_gqa_decode_attn";
+namespace lq {
+lq_status check_attention_args(const char* fn, const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                               const void* k_cache, const void* v_cache, int32_t kv_dtype, int64_t head_stride,
+                               int64_t pos_stride, int64_t max_ctx, int64_t start, int64_t len, const float* out) {
     if (n_q < 0 || n_kv <= 0 || head_dim <= 0 || (n_q % n_kv) || head_dim % 4)
         return fail(LQ_ERR_SHAPE, "%s: n_q=%lld n_kv=%lld head_dim=%lld (need n_q %% n_kv == 0, head_dim %% 4 == 0)",
                     fn, (long long)n_q, (long long)n_kv, (long long)head_dim);
@@ -1038,11 +1047,24 @@ extern "C" lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_k
                     (head_stride * es) % 16))
         return fail(LQ_ERR_ALIGN, "%s: caches and strides must be 16-byte aligned", fn);
     if (!aligned(q, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "%s: q/out misaligned", fn);
+    if (n_q > 65535) return fail(LQ_ERR_UNSUPPORTED, "%s: too many query heads", fn);
+    return LQ_OK;
+}
+}  // namespace lq
+
+extern "C" lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                                        const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                        int64_t head_stride, int64_t pos_stride, int64_t max_ctx,
+                                        int64_t start, int64_t len, float scale, float* out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "lq_gqa_decode_attn";
+    lq_status st = check_attention_args(fn, q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_stride,
+                                        pos_stride, max_ctx, start, len, out);
+    if (st != LQ_OK || n_q == 0) return st;
     const size_t need = attn_workspace_bytes(n_q, n_kv, head_dim, len);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return fail(LQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn, need,
                     workspace_bytes);
-    if (n_q > 65535) return fail(LQ_ERR_UNSUPPORTED, "%s: too many query heads", fn);
     return launch_attention(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_stride, pos_stride, start,
                             len, scale, out, workspace, as_stream(stream));
 }

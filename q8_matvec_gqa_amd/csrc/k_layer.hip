@@ -117,7 +117,7 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
 
 lq_status validate_taps(const lq_layer_taps* t) {
     if (!t) return LQ_OK;
-    const void* f32s[] = {t->qkv, t->attn, t->x1, t->h, t->xq, t->aq, t->nq, t->hq};
+    const void* f32s[] = {t->qkv, t->attn, t->x1, t->h, t->xq, t->aq, t->nq, t->hq, t->qkv_post};
     for (const void* p : f32s)
         if (p && !aligned(p, 16)) return fail(LQ_ERR_ALIGN, "lq_decode_layer: tap buffers must be 16-byte aligned");
     const void* d16[] = {t->xd, t->ad, t->nd, t->hd};
@@ -206,7 +206,7 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
                                      L->rope_cos + pos * half, L->rope_sin + pos * half, L->k_cache, L->v_cache,
                                      L->kv_dtype, head_stride, pos_stride, start, len, L->attn_scale,
                                      L->attn_softcap, b.attn,
-                                     b.attn_ws, s, &mk)) != LQ_OK)
+                                     b.attn_ws, s, &mk, T.qkv_post)) != LQ_OK)
         return st;
     // O projection, quantizing the attention output in-kernel
     m = MvArgs{};

@@ -240,6 +240,27 @@ __device__ __forceinline__ float gate_act(float z, int act) {
 template <int NCH, int RPW, int EPI, bool XL>
 __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int lane, const RowGroup<NCH, RPW>& G,
                                               const XAct<NCH, XL>& x, float* hs) {
+    if constexpr (EPI == EPI_DOTS) {
+        // the block dots exactly as the other epilogues form them; the even
+        // lane of each block writes it (slices past the last column, whose
+        // loads were clamped, and rows past the end write nothing)
+        const int nb = a.cols >> 5;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int64_t r = g * RPW + i;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                int4 x4;
+                float xsc;
+                x.get(c, lane, x4, xsc);
+                const int p = dot16(G.w[i][c], x4);
+                const int blk = p + dpp_i<kQuadXor1>(p);
+                const int off = c * 1024 + lane * 16;
+                if (!(lane & 1) && r < a.rows && off < a.cols) a.dots[r * nb + (off >> 5)] = blk;
+            }
+        }
+        return;
+    }
     float acc[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -342,7 +363,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
             const int b = threadIdx.x + NT * k;
-            sc_early[k] = a.xd[b < nb ? b : nb - 1];
+            sc_early[k] = EPI == EPI_DOTS ? 0u : a.xd[b < nb ? b : nb - 1];   // the dots use no scales
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -360,7 +381,7 @@ __global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvA
             x.s[c] = 0.0f;
             if (off < a.cols) {
                 x.v[c] = *reinterpret_cast<const int4*>(a.xq + off);
-                x.s[c] = f16_to_f32(a.xd[off >> 5]);
+                x.s[c] = EPI == EPI_DOTS ? 0.0f : f16_to_f32(a.xd[off >> 5]);
             }
         }
     } else {
@@ -561,6 +582,7 @@ lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per
     LQ_PE(PRO_Q8, EPI_STORE) LQ_PE(PRO_Q8, EPI_RESID)
     LQ_PE(PRO_QUANT, EPI_STORE) LQ_PE(PRO_QUANT, EPI_RESID)
     LQ_PE(PRO_NORM, EPI_STORE) LQ_PE(PRO_NORM, EPI_SWIGLU_Q8)
+    LQ_PE(PRO_Q8, EPI_DOTS) LQ_PE(PRO_QUANT, EPI_DOTS) LQ_PE(PRO_NORM, EPI_DOTS)
 #undef LQ_PE
     return fail(LQ_ERR_UNSUPPORTED, "fused matvec: prologue %d / epilogue %d not built", pro, epi);
 }
@@ -653,6 +675,35 @@ extern "C" lq_status lq_q8_block_dots(const lq_q8_weight* w, const int8_t* x_qs,
     if (!aligned(x_qs, 16) || !aligned(dots, 4))
         return fail(LQ_ERR_ALIGN, "lq_q8_block_dots: x_qs must be 16-byte aligned");
     if (w->cols > 0x7fffffffLL) return fail(LQ_ERR_UNSUPPORTED, "lq_q8_block_dots: cols too large");
+    if (w->cols <= kMaxCols && w->rows <= 0x7fffffffLL) {
+        // the fused kernel lq_q8_matvec runs, with its dots written out
+        MvArgs a{};
+        a.wq = w->qs; a.wd = w->d; a.rows = (int)w->rows; a.cols = (int)w->cols;
+        a.xq = x_qs; a.dots = dots;
+        return launch_mv(a, PRO_Q8, EPI_DOTS, as_stream(stream), kMvWgPerCu);
+    }
     return launch_q8_matvec(w->qs, w->d, w->rows, w->cols, x_qs, nullptr, nullptr, nullptr, dots,
                             as_stream(stream));
+}
+
+extern "C" lq_status lq_q8_block_dots_f32(const lq_q8_weight* w, const float* x, int32_t norm, const float* gamma,
+                                          float eps, int32_t* dots, int8_t* x_qs_out, uint16_t* x_d_out,
+                                          void* stream) {
+    const char* fn = "lq_q8_block_dots_f32";
+    if (!w) return fail(LQ_ERR_NULL, "%s: weight descriptor is NULL", fn);
+    lq_status st = check_weight(w, fn);
+    if (st != LQ_OK || w->rows == 0) return st;
+    if (!x || !dots || !x_qs_out || !x_d_out) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);
+    if (norm != 0 && norm != 1) return fail(LQ_ERR_SHAPE, "%s: norm must be 0 or 1", fn);
+    if (!(eps >= 0.0f)) return fail(LQ_ERR_SHAPE, "%s: eps must be >= 0", fn);
+    if (!aligned(x, 16) || (gamma && !aligned(gamma, 16)) || !aligned(dots, 4) || !aligned(x_qs_out, 8) ||
+        !aligned(x_d_out, 2))
+        return fail(LQ_ERR_ALIGN, "%s: x and gamma must be 16-byte aligned, x_qs_out 8-byte aligned", fn);
+    if (w->cols > kMaxCols || w->rows > 0x7fffffffLL)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: cols > %d", fn, kMaxCols);
+    MvArgs a{};
+    a.wq = w->qs; a.wd = w->d; a.rows = (int)w->rows; a.cols = (int)w->cols;
+    a.x = x; a.gamma = norm ? gamma : nullptr; a.eps = eps; a.dots = dots;
+    a.tap_q = x_qs_out; a.tap_d = x_d_out;
+    return launch_mv(a, norm ? PRO_NORM : PRO_QUANT, EPI_DOTS, as_stream(stream), kMvWgPerCu);
 }

@@ -10,7 +10,10 @@
 // Decode batches are small (16 tokens x top-8 here), so a (token, slot)
 // touches few rows per expert; what matters is that every touched expert's
 // weights stream from HBM exactly once.  A gather step lists, per active
-// expert, its (token, slot) rows in ascending order; the matvec then gives
+// expert, its (token, slot) rows (in the order the gather's LDS atomics hand
+// out places, which may vary between runs: each row is computed on its own
+// and written to its own slot, so the results do not depend on it); the
+// matvec then gives
 // each workgroup one expert and a block of rows, loads those weight rows
 // into VGPRs once, and applies them to every listed slot.  No float atomics
 // are used, so results are deterministic.
@@ -917,8 +920,9 @@ extern "C" lq_status lq_moe_block_ggml(const lq_moe_ggml_desc* m, const float* x
     lq_status st = ggml_mat(fn, "gate_up", m->gate_up_format, m->gate_up_q4_0, m->gate_up_q6_k, 2 * I, H, &gu);
     if (st == LQ_OK) st = ggml_mat(fn, "down", m->down_format, m->down_q4_0, m->down_q6_k, H, I, &dn);
     if (st != LQ_OK) return st;
-    if (H > 8192 || I > 8192 || E > kMoeMaxExperts || k > 32 || 2 * I * E > 0x7fffffffLL || H * E > 0x7fffffffLL)
-        return fail(LQ_ERR_UNSUPPORTED, "%s: hidden and ffn <= 8192, E <= %d, k <= 32", fn, kMoeMaxExperts);
+    // the router in k_moe_prep holds at most 1024 logits per token
+    if (H > 8192 || I > 8192 || E > 1024 || k > 32 || 2 * I * E > 0x7fffffffLL || H * E > 0x7fffffffLL)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: hidden and ffn <= 8192, E <= 1024, k <= 32", fn);
     if (T * k > kMoeMaxSlots) return fail(LQ_ERR_UNSUPPORTED, "%s: T*k > %d", fn, kMoeMaxSlots);
     if (T == 0) return LQ_OK;
     if (!x || !logits || !out) return fail(LQ_ERR_NULL, "%s: NULL pointer", fn);

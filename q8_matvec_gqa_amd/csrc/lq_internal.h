@@ -75,7 +75,9 @@ lq_status launch_q8_matvec(const int8_t* wq, const uint16_t* wd, int64_t rows, i
 // EPI_SWIGLU_Q8 also quantizes the SwiGLU output to Q8_0 (yq, yd), each
 // workgroup owning whole 32-value blocks.
 enum { PRO_Q8 = 0, PRO_QUANT = 1, PRO_NORM = 2 };
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_SWIGLU_Q8 = 3 };
+// EPI_DOTS writes every int32 block dot (dots[r*cols/32 + b]) instead of y:
+// the test tap of the block dots this kernel forms.
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_SWIGLU_Q8 = 3, EPI_DOTS = 4 };
 constexpr int kMvWgPerCu = 4;   // upper bound on resident workgroups of 4 waves per CU
 struct MvArgs {
     const int8_t* wq;
@@ -94,6 +96,7 @@ struct MvArgs {
     int8_t* tap_q;       // optional: workgroup 0 writes the Q8_0 input it built
     uint16_t* tap_d;
     int act;             // EPI_SWIGLU*: gate activation, LQ_ACT_SILU or LQ_ACT_GELU_TANH
+    int32_t* dots;       // EPI_DOTS: int32 [rows, cols/32]
 };
 lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per_cu,
                     LaunchMarks* mk = nullptr);
@@ -119,6 +122,10 @@ bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype);
 size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len);
 // splits the layer's attention uses (1: no combine launch); vec_ok: 16-byte aligned query rows
 int attn_nsplit(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t kv_dtype, bool vec_ok);
+// The host-side checks of lq_gqa_decode_attn other than the workspace's.
+lq_status check_attention_args(const char* fn, const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                               const void* k_cache, const void* v_cache, int32_t kv_dtype, int64_t head_stride,
+                               int64_t pos_stride, int64_t max_ctx, int64_t start, int64_t len, const float* out);
 lq_status launch_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd, const void* kc,
                            const void* vc, int32_t kv_dtype, int64_t head_stride,
                            int64_t pos_stride, int64_t start, int64_t len, float scale,
@@ -126,12 +133,14 @@ lq_status launch_attention(const float* q, int64_t n_q, int64_t n_kv, int64_t hd
 // Decode-layer attention with the per-head q/k RMSNorm + NeoX RoPE, the v
 // unit norm and the KV append (at start + len - 1) done in the kernel's
 // prologue; qkv is the raw fused projection.  rope rows are at that position.
+// tap_post (optional, [n_q*hd + 2*n_kv*hd]) receives q, k and v after that
+// prologue, before the attention scale and the cache conversion.
 lq_status launch_attention_fused(const float* qkv, int64_t n_q, int64_t n_kv, int64_t hd, const float* g_q,
                                  const float* g_k, int32_t qk_norm, int32_t v_unit_norm, float eps,
                                  const float* rope_cos_row, const float* rope_sin_row, void* kc, void* vc,
                                  int32_t kv_dtype, int64_t head_stride, int64_t pos_stride, int64_t start,
                                  int64_t len, float scale, float softcap, float* out, void* ws, hipStream_t s,
-                                 LaunchMarks* marks = nullptr);
+                                 LaunchMarks* marks = nullptr, float* tap_post = nullptr);
 
 // ---- launchers (k_moe.hip) ----------------------------------------------------
 size_t moe_ws_bytes(int64_t T, int64_t k, int64_t n_experts);

@@ -56,6 +56,7 @@ class DeviceLayer:
         qd = nq * hd
         e = lambda n, dt: torch.empty(n, dtype=dt, device="cuda")
         bufs = dict(xq=e(H, torch.int8), xd=e(H // 32, torch.int16), qkv=e(qd + 2 * nkv * hd, torch.float32),
+                    qkv_post=e(qd + 2 * nkv * hd, torch.float32),
                     attn=e(qd, torch.float32), aq=e(qd, torch.int8), ad=e(qd // 32, torch.int16),
                     x1=e(H, torch.float32))
         if I:

@@ -75,6 +75,14 @@ def test_matvec_validation():
     assert st(lq.lq_q8_matvec, w, A, A, None, None) == lq.LQ_ERR_NULL
     assert st(lq.lq_q8_matvec, lq.lq_q8_weight(None, None, 0, 64), None, None, None, None) == lq.LQ_OK
     assert st(lq.lq_q8_block_dots, w, A, None) == lq.LQ_ERR_NULL
+    f = lq.lq_q8_block_dots_f32
+    assert st(f, w, A, 1, A, 1e-6, A, A, None) == lq.LQ_ERR_NULL
+    assert st(f, w, A, 2, A, 1e-6, A, A, A) == lq.LQ_ERR_SHAPE
+    assert st(f, w, A, 1, A, -1.0, A, A, A) == lq.LQ_ERR_SHAPE
+    assert st(f, w, A + 4, 1, A, 1e-6, A, A, A) == lq.LQ_ERR_ALIGN
+    assert st(f, w, A, 0, None, 0.0, A, A + 4, A) == lq.LQ_ERR_ALIGN
+    assert st(f, lq.lq_q8_weight(A, A, 10, 16384 + 32), A, 0, None, 0.0, A, A, A) == lq.LQ_ERR_UNSUPPORTED
+    assert st(f, lq.lq_q8_weight(None, None, 0, 64), None, 0, None, 0.0, None, None, None) == lq.LQ_OK
 
 
 def test_ggml_format_validation():
@@ -250,6 +258,10 @@ def test_moe_block_ggml_validation():
               need) == lq.LQ_ERR_SHAPE
     assert st(lq.lq_moe_block_ggml, desc(dn=lq.lq_q4_0_weight(A + 4, A, H, I)), A, A, 16, A, None, A,
               need) == lq.LQ_ERR_ALIGN
+    # the router holds at most 1024 logits per token, as in lq_moe_block
+    big = lq.lq_moe_ggml_desc(H, I, 1025, k, lq.LQ_FMT_Q6_K, lq.LQ_FMT_Q4_0, gate_up_q6_k=gu6, down_q4_0=dn4)
+    nbig = lq.lq_moe_block_ggml_workspace_size(big, 16)
+    assert st(lq.lq_moe_block_ggml, big, A, A, 16, A, None, A, nbig) == lq.LQ_ERR_UNSUPPORTED
 
 
 def _layer_desc(**over):

@@ -103,6 +103,52 @@ def test_block_dots_bit_exact(rows, cols):
     assert np.array_equal(host(dots), ref)
 
 
+def _layer_projections():
+    """(tag, rows, cols, prologue) for every projection of the five workloads:
+    QKV and gate_up build their input with the RMSNorm prologue, O with the
+    quantize prologue, down reads the Q8_0 of h; plus the MoE experts' shapes."""
+    out = []
+    for name, c in synthetic.WORKLOADS.items():
+        H, qd, kvd, I = c["hidden"], c["n_q"] * c["head_dim"], c["n_kv"] * c["head_dim"], c["ffn"]
+        out += [(name + ":qkv", qd + 2 * kvd, H, "norm"), (name + ":o", H, qd, "quant")]
+        if I:
+            out += [(name + ":gate_up", 2 * I, H, "norm"), (name + ":down", H, I, "q8")]
+    m = synthetic.MOE_WORKLOADS["moe_e128_top8_t16"]
+    out += [("moe:gate_up", 2 * m["ffn"], m["hidden"], "q8"), ("moe:down", m["hidden"], m["ffn"], "q8")]
+    return out
+
+
+@pytest.mark.parametrize("tag,rows,cols,pro", _layer_projections(), ids=lambda v: str(v))
+def test_block_dots_layer_projections(tag, rows, cols, pro):
+    """The int32 block dots of the fused matvec kernel the layer runs, at every
+    projection shape of the five workloads, through the prologue each one
+    uses there: bit-exact against the oracle's integer sums of the Q8_0 input
+    the kernel built (which itself must match the oracle's quantization)."""
+    r = rng(rows + 11 * cols)
+    wq, wd = synthetic.q8_weight(r, rows, cols)
+    wq[rows - 1, -32:] = -128                              # extreme block in the last row
+    W = lq.q8_weight(dev(wq), dev(wd))
+    dots = empty((rows, cols // 32), np.int32)
+    print(f"[dots] {tag} {rows}x{cols} prologue {pro}", flush=True)
+    if pro == "q8":
+        xq, _ = oracle.q8_quantize(synthetic.activations(r, cols))
+        lq.lq_q8_block_dots(W, dev(xq), dots)
+        sync()
+    else:
+        x = synthetic.activations(r, cols) * 2
+        g = synthetic.gamma(r, cols)
+        xq_d, xd_d = empty(cols, np.int8), empty(cols // 32, np.uint16)
+        lq.lq_q8_block_dots_f32(W, dev(x), pro == "norm", dev(g), 1e-6, dots, xq_d, xd_d)
+        sync()
+        xq, xd = host(xq_d), host(xd_d, np.uint16)
+        if pro == "norm":
+            assert_q8_near(xq, xd, oracle.rmsnorm(x, g, 1e-6), tag + " input Q8")
+        else:
+            rq, rd = oracle.q8_quantize(x)                  # identical float input: bit-exact
+            assert np.array_equal(xq, rq) and np.array_equal(xd, rd)
+    assert np.array_equal(host(dots), oracle.q8_block_dots(wq, xq)), tag
+
+
 MATVEC_SHAPES = DOT_SHAPES[1:] + [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288),
                                   (10240, 2816), (2816, 8192), (1, 4096), (255, 3072)]
 

@@ -4,10 +4,13 @@ lq_moe_block on every workload at full size.
 Teacher-forced: every stage of the oracle is fed the GPU's own input to that
 stage (read back from the tap buffers) and must match the GPU's output of the
 stage (bit-exact for Q8_0 of an identical float input; the near-boundary rule
-for Q8_0 of a recomputed float; 1e-3 / 1e-4 for floats).  Free-running: the
-whole oracle layer must match the GPU layer to the same float tolerance
-whenever no quantization code flipped upstream (a flip moves whole rows by
-about one code step, which the pages' quantized arithmetic makes legitimate).
+for Q8_0 of a recomputed float; 1e-3 / 1e-4 for floats).  The KV append is
+checked byte for byte (tests/layercheck.py: check_kv_row).  Free-running: the
+oracle's whole layer from the original inputs, carrying the GPU's discrete
+values forward only at counted, checked rounding-boundary flips
+(layercheck.free_running), must match the GPU's layer output to the float
+tolerance; with no flip at all, so must the oracle's own composed layer
+(orc_decode_layer).
 """
 import numpy as np
 import pytest
@@ -20,6 +23,7 @@ pytestmark = pytest.mark.gpu
 lq = pytest.importorskip("q8_matvec_gqa_amd")
 from q8_matvec_gqa_amd.layers import DeviceLayer, DeviceMoe  # noqa: E402
 from lqtest import assert_close, assert_q8_near, dev, host, sync, torch_mod  # noqa: E402
+from layercheck import check_kv_row, free_running, post_rope  # noqa: E402
 
 LAYERS = list(synthetic.WORKLOADS)
 
@@ -85,21 +89,17 @@ def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
     flips += assert_q8_near(T["xq"], T["xd"], oracle.rmsnorm(w["x"], w["g_in"], eps), "input norm Q8")
     # 2. raw QKV projection from the GPU's Q8 input
     assert_close(T["qkv"], oracle.q8_matvec(w["qkv_qs"], w["qkv_d"], T["xq"], T["xd"]), "qkv projection")
-    # per-head norms and RoPE of the GPU's raw projection (the oracle's steps)
-    post = T["qkv"].copy()
-    for h in range(nq + nkv):
-        v = oracle.rmsnorm(post[h * hd:(h + 1) * hd], w["g_q"] if h < nq else w["g_k"], eps)
-        post[h * hd:(h + 1) * hd] = oracle.rope_neox(v, oc[pos], os_[pos])
-    if cfg["v_unit_norm"]:
-        for g in range(nkv):
-            post[qd + kvd + g * hd:qd + kvd + (g + 1) * hd] = oracle.rmsnorm(
-                post[qd + kvd + g * hd:qd + kvd + (g + 1) * hd], None, eps)
-    # 3. KV append: the cache row at pos holds the normed/rotated k and v (float tolerance
-    # before the bf16 rounding; the rounding itself is checked bit-exact in the op tests)
-    dec = (lambda a: a.astype(np.float32)) if cfg["kv_dtype"] == 0 else \
-        (lambda a: (a.astype(np.uint32) << 16).view(np.float32))
-    assert_close(dec(kc_gpu[:, pos]).ravel(), post[qd:qd + kvd], "k appended", rtol=5e-3)
-    assert_close(dec(vc_gpu[:, pos]).ravel(), post[qd + kvd:], "v appended", rtol=5e-3)
+    # per-head norms and RoPE of the GPU's raw projection (the oracle's steps),
+    # against the attention prologue's own f32 results
+    post = post_rope(cfg, T["qkv"], w["g_q"], w["g_k"], oc[pos], os_[pos])
+    assert_close(T["qkv_post"][:qd], post[:qd], "q after norm and RoPE")
+    # 3. KV append, byte for byte: the row at pos is exactly cvt() of the
+    # prologue's k and v, which meet the tolerance against the oracle's; any
+    # code differing from cvt() of the oracle's value is a checked bf16 flip
+    flips += check_kv_row(kc_gpu[:, pos], T["qkv_post"][qd:qd + kvd], post[qd:qd + kvd], cfg["kv_dtype"],
+                          "k appended")
+    flips += check_kv_row(vc_gpu[:, pos], T["qkv_post"][qd + kvd:], post[qd + kvd:], cfg["kv_dtype"],
+                          "v appended")
     others = np.ones(cfg["max_ctx"], bool)
     others[pos] = False
     assert np.array_equal(kc_gpu[:, others], w["k_cache"][:, others])
@@ -128,16 +128,18 @@ def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
         n = oracle.rmsnorm(T["x1"], w["g_post"], eps)
         assert_close(out_gpu, (w["x"].astype(np.float64) + n).astype(np.float32), "block output")
 
-    # free-running: the whole oracle layer from the original inputs
+    # free-running: the oracle's layer from the original inputs, the GPU's
+    # discrete values carried forward only at checked boundary flips
+    ref_fr, fr_flips = free_running(cfg, w, T, kc_gpu, vc_gpu, oc, os_, name)
+    err = assert_close(out_gpu, ref_fr, "free-running layer output")
     ow = dict(w)
     ow["rope_cos"], ow["rope_sin"] = oc, os_
-    ref_out, ref_k, ref_v, _ = oracle.decode_layer(oracle_cfg(cfg), ow, w["x"], pos, w["k_cache"], w["v_cache"])
-    if flips == 0:
-        err = assert_close(out_gpu, ref_out, "free-running layer output")
-        print(f"[layer] {name}: free-running max rel err {err:.2e}, no code flips", flush=True)
-    else:
-        print(f"[layer] {name}: {flips} quantization code(s) at a rounding boundary; free-running "
-              f"comparison reported only: max |diff| {np.abs(out_gpu - ref_out).max():.3e}", flush=True)
+    ref_out, _, _, _ = oracle.decode_layer(oracle_cfg(cfg), ow, w["x"], pos, w["k_cache"], w["v_cache"])
+    n_fr = sum(fr_flips.values())
+    if n_fr == 0:
+        assert_close(out_gpu, ref_out, "free-running layer output (orc_decode_layer)")
+    print(f"[layer] {name}: free-running max rel err {err:.2e}; flips carried forward {fr_flips}; "
+          f"teacher-forced flips {flips}", flush=True)
 
 
 def test_layer_deterministic_and_repeatable():
@@ -198,8 +200,11 @@ def test_layer_positions_sliding(pos):
     kc_gpu = host(L.t["k_cache"], np.uint16)
     vc_gpu = host(L.t["v_cache"], np.uint16)
     qkv = host(bufs["qkv"])
-    q = np.concatenate([oracle.rope_neox(oracle.rmsnorm(qkv[h * hd:(h + 1) * hd], w["g_q"], cfg["eps"]),
-                                         oc[pos], os_[pos]) for h in range(nq)])
+    post = post_rope(dict(cfg, pos=pos), qkv, w["g_q"], w["g_k"], oc[pos], os_[pos])
+    q = post[:nq * hd]
+    kvd, tap = nkv * hd, host(bufs["qkv_post"])
+    check_kv_row(kc_gpu[:, pos], tap[nq * hd:nq * hd + kvd], post[nq * hd:nq * hd + kvd], 1, f"k at pos {pos}")
+    check_kv_row(vc_gpu[:, pos], tap[nq * hd + kvd:], post[nq * hd + kvd:], 1, f"v at pos {pos}")
     start = max(0, pos - cfg["window"] + 1)
     att = oracle.attention(q, nq, nkv, hd, kc_gpu, vc_gpu, 1, cfg["max_ctx"] * hd, hd, start,
                            pos - start + 1, cfg["attn_scale"])
@@ -247,14 +252,27 @@ def test_moe_block_teacher_forced(scaled):
     want = np.einsum("ts,tsh->th", ws, y2.astype(np.float64))
     got = host(out).reshape(T_, H)
     assert_close(got, want, "weighted sum")
+    # free-running: the oracle's block from the original inputs (routing and
+    # Q8(x) are bit-exact above), carrying the GPU's Q8_0 of h forward only
+    # where it is a checked boundary flip of the oracle's own h
+    ref_fr = np.zeros((T_, H), np.float64)
+    fr_flips = 0
+    for t in range(T_):
+        for s in range(k):
+            e = rid[t, s]
+            y1o = oracle.q8_matvec(w["gu_qs"][e], w["gu_d"][e], xq[t], xd[t])
+            fr_flips += assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1o[:I], y1o[I:]), f"free-running h {t},{s}")
+            y2o = oracle.q8_matvec(w["dn_qs"][e], w["dn_d"][e], hq[t, s], hd[t, s])
+            ws_ = float(rw[t, s]) * (float(escale[e]) if scaled else 1.0)
+            ref_fr[t] += ws_ * y2o.astype(np.float64)
+    err = assert_close(got, ref_fr, "free-running MoE block")
     ref = oracle.moe_block(H, I, E, k, w["gu_qs"], w["gu_d"], w["dn_qs"], w["dn_d"], w["x"], w["logits"],
                            expert_scale=escale)
+    if fr_flips == 0:
+        assert_close(got, ref, "free-running MoE block (orc_moe_block)")
     touched = len(np.unique(ids))
-    if flips == 0:
-        err = assert_close(got, ref, "free-running MoE block")
-        print(f"[moe] free-running max rel err {err:.2e}; {touched} experts touched", flush=True)
-    else:
-        print(f"[moe] {flips} code flips at rounding boundaries; {touched} experts touched", flush=True)
+    print(f"[moe] free-running max rel err {err:.2e}; flips carried forward {fr_flips}; "
+          f"{touched} experts touched", flush=True)
 
 
 def _ggml_experts(fmt, r, rows, cols, E):
