@@ -155,24 +155,35 @@ def layer_kernels(cfg, nsplit_used):
 def kernel_measurements(cfg, layers, xs, torch, rounds):
     """Times every kernel of the decode layer with start/stop HIP events that
     the runtime stamps at each dispatch of the layer (lq_decode_layer_timed),
-    on the stream the layer runs on."""
+    on the stream the layer runs on.  Each round enqueues all R layers back
+    to back behind a ~1 ms device copy, so the host has queued every launch
+    before the first one starts and the kernels run one after another as in
+    the graph replay (no host gaps, each kernel starting as the previous one
+    drains)."""
     import q8_matvec_gqa_amd as lq
     n_k = lq.lq_decode_layer_kernel_count(layers[0].desc)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_k)]
-    for e in evs:
-        e.record()
+    R = len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_k)] for _ in range(R)]
+    for row in evs:
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
     names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5))
     assert len(names) == n_k, (len(names), n_k)
+    busy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    busy_dst = torch.empty_like(busy_src)
     times = [[] for _ in range(n_k)]
     for r in range(rounds + 1):
+        busy_dst.copy_(busy_src)                  # ~2 GB of traffic: keeps the GPU busy while the host enqueues
         for li, lay in enumerate(layers):
-            lq.lq_decode_layer_timed(lay.desc, xs[li], cfg["pos"], None, lay.ws, lay.ws_bytes, evs)
-            torch.cuda.synchronize()
-            if r == 0:
-                continue                      # warm round
+            lq.lq_decode_layer_timed(lay.desc, xs[li], cfg["pos"], None, lay.ws, lay.ws_bytes, evs[li])
+        torch.cuda.synchronize()
+        if r == 0:
+            continue                              # warm round
+        for li in range(R):
             for k in range(n_k):
-                times[k].append(evs[2 * k].elapsed_time(evs[2 * k + 1]) * 1e3)
+                times[k].append(evs[li][2 * k].elapsed_time(evs[li][2 * k + 1]) * 1e3)
+    del busy_src, busy_dst
     per = {}
     for (tag, kernel, b), ts in zip(names, times):
         per[tag] = dict(kernel=kernel, launches=len(ts), avg_us=float(np.mean(ts)), min_us=float(np.min(ts)),
@@ -187,7 +198,7 @@ def measure_layer(workload, steps, warmup, rounds, min_stack_bytes, torch):
     from q8_matvec_gqa_amd.layers import DeviceLayer
     cfg = synthetic.layer_cfg(workload)
     mv_b, at_b = layer_bytes(cfg)
-    R = max(8, math.ceil(min_stack_bytes / (mv_b + at_b)))
+    R = stack_layers(cfg, min_stack_bytes)
     log(f"workload {workload}: {(mv_b + at_b) / 1e6:.1f} MB/layer, stack of {R} layers")
     layers, xs = [], []
     for i in range(R):
@@ -613,14 +624,20 @@ def calib_copy(torch, nbytes=1 << 30, reps=3):
 
 # ---------------------------------------------------------------- profiles
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["q8_matvec_gqa_amd/csrc/k_matvec.hip", "q8_matvec_gqa_amd/csrc/lq_device.h",
-                  "q8_matvec_gqa_amd/csrc/lq_internal.h"]
+CSRC = os.path.join("q8_matvec_gqa_amd", "csrc")
 
 
-def source_hash(paths):
+def kernel_sources():
+    """Every device source of the library: a summary taken before any of them
+    changed no longer describes the kernels that run."""
+    d = os.path.join(ROOT, CSRC)
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(d) if f.endswith((".hip", ".h")))
+
+
+def source_hash(paths=None):
     import hashlib
     h = hashlib.sha256()
-    for p in paths:
+    for p in (kernel_sources() if paths is None else paths):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -640,27 +657,49 @@ def _find(dirpath, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirpath}")
 
 
-def _kernel_match(name, tag):
-    """rocprofv3 kernel names -> the layer's kernel tags."""
-    if tag == "gate_up_matvec":
-        import re
-        return re.search(r"k_mv<\d+, \d+, 2, 3, \d+>", name) is not None     # RMSNorm prologue, SwiGLU + Q8_0 epilogue
+def layer_kernel_patterns(cfg):
+    """rocprofv3 kernel-name patterns of the decode layer's kernels (template
+    arguments: NCH, RPW, prologue, epilogue, waves for k_mv)."""
+    import re
+    H, qd, I = cfg["hidden"], cfg["n_q"] * cfg["head_dim"], cfg["ffn"]
+    nch = lambda c: math.ceil(c / 1024)
+    kv = "float" if cfg["kv_dtype"] == 0 else "unsigned short"
+    ce = 4 if cfg["kv_dtype"] == 0 else 8
+    pats = {"qkv_matvec": r"k_mv<%d, \d+, 2, 0, \d+>" % nch(H),
+            "attn_split": r"k_attn_split<%s, %d, %d, " % (kv, cfg["head_dim"] // ce, cfg["n_q"] // cfg["n_kv"]),
+            "attn_combine": r"k_attn_combine",
+            "o_matvec": r"k_mv<%d, \d+, 1, %d, \d+>" % (nch(qd), 1 if cfg["kind"] == 0 else 0)}
+    if cfg["kind"] == 0:
+        pats["gate_up_matvec"] = r"k_mv<%d, \d+, 2, 3, \d+>" % nch(H)
+        pats["down_matvec"] = r"k_mv<%d, \d+, 0, 1, \d+>" % nch(I)
+    else:
+        pats["post_norm_add"] = r"k_rmsnorm_add"
+    return {t: re.compile(p) for t, p in pats.items()}
+
+
+def _kernel_match(name, tag, cfg=None):
+    """rocprofv3 kernel names -> the layer's kernel tags (headline workload by default)."""
     if tag == "copy":
         return "neg" in name.lower()
-    raise ValueError(tag)
+    pats = layer_kernel_patterns(cfg or synthetic.layer_cfg(synthetic.HEADLINE))
+    return pats[tag].search(name) is not None
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, out_path, command):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel and of
-    the calibration copy -> HBM bytes per launch, written as a text summary."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel of the layer
+    and of the calibration copy -> HBM bytes per launch, written as a text
+    summary (one line per kernel)."""
+    cfg = synthetic.layer_cfg(workload)
+    tags = list(layer_kernel_patterns(cfg)) + ["copy"]
+
     def per_kernel(d, counter):
         rows = _read_csv(_find(d, "counter_collection.csv"))
-        out = {"gate_up_matvec": [], "copy": []}
+        out = {t: [] for t in tags}
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
             for tag in out:
-                if _kernel_match(r["Kernel_Name"], tag):
+                if _kernel_match(r["Kernel_Name"], tag, cfg):
                     out[tag].append(float(r["Counter_Value"]))
         return {k: (sum(v) / len(v) if v else float("nan"), len(v)) for k, v in out.items()}
 
@@ -669,51 +708,94 @@ def summarize_pmc(fetch_dir, write_dir, workload, out_path, command):
     copy_bytes = 1 << 30
     f_scale = copy_bytes / (f["copy"][0] * 1024.0)
     w_scale = copy_bytes / (w["copy"][0] * 1024.0)
-    fetch_b = f["gate_up_matvec"][0] * 1024.0 * f_scale
-    write_b = w["gate_up_matvec"][0] * 1024.0 * w_scale
-    cfg = synthetic.layer_cfg(workload)
-    algo = dict((t, b) for t, _, b in layer_kernels(cfg, True))["gate_up_matvec"]
+    algo = dict((t, b) for t, _, b in layer_kernels(cfg, True))
     lines = [
-        f"# HBM traffic of the gate_up matvec (k_mv<NCH, RPW, NORM, SWIGLU_Q8, WAVES>), {workload}",
+        f"# HBM traffic per launch of the decode layer's kernels, {workload}",
         f"command_fetch: {command.replace('WRITE_SIZE', 'FETCH_SIZE')}",
         f"command_write: {command.replace('FETCH_SIZE', 'WRITE_SIZE')}",
-        f"source_sha256: {source_hash(KERNEL_SOURCES)}",
-        f"dispatches_fetch: {f['gate_up_matvec'][1]}",
-        f"dispatches_write: {w['gate_up_matvec'][1]}",
-        f"fetch_kib_per_dispatch: {f['gate_up_matvec'][0]:.1f}",
-        f"write_kib_per_dispatch: {w['gate_up_matvec'][0]:.1f}",
+        f"source_sha256: {source_hash()}",
         f"copy_calibration_bytes: {copy_bytes}",
         f"copy_fetch_kib: {f['copy'][0]:.1f}  (scale {f_scale:.4f})",
         f"copy_write_kib: {w['copy'][0]:.1f}  (scale {w_scale:.4f})",
-        f"algorithmic_bytes_per_launch: {algo}",
-        f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
-        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}",
+        "kernel | dispatches | fetch_kib | write_kib | traffic_bytes | algorithmic_bytes | traffic_over_algorithmic",
     ]
+    for t in tags[:-1]:
+        fb, wb = f[t][0] * 1024.0 * f_scale, w[t][0] * 1024.0 * w_scale
+        a = algo.get(t, 0)
+        ratio = f"{(fb + wb) / a:.4f}" if a else "-"
+        lines.append(f"{t} | {f[t][1]} | {f[t][0]:.1f} | {w[t][0]:.1f} | {int(round(fb + wb))} | {a} | {ratio}")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def load_traffic(workload):
-    """traffic_bytes_per_launch from the committed PMC summary, or None when
-    the summary is missing or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"gate_up_matvec_{workload}.pmc.txt")
+def _summary(path):
+    """(key: value header, {kernel: [columns]}) of a committed summary, or None
+    when it is missing or the kernel sources changed since it was taken."""
     if not os.path.exists(path):
         return None
-    kv = {}
+    kv, rows = {}, {}
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith("#"):
+            line = line.rstrip("\n")
+            if " | " in line:
+                c = [x.strip() for x in line.split(" | ")]
+                rows[c[0]] = c[1:]
+            elif ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_hash(KERNEL_SOURCES):
+    if kv.get("source_sha256") != source_hash():
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    return kv, rows
 
 
-def summarize_trace(trace_dir, out_dir, workload, command):
-    """Kernel-trace statistics of a bench run -> one text summary per kernel
-    of the layer (average duration over the run's dispatches)."""
+def load_traffic(workload, tag="gate_up_matvec"):
+    """traffic_bytes per launch of a layer kernel from the committed PMC
+    summary, or None (missing, or the sources changed since it was taken)."""
+    s = _summary(os.path.join(PROFILES, f"decode_layer_{workload}.pmc.txt"))
+    if s is None or tag not in s[1]:
+        return None
+    v = s[1][tag][3]
+    return int(v) if v.isdigit() else None
+
+
+def load_trace_avg(workload, tag="gate_up_matvec", phase="timed"):
+    """Average duration (us) of a layer kernel in one phase of the committed
+    rocprofv3 kernel trace of the bench command ("timed": the dispatches
+    that the bench's per-kernel events time; "graph": the graph replays), or
+    None."""
+    s = _summary(os.path.join(PROFILES, f"decode_layer_{workload}.trace.txt"))
+    if s is None:
+        return None
+    key = f"{tag}@{phase}"
+    if key not in s[1]:
+        return None
+    return float(s[1][key][1])
+
+
+def stack_layers(cfg, min_stack_bytes=2.0e9):
+    mv_b, at_b = layer_bytes(cfg)
+    return max(8, math.ceil(min_stack_bytes / (mv_b + at_b)))
+
+
+def trace_phases(R, steps, warmup, rounds):
+    """Dispatch index ranges, per kernel of the measured workload's layer and
+    in launch order, of measure_layer's phases: the eager reference (one warm
+    and three timed calls of each of the R layers), the graph warmup, the
+    graph replays, then the per-kernel event rounds (one warm round)."""
+    a = 4 * R
+    b = a + warmup * R
+    c = b + steps * R
+    d = c + R
+    e = d + rounds * R
+    return {"eager": (0, a), "graph": (b, c), "timed": (d, e)}
+
+
+def summarize_trace(trace_dir, out_dir, workload, command, steps=20, warmup=5, rounds=5):
+    """Kernel-trace statistics of a bench run -> a text summary: every lq
+    kernel (average duration over all its dispatches), then each kernel of
+    the measured workload's layer per phase of the bench (the workload runs
+    first, so its dispatches lead each kernel's list)."""
     import statistics
     rows = _read_csv(_find(trace_dir, "kernel_trace.csv"))
     groups = {}
@@ -721,33 +803,107 @@ def summarize_trace(trace_dir, out_dir, workload, command):
         n = r["Kernel_Name"]
         if "lq::" not in n:
             continue
-        groups.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        groups.setdefault(n, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    cfg = synthetic.layer_cfg(workload)
+    R = stack_layers(cfg)
+    phases = trace_phases(R, steps, warmup, rounds)
     lines = [f"# rocprofv3 kernel trace of bench.py, {workload}", f"command: {command}",
+             f"source_sha256: {source_hash()}",
+             f"phases: {R} layers; per kernel and in launch order, dispatches [a, b) of each phase: "
+             + ", ".join(f"{k} {v}" for k, v in phases.items()),
              "kernel | dispatches | avg_us | median_us | min_us | max_us"]
-    for n, ts in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+    durs = {n: [(e - s_) / 1e3 for s_, e in sorted(v)] for n, v in groups.items()}
+    for n, ts in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{n} | {len(ts)} | {statistics.mean(ts):.3f} | {statistics.median(ts):.3f} | "
                      f"{min(ts):.3f} | {max(ts):.3f}")
+    lines.append("layer kernel@phase | dispatches | avg_us | median_us | min_us | max_us")
+    for tag, pat in layer_kernel_patterns(cfg).items():
+        names = [n for n in durs if pat.search(n)]
+        if len(names) != 1:
+            continue
+        ts = durs[names[0]]
+        for ph, (a, b) in phases.items():
+            sub = ts[a:b]
+            if sub:
+                lines.append(f"{tag}@{ph} | {len(sub)} | {statistics.mean(sub):.3f} | {statistics.median(sub):.3f} | "
+                             f"{min(sub):.3f} | {max(sub):.3f}")
     out = os.path.join(out_dir, f"decode_layer_{workload}.trace.txt")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(workload, seconds):
+    """The oracle (plain C, as it stands) on the same layer: full layer calls,
+    first on one host thread, then on one thread per available core (at most
+    16, the machine's CPU share per GPU; each thread runs whole calls on its own
+    copies, and ctypes releases the GIL during a call).  `value` is the
+    all-core wall time per layer call."""
+    import threading
+
     import oracle
     cfg, w = synthetic.layer_inputs(workload, seed=0)
     oc, os_ = oracle.rope_table(cfg["max_ctx"], cfg["head_dim"], cfg["theta"])
     ow = dict(w, rope_cos=oc, rope_sin=os_)
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_layer(cfg, ow, w["x"], cfg["pos"], w["k_cache"], w["v_cache"])
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+
+    def calls_until(deadline, counts, i):
+        n = 0
+        while True:
+            oracle.decode_layer(cfg, ow, w["x"], cfg["pos"], w["k_cache"], w["v_cache"])
+            n += 1
+            if time.perf_counter() >= deadline:
+                break
+        counts[i] = n
+
+    half = seconds / 2
+    counts = [0]
+    t0 = time.perf_counter()
+    calls_until(t0 + half, counts, 0)
+    dt1 = time.perf_counter() - t0
+    single_us = dt1 / counts[0] * 1e6
+    n_thr = max(1, min(16, len(os.sched_getaffinity(0))))
+    counts = [0] * n_thr
+    t0 = time.perf_counter()
+    ths = [threading.Thread(target=calls_until, args=(t0 + half, counts, i)) for i in range(n_thr)]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
     dt = time.perf_counter() - t0
-    return dict(value=round(dt / n * 1e6, 1), unit="us/token/layer", cores=1, kind="oracle",
-                sample=f"{n} full decode-layer calls of {workload} (pos {cfg['pos']}) on one host thread, "
-                       f"{dt:.1f} s; f64 accumulation, plain C, no SIMD intrinsics")
+    all_us = dt / sum(counts) * 1e6
+    return dict(value=round(all_us, 1), unit="us/token/layer", cores=n_thr, kind="oracle",
+                single_thread_us=round(single_us, 1), cpu_model=cpu_model(),
+                sample=f"{sum(counts)} full decode-layer calls of {workload} (pos {cfg['pos']}) on {n_thr} host "
+                       f"threads in {dt:.1f} s, after {dt1:.1f} s of single-thread calls; f64 "
+                       f"accumulation, plain C, no SIMD intrinsics")
+
+
+def context_figures(us_layer):
+    """The pages' own figures, on other hardware and other workloads: context,
+    not targets."""
+    return {
+        "hf2q_decode_tok_per_s": {
+            "value": [86, 105], "target": 102, "hardware": "Apple M5 Max",
+            "workload": "Gemma-4 26B MoE decode (whole model, DWQ weights)",
+            "source": "Target Inference Architecture: hf2q on mlx-native, header (Phase 0 verdict and target)"},
+        "larql_amx_f32_TFLOPS": {
+            "value": [2, 4], "hardware": "Apple M-series AMX through Accelerate (cblas_sgemm)",
+            "source": "Inference Engine (larql), Compute Backend: CPU Backend"},
+        "this_run_36_layer_stack_tok_per_s": {
+            "value": round(1e6 / (36 * us_layer), 1),
+            "note": "36 layers of this workload back to back (layers only: no embedding, head or sampling)"},
+    }
 
 
 # ---------------------------------------------------------------- main
@@ -759,7 +915,7 @@ def main():
     ap.add_argument("--workload", default=synthetic.HEADLINE, choices=list(synthetic.WORKLOADS))
     ap.add_argument("--min-stack-bytes", type=float, default=2.0e9)
     ap.add_argument("--rounds", type=int, default=5, help="rounds of per-launch kernel timing")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--headline-only", action="store_true", help="skip the other configs and the MoE block")
     ap.add_argument("--calib-copy", action="store_true", help="also run the PMC calibration copy (1 GiB)")
@@ -773,11 +929,12 @@ def main():
     if args.summarize_pmc:
         os.makedirs(args.profiles_dir, exist_ok=True)
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
-                      os.path.join(args.profiles_dir, f"gate_up_matvec_{args.workload}.pmc.txt"), args.command)
+                      os.path.join(args.profiles_dir, f"decode_layer_{args.workload}.pmc.txt"), args.command)
         return
     if args.summarize_trace:
         os.makedirs(args.profiles_dir, exist_ok=True)
-        summarize_trace(args.summarize_trace, args.profiles_dir, args.workload, args.command)
+        summarize_trace(args.summarize_trace, args.profiles_dir, args.workload, args.command, args.steps, args.warmup,
+                        args.rounds)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -820,9 +977,11 @@ def main():
         "eager_us_per_layer": round(m["eager_us_layer"], 3),
         "roofline": {"bound": "hbm", "kernel": dom["kernel"] + " (" + dom_tag + ")", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload) if dom_tag == "gate_up_matvec" else None,
-                     "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3)},
-        "attn_roofline": m["attn"],
+                     "traffic": load_traffic(args.workload, dom_tag),
+                     "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom["avg_us"], 3),
+                     "trace_avg_launch_us": load_trace_avg(args.workload, dom_tag, "timed"),
+                     "trace_graph_avg_launch_us": load_trace_avg(args.workload, dom_tag, "graph")},
+        "attn_roofline": dict(m["attn"], traffic_split=load_traffic(args.workload, "attn_split")),
         "matvec_total": m["matvec"],
         "kernels": {t: {k: (round(v, 3) if isinstance(v, float) else v) for k, v in p.items()}
                     for t, p in per.items()},
@@ -861,6 +1020,7 @@ def main():
         torch.cuda.empty_cache()
     if args.calib_copy:
         calib_copy(torch)
+    result["context"] = context_figures(us_layer)
     if not args.no_cpu:
         log("oracle CPU baseline")
         result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)

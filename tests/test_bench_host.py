@@ -44,3 +44,28 @@ def test_rocprof_kernel_name_matching():
     qkv = "void lq::k_mv<4, 2, 2, 0, 8>(lq::MvArgs)"
     assert bench._kernel_match(gate_up, "gate_up_matvec")
     assert not bench._kernel_match(qkv, "gate_up_matvec")
+
+
+def test_layer_kernel_patterns_are_exclusive():
+    """Each kernel the 8B-like layer launches matches exactly one tag of the
+    rocprofv3 summaries (names as rocprofv3 prints them)."""
+    names = {
+        "qkv_matvec": "void lq::k_mv<4, 2, 2, 0, 8>(lq::MvArgs)",
+        "attn_split": "void lq::k_attn_split<unsigned short, 16, 4, 8, 16, true, 2, 4>(lq::(anonymous "
+                      "namespace)::AttnArgs)",
+        "attn_combine": "lq::k_attn_combine(lq::(anonymous namespace)::AttnArgs)",
+        "o_matvec": "void lq::k_mv<4, 2, 1, 1, 8>(lq::MvArgs)",
+        "gate_up_matvec": "void lq::k_mv<4, 2, 2, 3, 4>(lq::MvArgs)",
+        "down_matvec": "void lq::k_mv<12, 1, 0, 1, 4>(lq::MvArgs)",
+    }
+    pats = bench.layer_kernel_patterns(synthetic.layer_cfg(synthetic.HEADLINE))
+    assert set(pats) == set(names)
+    for tag, name in names.items():
+        hits = [t for t, p in pats.items() if p.search(name)]
+        assert hits == [tag], (name, hits)
+
+
+def test_context_figures_are_the_pages():
+    c = bench.context_figures(57.5)
+    assert c["hf2q_decode_tok_per_s"]["value"] == [86, 105]
+    assert c["larql_amx_f32_TFLOPS"]["value"] == [2, 4]
