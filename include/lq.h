@@ -287,6 +287,22 @@ lq_status lq_gqa_decode_attn(const float* q, int64_t n_q, int64_t n_kv, int64_t 
                              int64_t start, int64_t len, float scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same attention for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): arguments,
+ * results and errors as lq_gqa_decode_attn, with no workspace.  The split
+ * partials go to a device array inside the library, 16 MiB on each GPU,
+ * held from module load until the process ends.  Shapes whose partials
+ * (lq_gqa_decode_attn_workspace_size) exceed it are refused with
+ * LQ_ERR_UNSUPPORTED: every shape of up to 510 kv heads fits.  Every call on
+ * a GPU shares that GPU's array, so calls that overlap on one GPU (several
+ * streams or host threads) race on it; calls in one stream do not.  The
+ * first call on a device looks up the array's address there (the current
+ * device must be the stream's); no call allocates or frees memory. */
+lq_status lq_gqa_decode_attn_noalloc(const float* q, int64_t n_q, int64_t n_kv, int64_t head_dim,
+                                     const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                     int64_t head_stride, int64_t pos_stride, int64_t max_ctx,
+                                     int64_t start, int64_t len, float scale, float* out, void* stream);
+
 /* ---------------------------------------------------------------- output head */
 /* Final norm, vocab projection on f16 weights and logit softcapping
  * ([CUR] section 3, forward pass steps 4, 5 and 7; section 4,

@@ -115,6 +115,8 @@ _SIGS = {
     "lq_gqa_decode_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "lq_gqa_decode_attn": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
                                   _F, _P, _P, _SZ, _P]),
+    "lq_gqa_decode_attn_noalloc": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
+                                          _F, _P, _P]),
     "lq_rope_table_freqs": (_I32, [_I64, _I64, C.c_double, _P, _P, _P]),
     "lq_q8_matmul_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lq_q8_matmul": (_I32, [_W, _P, _P, _I64, _P, _P, _P, _SZ, _P]),
@@ -301,6 +303,13 @@ def lq_gqa_decode_attn(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_
                                           kv_dtype, head_stride, pos_stride, max_ctx, start, length,
                                           scale, _ptr(out), _ptr(workspace), workspace_bytes,
                                           _stream(stream)), check)
+
+
+def lq_gqa_decode_attn_noalloc(q, n_q, n_kv, head_dim, k_cache, v_cache, kv_dtype, head_stride, pos_stride,
+                               max_ctx, start, length, scale, out, stream=None, check=True):
+    return _check(_lib.lq_gqa_decode_attn_noalloc(_ptr(q), n_q, n_kv, head_dim, _ptr(k_cache), _ptr(v_cache),
+                                                  kv_dtype, head_stride, pos_stride, max_ctx, start, length,
+                                                  scale, _ptr(out), _stream(stream)), check)
 
 
 # ---------------------------------------------------------------- MoE

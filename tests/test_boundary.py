@@ -107,6 +107,27 @@ def test_ggml_format_validation():
         lq.LQ_OK
 
 
+def test_attention_noalloc_validation():
+    """The allocation-free attention validates like lq_gqa_decode_attn, and
+    refuses shapes whose split partials exceed its 16 MiB array (the size
+    query proves each refused shape needs more, so nothing can launch)."""
+    f = lq.lq_gqa_decode_attn_noalloc
+    assert st(f, A, 32, 8, 128, A, A, 1, 8192 * 128, 128, 8192, 0, 8192, 0.1, None) == lq.LQ_ERR_NULL
+    assert st(f, A, 30, 8, 128, A, A, 1, 8192 * 128, 128, 8192, 0, 8192, 0.1, A) == lq.LQ_ERR_SHAPE
+    assert st(f, A, 32, 8, 128, A, A, 1, 8192 * 128, 128, 8192, 100, 8192, 0.1, A) == lq.LQ_ERR_SHAPE
+    assert st(f, A, 32, 8, 128, A + 8, A, 1, 8192 * 128, 128, 8192, 0, 8192, 0.1, A) == lq.LQ_ERR_ALIGN
+    assert st(f, A, 32, 8, 1024, A, A, 1, 8192 * 1024, 1024, 8192, 0, 8192, 0.1, A) == lq.LQ_ERR_UNSUPPORTED
+    assert st(f, None, 0, 8, 128, None, None, 1, 8192 * 128, 128, 8192, 0, 8192, 0.1, None) == lq.LQ_OK
+    n_q, n_kv, hd, ctx = 511 * 8, 511, 512, 4096
+    assert lq.lq_gqa_decode_attn_workspace_size(n_q, n_kv, hd, ctx) > 16 << 20
+    assert st(f, A, n_q, n_kv, hd, A, A, 0, ctx * hd, hd, ctx, 0, ctx, 0.05, A) == lq.LQ_ERR_UNSUPPORTED
+    assert "scratch" in lq.lq_last_error()
+    # every shape of up to 510 kv heads fits
+    worst = max(lq.lq_gqa_decode_attn_workspace_size(n * g, n, d, 65536)
+                for n in (1, 2, 8, 64, 255, 256, 257, 500, 510) for g in (1, 2, 4, 8) for d in (64, 128, 256, 512))
+    assert worst <= 16 << 20
+
+
 def test_moe_ggml_format_validation():
     w4 = lq.lq_q4_0_weight(A, A, 64, 704)
     w6 = lq.lq_q6_k_weight(A, A, A, A, 64, 512)
