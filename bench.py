@@ -39,17 +39,43 @@ def log(msg):
 
 
 # ---------------------------------------------------------------- inputs
-def device_layer_inputs(cfg, seed, torch):
+FMT_BYTES = {"q8_0": 34 / 32, "q4_0": 18 / 32, "q6_k": 210 / 256}   # weight bytes per value
+
+
+def device_layer_inputs(cfg, seed, torch, formats=None):
     """Layer inputs drawn directly on the GPU (same distributions as
-    synthetic.py; bf16 KV drawn as the top half of float32 normals)."""
+    synthetic.py; bf16 KV drawn as the top half of float32 normals).
+    formats: optional {"qkv" | "o" | "gu" | "dn": "q4_0" | "q6_k"}; those
+    projections are random GGML arrays in the library's device layout (code
+    bytes uniform, f16 scales as synthetic.py's blocks)."""
+    import q8_matvec_gqa_amd as lq
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+
+    def rbytes(*shape):
+        return torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=g)
+
+    def f16(shape, scale):
+        return (torch.randn(shape, device="cuda", generator=g).abs() * scale).half().view(torch.int16)
 
     def q8(rows, cols):
         qs = torch.randint(-127, 128, (rows, cols), dtype=torch.int8, device="cuda", generator=g)
         d = (torch.randn(rows, cols // 32, device="cuda", generator=g).abs() * (0.02 / 127)).half()
         return qs, d.view(torch.int16)
+
+    def proj(w, key, rows, cols):
+        f = (formats or {}).get(key)
+        if f is None:
+            w[key + "_qs"], w[key + "_d"] = q8(rows, cols)
+        elif f == "q4_0":
+            w[key + "_fmt"] = f
+            w[key + "_dev"] = lq.q4_0_weight(rbytes(rows, cols // 2), f16((rows, cols // 32), 0.02 / 8), rows, cols)
+        else:
+            w[key + "_fmt"] = f
+            w[key + "_dev"] = lq.q6_k_weight(rbytes(rows, cols // 2), rbytes(rows, cols // 4),
+                                             rbytes(rows, cols // 16).view(torch.int8), f16((rows, cols // 256), 2e-5),
+                                             rows, cols)
 
     def gamma(n):
         return 1.0 + 0.1 * torch.randn(n, device="cuda", generator=g)
@@ -61,31 +87,32 @@ def device_layer_inputs(cfg, seed, torch):
         return (a.view(torch.int32) >> 16).to(torch.int16)
 
     w = {"x": torch.randn(H, device="cuda", generator=g), "g_in": gamma(H)}
-    w["qkv_qs"], w["qkv_d"] = q8(nq * hd + 2 * nkv * hd, H)
+    proj(w, "qkv", nq * hd + 2 * nkv * hd, H)
     w["g_q"], w["g_k"] = gamma(hd), gamma(hd)
-    w["o_qs"], w["o_d"] = q8(H, nq * hd)
+    proj(w, "o", H, nq * hd)
     w["g_post"] = gamma(H)
     if I:
-        w["gu_qs"], w["gu_d"] = q8(2 * I, H)
-        w["dn_qs"], w["dn_d"] = q8(H, I)
+        proj(w, "gu", 2 * I, H)
+        proj(w, "dn", H, I)
     w["k_cache"], w["v_cache"] = kv(), kv()
     return w
 
 
-def layer_bytes(cfg):
-    """Algorithmic HBM bytes of one decode layer: Q8_0 weights at 34 B per 32,
-    the KV positions attended (read once), activations in and out."""
+def layer_bytes(cfg, formats=None):
+    """Algorithmic HBM bytes of one decode layer: weights in their format
+    (Q8_0 34 B per 32 values; Q4_0 18 per 32, Q6_K 210 per 256), the KV
+    positions attended (read once), activations in and out."""
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
     es = 4 if cfg["kv_dtype"] == 0 else 2
     L = min(cfg["window"], cfg["pos"] + 1) if cfg["window"] else cfg["pos"] + 1
-    mats = [(nq * hd + 2 * nkv * hd, H), (H, nq * hd)] + ([(2 * I, H), (H, I)] if I else [])
-    mv = sum(matvec_bytes(r, c) for r, c in mats)
+    mats = [("qkv", nq * hd + 2 * nkv * hd, H), ("o", H, nq * hd)] + ([("gu", 2 * I, H), ("dn", H, I)] if I else [])
+    mv = sum(matvec_bytes(r, c, fmt=(formats or {}).get(k, "q8_0")) for k, r, c in mats)
     attn = attn_bytes(nq, nkv, hd, L, es)
     return mv, attn
 
 
-def matvec_bytes(rows, cols, residual=False):
-    return rows * cols * 34 // 32 + cols + cols // 16 + 4 * rows + (4 * rows if residual else 0)
+def matvec_bytes(rows, cols, residual=False, fmt="q8_0"):
+    return int(rows * cols * FMT_BYTES[fmt]) + cols + cols // 16 + 4 * rows + (4 * rows if residual else 0)
 
 
 def attn_bytes(nq, nkv, hd, L, es):
@@ -128,7 +155,7 @@ def time_stack(layers, xs, pos, steps, warmup, torch):
     return start.elapsed_time(end) / steps, eager_ms
 
 
-def layer_kernels(cfg, nsplit_used):
+def layer_kernels(cfg, nsplit_used, formats=None):
     """Names and algorithmic bytes of the kernels the decode layer launches,
     in launch order (matching lq_decode_layer_timed's events)."""
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
@@ -136,23 +163,26 @@ def layer_kernels(cfg, nsplit_used):
     pos = cfg["pos"]
     L = min(cfg["window"], pos + 1) if cfg["window"] else pos + 1
     qkv_rows = nq * hd + 2 * nkv * hd
+    fm = formats or {}
+    wb = {("qkv", qkv_rows, H), ("o", H, nq * hd), ("gu", 2 * I, H), ("dn", H, I)}
+    wbytes = {k: int(r * c * FMT_BYTES[fm.get(k, "q8_0")]) for k, r, c in wb}
     q8w = lambda r, c: r * c * 34 // 32
     ks = [("qkv_matvec", "k_mv<NCH=%d,NORM,STORE>" % math.ceil(H / 1024),
-           q8w(qkv_rows, H) + 8 * H + 4 * qkv_rows),
+           wbytes["qkv"] + 8 * H + 4 * qkv_rows),
           ("attn_split", "k_attn_split", attn_bytes(nq, nkv, hd, L, es) + 4 * qkv_rows)]
     if nsplit_used:
         ks.append(("attn_combine", "k_attn_combine", 0))
     if cfg["kind"] == 0:
-        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 8 * H),
-               ("gate_up_matvec", "k_mv<NCH=%d,NORM,SWIGLU_Q8>" % math.ceil(H / 1024), q8w(2 * I, H) + 8 * H + q8w(1, I)),
-               ("down_matvec", "k_mv<NCH=%d,Q8,RESID>" % math.ceil(I / 1024), q8w(H, I) + q8w(1, I) + 8 * H)]
+        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,RESID>" % math.ceil(nq * hd / 1024), wbytes["o"] + 4 * nq * hd + 8 * H),
+               ("gate_up_matvec", "k_mv<NCH=%d,NORM,SWIGLU_Q8>" % math.ceil(H / 1024), wbytes["gu"] + 8 * H + q8w(1, I)),
+               ("down_matvec", "k_mv<NCH=%d,Q8,RESID>" % math.ceil(I / 1024), wbytes["dn"] + q8w(1, I) + 8 * H)]
     else:
-        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,STORE>" % math.ceil(nq * hd / 1024), q8w(H, nq * hd) + 4 * nq * hd + 4 * H),
+        ks += [("o_matvec", "k_mv<NCH=%d,QUANT,STORE>" % math.ceil(nq * hd / 1024), wbytes["o"] + 4 * nq * hd + 4 * H),
                ("post_norm_add", "k_rmsnorm_add", 16 * H)]
     return ks
 
 
-def kernel_measurements(cfg, layers, xs, torch, rounds):
+def kernel_measurements(cfg, layers, xs, torch, rounds, formats=None):
     """Times every kernel of the decode layer with start/stop HIP events that
     the runtime stamps at each dispatch of the layer (lq_decode_layer_timed),
     on the stream the layer runs on.  Each round enqueues all R layers back
@@ -168,7 +198,7 @@ def kernel_measurements(cfg, layers, xs, torch, rounds):
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5))
+    names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5), formats)
     assert len(names) == n_k, (len(names), n_k)
     busy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     busy_dst = torch.empty_like(busy_src)
@@ -191,25 +221,27 @@ def kernel_measurements(cfg, layers, xs, torch, rounds):
     return per
 
 
-def measure_layer(workload, steps, warmup, rounds, min_stack_bytes, torch):
+def measure_layer(workload, steps, warmup, rounds, min_stack_bytes, torch, formats=None):
     """A graph-captured stack of R distinct layers (>= min_stack_bytes of
     weights and KV, so the Infinity Cache cannot serve them), timed over
-    `steps` replays, plus per-kernel launch durations from HIP events."""
+    `steps` replays, plus per-kernel launch durations from HIP events.
+    formats: GGML weight formats of some projections (see device_layer_inputs)."""
     from q8_matvec_gqa_amd.layers import DeviceLayer
     cfg = synthetic.layer_cfg(workload)
-    mv_b, at_b = layer_bytes(cfg)
-    R = stack_layers(cfg, min_stack_bytes)
-    log(f"workload {workload}: {(mv_b + at_b) / 1e6:.1f} MB/layer, stack of {R} layers")
+    mv_b, at_b = layer_bytes(cfg, formats)
+    R = max(8, math.ceil(min_stack_bytes / (mv_b + at_b)))
+    tag = workload + (" " + ",".join(f"{k}={v}" for k, v in formats.items()) if formats else "")
+    log(f"workload {tag}: {(mv_b + at_b) / 1e6:.1f} MB/layer, stack of {R} layers")
     layers, xs = [], []
     for i in range(R):
-        w = device_layer_inputs(cfg, seed=1000 + i, torch=torch)
+        w = device_layer_inputs(cfg, seed=1000 + i, torch=torch, formats=formats)
         layers.append(DeviceLayer(cfg, w, torch))
         xs.append(w["x"])
     torch.cuda.synchronize()
     ms_step, eager_ms = time_stack(layers, xs, cfg["pos"], steps, warmup, torch)
     us_layer = ms_step * 1e3 / R
-    log(f"{workload}: {us_layer:.2f} us/token/layer (graph), eager {eager_ms * 1e3 / R:.2f}")
-    per = kernel_measurements(cfg, layers, xs, torch, rounds)
+    log(f"{tag}: {us_layer:.2f} us/token/layer (graph), eager {eager_ms * 1e3 / R:.2f}")
+    per = kernel_measurements(cfg, layers, xs, torch, rounds, formats)
     at_us = per["attn_split"]["avg_us"] + (per["attn_combine"]["avg_us"] if "attn_combine" in per else 0.0)
     at_bytes = per["attn_split"]["bytes"]
     at_gbs = at_bytes / (at_us * 1e3)
@@ -1003,6 +1035,21 @@ def main():
             del o
             torch.cuda.empty_cache()
         result["other_configs"] = others
+        # the headline layer with GGML-format projections (same launches, other weight bytes)
+        gl = {}
+        for name, fm in (("gu_q6_k+dn_q4_0", {"gu": "q6_k", "dn": "q4_0"}),
+                         ("all_q4_0", {"qkv": "q4_0", "o": "q4_0", "gu": "q4_0", "dn": "q4_0"}),
+                         ("all_q6_k", {"qkv": "q6_k", "o": "q6_k", "gu": "q6_k", "dn": "q6_k"})):
+            o = measure_layer(args.workload, max(10, args.steps // 4), 3, 2, args.min_stack_bytes, torch, formats=fm)
+            gl[name] = {"us_per_layer": round(o["us_layer"], 3), "layers_per_step": o["R"],
+                        "layer_bytes": o["layer_bytes"],
+                        "layer_GBps": round(o["layer_bytes"] / (o["us_layer"] * 1e3), 1),
+                        "layer_frac": round(o["layer_bytes"] / (o["us_layer"] * 1e3) / HBM_PEAK_GBS, 4),
+                        "matvec": o["matvec"],
+                        "kernels_us": {t: round(p["avg_us"], 3) for t, p in o["per"].items()}}
+            del o
+            torch.cuda.empty_cache()
+        result["ggml_layers"] = gl
         for name in synthetic.MOE_WORKLOADS:
             result["moe_block"] = measure_moe(name, max(10, args.steps // 2), torch)
             torch.cuda.empty_cache()

@@ -75,6 +75,13 @@ typedef struct lq_q8_weight {
     int64_t cols;
 } lq_q8_weight;
 
+/* Weight formats.  Q8_0 is this library's native format; Q4_0 and Q6_K are
+ * the other GGML block formats the pages name.  Zero (a zero-initialized
+ * descriptor) is Q8_0. */
+#define LQ_FMT_Q8_0  0
+#define LQ_FMT_Q4_0  1
+#define LQ_FMT_Q6_K  2
+
 /* Other GGML weight formats ([CUR] section 4: the current path's MoE kernel
  * runs on Q6_K weights; [TGT] section 8, Q1: GGML block order).  Device
  * layout, SoA (lq_q4_0_pack_ggml / lq_q6_k_pack_ggml convert GGML blocks):
@@ -409,8 +416,6 @@ lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const float* logits
  * multiples of 32 (Q4_0) or 256 (Q6_K) where they are a weight's columns.
  * Taps, workspace, expert_scale and errors as for lq_moe_block; the y1 tap
  * holds the gate_up outputs before SwiGLU. */
-#define LQ_FMT_Q4_0  0
-#define LQ_FMT_Q6_K  1
 typedef struct lq_moe_ggml_desc {
     int64_t hidden, ffn, n_experts, top_k;
     int32_t gate_up_format, down_format;
@@ -459,6 +464,16 @@ typedef struct lq_layer_desc {
     float attn_softcap;       /* > 0: each scaled score s becomes cap * tanh(s / cap) before the softmax
                                  (the optional Gemma score softcap of [ENG] BLAS-Fused Attention);
                                  0: none */
+    int32_t w_format[4];      /* formats of the projections, in the order qkv, o, gate_up, down
+                                 ([CUR] section 4: the current path runs GGML Q6_K weights; [TGT]
+                                 section 8, Q1: GGML block order).  LQ_FMT_Q8_0 (0, the default)
+                                 takes w_qkv / w_o / w_gate_up / w_down above; LQ_FMT_Q4_0 and
+                                 LQ_FMT_Q6_K take w_q4_0[i] / w_q6_k[i] below, with the same rows
+                                 and cols (Q6_K: cols % 256 == 0; a Q6_K gate_up needs hidden <=
+                                 12288, else LQ_ERR_UNSUPPORTED).  The activations stay Q8_0, the
+                                 prologues and epilogues are the same, so is the launch count. */
+    lq_q4_0_weight w_q4_0[4];
+    lq_q6_k_weight w_q6_k[4];
 } lq_layer_desc;
 
 /* Optional device buffers for the layer's intermediates; read them after

@@ -65,7 +65,7 @@ class lq_moe_taps(C.Structure):
     _fields_ = [(n, _P) for n in ("ids", "w", "xq", "xd", "y1", "hq", "hd", "y2")]
 
 
-LQ_FMT_Q4_0, LQ_FMT_Q6_K = 0, 1
+LQ_FMT_Q8_0, LQ_FMT_Q4_0, LQ_FMT_Q6_K = 0, 1, 2
 
 
 class lq_moe_ggml_desc(C.Structure):
@@ -85,6 +85,7 @@ class lq_layer_desc(C.Structure):
         ("g_in", _P), ("g_q", _P), ("g_k", _P), ("g_post", _P),
         ("k_cache", _P), ("v_cache", _P), ("rope_cos", _P), ("rope_sin", _P),
         ("ffn_act", _I32), ("attn_softcap", _F),
+        ("w_format", _I32 * 4), ("w_q4_0", lq_q4_0_weight * 4), ("w_q6_k", lq_q6_k_weight * 4),
     ]
 
 

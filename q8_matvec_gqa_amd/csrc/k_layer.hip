@@ -59,9 +59,19 @@ LayerBuffers layout(const lq_layer_desc* L, char* base, const lq_layer_taps* tap
     return b;
 }
 
-bool weight_is(const lq_q8_weight& w, int64_t rows, int64_t cols) { return w.rows == rows && w.cols == cols; }
+// rows x cols of projection i (qkv, o, gate_up, down) as its format's descriptor states them
+bool weight_is(const lq_layer_desc* L, int i, int64_t rows, int64_t cols) {
+    const lq_q8_weight* q8[4] = {&L->w_qkv, &L->w_o, &L->w_gate_up, &L->w_down};
+    int64_t r = q8[i]->rows, c = q8[i]->cols;
+    if (L->w_format[i] == LQ_FMT_Q4_0) {
+        r = L->w_q4_0[i].rows; c = L->w_q4_0[i].cols;
+    } else if (L->w_format[i] == LQ_FMT_Q6_K) {
+        r = L->w_q6_k[i].rows; c = L->w_q6_k[i].cols;
+    }
+    return r == rows && c == cols;
+}
 
-lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
+lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos, ProjWeight (&pw)[4]) {
     const char* fn = "lq_decode_layer";
     if (!L) return fail(LQ_ERR_NULL, "%s: descriptor is NULL", fn);
     const int64_t H = L->hidden, nq = L->n_q, nkv = L->n_kv, hd = L->head_dim;
@@ -80,12 +90,15 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
         return fail(LQ_ERR_SHAPE, "%s: ffn_act %d", fn, L->ffn_act);
     if (!(L->attn_softcap >= 0.0f) || L->attn_softcap == INFINITY)
         return fail(LQ_ERR_SHAPE, "%s: attn_softcap must be finite and >= 0", fn);
-    if (!weight_is(L->w_qkv, nq * hd + 2 * nkv * hd, H) || !weight_is(L->w_o, H, nq * hd))
+    for (int i = 0; i < 4; ++i)
+        if (L->w_format[i] != LQ_FMT_Q8_0 && L->w_format[i] != LQ_FMT_Q4_0 && L->w_format[i] != LQ_FMT_Q6_K)
+            return fail(LQ_ERR_SHAPE, "%s: w_format[%d] = %d", fn, i, L->w_format[i]);
+    if (!weight_is(L, 0, nq * hd + 2 * nkv * hd, H) || !weight_is(L, 1, H, nq * hd))
         return fail(LQ_ERR_SHAPE, "%s: w_qkv must be [%lld, %lld] and w_o [%lld, %lld]", fn,
                     (long long)(nq * hd + 2 * nkv * hd), (long long)H, (long long)H, (long long)(nq * hd));
     if (L->kind == LQ_LAYER_PRENORM_FFN) {
         const int64_t I = L->ffn;
-        if (I <= 0 || I % 32 || !weight_is(L->w_gate_up, 2 * I, H) || !weight_is(L->w_down, H, I))
+        if (I <= 0 || I % 32 || !weight_is(L, 2, 2 * I, H) || !weight_is(L, 3, H, I))
             return fail(LQ_ERR_SHAPE, "%s: ffn=%lld with w_gate_up [2*ffn, hidden] and w_down [hidden, ffn]", fn,
                         (long long)I);
     }
@@ -93,13 +106,17 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
         return fail(LQ_ERR_UNSUPPORTED, "%s: head_dim=%lld G=%lld kv_dtype=%d not built", fn, (long long)hd,
                     (long long)(nq / nkv), L->kv_dtype);
     lq_status st;
-    if ((st = check_weight(&L->w_qkv, fn)) != LQ_OK) return st;
-    if ((st = check_weight(&L->w_o, fn)) != LQ_OK) return st;
-    if (L->kind == LQ_LAYER_PRENORM_FFN) {
-        if ((st = check_weight(&L->w_gate_up, fn)) != LQ_OK) return st;
-        if ((st = check_weight(&L->w_down, fn)) != LQ_OK) return st;
-        if (!L->g_post) return fail(LQ_ERR_NULL, "%s: g_post is NULL", fn);
+    const lq_q8_weight* q8[4] = {&L->w_qkv, &L->w_o, &L->w_gate_up, &L->w_down};
+    const char* names[4] = {"w_qkv", "w_o", "w_gate_up", "w_down"};
+    const int n_proj = L->kind == LQ_LAYER_PRENORM_FFN ? 4 : 2;
+    for (int i = 0; i < n_proj; ++i) {
+        const int64_t rows = i == 0 ? nq * hd + 2 * nkv * hd : i == 2 ? 2 * L->ffn : H;
+        const int64_t cols = i == 1 ? nq * hd : i == 3 ? L->ffn : H;
+        if ((st = check_proj_weight(fn, names[i], L->w_format[i], *q8[i], L->w_q4_0[i], L->w_q6_k[i], rows, cols,
+                                    &pw[i])) != LQ_OK)
+            return st;
     }
+    if (L->kind == LQ_LAYER_PRENORM_FFN && !L->g_post) return fail(LQ_ERR_NULL, "%s: g_post is NULL", fn);
     if (!x || !L->g_in || !L->k_cache || !L->v_cache || !L->rope_cos || !L->rope_sin)
         return fail(LQ_ERR_NULL, "%s: NULL pointer (x, g_in, caches and RoPE tables are required)", fn);
     if (L->qk_norm && (!L->g_q || !L->g_k)) return fail(LQ_ERR_NULL, "%s: qk_norm needs g_q and g_k", fn);
@@ -110,8 +127,10 @@ lq_status validate(const lq_layer_desc* L, const float* x, int64_t pos) {
     const size_t es = L->kv_dtype == LQ_KV_F32 ? 4 : 2;
     if ((hd * es) % 16) return fail(LQ_ERR_ALIGN, "%s: cache rows must be a multiple of 16 bytes", fn);
     if (H > 16384 || nq * hd > 16384 || (L->kind == LQ_LAYER_PRENORM_FFN && L->ffn > 16384) ||
-        L->w_qkv.rows > 0x7fffffffLL || 2 * L->ffn > 0x7fffffffLL)
+        nq * hd + 2 * nkv * hd > 0x7fffffffLL || 2 * L->ffn > 0x7fffffffLL)
         return fail(LQ_ERR_UNSUPPORTED, "%s: matvec inputs are limited to 16384 columns", fn);
+    if (L->kind == LQ_LAYER_PRENORM_FFN && L->w_format[2] == LQ_FMT_Q6_K && H > 12288)
+        return fail(LQ_ERR_UNSUPPORTED, "%s: a Q6_K gate_up needs hidden <= 12288", fn);
     return LQ_OK;
 }
 
@@ -178,7 +197,8 @@ extern "C" lq_status lq_decode_layer_timed(const lq_layer_desc* L, float* x, int
 namespace {
 lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_layer_taps* taps, void* workspace,
                     size_t workspace_bytes, Marks& mk, hipStream_t s) {
-    lq_status st = validate(L, x, pos);
+    ProjWeight pw[4] = {};
+    lq_status st = validate(L, x, pos, pw);
     if (st != LQ_OK) return st;
     if ((st = validate_taps(taps)) != LQ_OK) return st;
     const size_t need = layout(L, nullptr, nullptr).total;
@@ -197,9 +217,9 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
 
     // attention block: QKV projection with the input RMSNorm + Q8 built in-kernel
     m = MvArgs{};
-    m.wq = L->w_qkv.qs; m.wd = L->w_qkv.d; m.rows = (int)L->w_qkv.rows; m.cols = (int)H;
+    m.rows = (int)(nq * hd + 2 * nkv * hd); m.cols = (int)H;
     m.x = x; m.gamma = L->g_in; m.eps = L->eps; m.y = b.qkv; m.tap_q = T.xq; m.tap_d = T.xd;
-    if ((st = launch_mv(m, PRO_NORM, EPI_STORE, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    if ((st = launch_proj(pw[0], m, PRO_NORM, EPI_STORE, s, &mk)) != LQ_OK) return st;
     // attention, with the per-head norms, RoPE and the KV append in its prologue
     const int64_t half = hd / 2;
     if ((st = launch_attention_fused(b.qkv, nq, nkv, hd, L->g_q, L->g_k, L->qk_norm, L->v_unit_norm, L->eps,
@@ -210,27 +230,27 @@ lq_status run_layer(const lq_layer_desc* L, float* x, int64_t pos, const lq_laye
         return st;
     // O projection, quantizing the attention output in-kernel
     m = MvArgs{};
-    m.wq = L->w_o.qs; m.wd = L->w_o.d; m.rows = (int)H; m.cols = (int)qd;
+    m.rows = (int)H; m.cols = (int)qd;
     m.x = b.attn; m.y = b.x1; m.tap_q = T.aq; m.tap_d = T.ad;
     if (L->kind == LQ_LAYER_ATTN_POSTNORM) {
-        if ((st = launch_mv(m, PRO_QUANT, EPI_STORE, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+        if ((st = launch_proj(pw[1], m, PRO_QUANT, EPI_STORE, s, &mk)) != LQ_OK) return st;
         return launch_rmsnorm_add(b.x1, H, L->g_post, L->eps, x, x, s, &mk);
     }
     m.res = x;
-    if ((st = launch_mv(m, PRO_QUANT, EPI_RESID, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    if ((st = launch_proj(pw[1], m, PRO_QUANT, EPI_RESID, s, &mk)) != LQ_OK) return st;
     // FFN: gate/up with the post-attention RMSNorm + Q8 in-kernel, SwiGLU on
     // row pairs, and the Q8_0 of the SwiGLU output built by the workgroup that
     // owns each 32-value block
     const int64_t I = L->ffn;
     m = MvArgs{};
-    m.wq = L->w_gate_up.qs; m.wd = L->w_gate_up.d; m.rows = (int)I; m.cols = (int)H;
+    m.rows = (int)I; m.cols = (int)H;
     m.x = b.x1; m.gamma = L->g_post; m.eps = L->eps; m.y = T.h; m.yq = b.hq; m.yd = b.hd; m.act = L->ffn_act;
     m.tap_q = T.nq; m.tap_d = T.nd;
-    if ((st = launch_mv(m, PRO_NORM, EPI_SWIGLU_Q8, s, kMvWgPerCu, &mk)) != LQ_OK) return st;
+    if ((st = launch_proj(pw[2], m, PRO_NORM, EPI_SWIGLU_Q8, s, &mk)) != LQ_OK) return st;
     // down projection on the Q8_0 h, plus the residual
     m = MvArgs{};
-    m.wq = L->w_down.qs; m.wd = L->w_down.d; m.rows = (int)H; m.cols = (int)I;
+    m.rows = (int)H; m.cols = (int)I;
     m.xq = b.hq; m.xd = b.hd; m.res = b.x1; m.y = x;
-    return launch_mv(m, PRO_Q8, EPI_RESID, s, kMvWgPerCu, &mk);
+    return launch_proj(pw[3], m, PRO_Q8, EPI_RESID, s, &mk);
 }
 }  // namespace

@@ -935,13 +935,15 @@ extern "C" lq_status lq_moe_block_ggml(const lq_moe_ggml_desc* m, const float* x
                     workspace_bytes);
     MoeBuffers b = moe_layout(&d, T, static_cast<char*>(workspace), taps);
     hipStream_t s = as_stream(stream);
-    const int64_t S = T * k;
     const int64_t prep_grid = 1 + (T * (H / 32) + kPrepQuantBlocks - 1) / kPrepQuantBlocks;
     hipLaunchKernelGGL(k_moe_prep, dim3((unsigned)prep_grid), dim3(kGatherThreads), 0, s, logits, x, (int)T, (int)E,
                        (int)k, (int)H, b.ids, b.w, static_cast<int32_t*>(b.gather), b.xq, b.xd, b.y1, 2 * I, b.y2, H);
     if ((st = check_launch("moe_prep")) != LQ_OK) return st;
+    // gate/up, then SwiGLU + Q8_0 of h in a launch of its own (measured: a
+    // gate/up id-matvec with the SwiGLU and Q8_0 epilogue, one workgroup per
+    // 32 outputs as the Q8_0 block does it, was slower on these formats)
     if ((st = launch_ggml_id(gu, E, b.xq, b.xd, 0, k, b.gather, b.y1, s)) != LQ_OK) return st;
-    if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
+    if ((st = launch_swiglu_q8(b.y1, T * k, I, b.hq, b.hd, s)) != LQ_OK) return st;
     if ((st = launch_ggml_id(dn, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK) return st;
     return launch_moe_weighted_sum(b.y2, b.w, T, k, H, b.ids, m->expert_scale, m->n_experts, out, s);
 }

@@ -101,6 +101,28 @@ struct MvArgs {
 lq_status launch_mv(const MvArgs& a, int pro, int epi, hipStream_t s, int wg_per_cu,
                     LaunchMarks* mk = nullptr);
 
+// A projection weight in any of the library's formats: LQ_FMT_Q8_0 (q0 =
+// codes, d = scales), LQ_FMT_Q4_0 (q0 = qs, d) or LQ_FMT_Q6_K (q0 = ql, q1 =
+// qh, sc, d); device arrays as include/lq.h lays them out.
+struct ProjWeight {
+    int fmt;
+    const void* q0;
+    const void* q1;
+    const int8_t* sc;
+    const uint16_t* d;
+};
+// The fused matvec of MvArgs (prologue, epilogue, taps; wq/wd ignored) on a
+// weight of any format: the Q8_0 kernels for LQ_FMT_Q8_0, the Q4_0 / Q6_K
+// kernels of k_qk.hip otherwise (same prologues and epilogues; EPI_SWIGLU
+// without Q8 and EPI_DOTS only for Q8_0).
+lq_status launch_proj(const ProjWeight& w, const MvArgs& m, int pro, int epi, hipStream_t s,
+                      LaunchMarks* mk = nullptr);
+// Validates the weight of format fmt among the three descriptors (shape
+// rows x cols, pointers, alignment) and fills *out.
+lq_status check_proj_weight(const char* fn, const char* what, int32_t fmt, const lq_q8_weight& q8,
+                            const lq_q4_0_weight& q4, const lq_q6_k_weight& q6, int64_t rows, int64_t cols,
+                            ProjWeight* out);
+
 // ---- launchers (k_norm_rope.hip) ----------------------------------------------
 lq_status launch_rmsnorm_rope(float* x, int64_t n_heads, int64_t hd, int64_t head_stride,
                               const float* gamma, float eps, const float* rope_cos,

@@ -3,9 +3,28 @@ uploads with torch, fills the lq_layer_desc / lq_moe_desc descriptors and
 owns the workspace.  Marshalling only; every computation runs in liblq."""
 import numpy as np
 
-from . import (lq_decode_layer, lq_decode_layer_workspace_size, lq_layer_desc, lq_layer_taps,
-               lq_moe_block, lq_moe_block_workspace_size, lq_moe_desc, lq_moe_taps, lq_q8_weight,
-               lq_rope_table, lq_rope_table_freqs, q8_weight)
+from . import (LQ_FMT_Q4_0, LQ_FMT_Q6_K, lq_decode_layer, lq_decode_layer_workspace_size, lq_layer_desc,
+               lq_layer_taps, lq_moe_block, lq_moe_block_workspace_size, lq_moe_desc, lq_moe_taps, lq_q4_0_pack_ggml,
+               lq_q6_k_pack_ggml, lq_q8_weight, lq_rope_table, lq_rope_table_freqs, q4_0_weight, q6_k_weight,
+               q8_weight)
+
+PROJECTIONS = ("qkv", "o", "gu", "dn")     # lq_layer_desc.w_format order
+
+
+def ggml_device_weight(fmt, blocks, rows, cols, torch):
+    """GGML blocks (host, AoS) -> the library's SoA device arrays (packed by
+    its host helper) and the matching weight descriptor."""
+    if fmt == "q4_0":
+        qs = np.zeros((rows, cols // 2), np.uint8)
+        d = np.zeros((rows, cols // 32), np.uint16)
+        lq_q4_0_pack_ggml(blocks, rows, cols, qs, d)
+        return q4_0_weight(_dev(qs, torch), _dev(d, torch), rows, cols)
+    ql = np.zeros((rows, cols // 2), np.uint8)
+    qh = np.zeros((rows, cols // 4), np.uint8)
+    sc = np.zeros((rows, cols // 16), np.int8)
+    d = np.zeros((rows, cols // 256), np.uint16)
+    lq_q6_k_pack_ggml(blocks, rows, cols, ql, qh, sc, d)
+    return q6_k_weight(_dev(ql, torch), _dev(qh, torch), _dev(sc, torch), _dev(d, torch), rows, cols)
 
 
 def _dev(a, torch):
@@ -24,7 +43,8 @@ class DeviceLayer:
     def __init__(self, cfg, w, torch):
         self.cfg, self.torch = cfg, torch
         H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
-        self.t = {k: _dev(v, torch) for k, v in w.items() if k != "x"}
+        self.t = {k: _dev(v, torch) for k, v in w.items()
+                  if k != "x" and not k.endswith(("_fmt", "_blocks", "_dev"))}
         c = np.zeros((cfg["max_ctx"], hd // 2), np.float32)
         s = np.zeros((cfg["max_ctx"], hd // 2), np.float32)
         if cfg.get("rope_freqs") is not None:
@@ -34,8 +54,8 @@ class DeviceLayer:
             lq_rope_table(cfg["max_ctx"], hd, cfg["theta"], c, s)
         self.t["rope_cos"], self.t["rope_sin"] = _dev(c, torch), _dev(s, torch)
         t = self.t
-        W = lambda name: q8_weight(t[name + "_qs"], t[name + "_d"])
         empty_w = lq_q8_weight(None, None, 0, 32)
+        W = lambda name: q8_weight(t[name + "_qs"], t[name + "_d"]) if name + "_qs" in t else empty_w
         self.desc = lq_layer_desc(
             hidden=H, n_q=nq, n_kv=nkv, head_dim=hd, ffn=I, max_ctx=cfg["max_ctx"],
             window=cfg["window"], eps=cfg["eps"], attn_scale=cfg["attn_scale"], kind=cfg["kind"],
@@ -47,6 +67,21 @@ class DeviceLayer:
             v_cache=t["v_cache"].data_ptr(), rope_cos=t["rope_cos"].data_ptr(),
             rope_sin=t["rope_sin"].data_ptr(), ffn_act=cfg.get("ffn_act", 0),
             attn_softcap=cfg.get("attn_softcap", 0.0))
+        # projections in GGML formats
+        shapes = {"qkv": (nq * hd + 2 * nkv * hd, H), "o": (H, nq * hd), "gu": (2 * I, H), "dn": (H, I)}
+        self.ggml = []
+        for i, key in enumerate(PROJECTIONS):
+            f = w.get(key + "_fmt")
+            if f is None:
+                continue
+            # host GGML blocks (packed here), or a device weight built by the caller
+            gw = w[key + "_dev"] if key + "_dev" in w else ggml_device_weight(f, w[key + "_blocks"], *shapes[key], torch)
+            self.ggml.append(gw)                      # keeps the device arrays alive
+            self.desc.w_format[i] = LQ_FMT_Q4_0 if f == "q4_0" else LQ_FMT_Q6_K
+            if f == "q4_0":
+                self.desc.w_q4_0[i] = gw
+            else:
+                self.desc.w_q6_k[i] = gw
         self.ws_bytes = lq_decode_layer_workspace_size(self.desc)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
 

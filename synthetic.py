@@ -114,22 +114,38 @@ def kv_cache(rng, n_kv, ctx, hd, kv_dtype):
     return (a.view(np.uint32) >> 16).astype(np.uint16)
 
 
-def layer_inputs(name, seed=0):
-    """All inputs of one decode layer of workload `name` (numpy, CPU)."""
+PROJECTIONS = ("qkv", "o", "gu", "dn")     # the layer's four weights, in lq_layer_desc.w_format order
+
+
+def layer_inputs(name, seed=0, formats=None):
+    """All inputs of one decode layer of workload `name` (numpy, CPU).
+    formats: optional {"qkv" | "o" | "gu" | "dn": "q4_0" | "q6_k"}; those
+    projections are drawn as GGML blocks (w[key + "_blocks"], with
+    w[key + "_fmt"]) in place of Q8_0 codes and scales, in the same draw
+    order."""
     c = layer_cfg(name)
     rng = np.random.Generator(np.random.PCG64(seed))
     H, nq, nkv, hd, I = c["hidden"], c["n_q"], c["n_kv"], c["head_dim"], c["ffn"]
     w = {}
+
+    def proj(key, rows, cols):
+        f = (formats or {}).get(key)
+        if f is None:
+            w[key + "_qs"], w[key + "_d"] = q8_weight(rng, rows, cols)
+        else:
+            w[key + "_fmt"] = f
+            w[key + "_blocks"] = (q4_0_blocks if f == "q4_0" else q6_k_blocks)(rng, rows, cols)
+
     w["x"] = activations(rng, H)
     w["g_in"] = gamma(rng, H)
-    w["qkv_qs"], w["qkv_d"] = q8_weight(rng, nq * hd + 2 * nkv * hd, H)
+    proj("qkv", nq * hd + 2 * nkv * hd, H)
     w["g_q"] = gamma(rng, hd)
     w["g_k"] = gamma(rng, hd)
-    w["o_qs"], w["o_d"] = q8_weight(rng, H, nq * hd)
+    proj("o", H, nq * hd)
     w["g_post"] = gamma(rng, H)
     if I > 0:
-        w["gu_qs"], w["gu_d"] = q8_weight(rng, 2 * I, H)
-        w["dn_qs"], w["dn_d"] = q8_weight(rng, H, I)
+        proj("gu", 2 * I, H)
+        proj("dn", H, I)
     w["k_cache"] = kv_cache(rng, nkv, c["max_ctx"], hd, c["kv_dtype"])
     w["v_cache"] = kv_cache(rng, nkv, c["max_ctx"], hd, c["kv_dtype"])
     return c, w

@@ -59,6 +59,18 @@ def check_kv_row(row_gpu, tap, ref, kv_dtype, what):
     return int(diff.size)
 
 
+def proj_matvec(w, key, xq, xd, residual=None):
+    """The oracle's product of projection `key` ("qkv", "o", "gu", "dn") with a
+    Q8_0 activation: its Q8_0 matvec, or the GGML-format matvec when the
+    inputs carry that projection as Q4_0 / Q6_K blocks."""
+    f = w.get(key + "_fmt")
+    if f is None:
+        return oracle.q8_matvec(w[key + "_qs"], w[key + "_d"], xq, xd, residual=residual)
+    blocks = w[key + "_blocks"]
+    rows, cols = blocks.shape[0], blocks.shape[1] * (32 if f == "q4_0" else 256)
+    return oracle.q_matvec(f, blocks, rows, cols, xq, xd, residual=residual)
+
+
 def post_rope(cfg, qkv, gq, gk, cos_row, sin_row):
     """The oracle's per-head steps after the QKV projection: RMSNorm (g_q / g_k)
     and NeoX RoPE of every q and k head, the optional unit norm of v."""
@@ -91,7 +103,7 @@ def free_running(cfg, w, T, kc_gpu, vc_gpu, rope_cos, rope_sin, what="layer"):
     # input RMSNorm and its Q8_0
     xn = oracle.rmsnorm(w["x"], w["g_in"], eps)
     flips["xq"] = assert_q8_near(T["xq"], T["xd"], xn, what + ": input norm Q8")
-    qkv = oracle.q8_matvec(w["qkv_qs"], w["qkv_d"], T["xq"], T["xd"])
+    qkv = proj_matvec(w, "qkv", T["xq"], T["xd"])
     post = post_rope(cfg, qkv, w.get("g_q"), w.get("g_k"), rope_cos[pos], rope_sin[pos])
     # the appended row: the oracle's conversion, or the GPU's at boundary flips
     kc, vc = w["k_cache"].copy(), w["v_cache"].copy()
@@ -109,14 +121,14 @@ def free_running(cfg, w, T, kc_gpu, vc_gpu, rope_cos, rope_sin, what="layer"):
                            pos - start + 1, cfg["attn_scale"], softcap=cap)
     flips["aq"] = assert_q8_near(T["aq"], T["ad"], att, what + ": attention Q8")
     if kind == 0:
-        x1 = oracle.q8_matvec(w["o_qs"], w["o_d"], T["aq"], T["ad"], residual=w["x"])
+        x1 = proj_matvec(w, "o", T["aq"], T["ad"], residual=w["x"])
         flips["nq"] = assert_q8_near(T["nq"], T["nd"], oracle.rmsnorm(x1, w["g_post"], eps), what + ": post norm Q8")
-        gu = oracle.q8_matvec(w["gu_qs"], w["gu_d"], T["nq"], T["nd"])
+        gu = proj_matvec(w, "gu", T["nq"], T["nd"])
         gate = oracle.gelu_mul if act == 1 else oracle.silu_mul
         h = gate(gu[:I], gu[I:])
         flips["hq"] = assert_q8_near(T["hq"], T["hd"], h, what + ": Q8 of act(gate) * up")
-        out = oracle.q8_matvec(w["dn_qs"], w["dn_d"], T["hq"], T["hd"], residual=x1)
+        out = proj_matvec(w, "dn", T["hq"], T["hd"], residual=x1)
     else:
-        o = oracle.q8_matvec(w["o_qs"], w["o_d"], T["aq"], T["ad"])
+        o = proj_matvec(w, "o", T["aq"], T["ad"])
         out = (w["x"].astype(np.float64) + oracle.rmsnorm(o, w["g_post"], eps)).astype(np.float32)
     return out, flips

@@ -321,6 +321,52 @@ def test_layer_validation():
     assert st(lq.lq_decode_layer_timed, d, A, 8192, None, A, need, [A] * (2 * n)) == lq.LQ_ERR_SHAPE
 
 
+def test_layer_ggml_format_validation():
+    """Projections in GGML formats (lq_layer_desc.w_format): the chosen
+    descriptor's shape, pointers and alignment are checked before any launch."""
+    H, nq, nkv, hd, I = 4096, 32, 8, 128, 12288
+    d = _layer_desc()
+    need = lq.lq_decode_layer_workspace_size(d)
+    call = lambda desc: st(lq.lq_decode_layer, desc, A, 8191, None, A, need)
+
+    def with_formats(fmts, q4=None, q6=None):
+        desc = _layer_desc()
+        for i, f in enumerate(fmts):
+            desc.w_format[i] = f
+        for i, w in (q4 or {}).items():
+            desc.w_q4_0[i] = w
+        for i, w in (q6 or {}).items():
+            desc.w_q6_k[i] = w
+        return desc
+
+    Q8, Q4, Q6 = lq.LQ_FMT_Q8_0, lq.LQ_FMT_Q4_0, lq.LQ_FMT_Q6_K
+    good_q6_gu = lq.lq_q6_k_weight(A, A, A, A, 2 * I, H)
+    good_q4_dn = lq.lq_q4_0_weight(A, A, H, I)
+    assert call(with_formats([Q8, Q8, 7, Q8])) == lq.LQ_ERR_SHAPE                           # unknown format
+    assert call(with_formats([Q8, Q8, Q6, Q4])) == lq.LQ_ERR_SHAPE                          # descriptors left empty
+    assert call(with_formats([Q8, Q8, Q6, Q4], q4={3: lq.lq_q4_0_weight(A, A, H, I + 32)},
+                             q6={2: good_q6_gu})) == lq.LQ_ERR_SHAPE                         # wrong cols
+    assert call(with_formats([Q8, Q8, Q6, Q4], q4={3: lq.lq_q4_0_weight(None, A, H, I)},
+                             q6={2: good_q6_gu})) == lq.LQ_ERR_NULL
+    assert call(with_formats([Q8, Q8, Q6, Q4], q4={3: good_q4_dn},
+                             q6={2: lq.lq_q6_k_weight(A, A, A + 4, A, 2 * I, H)})) == lq.LQ_ERR_ALIGN
+    assert call(with_formats([Q8, Q6, Q8, Q8], q6={1: lq.lq_q6_k_weight(A, A, A, A, H, 4000)})) == lq.LQ_ERR_SHAPE
+    # a Q6_K QKV needs cols % 256 == 0
+    d6 = _layer_desc(hidden=4000, w_qkv=lq.lq_q8_weight(A, A, nq * hd + 2 * nkv * hd, 4000),
+                     w_o=lq.lq_q8_weight(A, A, 4000, nq * hd), w_gate_up=lq.lq_q8_weight(A, A, 2 * I, 4000),
+                     w_down=lq.lq_q8_weight(A, A, 4000, I))
+    d6.w_format[0] = Q6
+    d6.w_q6_k[0] = lq.lq_q6_k_weight(A, A, A, A, nq * hd + 2 * nkv * hd, 4000)
+    assert call(d6) == lq.LQ_ERR_SHAPE
+    # a Q6_K gate_up over more than 12288 columns is refused up front
+    big = _layer_desc(hidden=16384, w_qkv=lq.lq_q8_weight(A, A, nq * hd + 2 * nkv * hd, 16384),
+                      w_o=lq.lq_q8_weight(A, A, 16384, nq * hd), w_down=lq.lq_q8_weight(A, A, 16384, I))
+    big.w_format[2] = Q6
+    big.w_q6_k[2] = lq.lq_q6_k_weight(A, A, A, A, 2 * I, 16384)
+    assert st(lq.lq_decode_layer, big, A, 8191, None, A, lq.lq_decode_layer_workspace_size(big)) == \
+        lq.LQ_ERR_UNSUPPORTED
+
+
 def test_pack_ggml_host():
     rng = np.random.default_rng(0)
     rows, cols = 5, 96

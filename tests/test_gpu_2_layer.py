@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 lq = pytest.importorskip("q8_matvec_gqa_amd")
 from q8_matvec_gqa_amd.layers import DeviceLayer, DeviceMoe  # noqa: E402
 from lqtest import assert_close, assert_q8_near, dev, host, sync, torch_mod  # noqa: E402
-from layercheck import check_kv_row, free_running, post_rope  # noqa: E402
+from layercheck import check_kv_row, free_running, post_rope, proj_matvec  # noqa: E402
 
 LAYERS = list(synthetic.WORKLOADS)
 
@@ -57,14 +57,28 @@ def test_layer_rope_freqs_teacher_forced():
     run_teacher_forced("gemma4_global_h2816", freqs=f)
 
 
-def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
+# GGML weight formats in the layer ("Current Inference Path -- Architecture Map",
+# section 4: the current path runs GGML Q6_K weights): the 8B-like layer with
+# a Q6_K gate_up and a Q4_0 down, every projection Q4_0, the other pairing,
+# and the Gemma block with Q6_K QKV and Q4_0 O
+@pytest.mark.parametrize("name,formats", [
+    ("qwen3_8b_like_h4096", {"gu": "q6_k", "dn": "q4_0"}),
+    ("qwen3_4b_like_h2560", {"qkv": "q4_0", "o": "q4_0", "gu": "q4_0", "dn": "q4_0"}),
+    ("tiny_h1024", {"qkv": "q6_k", "o": "q6_k", "gu": "q4_0", "dn": "q6_k"}),
+    ("gemma4_sliding_h2816", {"qkv": "q6_k", "o": "q4_0"}),
+], ids=["8b-gu_q6k-dn_q40", "4b-all_q40", "tiny-mixed", "gemma_sliding-q6k_q40"])
+def test_layer_ggml_formats_teacher_forced(name, formats):
+    run_teacher_forced(name, formats=formats)
+
+
+def run_teacher_forced(name, act=0, cap=0.0, freqs=None, formats=None):
     torch = torch_mod()
-    cfg, w = synthetic.layer_inputs(name, seed=0)
+    cfg, w = synthetic.layer_inputs(name, seed=0, formats=formats)
     cfg = dict(cfg, ffn_act=act, attn_softcap=cap, rope_freqs=freqs)
     H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
     pos, kind = cfg["pos"], cfg["kind"]
     qd, kvd = nq * hd, nkv * hd
-    print(f"[layer] {name} pos={pos} act={act} softcap={cap}", flush=True)
+    print(f"[layer] {name} pos={pos} act={act} softcap={cap} formats={formats}", flush=True)
     L = DeviceLayer(cfg, w, torch)
     taps, bufs = L.make_taps()
     x = dev(w["x"])
@@ -88,7 +102,7 @@ def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
     # 1. input norm + quantize
     flips += assert_q8_near(T["xq"], T["xd"], oracle.rmsnorm(w["x"], w["g_in"], eps), "input norm Q8")
     # 2. raw QKV projection from the GPU's Q8 input
-    assert_close(T["qkv"], oracle.q8_matvec(w["qkv_qs"], w["qkv_d"], T["xq"], T["xd"]), "qkv projection")
+    assert_close(T["qkv"], proj_matvec(w, "qkv", T["xq"], T["xd"]), "qkv projection")
     # per-head norms and RoPE of the GPU's raw projection (the oracle's steps),
     # against the attention prologue's own f32 results
     post = post_rope(cfg, T["qkv"], w["g_q"], w["g_k"], oc[pos], os_[pos])
@@ -114,17 +128,17 @@ def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
     assert np.array_equal(T["aq"], aq) and np.array_equal(T["ad"], ad)
     # 6. O projection (+ residual for the pre-norm layer)
     if kind == 0:
-        assert_close(T["x1"], oracle.q8_matvec(w["o_qs"], w["o_d"], T["aq"], T["ad"], residual=w["x"]), "x1")
+        assert_close(T["x1"], proj_matvec(w, "o", T["aq"], T["ad"], residual=w["x"]), "x1")
         flips += assert_q8_near(T["nq"], T["nd"], oracle.rmsnorm(T["x1"], w["g_post"], eps), "post norm Q8")
-        gu = oracle.q8_matvec(w["gu_qs"], w["gu_d"], T["nq"], T["nd"])
+        gu = proj_matvec(w, "gu", T["nq"], T["nd"])
         gate = oracle.gelu_mul if act == 1 else oracle.silu_mul
         assert_close(T["h"], gate(gu[:I], gu[I:]), "act(gate) * up")
         hq, hd_ = oracle.q8_quantize(T["h"])                 # identical float input -> bit-exact
         assert np.array_equal(T["hq"], hq) and np.array_equal(T["hd"], hd_)
-        assert_close(out_gpu, oracle.q8_matvec(w["dn_qs"], w["dn_d"], T["hq"], T["hd"], residual=T["x1"]),
+        assert_close(out_gpu, proj_matvec(w, "dn", T["hq"], T["hd"], residual=T["x1"]),
                      "layer output")
     else:
-        assert_close(T["x1"], oracle.q8_matvec(w["o_qs"], w["o_d"], T["aq"], T["ad"]), "o projection")
+        assert_close(T["x1"], proj_matvec(w, "o", T["aq"], T["ad"]), "o projection")
         n = oracle.rmsnorm(T["x1"], w["g_post"], eps)
         assert_close(out_gpu, (w["x"].astype(np.float64) + n).astype(np.float32), "block output")
 
@@ -132,11 +146,12 @@ def run_teacher_forced(name, act=0, cap=0.0, freqs=None):
     # discrete values carried forward only at checked boundary flips
     ref_fr, fr_flips = free_running(cfg, w, T, kc_gpu, vc_gpu, oc, os_, name)
     err = assert_close(out_gpu, ref_fr, "free-running layer output")
-    ow = dict(w)
-    ow["rope_cos"], ow["rope_sin"] = oc, os_
-    ref_out, _, _, _ = oracle.decode_layer(oracle_cfg(cfg), ow, w["x"], pos, w["k_cache"], w["v_cache"])
     n_fr = sum(fr_flips.values())
-    if n_fr == 0:
+    if n_fr == 0 and not formats:
+        # the oracle's own composed layer (Q8_0 weights only)
+        ow = dict(w)
+        ow["rope_cos"], ow["rope_sin"] = oc, os_
+        ref_out, _, _, _ = oracle.decode_layer(oracle_cfg(cfg), ow, w["x"], pos, w["k_cache"], w["v_cache"])
         assert_close(out_gpu, ref_out, "free-running layer output (orc_decode_layer)")
     print(f"[layer] {name}: free-running max rel err {err:.2e}; flips carried forward {fr_flips}; "
           f"teacher-forced flips {flips}", flush=True)
@@ -296,6 +311,7 @@ def _ggml_experts(fmt, r, rows, cols, E):
 @pytest.mark.parametrize("gu_fmt,dn_fmt,small", [
     ("q6_k", "q4_0", False),     # the MoE workload at full size, with the pages' formats (Q6_K gate/up, Q4_0 down)
     ("q4_0", "q6_k", True),      # the other pairing: 16 experts, 5 tokens, top-4, hidden 512, ffn 256
+    ("q6_k", "q4_0", "wide"),    # hidden 8192 (> 4096: the id-matvec and a separate SwiGLU launch)
 ])
 def test_moe_block_ggml_teacher_forced(gu_fmt, dn_fmt, small):
     """The MoE block on GGML-format experts: routing, Q8(x), each slot's
@@ -303,9 +319,9 @@ def test_moe_block_ggml_teacher_forced(gu_fmt, dn_fmt, small):
     expert fed the GPU's own inputs, the Q8_0 of h near the oracle's, and the
     weighted sum."""
     torch = torch_mod()
-    r = np.random.default_rng(31 if small else 32)
+    r = np.random.default_rng(31 if small is True else 33 if small else 32)
     if small:
-        T_, H, I, E, k = 5, 512, 256, 16, 4
+        T_, H, I, E, k = (5, 512, 256, 16, 4) if small is True else (3, 8192, 128, 8, 2)
         x = synthetic.activations(r, T_, H)
         logits = r.standard_normal((T_, E)).astype(np.float32)
     else:

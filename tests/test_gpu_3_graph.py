@@ -40,13 +40,15 @@ def capture(torch, fn):
     return g
 
 
-@pytest.mark.parametrize("name", ["tiny_h1024", synthetic.HEADLINE, "gemma4_global_h2816"])
-def test_layer_graph_replays(name):
+@pytest.mark.parametrize("name,formats", [("tiny_h1024", None), (synthetic.HEADLINE, None),
+                                          ("gemma4_global_h2816", None),
+                                          (synthetic.HEADLINE, {"gu": "q6_k", "dn": "q4_0"})])
+def test_layer_graph_replays(name, formats):
     """Three chained decode steps (x updated in place, the new position's
     k/v rewritten each step): the graph's replays equal the eager steps."""
     torch = torch_mod()
-    cfg, w = synthetic.layer_inputs(name, seed=5)
-    print(f"[graph] layer {name}", flush=True)
+    cfg, w = synthetic.layer_inputs(name, seed=5, formats=formats)
+    print(f"[graph] layer {name} formats={formats}", flush=True)
     L = DeviceLayer(cfg, w, torch)
 
     def reset():
