@@ -823,6 +823,33 @@ def trace_phases(R, steps, warmup, rounds):
     return {"eager": (0, a), "graph": (b, c), "timed": (d, e)}
 
 
+def summarize_counters(dirs, out_path, command, title):
+    """Per-kernel averages (over dispatches) of every counter in one or more
+    rocprofv3 --pmc output folders (one pass each) -> a text summary."""
+    import statistics
+    per = {}
+    for d in dirs:
+        rows = _read_csv(_find(d, "counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            n = r["Kernel_Name"]
+            if "lq::" not in n:
+                continue
+            key = (n, r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (n, _, c), v in acc.items():
+            per.setdefault(n, {}).setdefault(c, []).append(v)
+    lines = [f"# {title}", f"command: {command}", f"source_sha256: {source_hash()}",
+             "kernel | counter | dispatches | average per dispatch"]
+    for n in sorted(per):
+        for c in sorted(per[n]):
+            v = per[n][c]
+            lines.append(f"{n} | {c} | {len(v)} | {statistics.mean(v):.1f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, out_dir, workload, command, steps=20, warmup=5, rounds=5):
     """Kernel-trace statistics of a bench run -> a text summary: every lq
     kernel (average duration over all its dispatches), then each kernel of
@@ -955,6 +982,10 @@ def main():
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write the kernel-trace summary from a rocprofv3 --kernel-trace folder and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar=("NAME", "DIR"),
+                    help="write profiles/NAME.txt: per-kernel counter averages from rocprofv3 --pmc folders, and exit")
+    ap.add_argument("--only", choices=["attn_long_context", "moe_block", "lm_head"],
+                    help="run only this extra measurement (for profiling) and print its JSON")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     ap.add_argument("--profiles-dir", default=PROFILES, help="where the summaries are written")
     args = ap.parse_args()
@@ -968,6 +999,12 @@ def main():
         summarize_trace(args.summarize_trace, args.profiles_dir, args.workload, args.command, args.steps, args.warmup,
                         args.rounds)
         return
+    if args.summarize_counters:
+        name, dirs = args.summarize_counters[0], args.summarize_counters[1:]
+        os.makedirs(args.profiles_dir, exist_ok=True)
+        summarize_counters(dirs, os.path.join(args.profiles_dir, name + ".txt"), args.command,
+                           f"rocprofv3 counters per kernel ({name})")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -977,6 +1014,12 @@ def main():
     import q8_matvec_gqa_amd as lq  # noqa: F401  (fails loudly without liblq.so)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.only:
+        fn = {"attn_long_context": lambda: measure_attn_context(max(5, args.steps // 5), torch),
+              "moe_block": lambda: measure_moe(list(synthetic.MOE_WORKLOADS)[0], max(10, args.steps // 2), torch),
+              "lm_head": lambda: measure_head(max(10, args.steps // 2), torch)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
     cfg = synthetic.layer_cfg(args.workload)
     m = measure_layer(args.workload, args.steps, args.warmup, args.rounds, args.min_stack_bytes, torch)
     per, us_layer, R = m["per"], m["us_layer"], m["R"]

@@ -532,9 +532,10 @@ template <int NCH>
 static void launch_id_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int rows, int cols,
                           const int8_t* xq, const uint16_t* xd, int x_per_slot, int k,
                           const int32_t* ws, int E, float* y) {
-    // rows per wave: short rows (<= 2 KB) 4, longer ones 2 (measured on the
-    // 128-expert block: more, smaller workgroups keep more loads in flight)
-    constexpr int RPW = NCH <= 2 ? 4 : 2;
+    // rows per wave: short rows (<= 2 KB) 8, longer ones 2.  Measured on the
+    // 128-expert block (704-byte down rows): 2 rows per wave 133-139 us, 4
+    // rows 121-126, 8 rows 118-123, 16 rows 127-131 per block
+    constexpr int RPW = NCH <= 2 ? 8 : 2;
     const int rowblocks = (rows + 4 * RPW - 1) / (4 * RPW);
     hipLaunchKernelGGL((k_moe_matvec_id<NCH, RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, wq, wd,
                        rows, cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
