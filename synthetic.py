@@ -151,8 +151,11 @@ def layer_inputs(name, seed=0, formats=None):
     return c, w
 
 
-def moe_inputs(name, seed=0):
+def moe_inputs(name, seed=0, **over):
+    """The MoE workload `name`, or its shape with fields replaced by `over`
+    (tokens, hidden, ffn, n_experts, top_k)."""
     c = dict(MOE_WORKLOADS[name])
+    c.update(over)
     rng = np.random.Generator(np.random.PCG64(seed))
     H, I, E, T = c["hidden"], c["ffn"], c["n_experts"], c["tokens"]
     w = {}

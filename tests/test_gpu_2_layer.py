@@ -226,16 +226,15 @@ def test_layer_positions_sliding(pos):
     assert_close(host(bufs["attn"]), att, f"attention at pos {pos}")
 
 
-@pytest.mark.parametrize("scaled", [False, True])
-def test_moe_block_teacher_forced(scaled):
+def _check_moe_block(cfg, w, escale, tag):
+    """One MoE block on the GPU with every tap, checked stage by stage against
+    the oracle fed the GPU's own inputs (teacher-forced), then free-running
+    from the original inputs with only checked Q8_0 flips of h carried
+    forward.  Returns (max rel err free-running, flips)."""
     torch = torch_mod()
-    name = list(synthetic.MOE_WORKLOADS)[0]
-    cfg, w = synthetic.moe_inputs(name, seed=0)
     T_, H, I, E, k = cfg["tokens"], cfg["hidden"], cfg["ffn"], cfg["n_experts"], cfg["top_k"]
-    escale = synthetic.gamma(np.random.default_rng(77), E) if scaled else None
-    if scaled:
+    if escale is not None:
         w = dict(w, expert_scale=escale)
-    print(f"[moe] {name} per-expert scale={scaled}", flush=True)
     M = DeviceMoe(cfg, w, torch)
     taps, bufs = M.make_taps()
     x, logits = dev(w["x"]), dev(w["logits"])
@@ -246,27 +245,28 @@ def test_moe_block_teacher_forced(scaled):
     G["xd"], G["hd"] = G["xd"].view(np.uint16), G["hd"].view(np.uint16)
     ids = G["ids"].reshape(T_, k)
     rid, rw = oracle.moe_route(w["logits"], k)
-    assert np.array_equal(ids, rid)
-    assert_close(G["w"].reshape(T_, k), rw, "route weights")
+    assert np.array_equal(ids, rid), f"{tag}: routing ids"
+    assert_close(G["w"].reshape(T_, k), rw, f"{tag}: route weights")
     xq, xd = oracle.q8_quantize(w["x"])
-    assert np.array_equal(G["xq"].reshape(T_, H), xq) and np.array_equal(G["xd"].reshape(T_, H // 32), xd)
+    assert np.array_equal(G["xq"].reshape(T_, H), xq) and np.array_equal(G["xd"].reshape(T_, H // 32), xd), \
+        f"{tag}: Q8_0 of x"
     y1 = G["y1"].reshape(T_, k, 2 * I)
     hq = G["hq"].reshape(T_, k, I)
     hd = G["hd"].reshape(T_, k, I // 32)
     y2 = G["y2"].reshape(T_, k, H)
-    flips = 0
     for t in range(T_):
         for s in range(k):
             e = ids[t, s]
-            assert_close(y1[t, s], oracle.q8_matvec(w["gu_qs"][e], w["gu_d"][e], xq[t], xd[t]), f"y1 {t},{s}")
-            flips += assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1[t, s, :I], y1[t, s, I:]), f"h {t},{s}")
-            assert_close(y2[t, s], oracle.q8_matvec(w["dn_qs"][e], w["dn_d"][e], hq[t, s], hd[t, s]), f"y2 {t},{s}")
+            assert_close(y1[t, s], oracle.q8_matvec(w["gu_qs"][e], w["gu_d"][e], xq[t], xd[t]), f"{tag}: y1 {t},{s}")
+            assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1[t, s, :I], y1[t, s, I:]), f"{tag}: h {t},{s}")
+            assert_close(y2[t, s], oracle.q8_matvec(w["dn_qs"][e], w["dn_d"][e], hq[t, s], hd[t, s]),
+                         f"{tag}: y2 {t},{s}")
     ws = G["w"].reshape(T_, k).astype(np.float64)
-    if scaled:
+    if escale is not None:
         ws = ws * escale[ids].astype(np.float64)
     want = np.einsum("ts,tsh->th", ws, y2.astype(np.float64))
     got = host(out).reshape(T_, H)
-    assert_close(got, want, "weighted sum")
+    assert_close(got, want, f"{tag}: weighted sum")
     # free-running: the oracle's block from the original inputs (routing and
     # Q8(x) are bit-exact above), carrying the GPU's Q8_0 of h forward only
     # where it is a checked boundary flip of the oracle's own h
@@ -276,18 +276,57 @@ def test_moe_block_teacher_forced(scaled):
         for s in range(k):
             e = rid[t, s]
             y1o = oracle.q8_matvec(w["gu_qs"][e], w["gu_d"][e], xq[t], xd[t])
-            fr_flips += assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1o[:I], y1o[I:]), f"free-running h {t},{s}")
+            fr_flips += assert_q8_near(hq[t, s], hd[t, s], oracle.silu_mul(y1o[:I], y1o[I:]),
+                                       f"{tag}: free-running h {t},{s}")
             y2o = oracle.q8_matvec(w["dn_qs"][e], w["dn_d"][e], hq[t, s], hd[t, s])
-            ws_ = float(rw[t, s]) * (float(escale[e]) if scaled else 1.0)
+            ws_ = float(rw[t, s]) * (float(escale[e]) if escale is not None else 1.0)
             ref_fr[t] += ws_ * y2o.astype(np.float64)
-    err = assert_close(got, ref_fr, "free-running MoE block")
-    ref = oracle.moe_block(H, I, E, k, w["gu_qs"], w["gu_d"], w["dn_qs"], w["dn_d"], w["x"], w["logits"],
-                           expert_scale=escale)
+    err = assert_close(got, ref_fr, f"{tag}: free-running MoE block")
     if fr_flips == 0:
-        assert_close(got, ref, "free-running MoE block (orc_moe_block)")
-    touched = len(np.unique(ids))
-    print(f"[moe] free-running max rel err {err:.2e}; flips carried forward {fr_flips}; "
+        ref = oracle.moe_block(H, I, E, k, w["gu_qs"], w["gu_d"], w["dn_qs"], w["dn_d"], w["x"], w["logits"],
+                               expert_scale=escale)
+        assert_close(got, ref, f"{tag}: free-running MoE block (orc_moe_block)")
+    return err, fr_flips, len(np.unique(ids))
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_moe_block_teacher_forced(scaled):
+    """The MoE workload at full size."""
+    name = list(synthetic.MOE_WORKLOADS)[0]
+    cfg, w = synthetic.moe_inputs(name, seed=0)
+    escale = synthetic.gamma(np.random.default_rng(77), cfg["n_experts"]) if scaled else None
+    print(f"[moe] {name} per-expert scale={scaled}", flush=True)
+    err, flips, touched = _check_moe_block(cfg, w, escale, name)
+    print(f"[moe] free-running max rel err {err:.2e}; flips carried forward {flips}; "
           f"{touched} experts touched", flush=True)
+
+
+# (tokens, hidden, ffn, experts, top_k, scaled, tied logits): the block's
+# shape limits and edge cases beside the workload.
+MOE_SHAPES = [
+    (1, 512, 256, 8, 2, False, False),       # one token
+    (16, 512, 256, 100, 6, True, False),     # experts not a multiple of 64
+    (8, 2048, 1536, 8, 2, False, False),     # 2 KB rows in both matrices
+    (4, 3072, 2560, 4, 2, False, False),     # 3 KB rows
+    (5, 4096, 4096, 4, 2, False, False),     # the widest fused gate/up rows (4 KB)
+    (16, 256, 128, 64, 32, False, False),    # 512 slots, top-32
+    (8, 512, 256, 32, 4, False, True),       # tied logits: the lower id first
+    (16, 256, 128, 1024, 8, False, False),   # 1024 experts
+    (40, 512, 256, 16, 4, True, False),      # 40 tokens
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,scaled,tied", MOE_SHAPES)
+def test_moe_block_shapes(T, H, I, E, k, scaled, tied):
+    name = list(synthetic.MOE_WORKLOADS)[0]
+    cfg, w = synthetic.moe_inputs(name, seed=40 + T + E, tokens=T, hidden=H, ffn=I, n_experts=E, top_k=k)
+    if tied:
+        w["logits"] = np.round(w["logits"]).astype(np.float32)      # few distinct values: many ties
+    escale = synthetic.gamma(np.random.default_rng(78), E) if scaled else None
+    tag = f"moe T={T} H={H} I={I} E={E} k={k}"
+    print(f"[moe] {tag} scaled={scaled} tied={tied}", flush=True)
+    err, flips, touched = _check_moe_block(cfg, w, escale, tag)
+    print(f"[moe] max rel err {err:.2e}; flips {flips}; {touched} experts touched", flush=True)
 
 
 def _ggml_experts(fmt, r, rows, cols, E):
