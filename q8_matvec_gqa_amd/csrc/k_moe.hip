@@ -377,13 +377,20 @@ __global__ __launch_bounds__(256) void k_moe_qk_matvec_id(QkMat m, int rows, int
         const int64_t xrow = x_per_slot ? slot : slot / k;
         const int8_t* xr = xq + xrow * cols;
         const uint16_t* xdr = xd + xrow * (cols >> 5);
+        // the slot's activation, loaded once for all RPW rows
+        QkAct<FMT> A[ST];
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+            const int u = st * 64 + lane;
+            qk_load_act(xr, xdr, u < units ? u : 0, A[st]);
+        }
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             float acc = 0.0f;
 #pragma unroll
             for (int st = 0; st < ST; ++st) {
                 const int u = st * 64 + lane;
-                if (u < units) acc += qk_unit_dot_h(U[i][st], u, xr, xdr);
+                if (u < units) acc += qk_unit_dot_a(U[i][st], u, A[st]);
             }
             acc = wave_sum(acc);
             const int r = r0 + i;
@@ -601,14 +608,17 @@ static void launch_qk_id_st(hipStream_t s, const QkMat& m, int rows, int cols, i
 }
 
 // The id-matvec on an already gathered workspace.  Steps per row: Q4_0 up
-// to 4, Q6_K up to 2 (cols <= 8192).
+// to 4, Q6_K up to 2 (cols <= 8192).  Rows per wave: 4 for rows of one step
+// (measured on the 128-expert block, Q6_K gate/up and Q4_0 down: 129-134
+// us per block against 137-140 with 2 and 137-141 with 8 for Q4_0), else
+// 2 (1 for Q4_0's 4 steps).
 template <int FMT>
 static lq_status launch_qk_id_gathered(const QkMat& m, int64_t rows, int64_t cols, int64_t E, const int8_t* xq,
                                        const uint16_t* xd, int32_t x_per_slot, int64_t k, const void* ws, float* y,
                                        hipStream_t s) {
     const int32_t* w32 = static_cast<const int32_t*>(ws);
     switch ((qk_units<FMT>((int)cols) + 63) / 64) {
-        case 1: launch_qk_id_st<FMT, 1, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
+        case 1: launch_qk_id_st<FMT, 1, 4>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
         case 2: launch_qk_id_st<FMT, 2, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
         default:
             if constexpr (FMT == QK_Q4_0) {

@@ -107,15 +107,37 @@ __device__ __forceinline__ void qk_group_use(const QkArgs& a, int64_t grp, int l
                                              const QkRows<FMT, ST, RPW>& R, const int8_t* xl, const float* xs,
                                              float* hs) {
     float acc[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        float t = 0.0f;
+    // each unit's activation read from LDS once for the RPW rows, where the
+    // registers allow (the widest rows read it per row)
+    constexpr bool HOLD = FMT == QK_Q4_0 ? ST <= 4 : ST <= 2;
+    if constexpr (HOLD) {
+        QkAct<FMT> A[ST];
 #pragma unroll
         for (int st = 0; st < ST; ++st) {
             const int u = st * kWave + lane;
-            if (u < units) t += qk_unit_dot(R.u[i][st], u, xl, xs);
+            qk_load_act_l(xl, xs, u < units ? u : 0, A[st]);
         }
-        acc[i] = wave_sum(t);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float t = 0.0f;
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+                const int u = st * kWave + lane;
+                if (u < units) t += qk_unit_dot_a(R.u[i][st], u, A[st]);
+            }
+            acc[i] = wave_sum(t);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            float t = 0.0f;
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+                const int u = st * kWave + lane;
+                if (u < units) t += qk_unit_dot(R.u[i][st], u, xl, xs);
+            }
+            acc[i] = wave_sum(t);
+        }
     }
     if (lane != 0) return;
     if constexpr (EPI == EPI_SWIGLU_Q8) {

@@ -147,6 +147,66 @@ __device__ __forceinline__ float qk_unit_dot(const QkUnit<QK_Q6_K>& U, int u, co
     return f16_to_f32(U.d) * s;
 }
 
+// A unit's activation held in registers, so that the rows of one wave share
+// one load of it: Q4_0 the block's 32 codes and scale, Q6_K the four groups'
+// 16 codes each and the scales of their Q8_0 blocks.
+template <int FMT>
+struct QkAct;
+template <>
+struct QkAct<QK_Q4_0> {
+    int4 lo, hi;
+    float s;
+};
+template <>
+struct QkAct<QK_Q6_K> {
+    int4 x[4];
+    float s[4];
+};
+__device__ __forceinline__ void qk_load_act(const int8_t* xq, const uint16_t* xd, int u, QkAct<QK_Q4_0>& A) {
+    A.lo = *reinterpret_cast<const int4*>(xq + 32 * u);
+    A.hi = *reinterpret_cast<const int4*>(xq + 32 * u + 16);
+    A.s = f16_to_f32(xd[u]);
+}
+__device__ __forceinline__ void qk_load_act(const int8_t* xq, const uint16_t* xd, int u, QkAct<QK_Q6_K>& A) {
+    const int v0 = qk6_v0(u);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        A.x[g] = *reinterpret_cast<const int4*>(xq + v0 + 32 * g);
+        A.s[g] = f16_to_f32(xd[(v0 >> 5) + g]);
+    }
+}
+// The same from the activation in LDS (codes xq, f32 scales xs per block).
+__device__ __forceinline__ void qk_load_act_l(const int8_t* xq, const float* xs, int u, QkAct<QK_Q4_0>& A) {
+    A.lo = *reinterpret_cast<const int4*>(xq + 32 * u);
+    A.hi = *reinterpret_cast<const int4*>(xq + 32 * u + 16);
+    A.s = xs[u];
+}
+__device__ __forceinline__ void qk_load_act_l(const int8_t* xq, const float* xs, int u, QkAct<QK_Q6_K>& A) {
+    const int v0 = qk6_v0(u);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        A.x[g] = *reinterpret_cast<const int4*>(xq + v0 + 32 * g);
+        A.s[g] = xs[(v0 >> 5) + g];
+    }
+}
+// qk_unit_dot's and qk_unit_dot_h's arithmetic, in the same order, on a held
+// activation.
+__device__ __forceinline__ float qk_unit_dot_a(const QkUnit<QK_Q4_0>& U, int, const QkAct<QK_Q4_0>& A) {
+    const int dot = qk4_dot(U, A.lo, A.hi);
+    return (f16_to_f32(U.d) * A.s) * (float)dot;
+}
+__device__ __forceinline__ float qk_unit_dot_a(const QkUnit<QK_Q6_K>& U, int u, const QkAct<QK_Q6_K>& A) {
+    int dots[4];
+    qk6_dots(U, A.x, dots);
+    float c[4];
+    qk6_subscales(U, u, c);
+    float s = (c[0] * A.s[0]) * (float)dots[0];
+    s = fmaf(c[1] * A.s[1], (float)dots[1], s);
+    s = fmaf(c[2] * A.s[2], (float)dots[2], s);
+    s = fmaf(c[3] * A.s[3], (float)dots[3], s);
+    return f16_to_f32(U.d) * s;
+}
+
 // The same with the activation scales as f16 bits in global memory.
 __device__ __forceinline__ float qk_unit_dot_h(const QkUnit<QK_Q4_0>& U, int u, const int8_t* xq,
                                                const uint16_t* xd) {
