@@ -257,6 +257,12 @@ ATTN_CASES = [
     (8, 2, 512, 0, 200, 0, 200),          # f32, head_dim 512 (two chunks per lane in V)
     (4, 4, 8, 1, 130, 0, 130),            # head_dim 8: one 16-byte chunk per row
     (32, 8, 128, 1, 65536, 0, 65536),     # long context: 64 splits of 1024 positions (16 tiles per wave)
+    # head_dim 512, G 8, bf16 (the Gemma-global instance): ragged tiles, one and four kv heads, long context
+    (16, 2, 512, 1, 300, 0, 1),           # one position
+    (16, 2, 512, 1, 300, 0, 17),          # a few tiles and one position
+    (8, 1, 512, 1, 1000, 5, 995),         # one kv head, start > 0, a ragged last tile
+    (32, 4, 512, 1, 3000, 100, 1500),     # four kv heads, a window
+    (16, 2, 512, 1, 65536, 0, 65536),     # long context: several tiles per wave
 ]
 
 

@@ -199,12 +199,15 @@ def test_layer_timed_matches():
     assert all(t > 0 for t in ts), ts
 
 
-@pytest.mark.parametrize("pos", [0, 1, 63, 64, 1023, 1024, 5000])
-def test_layer_positions_sliding(pos):
+@pytest.mark.parametrize("name,pos", [("gemma4_sliding_h2816", p) for p in (0, 1, 63, 64, 1023, 1024, 5000)]
+                         + [("gemma4_global_h2816", p) for p in (0, 1, 15, 16, 17, 100, 2000)])
+def test_layer_positions(name, pos):
     """Early positions (window not full yet, start 0) and late ones (start > 0)
-    of the sliding-window block against the free-running oracle."""
+    of the sliding-window block, and early and late positions of the
+    full-context block (the new row at different places of its tile and
+    split), against the free-running oracle."""
     torch = torch_mod()
-    cfg, w = synthetic.layer_inputs("gemma4_sliding_h2816", seed=2)
+    cfg, w = synthetic.layer_inputs(name, seed=2)
     L = DeviceLayer(cfg, w, torch)
     taps, bufs = L.make_taps()
     x = dev(w["x"])
@@ -220,10 +223,10 @@ def test_layer_positions_sliding(pos):
     kvd, tap = nkv * hd, host(bufs["qkv_post"])
     check_kv_row(kc_gpu[:, pos], tap[nq * hd:nq * hd + kvd], post[nq * hd:nq * hd + kvd], 1, f"k at pos {pos}")
     check_kv_row(vc_gpu[:, pos], tap[nq * hd + kvd:], post[nq * hd + kvd:], 1, f"v at pos {pos}")
-    start = max(0, pos - cfg["window"] + 1)
+    start = max(0, pos - cfg["window"] + 1) if cfg["window"] else 0
     att = oracle.attention(q, nq, nkv, hd, kc_gpu, vc_gpu, 1, cfg["max_ctx"] * hd, hd, start,
                            pos - start + 1, cfg["attn_scale"])
-    assert_close(host(bufs["attn"]), att, f"attention at pos {pos}")
+    assert_close(host(bufs["attn"]), att, f"{name}: attention at pos {pos}")
 
 
 def _check_moe_block(cfg, w, escale, tag):
