@@ -35,8 +35,11 @@ namespace lq {
 namespace {
 
 constexpr int kQkWaves = 8;
-constexpr int kQkNT = kQkWaves * 64;
 constexpr int kQkMaxCols = 16384;
+// Waves per workgroup: 8, or 4 for the SwiGLU + Q8_0 epilogue, whose grid is
+// one workgroup per 32-output block of h: two 4-wave workgroups fit a CU, so
+// the whole grid of the 8B-like gate_up (384 blocks) is one resident round.
+template <int EPI> constexpr int qk_waves() { return EPI == EPI_SWIGLU_Q8 ? 4 : kQkWaves; }
 
 // Arguments of the fused format matvec; prologue and epilogue kinds are the
 // Q8_0 matvec's (PRO_* and EPI_* of lq_internal.h).
@@ -157,36 +160,37 @@ __device__ __forceinline__ void qk_group_use(const QkArgs& a, int64_t grp, int l
 
 // Float prologue: quarter blocks (8 values) per thread, the four lanes of a
 // quad holding one 32-value block.  QPT quarter blocks per thread at most.
-template <int ST, int FMT> struct QkPro {
+template <int ST, int FMT, int NT> struct QkPro {
     static constexpr int MAXC = FMT == QK_Q4_0 ? ST * 2048 : ST * 4096;          // columns an ST covers
-    static constexpr int QPT = ((MAXC < kQkMaxCols ? MAXC : kQkMaxCols) / 8 + kQkNT - 1) / kQkNT;
+    static constexpr int QPT = ((MAXC < kQkMaxCols ? MAXC : kQkMaxCols) / 8 + NT - 1) / NT;
 };
 // VGPRs the weight double buffer takes: the norm weights are loaded with
 // the input (ahead of the first weights) only while both fit beside it in
 // the 256 VGPRs of two waves per SIMD.
-template <int FMT, int ST, int RPW, int PRO> struct QkOcc {
+template <int FMT, int ST, int RPW, int PRO, int NT> struct QkOcc {
     static constexpr int UNIT = FMT == QK_Q4_0 ? 5 : 15;
     static constexpr int BUF = 2 * RPW * ST * UNIT;
-    static constexpr int XREGS = PRO == PRO_Q8 ? 0 : 8 * QkPro<ST, FMT>::QPT;
+    static constexpr int XREGS = PRO == PRO_Q8 ? 0 : 8 * QkPro<ST, FMT, NT>::QPT;
     static constexpr bool EARLY_G = PRO == PRO_NORM && BUF + 2 * XREGS <= 160;
 };
 
 template <int FMT, int ST, int RPW, int PRO, int EPI>
-__global__ __launch_bounds__(kQkNT, 2) void k_qk_mv(QkArgs a) {
+__global__ __launch_bounds__(qk_waves<EPI>() * 64, 2) void k_qk_mv(QkArgs a) {
     static_assert(EPI != EPI_SWIGLU_Q8 || RPW == 2, "SwiGLU groups are (gate, up) row pairs");
+    constexpr int kQkW = qk_waves<EPI>(), kQkNT = kQkW * 64;
     __shared__ __attribute__((aligned(16))) int8_t xl[kQkMaxCols];
     __shared__ float xs[kQkMaxCols / 32];
-    __shared__ float red[kQkWaves];
+    __shared__ float red[kQkW];
     __shared__ float hs[EPI == EPI_SWIGLU_Q8 ? 32 : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int units = qk_units<FMT>(a.cols);
     // groups: grid-stride over row groups, or for the SwiGLU epilogue the
     // workgroup's 32 outputs, four per wave
     constexpr bool SW = EPI == EPI_SWIGLU_Q8;
-    constexpr int OPW = 32 / kQkWaves;
+    constexpr int OPW = 32 / kQkW;
     const int64_t ngroups = SW ? a.rows : (a.rows + RPW - 1) / RPW;
-    const int64_t gstride = SW ? 1 : (int64_t)gridDim.x * kQkWaves;
-    int64_t g = SW ? (int64_t)blockIdx.x * 32 + wave * OPW : (int64_t)blockIdx.x * kQkWaves + wave;
+    const int64_t gstride = SW ? 1 : (int64_t)gridDim.x * kQkW;
+    int64_t g = SW ? (int64_t)blockIdx.x * 32 + wave * OPW : (int64_t)blockIdx.x * kQkW + wave;
     const int64_t gend = SW ? (g + OPW < ngroups ? g + OPW : ngroups) : ngroups;
     const int n16 = a.cols >> 4, nb = a.cols >> 5;
     QkRows<FMT, ST, RPW> A, B;
@@ -219,8 +223,8 @@ __global__ __launch_bounds__(kQkNT, 2) void k_qk_mv(QkArgs a) {
         // f32 input (and the norm weights when the registers allow) first,
         // then the first weights; then RMSNorm (PRO_NORM) and the Q8_0 of the
         // input into LDS, the same rule as every quantizer here
-        constexpr int QPT = QkPro<ST, FMT>::QPT;
-        constexpr bool EARLY_G = QkOcc<FMT, ST, RPW, PRO>::EARLY_G;
+        constexpr int QPT = QkPro<ST, FMT, kQkNT>::QPT;
+        constexpr bool EARLY_G = QkOcc<FMT, ST, RPW, PRO, kQkNT>::EARLY_G;
         const int nqb = a.cols >> 3;
         float xf[QPT][8], gf[EARLY_G ? QPT : 1][8];
 #pragma unroll
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kQkNT, 2) void k_qk_mv(QkArgs a) {
             __syncthreads();
             ss = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kQkWaves; ++w) ss += red[w];
+            for (int w = 0; w < kQkW; ++w) ss += red[w];
             rinv = 1.0f / sqrtf(ss / (float)a.cols + a.eps);
         }
         const bool tap = a.tap_q != nullptr && blockIdx.x == 0;
@@ -334,6 +338,7 @@ __global__ __launch_bounds__(kQkNT, 2) void k_qk_mv(QkArgs a) {
 template <int FMT, int ST, int RPW, int PRO, int EPI>
 void launch_qk(const QkArgs& a, hipStream_t s, LaunchMarks* mk) {
     auto kern = k_qk_mv<FMT, ST, RPW, PRO, EPI>;
+    constexpr int kQkNT = qk_waves<EPI>() * 64;
     int64_t grid;
     if constexpr (EPI == EPI_SWIGLU_Q8) {
         grid = (a.rows + 31) / 32;                   // one workgroup per 32-output block of h
