@@ -71,6 +71,16 @@ def test_layer_ggml_formats_teacher_forced(name, formats):
     run_teacher_forced(name, formats=formats)
 
 
+@pytest.mark.parametrize("fmt", ["q6_k", "q4_0"])
+def test_layer_ggml_wide_rows(fmt, monkeypatch):
+    """Every projection in one GGML format on 6144-wide rows: two 64-unit
+    steps per Q6_K row (QKV, and gate_up through the SwiGLU + Q8_0 epilogue)
+    and three per Q4_0 row, which no workload shape reaches."""
+    cfg = dict(synthetic.WORKLOADS["qwen3_8b_like_h4096"], hidden=6144, ffn=2048, ctx=256)
+    monkeypatch.setitem(synthetic.WORKLOADS, "wide_h6144", cfg)
+    run_teacher_forced("wide_h6144", formats={"qkv": fmt, "o": fmt, "gu": fmt, "dn": fmt})
+
+
 def run_teacher_forced(name, act=0, cap=0.0, freqs=None, formats=None):
     torch = torch_mod()
     cfg, w = synthetic.layer_inputs(name, seed=0, formats=formats)
