@@ -13,11 +13,13 @@
 // expert, its (token, slot) rows (in the order the gather's LDS atomics hand
 // out places, which may vary between runs: each row is computed on its own
 // and written to its own slot, so the results do not depend on it); the
-// matvec then gives
-// each workgroup one expert and a block of rows, loads those weight rows
-// into VGPRs once, and applies them to every listed slot.  No float atomics
-// are used, so results are deterministic.
+// matvec then walks (expert, row block) items over one resident round of
+// workgroups, loads each item's weight rows into VGPRs once (the next
+// item's while the current one is computed), and applies them to every
+// listed slot.  No float atomics are used, so results are deterministic.
 #include <math.h>
+
+#include <atomic>
 
 #include "lq_device.h"
 #include "lq_internal.h"
@@ -267,76 +269,209 @@ __device__ __forceinline__ int dot16(int4 a, int4 b) {
 }
 
 // ---- index-driven matvec ------------------------------------------------------
-// blockIdx.x = active-expert index * rowblocks + row block.  Each wave holds
-// RPW weight rows (NCH 1 KB chunks each) in VGPRs and applies them to every
-// slot of its expert: same lane mapping and block-dot arithmetic as the
-// dense Q8_0 matvec.
-template <int NCH, int RPW>
-__global__ __launch_bounds__(256) void k_moe_matvec_id(const int8_t* __restrict__ wq,
-                                                       const uint16_t* __restrict__ wd, int rows,
-                                                       int cols, const int8_t* __restrict__ xq,
-                                                       const uint16_t* __restrict__ xd, int x_per_slot,
-                                                       int k, const int32_t* __restrict__ wsbase, int E,
-                                                       int rowblocks, float* __restrict__ y) {
-    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
-    const int ai = blockIdx.x / rowblocks, rb = blockIdx.x - ai * rowblocks;
-    if (ai >= *ws.n_active()) return;
-    const int e = ws.active()[ai];
-    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nb = cols >> 5;
-    const int r0 = (rb * 4 + wave) * RPW;
-    if (r0 >= rows) return;
-    const int8_t* we = wq + (int64_t)e * rows * cols;
-    const uint16_t* de = wd + (int64_t)e * rows * nb;
+// Items are (active expert ai, row block rb), item = ai * rowblocks + rb for
+// ai < n_active.  One resident round of workgroups walks them (workgroup b
+// takes items b, b + grid, ...).  Each wave holds RPW weight rows (NCH 1 KB
+// chunks each) of its item in VGPRs and applies them to every slot of the
+// item's expert, with the dense Q8_0 matvec's lane mapping and block-dot
+// arithmetic.  The rows of the workgroup's next item are requested before
+// the current item's slots are computed, so each wave keeps a weight stream
+// in flight while it computes; workgroups that each load one item and exit
+// all load, then all compute, and the memory system idles in between.
+//
+// Epilogues: ID_STORE writes y[slot, r]; ID_SWIGLU takes the weight's rows
+// as gate rows then up rows (rows = 2 * outputs), holds gate row o and up
+// row o side by side and writes h[slot, o] = silu(gate) * up (and, when
+// given, the gate and up values to y1[slot, :]).
+enum { ID_STORE = 0, ID_SWIGLU = 1 };
 
-    int4 wv[RPW][NCH];
-    float wsc[RPW][NCH];
+struct IdArgs {
+    const int8_t* wq;
+    const uint16_t* wd;
+    int rows, cols;              // weight rows per expert (ID_SWIGLU: 2 * outputs), columns
+    const int8_t* xq;            // Q8_0 activation rows [*, cols] and scales [*, cols/32]
+    const uint16_t* xd;
+    int x_per_slot, k;           // activation row of slot s: s (x_per_slot) or s / k
+    const int32_t* ws;
+    int E, rowblocks;
+    float* y;                    // ID_STORE: [slots, rows]; ID_SWIGLU: [slots, rows / 2]
+    float* y1;                   // ID_SWIGLU: optional [slots, rows]
+};
+
+// Rows and activations are loaded without branches: rows past the expert
+// read its last row (never stored) and chunks past cols read the row's last
+// 16 bytes, whose products are zeroed through the activation.  The f16
+// scales stay raw until they are used: converting them where they are
+// loaded would wait for each load in turn.
+template <int NCH, int RPW>
+struct IdRows {
+    int4 w[RPW][NCH];
+    uint32_t s[RPW][NCH];      // f16 bits
+};
+
+// weight row of the wave's row i (-1: past the weight)
+template <int RPW, int EPI>
+__device__ __forceinline__ int id_row(const IdArgs& a, int u0, int i) {
+    if constexpr (EPI == ID_SWIGLU) {
+        const int o = u0 + i / 2, out = a.rows >> 1;
+        return o < out ? o + (i & 1) * out : -1;
+    } else {
+        return u0 + i < a.rows ? u0 + i : -1;
+    }
+}
+
+template <int NCH, int RPW, int EPI>
+__device__ __forceinline__ void id_load_rows(const IdArgs& a, int e, int u0, int lane, IdRows<NCH, RPW>& R) {
+    const int cols = a.cols, nb = cols >> 5;
+    const int8_t* we = a.wq + (int64_t)e * a.rows * cols;
+    const uint16_t* de = a.wd + (int64_t)e * a.rows * nb;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const int r = r0 + i;
+        const int rr = id_row<RPW, EPI>(a, u0, i);
+        const int r = rr >= 0 ? rr : a.rows - 1;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int off = c * 1024 + lane * 16;
-            if (r < rows && off < cols) {
-                wv[i][c] = load_stream16(we + (int64_t)r * cols + off);
-                wsc[i][c] = f16_to_f32(de[(int64_t)r * nb + (off >> 5)]);
-            } else {
-                wv[i][c] = make_int4(0, 0, 0, 0);
-                wsc[i][c] = 0.0f;
-            }
+            const int off = c * 1024 + lane * 16 < cols ? c * 1024 + lane * 16 : cols - 16;
+            R.w[i][c] = load_stream16(we + (int64_t)r * cols + off);
+            R.s[i][c] = de[(int64_t)r * nb + (off >> 5)];
         }
     }
-    for (int si = s0; si < s1; ++si) {
-        const int slot = ws.slots()[si];
-        const int64_t xrow = x_per_slot ? slot : slot / k;
-        int4 xv[NCH];
-        float xs[NCH];
+}
+
+template <int NCH>
+struct IdAct {
+    int4 v[NCH];
+    uint32_t s[NCH];           // f16 bits
+};
+
+template <int NCH>
+__device__ __forceinline__ void id_load_act(const IdArgs& a, int64_t xrow, int lane, IdAct<NCH>& X) {
+    const int cols = a.cols;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int off = c * 1024 + lane * 16 < cols ? c * 1024 + lane * 16 : cols - 16;
+        X.v[c] = *reinterpret_cast<const int4*>(a.xq + xrow * cols + off);
+        X.s[c] = a.xd[xrow * (cols >> 5) + (off >> 5)];
+    }
+}
+
+// One slot's codes and f32 scales, zero past cols.
+template <int NCH>
+__device__ __forceinline__ void id_cook(const IdArgs& a, const IdAct<NCH>& X, int lane, int4 (&xv)[NCH],
+                                        float (&xs)[NCH]) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const bool in = c * 1024 + lane * 16 < a.cols;
+        xv[c] = in ? X.v[c] : make_int4(0, 0, 0, 0);
+        xs[c] = in ? f16_to_f32((uint16_t)X.s[c]) : 0.0f;
+    }
+}
+
+// Products of the rows in R with one slot's activation, then the epilogue.
+template <int NCH, int RPW, int EPI>
+__device__ __forceinline__ void id_dots(const IdArgs& a, const IdRows<NCH, RPW>& R, const int4 (&xv)[NCH],
+                                        const float (&xs)[NCH], int u0, int slot, int lane) {
+    float acc[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float t = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int off = c * 1024 + lane * 16;
-            if (off < cols) {
-                xv[c] = *reinterpret_cast<const int4*>(xq + xrow * cols + off);
-                xs[c] = f16_to_f32(xd[xrow * nb + (off >> 5)]);
-            } else {
-                xv[c] = make_int4(0, 0, 0, 0);
-                xs[c] = 0.0f;
+            const int p = dot16(R.w[i][c], xv[c]);
+            const int blk = p + dpp_i<kQuadXor1>(p);
+            const float v = (float)blk * (f16_to_f32((uint16_t)R.s[i][c]) * xs[c]);
+            t += (lane & 1) ? 0.0f : v;
+        }
+        acc[i] = wave_sum(t);
+    }
+    if (lane != 0) return;
+    if constexpr (EPI == ID_SWIGLU) {
+        const int out = a.rows >> 1;
+#pragma unroll
+        for (int j = 0; j < RPW / 2; ++j) {
+            const int o = u0 + j;
+            if (o < out) {
+                const float gt = acc[2 * j], up = acc[2 * j + 1];
+                a.y[(int64_t)slot * out + o] = (gt / (1.0f + expf(-gt))) * up;
+                if (a.y1) {
+                    a.y1[(int64_t)slot * a.rows + o] = gt;
+                    a.y1[(int64_t)slot * a.rows + out + o] = up;
+                }
             }
         }
+    } else {
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int p = dot16(wv[i][c], xv[c]);
-                const int blk = p + dpp_i<kQuadXor1>(p);
-                const float t = (float)blk * (wsc[i][c] * xs[c]);
-                acc += (lane & 1) ? 0.0f : t;
-            }
-            acc = wave_sum(acc);
-            const int r = r0 + i;
-            if (lane == 0 && r < rows) y[(int64_t)slot * rows + r] = acc;
+        for (int i = 0; i < RPW; ++i)
+            if (u0 + i < a.rows) a.y[(int64_t)slot * a.rows + u0 + i] = acc[i];
+    }
+}
+
+template <int NCH, int RPW, int EPI>
+__global__ __launch_bounds__(256) void k_moe_matvec_id(IdArgs a) {
+    const MoeWs ws{const_cast<int32_t*>(a.ws), a.E};
+    const int rowblocks = a.rowblocks;
+    const int n_items = *ws.n_active() * rowblocks;
+    int it = blockIdx.x;
+    if (it >= n_items) return;
+    const int G = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int UPW = EPI == ID_SWIGLU ? RPW / 2 : RPW;       // outputs per wave
+    static_assert(EPI != ID_SWIGLU || RPW % 2 == 0, "gate/up pairs");
+    auto expert_of = [&](int item) { return ws.active()[item / rowblocks]; };
+    auto u0_of = [&](int item) { return ((item - (item / rowblocks) * rowblocks) * 4 + wave) * UPW; };
+    auto xrow_of = [&](int slot) -> int64_t { return a.x_per_slot ? slot : slot / a.k; };
+    // the activations of an item's first two slots (the first again when it
+    // has one); they are requested before the next item's rows, so waiting
+    // for them leaves those rows in flight (loads complete in issue order)
+    auto load_first = [&](int item, IdAct<NCH>& X0, IdAct<NCH>& X1) {
+        const int ai = item / rowblocks;
+        const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+        id_load_act<NCH>(a, xrow_of(ws.slots()[s0]), lane, X0);
+        id_load_act<NCH>(a, xrow_of(ws.slots()[s0 + 1 < s1 ? s0 + 1 : s0]), lane, X1);
+    };
+    auto one = [&](const IdRows<NCH, RPW>& R, const IdAct<NCH>& X, int item, int slot) {
+        int4 xv[NCH];
+        float xs[NCH];
+        id_cook<NCH>(a, X, lane, xv, xs);
+        id_dots<NCH, RPW, EPI>(a, R, xv, xs, u0_of(item), slot, lane);
+    };
+    auto consume = [&](int item, const IdRows<NCH, RPW>& R, const IdAct<NCH>& X0, const IdAct<NCH>& X1) {
+        const int ai = item / rowblocks;
+        const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+        one(R, X0, item, ws.slots()[s0]);
+        if (s0 + 1 < s1) one(R, X1, item, ws.slots()[s0 + 1]);
+        for (int si = s0 + 2; si < s1; ++si) {
+            const int slot = ws.slots()[si];
+            IdAct<NCH> X;
+            id_load_act<NCH>(a, xrow_of(slot), lane, X);
+            one(R, X, item, slot);
         }
+    };
+    // items it, it + G, ...: the next item's rows are requested before the
+    // current one is consumed, in straight-line code with the last step
+    // peeled (as in the dense matvec), so each wait covers exactly the loads
+    // it needs
+    IdRows<NCH, RPW> A, B;
+    IdAct<NCH> X0, X1;
+    id_load_rows<NCH, RPW, EPI>(a, expert_of(it), u0_of(it), lane, A);
+    for (;;) {
+        const int i1 = it + G;
+        load_first(it, X0, X1);
+        if (i1 >= n_items) {
+            consume(it, A, X0, X1);
+            break;
+        }
+        id_load_rows<NCH, RPW, EPI>(a, expert_of(i1), u0_of(i1), lane, B);
+        consume(it, A, X0, X1);
+        const int i2 = i1 + G;
+        load_first(i1, X0, X1);
+        if (i2 >= n_items) {
+            consume(i1, B, X0, X1);
+            break;
+        }
+        id_load_rows<NCH, RPW, EPI>(a, expert_of(i2), u0_of(i2), lane, A);
+        consume(i1, B, X0, X1);
+        it = i2;
     }
 }
 
@@ -399,102 +534,6 @@ __global__ __launch_bounds__(256) void k_moe_qk_matvec_id(QkMat m, int rows, int
     }
 }
 
-// ---- gate/up id-matvec with SwiGLU and the Q8_0 of h in the epilogue --------
-// blockIdx.x = active-expert index * (ffn/32) + h block.  A workgroup of 16
-// waves owns one 32-value block of h for its expert: wave w holds the gate
-// rows j and up rows j + ffn of its 2 outputs j (NCH 1 KB chunks each) in
-// VGPRs and, for every listed slot, computes h_j = silu(gate_j) * up_j; the
-// block is then quantized by wave 0 with the same rule as every other
-// quantizer here.  y1 (gate/up values, [slots, 2*ffn]) is written when given.
-constexpr int kGuWaves = 16, kGuPairs = 2;
-template <int NCH>
-__global__ __launch_bounds__(kGuWaves * 64) void k_moe_gu_swiglu_q8(const int8_t* __restrict__ wq,
-                                                                   const uint16_t* __restrict__ wd, int ffn,
-                                                                   int cols, const int8_t* __restrict__ xq,
-                                                                   const uint16_t* __restrict__ xd, int k,
-                                                                   const int32_t* __restrict__ wsbase, int E,
-                                                                   float* __restrict__ y1,
-                                                                   int8_t* __restrict__ hq,
-                                                                   uint16_t* __restrict__ hdq) {
-    constexpr int RPW = 2 * kGuPairs;
-    __shared__ float hs[32];
-    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
-    const int nblk = ffn >> 5;
-    const int ai = blockIdx.x / nblk, hb = blockIdx.x - ai * nblk;
-    if (ai >= *ws.n_active()) return;                 // uniform over the workgroup
-    const int e = ws.active()[ai];
-    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nb = cols >> 5;
-    const int rows = 2 * ffn;
-    const int8_t* we = wq + (int64_t)e * rows * cols;
-    const uint16_t* de = wd + (int64_t)e * rows * nb;
-    const int j0 = hb * 32 + wave * kGuPairs;         // this wave's outputs j0 .. j0+kGuPairs-1
-
-    int4 wv[RPW][NCH];
-    float wsc[RPW][NCH];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int r = j0 + (i >> 1) + (i & 1) * ffn;  // even i: gate row, odd i: up row
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            int off = c * 1024 + lane * 16;
-            if (off >= cols) off = cols - 16;         // a valid slice; its activation slice is zero
-            wv[i][c] = load_stream16(we + (int64_t)r * cols + off);
-            wsc[i][c] = f16_to_f32(de[(int64_t)r * nb + (off >> 5)]);
-        }
-    }
-    for (int si = s0; si < s1; ++si) {
-        const int slot = ws.slots()[si];
-        const int64_t xrow = slot / k;
-        int4 xv[NCH];
-        float xs[NCH];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int off = c * 1024 + lane * 16;
-            const int oc = off < cols ? off : cols - 16;
-            xv[c] = *reinterpret_cast<const int4*>(xq + xrow * cols + oc);
-            xs[c] = off < cols ? f16_to_f32(xd[xrow * nb + (oc >> 5)]) : 0.0f;
-            if (off >= cols) xv[c] = make_int4(0, 0, 0, 0);
-        }
-        float acc[RPW];
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            float t = 0.0f;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                const int p = dot16(wv[i][c], xv[c]);
-                const int blk = p + dpp_i<kQuadXor1>(p);
-                const float v = (float)blk * (wsc[i][c] * xs[c]);
-                t += (lane & 1) ? 0.0f : v;
-            }
-            acc[i] = wave_sum(t);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int jj = 0; jj < kGuPairs; ++jj) {
-                const float gt = acc[2 * jj], up = acc[2 * jj + 1];
-                hs[wave * kGuPairs + jj] = (gt / (1.0f + expf(-gt))) * up;
-                if (y1) {
-                    y1[(int64_t)slot * rows + j0 + jj] = gt;
-                    y1[(int64_t)slot * rows + ffn + j0 + jj] = up;
-                }
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const float v = lane < 32 ? hs[lane] : 0.0f;
-            const float amax = group_max<32>(fabsf(v));
-            const float d = amax / 127.0f;
-            const float inv = (d != 0.0f) ? 1.0f / d : 0.0f;
-            const float r = fminf(fmaxf(roundf(v * inv), -127.0f), 127.0f);
-            if (lane < 32) hq[(int64_t)slot * ffn + hb * 32 + lane] = (int8_t)(int32_t)r;
-            if (lane == 0) hdq[(int64_t)slot * nblk + hb] = f32_to_f16(d);
-        }
-        __syncthreads();                             // hs is rewritten by the next slot
-    }
-}
-
 // out[t] = sum_s w[t,s] * scale[ids[t,s]] * y[t,s] in slot order; without a
 // scale table (escale NULL) every scale is 1, and ids past the table (the
 // skipped invalid ids, whose y rows are zero) also count 1.
@@ -535,59 +574,53 @@ static lq_status launch_gather(const int32_t* ids, int64_t nslots, int64_t E, vo
     return check_launch("moe_gather");
 }
 
-template <int NCH>
-static void launch_id_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int rows, int cols,
-                          const int8_t* xq, const uint16_t* xd, int x_per_slot, int k,
-                          const int32_t* ws, int E, float* y) {
-    // rows per wave: short rows (<= 2 KB) 8, longer ones 2.  Measured on the
-    // 128-expert block (704-byte down rows): 2 rows per wave 133-139 us, 4
-    // rows 121-126, 8 rows 118-123, 16 rows 127-131 per block
-    constexpr int RPW = NCH <= 2 ? 8 : 2;
-    const int rowblocks = (rows + 4 * RPW - 1) / (4 * RPW);
-    hipLaunchKernelGGL((k_moe_matvec_id<NCH, RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, wq, wd,
-                       rows, cols, xq, xd, x_per_slot, k, ws, E, rowblocks, y);
+// One resident round of workgroups (queried once per instance), at most one
+// item each.
+template <int NCH, int RPW, int EPI>
+static void launch_id_t(IdArgs a, int outs, hipStream_t s) {
+    constexpr int UPW = EPI == ID_SWIGLU ? RPW / 2 : RPW;
+    a.rowblocks = (outs + 4 * UPW - 1) / (4 * UPW);
+    auto kern = k_moe_matvec_id<NCH, RPW, EPI>;
+    static std::atomic<int> resident_cache{-1};
+    int resident = resident_cache.load(std::memory_order_relaxed);
+    if (resident < 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+        resident = n * kNumCUs;
+        resident_cache.store(resident, std::memory_order_relaxed);
+    }
+    const int64_t items = (int64_t)a.E * a.rowblocks;
+    const unsigned grid = (unsigned)(items < resident ? items : resident);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+}
+
+// Rows per wave: short rows (<= 2 KB) 8, longer ones 2 (for SwiGLU, 4 and 1
+// gate/up pairs).  Measured on the 128-expert block with one-shot
+// workgroups (704-byte down rows): 2 rows per wave 133-139 us, 4 rows
+// 121-126, 8 rows 118-123, 16 rows 127-131 per block.
+template <int EPI>
+static lq_status launch_id(const IdArgs& a, int outs, hipStream_t s, const char* what) {
+    const int nch = (a.cols + 1023) / 1024;
+#define LQ_ID_CASE(N)                                              \
+    case N:                                                        \
+        launch_id_t<N, (N <= 2 ? 8 : 2), EPI>(a, outs, s);         \
+        break;
+    switch (nch) {
+        LQ_ID_CASE(1) LQ_ID_CASE(2) LQ_ID_CASE(3) LQ_ID_CASE(4)
+        LQ_ID_CASE(5) LQ_ID_CASE(6) LQ_ID_CASE(7) LQ_ID_CASE(8)
+        default: return fail(LQ_ERR_UNSUPPORTED, "%s: cols > 8192", what);
+    }
+#undef LQ_ID_CASE
+    return check_launch(what);
 }
 
 static lq_status launch_id_gathered(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
                                     int64_t E, const int8_t* xq, const uint16_t* xd, int32_t x_per_slot,
                                     int64_t k, const void* ws, float* y, hipStream_t s) {
-    const int nch = (int)((cols + 1023) / 1024);
-    const int32_t* w32 = static_cast<const int32_t*>(ws);
-#define LQ_ID_CASE(N)                                                                                      \
-    case N:                                                                                                \
-        launch_id_nch<N>(s, wq, wd, (int)rows, (int)cols, xq, xd, x_per_slot, (int)k, w32, (int)E, y); \
-        break;
-    switch (nch) {
-        LQ_ID_CASE(1) LQ_ID_CASE(2) LQ_ID_CASE(3) LQ_ID_CASE(4)
-        LQ_ID_CASE(5) LQ_ID_CASE(6) LQ_ID_CASE(7) LQ_ID_CASE(8)
-        default: return fail(LQ_ERR_UNSUPPORTED, "moe matvec: cols > 8192");
-    }
-#undef LQ_ID_CASE
-    return check_launch("moe_matvec_id");
-}
-
-template <int NCH>
-static void launch_gu_nch(hipStream_t s, const int8_t* wq, const uint16_t* wd, int ffn, int cols, const int8_t* xq,
-                          const uint16_t* xd, int k, const int32_t* ws, int E, float* y1, int8_t* hq, uint16_t* hd) {
-    hipLaunchKernelGGL((k_moe_gu_swiglu_q8<NCH>), dim3((unsigned)(E * (ffn / 32))), dim3(kGuWaves * 64), 0, s, wq,
-                       wd, ffn, cols, xq, xd, k, ws, E, y1, hq, hd);
-}
-
-static lq_status launch_gu_swiglu_q8(const int8_t* wq, const uint16_t* wd, int64_t ffn, int64_t cols, int64_t E,
-                                     const int8_t* xq, const uint16_t* xd, int64_t k, const void* ws, float* y1,
-                                     int8_t* hq, uint16_t* hd, hipStream_t s) {
-    const int nch = (int)((cols + 1023) / 1024);
-    const int32_t* w32 = static_cast<const int32_t*>(ws);
-#define LQ_GU_CASE(N)                                                                                     \
-    case N:                                                                                               \
-        launch_gu_nch<N>(s, wq, wd, (int)ffn, (int)cols, xq, xd, (int)k, w32, (int)E, y1, hq, hd); \
-        break;
-    switch (nch) {
-        LQ_GU_CASE(1) LQ_GU_CASE(2) LQ_GU_CASE(3) LQ_GU_CASE(4)
-        default: return fail(LQ_ERR_UNSUPPORTED, "moe gate/up: hidden > 4096 in the fused SwiGLU path");
-    }
-#undef LQ_GU_CASE
-    return check_launch("moe_gate_up_swiglu_q8");
+    IdArgs a{};
+    a.wq = wq; a.wd = wd; a.rows = (int)rows; a.cols = (int)cols; a.xq = xq; a.xd = xd;
+    a.x_per_slot = x_per_slot; a.k = (int)k; a.ws = static_cast<const int32_t*>(ws); a.E = (int)E; a.y = y;
+    return launch_id<ID_STORE>(a, (int)rows, s, "moe_matvec_id");
 }
 
 lq_status launch_moe_matvec_id(const int8_t* wq, const uint16_t* wd, int64_t rows, int64_t cols,
@@ -777,6 +810,7 @@ extern "C" lq_status lq_moe_weighted_sum(const float* y, const float* w, int64_t
 namespace {
 struct MoeBuffers {
     int32_t* ids; float* w; int8_t* xq; uint16_t* xd; float* y1; int8_t* hq; uint16_t* hd; float* y2;
+    float* h;     // Q8_0 block: act(gate) * up in f32, [T*k, ffn]
     void* gather;
     size_t total;
 };
@@ -799,6 +833,7 @@ MoeBuffers moe_layout(const lq_moe_desc* m, int64_t T, char* base, const lq_moe_
     b.hq = reinterpret_cast<int8_t*>(take(S * I));
     b.hd = reinterpret_cast<uint16_t*>(take(S * (I / 32) * 2));
     b.y2 = reinterpret_cast<float*>(take(S * H * 4));
+    b.h = reinterpret_cast<float*>(take(S * I * 4));
     b.total = off;
     if (taps) {
         if (taps->ids) b.ids = taps->ids;
@@ -850,16 +885,14 @@ extern "C" lq_status lq_moe_block(const lq_moe_desc* m, const float* x, const fl
     hipLaunchKernelGGL(k_moe_prep, dim3((unsigned)prep_grid), dim3(kGatherThreads), 0, s, logits, x, (int)T, (int)E, (int)k, (int)H,
                        b.ids, b.w, static_cast<int32_t*>(b.gather), b.xq, b.xd, b.y1, 2 * I, b.y2, H);
     if ((st = check_launch("moe_prep")) != LQ_OK) return st;
-    if (H <= 4096) {
-        if ((st = launch_gu_swiglu_q8(m->w_gate_up.qs, m->w_gate_up.d, I, H, E, b.xq, b.xd, k, b.gather,
-                                      taps ? taps->y1 : nullptr, b.hq, b.hd, s)) != LQ_OK)
-            return st;
-    } else {
-        if ((st = launch_id_gathered(m->w_gate_up.qs, m->w_gate_up.d, 2 * I, H, E, b.xq, b.xd, 0, k, b.gather,
-                                     b.y1, s)) != LQ_OK)
-            return st;
-        if ((st = launch_swiglu_q8(b.y1, S, I, b.hq, b.hd, s)) != LQ_OK) return st;
-    }
+    // gate/up with SwiGLU in the epilogue (h in f32), the Q8_0 of h, then
+    // the down projection
+    IdArgs g{};
+    g.wq = m->w_gate_up.qs; g.wd = m->w_gate_up.d; g.rows = (int)(2 * I); g.cols = (int)H;
+    g.xq = b.xq; g.xd = b.xd; g.x_per_slot = 0; g.k = (int)k;
+    g.ws = static_cast<const int32_t*>(b.gather); g.E = (int)E; g.y = b.h; g.y1 = taps ? taps->y1 : nullptr;
+    if ((st = launch_id<ID_SWIGLU>(g, (int)I, s, "moe gate/up")) != LQ_OK) return st;
+    if ((st = launch_q8_quantize(b.h, S * (I / 32), b.hq, b.hd, s)) != LQ_OK) return st;
     if ((st = launch_id_gathered(m->w_down.qs, m->w_down.d, H, I, E, b.hq, b.hd, 1, k, b.gather, b.y2, s)) != LQ_OK)
         return st;
     return launch_moe_weighted_sum(b.y2, b.w, T, k, H, b.ids, m->expert_scale, m->n_experts, out, s);
