@@ -594,16 +594,18 @@ static void launch_id_t(IdArgs a, int outs, hipStream_t s) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
 }
 
-// Rows per wave: short rows (<= 2 KB) 8, longer ones 2 (for SwiGLU, 4 and 1
-// gate/up pairs).  Measured on the 128-expert block with one-shot
-// workgroups (704-byte down rows): 2 rows per wave 133-139 us, 4 rows
-// 121-126, 8 rows 118-123, 16 rows 127-131 per block.
+// Rows per wave (for SwiGLU, half as many gate/up pairs): rows of at most 2
+// KB 8, of at most 4 KB 4, longer ones 2.  Measured on the 128-expert block
+// (704-byte down rows, 2816-byte gate/up rows): down with 4 / 8 / 16 rows
+// 118-120 / 116-121 / 125-133 us per block; gate/up with 2 / 4 / 6 / 8 rows
+// 118-121 / 110-114 / 115-118 / 120-127 us (4 rows take 238 VGPRs, two
+// waves per SIMD, and still stream faster than 2 rows at three).
 template <int EPI>
 static lq_status launch_id(const IdArgs& a, int outs, hipStream_t s, const char* what) {
     const int nch = (a.cols + 1023) / 1024;
 #define LQ_ID_CASE(N)                                              \
     case N:                                                        \
-        launch_id_t<N, (N <= 2 ? 8 : 2), EPI>(a, outs, s);         \
+        launch_id_t<N, (N <= 2 ? 8 : (N <= 4 ? 4 : 2)), EPI>(a, outs, s); \
         break;
     switch (nch) {
         LQ_ID_CASE(1) LQ_ID_CASE(2) LQ_ID_CASE(3) LQ_ID_CASE(4)
