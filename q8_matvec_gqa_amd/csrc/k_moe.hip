@@ -76,6 +76,10 @@ __device__ __forceinline__ void route_token_p(const float* __restrict__ lt, int 
 #pragma unroll
     for (int i = 0; i < PER; ++i) z += (lane + 64 * i < E) ? expf(v[i] - mx) : 0.0f;
     z = wave_sum(z);
+    // pick s lands in lane s; the weights are formed after the k picks, one
+    // per lane (k <= 32)
+    float pv = 0.0f;
+    int pid = 0;
     for (int s = 0; s < k; ++s) {
         // lane-local best (largest value, then lowest id)
         float bv = -INFINITY;
@@ -89,19 +93,27 @@ __device__ __forceinline__ void route_token_p(const float* __restrict__ lt, int 
             }
         }
         // wave argmax with the same ordering: the largest value, then the
-        // lowest id among the lanes holding it
+        // lowest id among the lanes holding it (read from the one lane that
+        // holds it unless several do)
         const float m = wave_max(bv);
-        bi = wave_min_i(bv == m ? bi : 0x7fffffff);
-        bv = m;
-        if (lane == 0) {
-            ids[s] = bi;
-            w[s] = expf(bv - mx) / z;
-            if (sids) sids[s] = bi;
+        const unsigned long long tied = __ballot(bv == m);
+        if (__popcll(tied) == 1)
+            bi = __builtin_amdgcn_readlane(bi, __ffsll((long long)tied) - 1);
+        else
+            bi = wave_min_i(bv == m ? bi : 0x7fffffff);
+        if (lane == s) {
+            pv = m;
+            pid = bi;
         }
         // remove the chosen expert, below every real value (NaN never wins)
 #pragma unroll
         for (int i = 0; i < PER; ++i)
             if (lane + 64 * i == bi) v[i] = __int_as_float(0xff800001u);
+    }
+    if (lane < k) {
+        ids[lane] = pid;
+        w[lane] = expf(pv - mx) / z;
+        if (sids) sids[lane] = pid;
     }
 }
 
