@@ -546,6 +546,52 @@ __global__ __launch_bounds__(256) void k_moe_qk_matvec_id(QkMat m, int rows, int
     }
 }
 
+// Q4_0 rows of at most 32 blocks (1024 values, the MoE down projection's
+// short rows): lane l holds block l & 31 of row 2p + (l >> 5) of its pair p,
+// so each load instruction carries two rows and a row's sum is a half-wave
+// sum; the per-row unit form above leaves two thirds of the lanes idle on
+// 704-value rows.  Otherwise the same decomposition and arithmetic.
+template <int RPW>
+__global__ __launch_bounds__(256) void k_moe_q4_id_half(QkMat m, int rows, int cols, const int8_t* __restrict__ xq,
+                                                        const uint16_t* __restrict__ xd, int x_per_slot, int k,
+                                                        const int32_t* __restrict__ wsbase, int E, int rowblocks,
+                                                        float* __restrict__ y) {
+    constexpr int NP = RPW / 2;
+    static_assert(RPW % 2 == 0, "row pairs");
+    const MoeWs ws{const_cast<int32_t*>(wsbase), E};
+    const int ai = blockIdx.x / rowblocks, rb = blockIdx.x - ai * rowblocks;
+    if (ai >= *ws.n_active()) return;
+    const int e = ws.active()[ai];
+    const int s0 = ws.offsets()[ai], s1 = ws.offsets()[ai + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, u = lane & 31;
+    const int units = cols >> 5;
+    const bool uin = u < units;
+    const int r0 = (rb * 4 + wave) * RPW;
+    if (r0 >= rows) return;
+    const int64_t er = (int64_t)e * rows;
+    QkUnit<QK_Q4_0> U[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int r = r0 + 2 * p + half;
+        const bool live = r < rows && uin;
+        qk_load_unit(m, cols, er + (live ? r : 0), live ? u : 0, U[p]);
+    }
+    for (int si = s0; si < s1; ++si) {
+        const int slot = ws.slots()[si];
+        const int64_t xrow = x_per_slot ? slot : slot / k;
+        QkAct<QK_Q4_0> A;
+        qk_load_act(xq + xrow * cols, xd + xrow * (cols >> 5), uin ? u : 0, A);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            float acc = uin ? qk_unit_dot_a(U[p], u, A) : 0.0f;
+            acc = group_sum<32>(acc);
+            const int r = r0 + 2 * p + half;
+            if (u == 0 && r < rows) y[(int64_t)slot * rows + r] = acc;
+        }
+    }
+}
+
 // out[t] = sum_s w[t,s] * scale[ids[t,s]] * y[t,s] in slot order; without a
 // scale table (escale NULL) every scale is 1, and ids past the table (the
 // skipped invalid ids, whose y rows are zero) also count 1.
@@ -664,6 +710,14 @@ static lq_status launch_qk_id_gathered(const QkMat& m, int64_t rows, int64_t col
                                        const uint16_t* xd, int32_t x_per_slot, int64_t k, const void* ws, float* y,
                                        hipStream_t s) {
     const int32_t* w32 = static_cast<const int32_t*>(ws);
+    if (FMT == QK_Q4_0 && cols <= 1024) {
+        // two rows per load instruction: 8 rows per wave
+        constexpr int RPW = 8;
+        const int rowblocks = (int)((rows + 4 * RPW - 1) / (4 * RPW));
+        hipLaunchKernelGGL((k_moe_q4_id_half<RPW>), dim3((unsigned)(E * rowblocks)), dim3(256), 0, s, m, (int)rows,
+                           (int)cols, xq, xd, x_per_slot, (int)k, w32, (int)E, rowblocks, y);
+        return check_launch("moe_q4_id_half");
+    }
     switch ((qk_units<FMT>((int)cols) + 63) / 64) {
         case 1: launch_qk_id_st<FMT, 1, 4>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;
         case 2: launch_qk_id_st<FMT, 2, 2>(s, m, (int)rows, (int)cols, (int)E, xq, xd, x_per_slot, (int)k, w32, y); break;

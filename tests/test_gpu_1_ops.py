@@ -549,6 +549,9 @@ def test_ggml_format_extreme_codes(fmt):
     ("q6_k", 12, 200, 512, 5, 3),
     ("q6_k", 128, 1408, 2816, 16, 8),    # the MoE workload's gate/up on Q6_K experts
     ("q4_0", 128, 2816, 704, 16, 8),     # its down projection on Q4_0 experts
+    ("q4_0", 6, 33, 1024, 4, 2),         # two rows per load: every lane of a half-wave holds a block
+    ("q4_0", 5, 97, 32, 3, 2),           # one block per row, odd rows
+    ("q4_0", 3, 17, 1056, 3, 2),         # 33 blocks: the one-row-per-load form again
     ("q4_0", 4, 64, 8192, 3, 2),         # widest rows (4 steps per lane)
     ("q6_k", 4, 33, 8192, 3, 2),         # Q6_K widest (2 steps), ragged row blocks
 ])
