@@ -380,41 +380,59 @@ __device__ __forceinline__ void id_cook(const IdArgs& a, const IdAct<NCH>& X, in
 }
 
 // Products of the rows in R with one slot's activation, then the epilogue.
+// With 4 to 8 rows the row sums come from one reduce-scatter over the wave
+// (row i's sum in lanes 8i..8i+7) instead of one full wave sum per row, and
+// each lane 16j finishes gate/up pair j (its up row's sum is in lane 16j+8).
 template <int NCH, int RPW, int EPI>
 __device__ __forceinline__ void id_dots(const IdArgs& a, const IdRows<NCH, RPW>& R, const int4 (&xv)[NCH],
                                         const float (&xs)[NCH], int u0, int slot, int lane) {
-    float acc[RPW];
+    float t[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        float t = 0.0f;
+        t[i] = 0.0f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int p = dot16(R.w[i][c], xv[c]);
             const int blk = p + dpp_i<kQuadXor1>(p);
             const float v = (float)blk * (f16_to_f32((uint16_t)R.s[i][c]) * xs[c]);
-            t += (lane & 1) ? 0.0f : v;
+            t[i] += (lane & 1) ? 0.0f : v;
         }
-        acc[i] = wave_sum(t);
     }
-    if (lane != 0) return;
-    if constexpr (EPI == ID_SWIGLU) {
-        const int out = a.rows >> 1;
+    const int out = EPI == ID_SWIGLU ? a.rows >> 1 : a.rows;
+    auto swiglu_store = [&](int o, float gt, float up) {
+        a.y[(int64_t)slot * out + o] = (gt / (1.0f + expf(-gt))) * up;
+        if (a.y1) {
+            a.y1[(int64_t)slot * a.rows + o] = gt;
+            a.y1[(int64_t)slot * a.rows + out + o] = up;
+        }
+    };
+    if constexpr (RPW >= 4 && RPW <= 8) {
+        float v8[8];
 #pragma unroll
-        for (int j = 0; j < RPW / 2; ++j) {
-            const int o = u0 + j;
-            if (o < out) {
-                const float gt = acc[2 * j], up = acc[2 * j + 1];
-                a.y[(int64_t)slot * out + o] = (gt / (1.0f + expf(-gt))) * up;
-                if (a.y1) {
-                    a.y1[(int64_t)slot * a.rows + o] = gt;
-                    a.y1[(int64_t)slot * a.rows + out + o] = up;
-                }
-            }
+        for (int h = 0; h < 8; ++h) v8[h] = h < RPW ? t[h] : 0.0f;
+        const float srow = wave_sum8_scatter(v8);
+        if constexpr (EPI == ID_SWIGLU) {
+            const float up = dpp<kRowRor8>(srow);
+            const int j = lane >> 4, o = u0 + j;
+            if ((lane & 15) == 0 && j < RPW / 2 && o < out) swiglu_store(o, srow, up);
+        } else {
+            const int h = lane >> 3;
+            if ((lane & 7) == 0 && h < RPW && u0 + h < out) a.y[(int64_t)slot * out + u0 + h] = srow;
         }
     } else {
+        float acc[RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i)
-            if (u0 + i < a.rows) a.y[(int64_t)slot * a.rows + u0 + i] = acc[i];
+        for (int i = 0; i < RPW; ++i) acc[i] = wave_sum(t[i]);
+        if (lane != 0) return;
+        if constexpr (EPI == ID_SWIGLU) {
+#pragma unroll
+            for (int j = 0; j < RPW / 2; ++j)
+                if (u0 + j < out) swiglu_store(u0 + j, acc[2 * j], acc[2 * j + 1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i)
+                if (u0 + i < out) a.y[(int64_t)slot * out + u0 + i] = acc[i];
+        }
     }
 }
 
