@@ -842,6 +842,7 @@ namespace {
 
 struct Plan {
     int nsplit, tiles_per_split;
+    int cap;     // splits before whole tiles per wave are rounded: no shorter length plans more
 };
 
 constexpr int kMaxSplits = kMaxSplitsC;
@@ -918,11 +919,12 @@ Plan make_plan(int64_t n_kv, int64_t len, const Pick& pk) {
     if (ns > by_tiles) ns = by_tiles;
     if (ns > kMaxSplits) ns = kMaxSplits;
     if (ns < 1) ns = 1;
+    const int64_t cap = ns;
     int64_t tps = (tiles + ns - 1) / ns;
     tps = (tps + nw - 1) / nw * nw;                                     // whole tiles per wave
     ns = (tiles + tps - 1) / tps;
     if (ns < 1) ns = 1;
-    return Plan{(int)ns, (int)tps};
+    return Plan{(int)ns, (int)tps, (int)cap};
 }
 
 }  // namespace
@@ -933,13 +935,18 @@ bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype) {
     return G >= 1 && G <= 8 && hd > 0 && hd <= 512 && hd % ce_of(kv_dtype) == 0 && hd % 4 == 0;
 }
 
-static size_t ws_bytes_for(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t dtype) {
+// Partials for the plan of len.  For the decode layer (`layer`): sized for
+// the split count before rounding, which bounds the splits of every shorter
+// length (the layer sizes its workspace for its longest attention and runs
+// shorter ones in it).
+static size_t ws_bytes_for(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t dtype, bool layer) {
     if (len <= 0 || n_kv <= 0) return 0;
     size_t most = 0;
     for (const bool vec_ok : {true, false}) {
         const Plan p = make_plan(n_kv, len, pick(dtype, hd, n_q / n_kv, vec_ok));
-        if (p.nsplit == 1) continue;
-        const int64_t slots = n_kv * p.nsplit * (n_q / n_kv);
+        const int64_t ns = layer ? p.cap : p.nsplit;
+        if (ns == 1) continue;
+        const int64_t slots = n_kv * ns * (n_q / n_kv);
         const size_t b = (size_t)(slots * (hd + 2)) * sizeof(float);
         most = b > most ? b : most;
     }
@@ -951,10 +958,10 @@ int attn_nsplit(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t kv_d
     return make_plan(n_kv, len, pick(kv_dtype, hd, n_q / n_kv, vec_ok)).nsplit;
 }
 
-size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len) {
+size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, bool layer) {
     // the larger of the two dtypes' plans, so one query serves both
-    const size_t a = ws_bytes_for(n_q, n_kv, hd, len, LQ_KV_F32);
-    const size_t b = hd % 8 == 0 ? ws_bytes_for(n_q, n_kv, hd, len, LQ_KV_BF16) : 0;
+    const size_t a = ws_bytes_for(n_q, n_kv, hd, len, LQ_KV_F32, layer);
+    const size_t b = hd % 8 == 0 ? ws_bytes_for(n_q, n_kv, hd, len, LQ_KV_BF16, layer) : 0;
     return a > b ? a : b;
 }
 

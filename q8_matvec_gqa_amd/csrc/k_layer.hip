@@ -45,7 +45,7 @@ LayerBuffers layout(const lq_layer_desc* L, char* base, const lq_layer_taps* tap
     b.x1 = reinterpret_cast<float*>(take(H * 4));
     b.hq = reinterpret_cast<int8_t*>(take(I));
     b.hd = reinterpret_cast<uint16_t*>(take(I / 32 * 2));
-    b.attn_ws = take(attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, max_attn_len(L)));
+    b.attn_ws = take(attn_workspace_bytes(L->n_q, L->n_kv, L->head_dim, max_attn_len(L), true));
     b.total = off;
     if (taps) {
         if (taps->qkv) b.qkv = taps->qkv;

@@ -141,7 +141,9 @@ lq_status launch_qkv_post(float* qkv, int64_t n_q, int64_t n_kv, int64_t hd, con
 
 // ---- launchers (k_attn.hip) ---------------------------------------------------
 bool attn_supported(int64_t n_q, int64_t n_kv, int64_t hd, int32_t kv_dtype);
-size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len);
+// Split partials of an attention over len positions; `layer`: the decode
+// layer's region, which also serves every shorter length.
+size_t attn_workspace_bytes(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, bool layer = false);
 // splits the layer's attention uses (1: no combine launch); vec_ok: 16-byte aligned query rows
 int attn_nsplit(int64_t n_q, int64_t n_kv, int64_t hd, int64_t len, int32_t kv_dtype, bool vec_ok);
 // The host-side checks of lq_gqa_decode_attn other than the workspace's.

@@ -321,6 +321,19 @@ def test_layer_validation():
     assert st(lq.lq_decode_layer_timed, d, A, 8192, None, A, need, [A] * (2 * n)) == lq.LQ_ERR_SHAPE
 
 
+def test_layer_workspace_covers_shorter_contexts():
+    """The decode layer sizes its attention partials for its longest
+    attention (max_ctx, or the window) and runs every shorter one in the same
+    region, so the workspace must never shrink as max_ctx grows: a shorter
+    attention can plan more splits than a longer one after the whole-tile
+    rounding (8192 positions: 64 splits per kv head; 8193: 43)."""
+    prev = 0
+    for ctx in list(range(8150, 8260)) + [16384, 16385, 65536, 65537]:
+        n = lq.lq_decode_layer_workspace_size(_layer_desc(max_ctx=ctx))
+        assert n >= prev, (ctx, n, prev)
+        prev = n
+
+
 def test_layer_ggml_format_validation():
     """Projections in GGML formats (lq_layer_desc.w_format): the chosen
     descriptor's shape, pointers and alignment are checked before any launch."""
