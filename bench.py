@@ -182,14 +182,30 @@ def layer_kernels(cfg, nsplit_used, formats=None):
     return ks
 
 
+def spin_cycles(torch, ms):
+    """Argument of torch.cuda._sleep (a spin kernel that touches no memory)
+    for about `ms` milliseconds on this device, from one timed probe."""
+    probe = 1 << 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(probe)
+    e0.record()
+    torch.cuda._sleep(probe)
+    e1.record()
+    torch.cuda.synchronize()
+    per_ms = probe / max(e0.elapsed_time(e1), 1e-3)
+    return int(min(max(per_ms * ms, 1 << 16), 1 << 34))
+
+
 def kernel_measurements(cfg, layers, xs, torch, rounds, formats=None):
     """Times every kernel of the decode layer with start/stop HIP events that
     the runtime stamps at each dispatch of the layer (lq_decode_layer_timed),
     on the stream the layer runs on.  Each round enqueues all R layers back
-    to back behind a ~1 ms device copy, so the host has queued every launch
-    before the first one starts and the kernels run one after another as in
-    the graph replay (no host gaps, each kernel starting as the previous one
-    drains)."""
+    to back behind a ~2 ms spin kernel (no memory traffic), so the host has
+    queued every launch before the first one starts and the kernels run one
+    after another as in the graph replay (no host gaps, each kernel starting
+    as the previous one drains).  A device copy as the wait would leave the
+    Infinity Cache full of dirty lines, whose write-back then competes with
+    the first layers' reads."""
     import q8_matvec_gqa_amd as lq
     n_k = lq.lq_decode_layer_kernel_count(layers[0].desc)
     R = len(layers)
@@ -200,11 +216,10 @@ def kernel_measurements(cfg, layers, xs, torch, rounds, formats=None):
     torch.cuda.synchronize()
     names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5), formats)
     assert len(names) == n_k, (len(names), n_k)
-    busy_src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    busy_dst = torch.empty_like(busy_src)
+    cycles = spin_cycles(torch, 2.0)
     times = [[] for _ in range(n_k)]
     for r in range(rounds + 1):
-        busy_dst.copy_(busy_src)                  # ~2 GB of traffic: keeps the GPU busy while the host enqueues
+        torch.cuda._sleep(cycles)                 # keeps the GPU busy while the host enqueues
         for li, lay in enumerate(layers):
             lq.lq_decode_layer_timed(lay.desc, xs[li], cfg["pos"], None, lay.ws, lay.ws_bytes, evs[li])
         torch.cuda.synchronize()
@@ -213,7 +228,6 @@ def kernel_measurements(cfg, layers, xs, torch, rounds, formats=None):
         for li in range(R):
             for k in range(n_k):
                 times[k].append(evs[li][2 * k].elapsed_time(evs[li][2 * k + 1]) * 1e3)
-    del busy_src, busy_dst
     per = {}
     for (tag, kernel, b), ts in zip(names, times):
         per[tag] = dict(kernel=kernel, launches=len(ts), avg_us=float(np.mean(ts)), min_us=float(np.min(ts)),
