@@ -533,10 +533,31 @@ template <int NCH> struct MvShape {
 template <int NCH, int PRO, int EPI> struct MvWaves {
     static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 4 : 8;
 };
-template <int NCH, int PRO, int EPI>
+template <int NCH, int PRO, int EPI, int RPW_OVER = 0>
 static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
     constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
-    constexpr int RPW = SW ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1) : MvShape<NCH>::RPW;
+    if constexpr (RPW_OVER == 0 && !SW && NCH <= 4 && EPI != EPI_DOTS) {
+        // Short rows and few of them: the default groups (4 rows for rows of
+        // at most 2 KB, 2 rows up to 4 KB) would put workgroups on only part
+        // of the CUs, or give the waves unequal counts.  With at most three
+        // rows per 8-wave workgroup slot of every CU, take that many rows
+        // per group instead: one group per wave, every CU busy.
+        const int64_t waves = (int64_t)kNumCUs * 8;
+        if (a.rows <= waves) {
+            launch_mv_nch<NCH, PRO, EPI, 1>(a, s, wg_per_cu, mk);
+            return;
+        }
+        if (a.rows <= 2 * waves && MvShape<NCH>::RPW != 2) {
+            launch_mv_nch<NCH, PRO, EPI, 2>(a, s, wg_per_cu, mk);
+            return;
+        }
+        if (a.rows > 2 * waves && a.rows <= 3 * waves) {
+            launch_mv_nch<NCH, PRO, EPI, 3>(a, s, wg_per_cu, mk);
+            return;
+        }
+    }
+    constexpr int RPW = RPW_OVER ? RPW_OVER
+                        : SW ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1) : MvShape<NCH>::RPW;
     constexpr int OUT = SW ? RPW / 2 : RPW;
     constexpr int WAVES = MvWaves<NCH, PRO, EPI>::value;
     auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
