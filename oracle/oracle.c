@@ -30,10 +30,11 @@
  * function.
  *
  * Pins (tests/test_oracle_pins.py) tie every function to something other
- * than itself, with two limits:
- *   orc_decode_layer -- parity unpinned as a whole: it is checked against an
- *          independent composition of its pinned stages, and no external
- *          value for a whole layer exists.
+ * than itself.  orc_decode_layer is pinned as a whole by special cases with
+ * closed forms (all-zero O and down projections return x bit for bit; at
+ * position 0 every head's attention output is its kv head's new v row) and
+ * against an independent composition of its pinned stages; no external value
+ * for a whole layer on random weights exists.  One limit:
  *   orc_q6_k_dequant / orc_q6_k_matvec -- parity unpinned against GGML
  *          itself: the element order is pinned to the layout as read from
  *          the pages (no GGML fixture is available offline).

@@ -536,7 +536,7 @@ template <int NCH, int PRO, int EPI> struct MvWaves {
 template <int NCH, int PRO, int EPI, int RPW_OVER = 0>
 static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
     constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
-    if constexpr (RPW_OVER == 0 && !SW && NCH <= 4 && EPI != EPI_DOTS) {
+    if constexpr (RPW_OVER == 0 && !SW && NCH <= 4) {
         // Short rows and few of them: the default groups (4 rows for rows of
         // at most 2 KB, 2 rows up to 4 KB) would put workgroups on only part
         // of the CUs, or give the waves unequal counts.  With at most three

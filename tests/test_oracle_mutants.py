@@ -24,6 +24,10 @@ ALL_PINS = [
     pins.pin_moe_block, lambda: pins.pin_layer(0, 1), lambda: pins.pin_layer(1, 1),
     lambda: pins.pin_layer(0, 0), pins.pin_f16, pins.pin_bf16, pins.pin_lm_head, pins.pin_gelu,
     pins.pin_attention_softcap, pins.pin_rope_freqs, pins.pin_matmul, pins.pin_q4_0, pins.pin_q6_k,
+    lambda: pins.test_layer_zero_projections_is_identity(0, 1),
+    lambda: pins.test_layer_zero_projections_is_identity(1, 1),
+    lambda: pins.test_layer_one_position_closed_form(0, 1),
+    lambda: pins.test_layer_one_position_closed_form(1, 1),
 ]
 
 # (name, text in oracle.c, replacement)
@@ -93,6 +97,12 @@ MUTANTS = [
     ("layer_no_v_norm", "if (L->v_unit_norm) {", "if (0) {"),
     ("layer_no_k_rope", "orc_rope_neox(k + g * hd, hd, c_row, s_row);", "(void)0;"),
     ("layer_post_norm_weight", "orc_rmsnorm(tmp, H, L->g_post, L->eps, n);", "orc_rmsnorm(tmp, H, L->g_in, L->eps, n);"),
+    ("layer_o_no_residual", "orc_q8_matvec(L->o_qs, L->o_d, H, qd, q8, d8, x, x1);",
+     "orc_q8_matvec(L->o_qs, L->o_d, H, qd, q8, d8, NULL, x1);"),
+    ("layer_down_residual_x", "orc_q8_matvec(L->dn_qs, L->dn_d, H, I, q8, d8, x1, x);",
+     "orc_q8_matvec(L->dn_qs, L->dn_d, H, I, q8, d8, x, x);"),
+    ("layer_postnorm_residual_doubled", "x1[i] = (float)((double)x[i] + (double)n[i]);",
+     "x1[i] = (float)(2.0 * (double)x[i] + (double)n[i]);"),
 ]
 
 

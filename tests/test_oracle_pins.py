@@ -743,3 +743,76 @@ def pin_layer(kind, kv_dtype, seed=11):
 @pytest.mark.parametrize("kind,kv_dtype", [(0, 0), (0, 1), (1, 1)])
 def test_layer_composition(kind, kv_dtype):
     pin_layer(kind, kv_dtype)
+
+
+# ---- whole-layer special cases: closed forms that do not go through the
+# oracle's attention or wiring ("Current Inference Path -- Architecture Map",
+# section 3: residual adds around the attention block and the MLP; "Inference
+# Engine" (larql), BLAS-Fused Attention: softmax over the attended positions)
+
+@pytest.mark.parametrize("kind,kv_dtype", [(0, 0), (0, 1), (1, 1)])
+def test_layer_zero_projections_is_identity(kind, kv_dtype):
+    """With all-zero O and down codes the attention block and the MLP add
+    exact zeros to the residual stream, so the layer returns x bit for bit
+    (the Gemma block: o = 0, RMSNorm(0) = 0).  A dropped, doubled or
+    misrouted residual fails this."""
+    cfg, w, x, kc, vc = _small_layer(kind, kv_dtype, 5)
+    w["o_qs"] = np.zeros_like(w["o_qs"])
+    if kind == 0:
+        w["dn_qs"] = np.zeros_like(w["dn_qs"])
+    got, _, _, _ = oracle.decode_layer(cfg, w, x, cfg["ctx"] - 1, kc, vc)
+    assert np.array_equal(got.view(np.uint32), x.astype(np.float32).view(np.uint32))
+
+
+def _deq(q, d):
+    return q.astype(np.float64) * np.repeat(d.view(np.float16).astype(np.float64), 32, axis=-1)
+
+
+@pytest.mark.parametrize("kind,kv_dtype", [(0, 0), (0, 1), (1, 1)])
+def test_layer_one_position_closed_form(kind, kv_dtype):
+    """At position 0 the attention covers one position, so every query head's
+    softmax weight is exactly 1 and its output is the new v row of its kv head
+    (as stored in the cache): no scores, no softmax.  RoPE at angle 0 is the
+    identity, so the new k row is the normed k.  The layer output is then a
+    closed form of the projections alone; two kv heads with distinct v rows
+    also pin the query-head -> kv-head map (h // G)."""
+    cfg, w, x, kc, vc = _small_layer(kind, kv_dtype, 7)
+    H, nq, nkv, hd, I = cfg["hidden"], cfg["n_q"], cfg["n_kv"], cfg["head_dim"], cfg["ffn"]
+    eps, G = cfg["eps"], nq // nkv
+    got, kc2, vc2, _ = oracle.decode_layer(cfg, w, x, 0, kc, vc)
+
+    def rms(v, g):
+        v = v.astype(np.float64)
+        r = v / np.sqrt(np.mean(v * v) + eps)
+        return (r * (1.0 if g is None else g.astype(np.float64))).astype(np.float32)
+
+    def mv(name, a):
+        aq, ad = oracle.q8_quantize(a)
+        return (_deq(w[name + "_qs"], w[name + "_d"]) @ _deq(aq, ad)).astype(np.float32)
+
+    def stored(v):           # the cache's own rounding of a row
+        if kv_dtype == 0:
+            return v.astype(np.float64)
+        import torch
+        b = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return _bf16_f64(b)
+
+    qkv = mv("qkv", rms(x, w["g_in"]))
+    qd, kvd = nq * hd, nkv * hd
+    v = qkv[qd + kvd:].reshape(nkv, hd)
+    if cfg["v_unit_norm"]:
+        v = np.stack([rms(v[g], None) for g in range(nkv)])
+    k = np.stack([rms(qkv[qd + g * hd:qd + (g + 1) * hd], w["g_k"]) for g in range(nkv)])
+    tol = lambda a, b: np.all(np.abs(a - b) <= np.maximum(1e-3 * np.abs(b), 1e-4))
+    read = (lambda c: c.astype(np.float64)) if kv_dtype == 0 else _bf16_f64
+    assert tol(read(kc2[:, 0]), stored(k)) and tol(read(vc2[:, 0]), stored(v))
+    att = np.concatenate([stored(v[h // G]) for h in range(nq)]).astype(np.float32)
+    assert not np.allclose(v[0], v[1])                  # distinct kv heads: the map is observable
+    if kind == 0:
+        x1 = (x.astype(np.float64) + mv("o", att)).astype(np.float32)
+        gu = mv("gu", rms(x1, w["g_post"])).astype(np.float64)
+        h = (gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]).astype(np.float32)
+        want = x1.astype(np.float64) + mv("dn", h)
+    else:
+        want = x.astype(np.float64) + rms(mv("o", att), w["g_post"])
+    assert tol(got.astype(np.float64), want), np.abs(got - want).max()
