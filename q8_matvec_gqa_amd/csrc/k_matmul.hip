@@ -356,12 +356,25 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul_wide(MmArgs a) {
         sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_mm, As), __builtin_bit_cast(v4h_mm, Bs),
                                                   v16f_mm{}, 0, 0, 0);
     };
+    // block u's operands are read from LDS while block u - 1 is rescaled,
+    // so the LDS latency hides behind the converts and FMAs
+    auto lds_ops = [&](int u, v4i_mm& A, v4i_mm& B, int& xs, int& ws) {
+        A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
+        B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
+        xs = dxl[u * kMwSS + tt * 32 + n];
+        ws = dwl[u * kMwSS + rt * 32 + n];
+    };
     auto compute = [&]() {
+        v4i_mm A, B;
+        int xs, ws;
+        lds_ops(0, A, B, xs, ws);
 #pragma unroll
         for (int u = 0; u < kMmKB; ++u) {
-            v16i_mm c;
-            v16f_mm sc;
-            mma(u, c, sc);
+            const v16i_mm c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
+            const v2i_mm As = {half ? 0 : xs, 0}, Bs = {half ? 0 : ws, 0};
+            const v16f_mm sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_mm, As),
+                                                                    __builtin_bit_cast(v4h_mm, Bs), v16f_mm{}, 0, 0, 0);
+            if (u + 1 < kMmKB) lds_ops(u + 1, A, B, xs, ws);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
