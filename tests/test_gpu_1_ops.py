@@ -85,9 +85,13 @@ def test_swiglu_q8(n_rows, ffn):
 # ------------------------------------------------------------------ block dots / matvec
 DOT_SHAPES = [(1, 32), (3, 64), (5, 1024), (37, 1056), (64, 2560), (9, 2816), (17, 4096), (4, 9728),
               (13, 12288), (3, 16384), (2, 17408)]     # 17408 > 16 KB: the generic path
+# rows at the thresholds where rows of at most 4 KB change rows per group
+# (one row up to 2048 rows, two up to 4096, three up to 6144), with ragged
+# last groups and a ragged last 1 KB chunk
+THRESHOLD_SHAPES = [(2048, 1024), (2049, 1024), (4096, 1056), (4097, 3072), (6143, 2080), (6145, 4096)]
 
 
-@pytest.mark.parametrize("rows,cols", DOT_SHAPES)
+@pytest.mark.parametrize("rows,cols", DOT_SHAPES + THRESHOLD_SHAPES)
 def test_block_dots_bit_exact(rows, cols):
     r = rng(rows * 7 + cols)
     wq = r.integers(-128, 128, size=(rows, cols), dtype=np.int8)
@@ -151,6 +155,7 @@ def test_block_dots_layer_projections(tag, rows, cols, pro):
 
 MATVEC_SHAPES = DOT_SHAPES[1:] + [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288),
                                   (10240, 2816), (2816, 8192), (1, 4096), (255, 3072)]
+MATVEC_SHAPES += THRESHOLD_SHAPES
 
 
 @pytest.mark.parametrize("rows,cols", MATVEC_SHAPES)
