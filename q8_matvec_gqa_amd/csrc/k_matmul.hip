@@ -75,41 +75,62 @@ struct MmStage {
     uint32_t dw[kMmNS], dx[kMmNS];
 };
 
-// Loads of the batch [bs, be) (be - bs <= kMmKB blocks).  Load j of thread
-// tid takes chunk idx % kMmCPR of row idx / kMmCPR (idx = tid + 256j), so
-// each wave instruction reads whole contiguous row runs; scales likewise
-// (consecutive lanes read one row's consecutive scales).  Chunks of blocks
-// past be and rows past the matrix read valid memory of their own row (block
-// 0, the last row) and are zeroed through their scales or never stored.
-// Tokens past T load nothing (every workgroup reads X, so clamped duplicates
-// would pile onto a few cache lines): their LDS rows and scales are zero.
-__device__ __forceinline__ void mm_load(const MmArgs& a, int row0, int bs, int be, int tid, MmStage& S) {
-    // a tile base (wave-uniform) plus a 32-bit offset inside the tile: the
-    // loads take the scalar-base form, with no 64-bit arithmetic per lane
+// A batch's loads (blocks [bs, bs + kMmKB) of every row of the tile).  Load j
+// of thread tid takes 16-byte chunk idx % kMmCPR of row idx / kMmCPR (idx =
+// tid + 256j), so each wave instruction reads whole contiguous row runs;
+// scales likewise (consecutive lanes read one row's consecutive scales).
+// They go through buffer resources over the tile's W rows and X tokens
+// (built once per workgroup): rows or tokens past the matrix, and the bytes
+// past the last row's end that a final partial batch touches, read as zeros
+// without a memory access (the range check); chunks of blocks past the
+// batch's end read the next blocks of the row and are zeroed through their
+// scales.  The per-lane offsets are fixed for the tile and a batch adds only
+// its start: one add per load, no 64-bit address arithmetic.  NL / NS:
+// chunk loads and scale loads per thread and matrix; R: rows of the tile.
+template <int NL, int NS>
+struct MmSrc {
+    __amdgpu_buffer_rsrc_t w, x, dw, dx;
+    uint32_t off[NL];     // row * cols + 16 * chunk
+    uint32_t doff[NS];    // 2 * (row * nb + block)
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int NL, int NS, int R>
+__device__ __forceinline__ void mm_src(const MmArgs& a, int row0, int t0, int Tc, int tid, MmSrc<NL, NS>& S) {
     const int nb = a.cols >> 5;
+    const int nr = a.rows - row0 < R ? a.rows - row0 : R;
+    S.w = mm_rsrc(a.wq + (int64_t)row0 * a.cols, (uint32_t)nr * (uint32_t)a.cols);
+    S.x = mm_rsrc(a.xq + (int64_t)t0 * a.cols, (uint32_t)Tc * (uint32_t)a.cols);
+    S.dw = mm_rsrc(a.wd + (int64_t)row0 * nb, 2u * (uint32_t)nr * (uint32_t)nb);
+    S.dx = mm_rsrc(a.xd + (int64_t)t0 * nb, 2u * (uint32_t)Tc * (uint32_t)nb);
     const int c = tid % kMmCPR;
-    const uint32_t coff = bs + (c >> 1) < be ? (uint32_t)bs * 32u + 16u * c : 16u * (c & 1);
-    const int rlast = a.rows - 1 - row0;                  // last row of the tile that exists
-    const int8_t* wt = a.wq + (int64_t)row0 * a.cols;
 #pragma unroll
-    for (int j = 0; j < kMmNL; ++j) {
-        const int r = (tid + kMmNT * j) / kMmCPR;
-        const uint32_t wr = (uint32_t)(r < rlast ? r : rlast) * (uint32_t)a.cols;
-        S.w[j] = load_stream16(wt + (wr + coff));
-        S.x[j] = make_int4(0, 0, 0, 0);
-        if (r < a.T) S.x[j] = *reinterpret_cast<const int4*>(a.xq + ((uint32_t)r * (uint32_t)a.cols + coff));
-    }
-    const char* wdt = reinterpret_cast<const char*>(a.wd + (int64_t)row0 * nb);
-    const char* xdt = reinterpret_cast<const char*>(a.xd);
+    for (int j = 0; j < NL; ++j) S.off[j] = (uint32_t)((tid + kMmNT * j) / kMmCPR) * (uint32_t)a.cols + 16u * c;
 #pragma unroll
-    for (int i = 0; i < kMmNS; ++i) {
-        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
-        const uint32_t b = bs + u < be ? (uint32_t)(bs + u) : 0u;
-        S.dw[i] = *reinterpret_cast<const uint16_t*>(wdt + 2u * ((uint32_t)(rr < rlast ? rr : rlast) * (uint32_t)nb + b));
-        S.dx[i] = 0;
-        if (rr < a.T) S.dx[i] = *reinterpret_cast<const uint16_t*>(xdt + 2u * ((uint32_t)rr * (uint32_t)nb + b));
+    for (int i = 0; i < NS; ++i) {
+        const int idx = tid + kMmNT * i;
+        S.doff[i] = 2u * ((uint32_t)(idx / kMmKB) * (uint32_t)nb + (uint32_t)(idx % kMmKB));
     }
 }
+template <int NL, int NS>
+__device__ __forceinline__ void mm_load_b(const MmSrc<NL, NS>& R, int bs, int4 (&w)[NL], int4 (&x)[NL],
+                                          uint32_t (&dw)[NS], uint32_t (&dx)[NS]) {
+    const uint32_t cb = (uint32_t)bs * 32u, db = 2u * (uint32_t)bs;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const auto vw = __builtin_amdgcn_raw_buffer_load_b128(R.w, (int)(R.off[j] + cb), 0, 2);   // nontemporal
+        const auto vx = __builtin_amdgcn_raw_buffer_load_b128(R.x, (int)(R.off[j] + cb), 0, 0);
+        w[j] = make_int4((int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3]);
+        x[j] = make_int4((int)vx[0], (int)vx[1], (int)vx[2], (int)vx[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        dw[i] = __builtin_amdgcn_raw_buffer_load_b16(R.dw, (int)(R.doff[i] + db), 0, 0);
+        dx[i] = __builtin_amdgcn_raw_buffer_load_b16(R.dx, (int)(R.doff[i] + db), 0, 0);
+    }
+}
+
 
 // LDS: W tile [32 rows][kMmRB], X tile [32 tokens][kMmRB], scales as f16
 // bits [block][kMmSS] (row or token fastest), zero for blocks past be and
@@ -202,26 +223,19 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul(MmArgs args) {
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
     };
+    MmSrc<kMmNL, kMmNS> src;
+    mm_src<kMmNL, kMmNS, 32>(a, row0, 0, a.T, tid, src);
     auto step = [&](int i, MmStage& S) {
         const int bs = batch_start(i), be = batch_end(bs);
         if (i > 0) __syncthreads();          // every wave is done with the previous batch
         mm_store(a, bs, be, tid, S, wl, xl, dwl, dxl);
         __syncthreads();
-        if (i + 2 < nbt) {
-            const int bn = batch_start(i + 2);
-            mm_load(a, row0, bn, batch_end(bn), tid, S);
-        }
+        if (i + 2 < nbt) mm_load_b(src, batch_start(i + 2), S.w, S.x, S.dw, S.dx);
         compute();
     };
     MmStage P, Q;
-    {
-        const int bs = batch_start(0);
-        mm_load(a, row0, bs, batch_end(bs), tid, P);
-    }
-    if (nbt > 1) {
-        const int bs = batch_start(1);
-        mm_load(a, row0, bs, batch_end(bs), tid, Q);
-    }
+    mm_load_b(src, batch_start(0), P.w, P.x, P.dw, P.dx);
+    if (nbt > 1) mm_load_b(src, batch_start(1), Q.w, Q.x, Q.dw, Q.dx);
     for (int i = 0; i < nbt; i += 2) {
         step(i, P);
         if (i + 1 < nbt) step(i + 1, Q);
@@ -266,38 +280,6 @@ struct MwStage {
     int4 w[kMwNL], x[kMwNL];
     uint32_t dw[kMwNS], dx[kMwNS];
 };
-
-// Addresses are a tile base (wave-uniform, 64-bit) plus a 32-bit offset
-// inside the tile (64 rows of at most 16 KB), so the loads take the
-// scalar-base form and need no 64-bit address arithmetic per lane.
-__device__ __forceinline__ void mw_load(const MmArgs& a, int row0, int t0, int Tc, int bs, int be, int tid,
-                                        MwStage& S) {
-    const int nb = a.cols >> 5;
-    const int c = tid % kMmCPR;
-    const uint32_t coff = bs + (c >> 1) < be ? (uint32_t)bs * 32u + 16u * c : 16u * (c & 1);
-    const int rlast = a.rows - 1 - row0;                  // last row of the tile that exists
-    const int8_t* wt = a.wq + (int64_t)row0 * a.cols;
-    const int8_t* xt = a.xq + (int64_t)t0 * a.cols;
-#pragma unroll
-    for (int j = 0; j < kMwNL; ++j) {
-        const int r = (tid + kMmNT * j) / kMmCPR;
-        const uint32_t wr = (uint32_t)(r < rlast ? r : rlast) * (uint32_t)a.cols;
-        S.w[j] = load_stream16(wt + (wr + coff));
-        S.x[j] = make_int4(0, 0, 0, 0);
-        if (r < Tc) S.x[j] = *reinterpret_cast<const int4*>(xt + ((uint32_t)r * (uint32_t)a.cols + coff));
-    }
-    const char* wdt = reinterpret_cast<const char*>(a.wd + (int64_t)row0 * nb);
-    const char* xdt = reinterpret_cast<const char*>(a.xd + (int64_t)t0 * nb);
-#pragma unroll
-    for (int i = 0; i < kMwNS; ++i) {
-        const int idx = tid + kMmNT * i, rr = idx / kMmKB, u = idx % kMmKB;
-        const uint32_t b = bs + u < be ? (uint32_t)(bs + u) : 0u;
-        const uint32_t wo = 2u * ((uint32_t)(rr < rlast ? rr : rlast) * (uint32_t)nb + b);
-        S.dw[i] = *reinterpret_cast<const uint16_t*>(wdt + wo);
-        S.dx[i] = 0;
-        if (rr < Tc) S.dx[i] = *reinterpret_cast<const uint16_t*>(xdt + 2u * ((uint32_t)rr * (uint32_t)nb + b));
-    }
-}
 
 __device__ __forceinline__ void mw_store(int Tc, int bs, int be, int tid, const MwStage& S, int8_t* wl, int8_t* xl,
                                          uint16_t* dwl, uint16_t* dxl) {
@@ -344,20 +326,11 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul_wide(MmArgs a) {
         return kMmKB * j;
     };
     auto batch_end = [&](int bs) { return bs + kMmKB < nb ? bs + kMmKB : nb; };
-    // block u: the block dots (i8 MFMA) and the scale products from the
-    // smallest f16 MFMA (32x32x8: two-register operands, half the cycles of
-    // the 32x32x16 one), its only nonzero k term f16(dX[t]) * f16(dW[r])
-    auto mma = [&](int u, v16i_mm& c, v16f_mm& sc) {
-        const v4i_mm A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
-        const v4i_mm B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
-        const int xs = dxl[u * kMwSS + tt * 32 + n], ws = dwl[u * kMwSS + rt * 32 + n];
-        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, v16i_mm{}, 0, 0, 0);
-        const v2i_mm As = {half ? 0 : xs, 0}, Bs = {half ? 0 : ws, 0};
-        sc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h_mm, As), __builtin_bit_cast(v4h_mm, Bs),
-                                                  v16f_mm{}, 0, 0, 0);
-    };
-    // block u's operands are read from LDS while block u - 1 is rescaled,
-    // so the LDS latency hides behind the converts and FMAs
+    // Block u: the block dots (i8 MFMA) and the scale products from the
+    // smallest f16 MFMA (32x32x8: two-register operands), its only nonzero k
+    // term f16(dX[t]) * f16(dW[r]).  Block u + 1's operands are read from LDS
+    // while block u is rescaled, so the LDS latency hides behind the
+    // converts and FMAs.
     auto lds_ops = [&](int u, v4i_mm& A, v4i_mm& B, int& xs, int& ws) {
         A = *reinterpret_cast<const v4i_mm*>(xl + (tt * 32 + n) * kMmRB + 32 * u + 16 * half);
         B = *reinterpret_cast<const v4i_mm*>(wl + (rt * 32 + n) * kMmRB + 32 * u + 16 * half);
@@ -379,24 +352,20 @@ __global__ __launch_bounds__(kMmNT, 3) void k_q8_matmul_wide(MmArgs a) {
             for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)c[i], sc[i], acc[i]);
         }
     };
+    MmSrc<kMwNL, kMwNS> src;
+    mm_src<kMwNL, kMwNS, kMwR>(a, row0, t0, Tc, tid, src);
     auto step = [&](int i, MwStage& S) {
         const int bs = batch_start(i), be = batch_end(bs);
         if (i > 0) __syncthreads();
         mw_store(Tc, bs, be, tid, S, wl, xl, dwl, dxl);
         __syncthreads();
-        if (i + 1 < nbt) {
-            const int bn = batch_start(i + 1);
-            mw_load(a, row0, t0, Tc, bn, batch_end(bn), tid, S);
-        }
+        if (i + 1 < nbt) mm_load_b(src, batch_start(i + 1), S.w, S.x, S.dw, S.dx);
         compute();
     };
     // one batch in flight in registers (the next batch's loads overlap this
-    // batch's math): 156 VGPRs, three workgroups per CU
+    // batch's math)
     MwStage P;
-    {
-        const int bs = batch_start(0);
-        mw_load(a, row0, t0, Tc, bs, batch_end(bs), tid, P);
-    }
+    mm_load_b(src, batch_start(0), P.w, P.x, P.dw, P.dx);
     for (int i = 0; i < nbt; ++i) step(i, P);
     // lane holds tokens 8*(r/4) + 4*half + r%4 of row n of the sub-tile
     const int row = row0 + rt * 32 + n;
