@@ -268,6 +268,10 @@ ATTN_CASES = [
     (8, 1, 512, 1, 1000, 5, 995),         # one kv head, start > 0, a ragged last tile
     (32, 4, 512, 1, 3000, 100, 1500),     # four kv heads, a window
     (16, 2, 512, 1, 65536, 0, 65536),     # long context: several tiles per wave
+    # the same heads from 2048 positions on, where the scores run on the matrix cores
+    (16, 2, 512, 1, 2048, 0, 2048),       # the first length that does
+    (8, 1, 512, 1, 3000, 7, 2501),        # one kv head, start > 0, a ragged last 16-position tile
+    (32, 4, 512, 1, 5000, 100, 4099),     # four kv heads, a window, ragged
 ]
 
 
