@@ -239,6 +239,35 @@ def test_layer_positions(name, pos):
     assert_close(host(bufs["attn"]), att, f"{name}: attention at pos {pos}")
 
 
+def test_layer_workspace_serves_shorter_attention():
+    """A layer sized for its longest attention (max_ctx 8193: 33 splits per
+    kv head after the whole-tile rounding) running a shorter one (8192
+    positions: 64 splits): the partials fit the workspace, nothing past it is
+    written (a guard region keeps its bytes), and the attention matches the
+    oracle."""
+    torch = torch_mod()
+    cfg, w = synthetic.layer_inputs("tiny_h1024", seed=5)
+    hd, nq, nkv, M, pos = cfg["head_dim"], cfg["n_q"], cfg["n_kv"], 8193, 8191
+    r = np.random.Generator(np.random.PCG64(8193))
+    cfg = dict(cfg, max_ctx=M)
+    w = dict(w, k_cache=synthetic.kv_cache(r, nkv, M, hd, 0), v_cache=synthetic.kv_cache(r, nkv, M, hd, 0))
+    print(f"[ws] tiny_h1024 with max_ctx {M} at pos {pos}", flush=True)
+    L = DeviceLayer(cfg, w, torch)
+    guard = 1 << 20
+    buf = torch.full((L.ws_bytes + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    L.ws = buf[:L.ws_bytes]
+    taps, bufs = L.make_taps()
+    x = dev(w["x"])
+    L.run(x, pos, taps)
+    sync()
+    assert bool((buf[L.ws_bytes:] == 0xA5).all()), "write past the layer workspace"
+    oc, os_ = oracle.rope_table(M, hd, cfg["theta"])
+    kc, vc = host(L.t["k_cache"]), host(L.t["v_cache"])
+    post = post_rope(dict(cfg, pos=pos), host(bufs["qkv"]), w["g_q"], w["g_k"], oc[pos], os_[pos])
+    att = oracle.attention(post[:nq * hd], nq, nkv, hd, kc, vc, 0, M * hd, hd, 0, pos + 1, cfg["attn_scale"])
+    assert_close(host(bufs["attn"]), att, "attention with 64 splits in a workspace sized at max_ctx")
+
+
 def _check_moe_block(cfg, w, escale, tag):
     """One MoE block on the GPU with every tap, checked stage by stage against
     the oracle fed the GPU's own inputs (teacher-forced), then free-running
