@@ -533,9 +533,18 @@ template <int NCH> struct MvShape {
 template <int NCH, int PRO, int EPI> struct MvWaves {
     static constexpr int value = (NCH > 8 || EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8) ? 4 : 8;
 };
-template <int NCH, int PRO, int EPI, int RPW_OVER = 0>
+template <int NCH, int PRO, int EPI, int RPW_OVER = 0, int WAVES_OVER = 0>
 static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchMarks* mk) {
     constexpr bool SW = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_Q8;
+    if constexpr (EPI == EPI_SWIGLU_Q8 && WAVES_OVER == 0 && NCH <= 4) {
+        // fewer 32-output blocks of h than CUs (a narrow FFN, or one GPU's
+        // share of a wide one): each block's workgroup takes 16 waves with a
+        // pair or two of rows each, so the few busy CUs keep more rows in flight
+        if ((a.rows + 31) / 32 < kNumCUs) {
+            launch_mv_nch<NCH, PRO, EPI, 0, 16>(a, s, wg_per_cu, mk);
+            return;
+        }
+    }
     if constexpr (RPW_OVER == 0 && !SW && NCH <= 4) {
         // Short rows and few of them: the default groups (4 rows for rows of
         // at most 2 KB, 2 rows up to 4 KB) would put workgroups on only part
@@ -559,7 +568,7 @@ static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchM
     constexpr int RPW = RPW_OVER ? RPW_OVER
                         : SW ? 2 * (MvShape<NCH>::RPW > 1 ? MvShape<NCH>::RPW / 2 : 1) : MvShape<NCH>::RPW;
     constexpr int OUT = SW ? RPW / 2 : RPW;
-    constexpr int WAVES = MvWaves<NCH, PRO, EPI>::value;
+    constexpr int WAVES = WAVES_OVER ? WAVES_OVER : MvWaves<NCH, PRO, EPI>::value;
     auto kern = k_mv<NCH, RPW, PRO, EPI, WAVES>;
     // workgroups per CU this instance can keep resident (queried once; the
     // value is the same for every caller, so concurrent first calls agree)

@@ -5,7 +5,7 @@ the method's arithmetic (no quantization, normalisation, rotation, softmax or
 dot products).  Both the GPU path and the CPU oracle receive exactly these
 arrays.
 
-Distributions (the five workloads below):
+Distributions (the workloads below):
   * Q8_0 weight codes: int8 uniform on [-127, 127].
   * Q8_0 weight scales: |N(0, 0.02)| / 127 stored as IEEE f16 (numpy's
     float16 cast); about 30% of them are f16 subnormals.
@@ -36,6 +36,12 @@ WORKLOADS = {
                                  kv_dtype=1, ctx=8192, window=1024),
     "gemma4_global_h2816": dict(kind=1, hidden=2816, n_q=16, n_kv=2, head_dim=512, ffn=0,
                                 kv_dtype=1, ctx=8192, window=0),
+    # one GPU's share of the 8B-like layer under 8-way tensor parallelism: 4
+    # query heads with their 1 kv head, a 1536-wide FFN slice (QKV 768 x 4096,
+    # O 4096 x 512, gate_up 3072 x 4096, down 4096 x 1536); on one GPU the
+    # residual is added locally where the sharded layer would all-reduce
+    "qwen3_8b_like_h4096_tp8_share": dict(kind=0, hidden=4096, n_q=4, n_kv=1, head_dim=128, ffn=1536,
+                                          kv_dtype=1, ctx=8192, window=0),
 }
 MOE_WORKLOADS = {
     "moe_e128_top8_t16": dict(hidden=2816, ffn=704, n_experts=128, top_k=8, tokens=16),

@@ -108,7 +108,7 @@ def test_block_dots_bit_exact(rows, cols):
 
 
 def _layer_projections():
-    """(tag, rows, cols, prologue) for every projection of the five workloads:
+    """(tag, rows, cols, prologue) for every projection of the layer workloads:
     QKV and gate_up build their input with the RMSNorm prologue, O with the
     quantize prologue, down reads the Q8_0 of h; plus the MoE experts' shapes."""
     out = []
@@ -125,7 +125,7 @@ def _layer_projections():
 @pytest.mark.parametrize("tag,rows,cols,pro", _layer_projections(), ids=lambda v: str(v))
 def test_block_dots_layer_projections(tag, rows, cols, pro):
     """The int32 block dots of the fused matvec kernel the layer runs, at every
-    projection shape of the five workloads, through the prologue each one
+    projection shape of the layer workloads, through the prologue each one
     uses there: bit-exact against the oracle's integer sums of the Q8_0 input
     the kernel built (which itself must match the oracle's quantization)."""
     r = rng(rows + 11 * cols)
