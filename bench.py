@@ -216,10 +216,16 @@ def kernel_measurements(cfg, layers, xs, torch, rounds, formats=None):
     torch.cuda.synchronize()
     names = layer_kernels(cfg, n_k == (6 if cfg["kind"] == 0 else 5), formats)
     assert len(names) == n_k, (len(names), n_k)
-    cycles = spin_cycles(torch, 2.0)
+    if hasattr(torch.cuda, "_sleep"):
+        cycles = spin_cycles(torch, 2.0)
+        busy = lambda: torch.cuda._sleep(cycles)
+    else:
+        # without torch's spin kernel: a read-only reduction (no dirty lines left behind)
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        busy = lambda: src.sum()
     times = [[] for _ in range(n_k)]
     for r in range(rounds + 1):
-        torch.cuda._sleep(cycles)                 # keeps the GPU busy while the host enqueues
+        busy()                                    # keeps the GPU busy while the host enqueues
         for li, lay in enumerate(layers):
             lq.lq_decode_layer_timed(lay.desc, xs[li], cfg["pos"], None, lay.ws, lay.ws_bytes, evs[li])
         torch.cuda.synchronize()
