@@ -470,10 +470,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
     int4 kr[KSTEPS][CPL];
     int4 vr[VSTEPS][VCPL];
     load_k(t, kr);
-    load_v(t, vr);
 #pragma unroll
     for (int i = 0; i < EARLY; ++i)
         if (i < n_items) item_run(i, hin[i], srcs[i]);
+    load_v(t, vr);
     for (int i = EARLY; i < n_items; ++i) {
         const HeadSrc src = item_src(i);
         item_load(hin[0], src);
