@@ -473,7 +473,6 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < EARLY; ++i)
         if (i < n_items) item_run(i, hin[i], srcs[i]);
-    load_v(t, vr);
     for (int i = EARLY; i < n_items; ++i) {
         const HeadSrc src = item_src(i);
         item_load(hin[0], src);
@@ -485,6 +484,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
             if (i / HDM >= G || i % HDM >= hd) q_lds[i] = 0.0f;
     }
     __syncthreads();
+    load_v(t, vr);
     float qr[GM][CPL][CE];
 #pragma unroll
     for (int h = 0; h < GM; ++h)
