@@ -896,9 +896,12 @@ def summarize_trace(trace_dir, out_dir, workload, command, steps=20, warmup=5, r
         lines.append(f"{n} | {len(ts)} | {statistics.mean(ts):.3f} | {statistics.median(ts):.3f} | "
                      f"{min(ts):.3f} | {max(ts):.3f}")
     lines.append("layer kernel@phase | dispatches | avg_us | median_us | min_us | max_us")
+    first = {n: min(v)[0] for n, v in groups.items()}
     for tag, pat in layer_kernel_patterns(cfg).items():
-        names = [n for n in durs if pat.search(n)]
-        if len(names) != 1:
+        # several instances can match (another workload's shape of the same
+        # step): the workload's own is the one dispatched first
+        names = sorted((n for n in durs if pat.search(n)), key=lambda n: first[n])
+        if not names:
             continue
         ts = durs[names[0]]
         for ph, (a, b) in phases.items():
