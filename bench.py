@@ -1007,7 +1007,7 @@ def main():
                     help="write the kernel-trace summary from a rocprofv3 --kernel-trace folder and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar=("NAME", "DIR"),
                     help="write profiles/NAME.txt: per-kernel counter averages from rocprofv3 --pmc folders, and exit")
-    ap.add_argument("--only", choices=["attn_long_context", "moe_block", "lm_head"],
+    ap.add_argument("--only", choices=["attn_long_context", "moe_block", "lm_head", "q8_matmul", "q8_matmul_prefill"],
                     help="run only this extra measurement (for profiling) and print its JSON")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     ap.add_argument("--profiles-dir", default=PROFILES, help="where the summaries are written")
@@ -1040,7 +1040,9 @@ def main():
     if args.only:
         fn = {"attn_long_context": lambda: measure_attn_context(max(5, args.steps // 5), torch),
               "moe_block": lambda: measure_moe(list(synthetic.MOE_WORKLOADS)[0], max(10, args.steps // 2), torch),
-              "lm_head": lambda: measure_head(max(10, args.steps // 2), torch)}[args.only]
+              "lm_head": lambda: measure_head(max(10, args.steps // 2), torch),
+              "q8_matmul": lambda: measure_matmul(32, max(5, args.steps // 10), torch),
+              "q8_matmul_prefill": lambda: measure_matmul(512, max(3, args.steps // 20), torch)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
     cfg = synthetic.layer_cfg(args.workload)
