@@ -69,3 +69,27 @@ def test_context_figures_are_the_pages():
     c = bench.context_figures(57.5)
     assert c["hf2q_decode_tok_per_s"]["value"] == [86, 105]
     assert c["larql_amx_f32_TFLOPS"]["value"] == [2, 4]
+
+
+def test_trace_summary_takes_the_workload_instance_dispatched_first(tmp_path):
+    """Two instances match the gate_up pattern (the headline's and another
+    workload's 16-wave one, dispatched later): the per-phase rows come from
+    the headline's, whose dispatches come first in the trace."""
+    import csv
+    trace = tmp_path / "trace"
+    trace.mkdir()
+    head = "void lq::k_mv<4, 2, 2, 3, 4>(lq::MvArgs)"
+    other = "void lq::k_mv<4, 2, 2, 3, 16>(lq::MvArgs)"
+    rows = []
+    for i in range(315):                       # the headline's dispatches: 10 us each
+        rows.append((head, 1_000_000 + 100_000 * i, 1_000_000 + 100_000 * i + 10_000))
+    for i in range(400):                       # another workload's, later: 5 us each
+        rows.append((other, 90_000_000 + 100_000 * i, 90_000_000 + 100_000 * i + 5_000))
+    with open(trace / "bt_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writerows(rows)
+    bench.summarize_trace(str(trace), str(tmp_path), synthetic.HEADLINE, "test", steps=20, warmup=5, rounds=5)
+    text = (tmp_path / f"decode_layer_{synthetic.HEADLINE}.trace.txt").read_text()
+    timed = [line for line in text.splitlines() if line.startswith("gate_up_matvec@timed")]
+    assert timed == ["gate_up_matvec@timed | 45 | 10.000 | 10.000 | 10.000 | 10.000"]
