@@ -24,6 +24,8 @@ CXXFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE-correct float division and sqrt (the quantizer's scale is amax/127)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # kernel arguments passed one by one are preloaded into SGPRs at dispatch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unused-result",
     "-I" + os.path.join(ROOT, "include"),
 ]

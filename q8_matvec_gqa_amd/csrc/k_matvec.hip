@@ -302,8 +302,16 @@ __device__ __forceinline__ void consume_group(const MvArgs& a, int64_t g, int la
     }
 }
 
+// The arguments come one by one, the ones every wave reads first leading:
+// the compiler can then preload them into SGPRs at dispatch instead of each
+// wave fetching them from the kernel-argument buffer before its first load.
 template <int NCH, int RPW, int PRO, int EPI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(MvArgs a) {
+__global__ __launch_bounds__(WAVES * 64, (MvWpe<NCH, EPI>::value)) void k_mv(
+    const float* p_x, const float* p_gamma, const int8_t* p_xq, const uint16_t* p_xd, const int8_t* p_wq,
+    const uint16_t* p_wd, int p_rows, int p_cols, float p_eps, const float* p_res, float* p_y, int8_t* p_yq,
+    uint16_t* p_yd, int8_t* p_tap_q, uint16_t* p_tap_d, int p_act, int32_t* p_dots) {
+    const MvArgs a{p_wq, p_wd, p_rows, p_cols, p_xq, p_xd, p_x, p_gamma, p_eps, p_res, p_y, p_yq, p_yd, p_tap_q,
+                   p_tap_d, p_act, p_dots};
     constexpr int NT = WAVES * 64;
     constexpr bool XL = NCH > 8;                          // activation slice from LDS
     constexpr bool LDS_X = (PRO != PRO_Q8) || XL;
@@ -588,7 +596,8 @@ static void launch_mv_nch(const MvArgs& a, hipStream_t s, int wg_per_cu, LaunchM
     int64_t grid = (groups + WAVES * iters - 1) / (WAVES * iters);
     if (EPI == EPI_SWIGLU_Q8) grid = (a.rows + 31) / 32;        // one workgroup per 32-output block
     if (grid < 1) grid = 1;
-    launch_marked(mk, kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a);
+    launch_marked(mk, kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, a.x, a.gamma, a.xq, a.xd, a.wq, a.wd,
+                  a.rows, a.cols, a.eps, a.res, a.y, a.yq, a.yd, a.tap_q, a.tap_d, a.act, a.dots);
 }
 
 template <int PRO, int EPI>
