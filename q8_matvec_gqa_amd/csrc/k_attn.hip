@@ -90,6 +90,27 @@ struct AttnArgs {
                              // attention scale and the cache conversion [n_q*hd + 2*n_kv*hd]
 };
 
+// The split kernel's arguments one by one, the ones its first loads need
+// leading (the query/projection rows, the caches and the window): the
+// compiler preloads the first 16 dwords into SGPRs at dispatch, so no wave
+// waits for the kernel-argument buffer before its first load.
+#define LQ_ATTN_PARAMS                                                                                      \
+    const float *p_q, const void *p_kc, void *p_vc_w, void *p_kc_w, int64_t p_head_stride,                   \
+        int64_t p_pos_stride, int64_t p_start, int64_t p_len, float *p_out, float *p_part_m, float *p_part_l, \
+        float *p_part_acc, const float *p_g_q, const float *p_g_k, const float *p_rope_cos,                  \
+        const float *p_rope_sin, int p_hd, int p_G, int p_n_q, int p_n_kv, int p_nsplit,                     \
+        int p_tiles_per_split, int p_fused, int p_qk_norm, int p_v_unit_norm, float p_qscale, float p_cap2,   \
+        float p_eps, float *p_tap_post
+#define LQ_ATTN_FIELDS(A)                                                                                   \
+    (A).q, (A).kc, (A).vc_w, (A).kc_w, (A).head_stride, (A).pos_stride, (A).start, (A).len, (A).out,         \
+        (A).part_m, (A).part_l, (A).part_acc, (A).g_q, (A).g_k, (A).rope_cos, (A).rope_sin, (A).hd, (A).G,   \
+        (A).n_q, (A).n_kv, (A).nsplit, (A).tiles_per_split, (A).fused, (A).qk_norm, (A).v_unit_norm,        \
+        (A).qscale, (A).cap2, (A).eps, (A).tap_post
+#define LQ_ATTN_REBUILD                                                                                      \
+    AttnArgs a{p_q, p_kc, p_vc_w, p_kc_w, p_out, p_part_m, p_part_l, p_part_acc, p_g_q, p_g_k, p_rope_cos,   \
+               p_rope_sin, p_head_stride, p_pos_stride, p_start, p_len, p_hd, p_G, p_n_q, p_n_kv, p_nsplit,   \
+               p_tiles_per_split, p_fused, p_qk_norm, p_v_unit_norm, p_qscale, p_cap2, p_eps, p_tap_post}
+
 }  // namespace
 
 // The prologue's head vectors, by one wave each: RMSNorm over the head
@@ -319,7 +340,8 @@ __device__ __forceinline__ int4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // Inexact shapes run the same loops over CM and GM: rows shorter than CM
 // chunks load zeros past their end and query heads past G are zero.
 template <typename KV, int CM, int GM, int NP, int TILE, bool EX, int WPE, int NW>
-__global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(LQ_ATTN_PARAMS) {
+    LQ_ATTN_REBUILD;
     constexpr int NT = NW * 64;
     constexpr int CE = KvTraits<KV>::CE;
     constexpr int HDM = CM * CE;                  // largest head_dim
@@ -766,7 +788,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void k_attn_split(AttnArgs a) {
 // sum of the wave's split j while every lane's partial-vector loads are
 // already in flight; the wave forms its weights exp2(m_s - M_w), sums its
 // splits, and wave 0 merges the four waves in a fixed order.
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_combine(const float* p_part_m, const float* p_part_l,
+                                                      const float* p_part_acc, float* p_out, int p_hd, int p_G,
+                                                      int p_nsplit) {
+    struct {
+        const float *part_m, *part_l, *part_acc;
+        float* out;
+        int hd, G, nsplit;
+    } const a{p_part_m, p_part_l, p_part_acc, p_out, p_hd, p_G, p_nsplit};
     constexpr int kBatch = 16;
     __shared__ float wts[kWavesPerWG][kWave];
     __shared__ float gm[kWavesPerWG], gl[kWavesPerWG], gacc[kWavesPerWG][kWave];
@@ -862,7 +891,7 @@ struct Variant {
 
 template <typename KV, int CM, int GM, int NP, int TILE, int WPE = 2, bool EX = true, int NW = 4>
 void launch_split(dim3 grid, hipStream_t s, const AttnArgs& a, LaunchMarks* mk) {
-    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE, EX, WPE, NW>, grid, dim3(NW * 64), 0, s, a);
+    launch_marked(mk, k_attn_split<KV, CM, GM, NP, TILE, EX, WPE, NW>, grid, dim3(NW * 64), 0, s, LQ_ATTN_FIELDS(a));
 }
 
 // Exact shapes of the common models: {dtype, chunks per row, G, positions per
@@ -988,7 +1017,8 @@ static lq_status launch_common(AttnArgs& a, int64_t n_q, int64_t n_kv, int64_t h
     lq_status st = check_launch("attention split");
     if (st != LQ_OK || p.nsplit == 1) return st;
     launch_marked(marks, k_attn_combine, dim3((unsigned)((hd + kWave - 1) / kWave), (unsigned)n_q), dim3(256), 0,
-                  s, a);
+                  s, (const float*)a.part_m, (const float*)a.part_l, (const float*)a.part_acc, a.out, a.hd, a.G,
+                  a.nsplit);
     return check_launch("attention combine");
 }
 
