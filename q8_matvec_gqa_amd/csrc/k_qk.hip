@@ -175,7 +175,14 @@ template <int FMT, int ST, int RPW, int PRO, int NT> struct QkOcc {
 };
 
 template <int FMT, int ST, int RPW, int PRO, int EPI>
-__global__ __launch_bounds__(qk_waves<EPI>() * 64, 2) void k_qk_mv(QkArgs a) {
+// Arguments one by one, the ones the first loads need leading, so the
+// compiler preloads them into SGPRs at dispatch.
+__global__ __launch_bounds__(qk_waves<EPI>() * 64, 2) void k_qk_mv(
+    const float* p_x, const float* p_gamma, const int8_t* p_xq, const uint16_t* p_xd, const uint8_t* p_q0,
+    const uint8_t* p_q1, const int8_t* p_sc, const uint16_t* p_d, int p_rows, int p_cols, float p_eps,
+    const float* p_res, float* p_y, int8_t* p_yq, uint16_t* p_yd, int8_t* p_tap_q, uint16_t* p_tap_d, int p_act) {
+    const QkArgs a{QkMat{p_q0, p_q1, p_sc, p_d}, p_rows, p_cols, p_xq, p_xd, p_x, p_gamma, p_eps, p_res, p_y, p_yq,
+                   p_yd, p_tap_q, p_tap_d, p_act};
     static_assert(EPI != EPI_SWIGLU_Q8 || RPW == 2, "SwiGLU groups are (gate, up) row pairs");
     constexpr int kQkW = qk_waves<EPI>(), kQkNT = kQkW * 64;
     __shared__ __attribute__((aligned(16))) int8_t xl[kQkMaxCols];
@@ -359,7 +366,8 @@ void launch_qk(const QkArgs& a, hipStream_t s, LaunchMarks* mk) {
         grid = (groups + kQkWaves * iters - 1) / (kQkWaves * iters);
     }
     if (grid < 1) grid = 1;
-    launch_marked(mk, kern, dim3((unsigned)grid), dim3(kQkNT), 0, s, a);
+    launch_marked(mk, kern, dim3((unsigned)grid), dim3(kQkNT), 0, s, a.x, a.gamma, a.xq, a.xd, a.m.q0, a.m.q1, a.m.sc,
+                  a.m.d, a.rows, a.cols, a.eps, a.res, a.y, a.yq, a.yd, a.tap_q, a.tap_d, a.act);
 }
 
 // steps per row: units / 64 rounded up (Q4_0 up to 8, Q6_K up to 4); two
